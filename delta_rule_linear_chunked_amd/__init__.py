@@ -1,0 +1,19 @@
+"""Chunked prefill of delta-rule linear attention (GDN, KDA) on MI355X.
+
+Python binding of the C ABI in ``include/drla.h`` (``libdrla.so``): argument
+marshalling only.  PyTorch provides device memory and the current stream;
+every step of the computation runs in the library's HIP kernels.  If the
+library is not built the calls raise; there is no other code path.
+"""
+from ._lib import (  # noqa: F401
+    DrlaError,
+    gdn_prefill,
+    kda_prefill,
+    lib_path,
+    load_library,
+    workspace_bytes,
+    workspace_layout,
+)
+
+__all__ = ["gdn_prefill", "kda_prefill", "workspace_bytes", "workspace_layout",
+           "load_library", "lib_path", "DrlaError"]

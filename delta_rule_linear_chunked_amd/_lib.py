@@ -1,0 +1,209 @@
+"""ctypes binding of libdrla.so.  Names and argument order follow
+include/drla.h; this module only converts torch tensors to pointers and
+sizes, allocates outputs and the workspace with torch, and passes torch's
+current HIP stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "_build", "libdrla.so")
+_lock = threading.Lock()
+_lib = None
+
+BF16, F32 = 0, 1
+STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported size or dtype",
+          4: "misaligned pointer", 5: "bad cu_seqlens", 6: "workspace too small",
+          7: "overlapping buffers", 8: "HIP error"}
+
+
+class DrlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"drla: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("h_qk", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in ("sched", "w", "kt", "u", "vp", "h", "gamma", "total")]
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load_library():
+    """Load libdrla.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            raise RuntimeError(
+                f"drla: {_LIB} is missing; build it with "
+                "`python -m delta_rule_linear_chunked_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(_LIB)
+        vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+        pp = ctypes.POINTER(Problem)
+        for name in ("gdn_prefill", "kda_prefill"):
+            f = getattr(lib, name)
+            f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp,
+                          ctypes.c_size_t, vp]
+            f.restype = ctypes.c_int
+        lib.drla_workspace_bytes.argtypes = [pp, i32p]
+        lib.drla_workspace_bytes.restype = ctypes.c_size_t
+        lib.drla_workspace_layout.argtypes = [pp, i32p, ctypes.POINTER(Layout)]
+        lib.drla_workspace_layout.restype = ctypes.c_int
+        lib.drla_status_str.argtypes = [ctypes.c_int]
+        lib.drla_status_str.restype = ctypes.c_char_p
+        lib.drla_last_error.argtypes = []
+        lib.drla_last_error.restype = ctypes.c_char_p
+        lib.drla_version.argtypes = []
+        lib.drla_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _host_cu(cu_seqlens, cu_seqlens_host):
+    if cu_seqlens is None:
+        return None
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu()  # synchronises; pass a host copy to avoid it
+    if isinstance(cu_seqlens_host, torch.Tensor):
+        arr = cu_seqlens_host.to(torch.int32).contiguous()
+    else:
+        arr = torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+    return arr
+
+
+def _problem(q, v, n_seqs, total):
+    if q.dtype != v.dtype:
+        raise ValueError("q, k and v must have the same dtype")
+    if q.dtype == torch.bfloat16:
+        io = BF16
+    elif q.dtype == torch.float32:
+        io = F32
+    else:
+        raise ValueError(f"q/k/v dtype must be bfloat16 or float32, got {q.dtype}")
+    return Problem(n_seqs, q.shape[-2], v.shape[-2], q.shape[-1], v.shape[-1], io, total)
+
+
+def _i32p(t):
+    if t is None:
+        return None
+    return ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+
+
+def workspace_bytes(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
+                    cu_seqlens_host: Optional[Sequence[int]] = None) -> int:
+    """Workspace size in bytes for packed q [T,h_qk,dk] and v [T,h_v,dv]."""
+    lib = load_library()
+    T = q_shape[0]
+    cu = None if cu_seqlens_host is None else torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+    if cu is not None:
+        n_seqs = len(cu) - 1
+    p = Problem(n_seqs, q_shape[1], v_shape[1], q_shape[2], v_shape[2],
+                BF16 if io_dtype == torch.bfloat16 else F32, T)
+    return int(lib.drla_workspace_bytes(ctypes.byref(p), _i32p(cu)))
+
+
+def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
+                     cu_seqlens_host: Optional[Sequence[int]] = None) -> dict:
+    lib = load_library()
+    cu = None if cu_seqlens_host is None else torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
+    if cu is not None:
+        n_seqs = len(cu) - 1
+    p = Problem(n_seqs, q_shape[1], v_shape[1], q_shape[2], v_shape[2],
+                BF16 if io_dtype == torch.bfloat16 else F32, q_shape[0])
+    out = Layout()
+    st = lib.drla_workspace_layout(ctypes.byref(p), _i32p(cu), ctypes.byref(out))
+    if st != 0:
+        raise DrlaError(st, lib.drla_last_error().decode())
+    return {n: getattr(out, n) for n, _ in Layout._fields_}
+
+
+def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
+             cu_seqlens_host=None, output_final_state=True, workspace=None,
+             out=None, final_state=None):
+    lib = load_library()
+    if q.dim() == 4:
+        # dense batch [B, T, H, d]: B equal-length sequences
+        if cu_seqlens is not None and q.shape[0] != 1:
+            raise ValueError("with cu_seqlens, pass packed [T, H, d] inputs (or batch 1)")
+        n_seqs = 1 if cu_seqlens is not None else q.shape[0]
+        q, k, v = (x.reshape(-1, x.shape[-2], x.shape[-1]) for x in (q, k, v))
+        beta = beta.reshape(-1, beta.shape[-1])
+        g = g.reshape(-1, *g.shape[2:])
+    elif q.dim() == 3:
+        n_seqs = 1
+    else:
+        raise ValueError("q must be [T, H, dk] or [B, T, H, dk]")
+    cu_host = _host_cu(cu_seqlens, cu_seqlens_host)
+    if cu_host is not None:
+        n_seqs = cu_host.numel() - 1
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+    T = q.shape[0]
+    for name, x in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g)):
+        if not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != q.shape or v.shape[0] != T:
+        raise ValueError("q, k must be [T, h_qk, dk] and v [T, h_v, dv]")
+    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("beta and g must be float32")
+    h_v, dk, dv = v.shape[1], q.shape[2], v.shape[2]
+    want_g = (T, h_v, dk) if kda else (T, h_v)
+    if tuple(beta.shape) != (T, h_v) or tuple(g.shape) != want_g:
+        raise ValueError(f"beta must be {(T, h_v)} and g {want_g}")
+    prob = _problem(q, v, n_seqs, T)
+    dev = q.device
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous() \
+                or tuple(initial_state.shape) != (n_seqs, h_v, dk, dv):
+            raise ValueError(f"initial_state must be contiguous float32 {(n_seqs, h_v, dk, dv)}")
+    o = out if out is not None else torch.empty((T, h_v, dv), dtype=q.dtype, device=dev)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else \
+            torch.empty((n_seqs, h_v, dk, dv), dtype=torch.float32, device=dev)
+    need = int(lib.drla_workspace_bytes(ctypes.byref(prob), _i32p(cu_host)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    fn = lib.kda_prefill if kda else lib.gdn_prefill
+    st = fn(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            beta.data_ptr(), g.data_ptr(),
+            None if initial_state is None else initial_state.data_ptr(),
+            None if cu_seqlens is None else cu_seqlens.data_ptr(),
+            _i32p(cu_host), o.data_ptr(), None if ht is None else ht.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), stream)
+    if st != 0:
+        raise DrlaError(st, lib.drla_last_error().decode())
+    return o, ht
+
+
+def gdn_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
+    """Gated DeltaNet chunked prefill.  q,k [T,h_qk,dk] (or [B,T,h_qk,dk]),
+    v [T,h_v,dv], beta [T,h_v] fp32, g [T,h_v] fp32 log-decay,
+    initial_state [N,h_v,dk,dv] fp32 or None, cu_seqlens int32 [N+1] device
+    tensor or None.  Returns (o [T,h_v,dv], final_state [N,h_v,dk,dv])."""
+    return _prefill(False, q, k, v, beta, g, initial_state, cu_seqlens, **kw)
+
+
+def kda_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
+    """Kimi Delta Attention chunked prefill; g is per key channel [T,h_v,dk]."""
+    return _prefill(True, q, k, v, beta, g, initial_state, cu_seqlens, **kw)

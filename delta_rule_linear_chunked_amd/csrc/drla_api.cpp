@@ -1,0 +1,232 @@
+// C ABI of drla: argument checks, chunk count and workspace layout, then
+// one call into the kernel launcher.  Every check runs before anything is
+// enqueued; on error nothing is launched or written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/drla.h"
+#include "drla_launch.h"
+
+static_assert(DRLA_CHUNK == DRLA_CHUNK_TOKENS, "chunk size mismatch");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+drla_status fail(drla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+drla_status fail(drla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Checks the problem description and host lengths; computes the chunk count.
+drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t* n_chunks) {
+  if (!p) return fail(DRLA_ERR_NULL, "problem is NULL");
+  if (p->n_seqs < 1) return fail(DRLA_ERR_SHAPE, "n_seqs must be >= 1 (got %d)", p->n_seqs);
+  if (p->h_qk < 1 || p->h_v < 1) return fail(DRLA_ERR_SHAPE, "head counts must be >= 1");
+  if (p->h_v % p->h_qk != 0)
+    return fail(DRLA_ERR_SHAPE, "h_v (%d) must be a multiple of h_qk (%d)", p->h_v, p->h_qk);
+  if (p->total_tokens < 0) return fail(DRLA_ERR_SHAPE, "total_tokens must be >= 0");
+  if (p->total_tokens > INT32_MAX) return fail(DRLA_ERR_SHAPE, "total_tokens must fit in int32");
+  if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
+    return fail(DRLA_ERR_UNSUPPORTED, "dk, dv must be 64 or 128 (got %d, %d)", p->dk, p->dv);
+  if (p->io_dtype != DRLA_BF16 && p->io_dtype != DRLA_F32)
+    return fail(DRLA_ERR_UNSUPPORTED, "unknown io dtype %d", p->io_dtype);
+  int64_t nc = 0;
+  if (cu_host) {
+    if (cu_host[0] != 0) return fail(DRLA_ERR_SEQLENS, "cu_seqlens[0] must be 0");
+    for (int s = 0; s < p->n_seqs; ++s) {
+      const int64_t L = (int64_t)cu_host[s + 1] - cu_host[s];
+      if (L < 0) return fail(DRLA_ERR_SEQLENS, "cu_seqlens decreases at %d", s);
+      nc += (L + DRLA_CHUNK - 1) / DRLA_CHUNK;
+    }
+    if (cu_host[p->n_seqs] != p->total_tokens)
+      return fail(DRLA_ERR_SEQLENS, "cu_seqlens[N] = %d != total_tokens %lld", cu_host[p->n_seqs],
+                  (long long)p->total_tokens);
+  } else {
+    if (p->total_tokens % p->n_seqs != 0)
+      return fail(DRLA_ERR_SHAPE, "dense batch: total_tokens %% n_seqs != 0");
+    const int64_t L = p->total_tokens / p->n_seqs;
+    nc = (int64_t)p->n_seqs * ((L + DRLA_CHUNK - 1) / DRLA_CHUNK);
+  }
+  if (nc * p->h_v > INT32_MAX) return fail(DRLA_ERR_SHAPE, "too many (chunk, head) pairs");
+  if ((int64_t)p->n_seqs * p->h_v * (p->dv / 16) > INT32_MAX) return fail(DRLA_ERR_SHAPE, "too many sequences");
+  *n_chunks = nc;
+  return DRLA_OK;
+}
+
+void layout_of(const drla_problem* p, int64_t nc, bool varlen, drla_layout* L) {
+  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t ncH = (size_t)nc * p->h_v;
+  size_t off = 0;
+  L->n_chunks = nc;
+  L->sched = off;
+  off = align_up(off + (varlen ? (2 * (size_t)nc + p->n_seqs + 1) * 4 : 0));
+  L->w = off;
+  off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  L->kt = off;
+  off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  L->u = off;
+  off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
+  L->vp = off;
+  off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
+  L->h = off;
+  off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
+  L->gamma = off;
+  off = align_up(off + ncH * p->dk * 4);
+  L->total = off;
+}
+
+drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, const void* v,
+                const float* beta, const float* g, const float* h0, const int32_t* cu_dev,
+                const int32_t* cu_host, void* o, float* ht, void* ws, size_t ws_bytes, void* stream) {
+  int64_t nc = 0;
+  if (!p) return fail(DRLA_ERR_NULL, "problem is NULL");
+  if ((cu_dev == nullptr) != (cu_host == nullptr))
+    return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
+  drla_status st = check_problem(p, cu_host, &nc);
+  if (st != DRLA_OK) return st;
+  const int64_t T = p->total_tokens;
+  if (T > 0 && (!q || !k || !v || !beta || !g || !o))
+    return fail(DRLA_ERR_NULL, "q, k, v, beta, g and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, beta, g, h0, cu_dev, o, ht, ws};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  drla_layout L;
+  layout_of(p, nc, cu_dev != nullptr, &L);
+  if (L.total > 0 && (!ws || ws_bytes < L.total))
+    return fail(DRLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : 0);
+  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t nq = (size_t)T * p->h_qk * p->dk * es, nv = (size_t)T * p->h_v * p->dv * es;
+  const size_t nb = (size_t)T * p->h_v * 4, ng = kda ? nb * p->dk : nb;
+  const size_t ns = (size_t)p->n_seqs * p->h_v * p->dk * p->dv * 4;
+  const size_t ncu = (size_t)(p->n_seqs + 1) * 4;
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {beta, nb}, {g, ng}, {h0, ns}, {cu_dev, ncu}};
+  const Buf outs[] = {{o, nv}, {ht, ns}, {ws, L.total}};
+  for (int i = 0; i < 3; ++i) {
+    for (const Buf& b : ins) {
+      if (i == 1 && b.p == h0 && ht == h0) continue;  // in-place state update
+      if (overlap(outs[i].p, outs[i].n, b.p, b.n))
+        return fail(DRLA_ERR_ALIAS, "an output buffer overlaps an input buffer");
+    }
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(DRLA_ERR_ALIAS, "output buffers overlap");
+  }
+
+  drla_launch_args a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.cu_dev = cu_dev;
+  a.o = o;
+  a.ht = ht;
+  a.workspace = ws;
+  a.off_sched = L.sched;
+  a.off_w = L.w;
+  a.off_kt = L.kt;
+  a.off_u = L.u;
+  a.off_vp = L.vp;
+  a.off_h = L.h;
+  a.off_gamma = L.gamma;
+  a.total_tokens = T;
+  a.n_chunks = nc;
+  a.n_seqs = p->n_seqs;
+  a.h_qk = p->h_qk;
+  a.h_v = p->h_v;
+  a.dk = p->dk;
+  a.dv = p->dv;
+  a.kda = kda ? 1 : 0;
+  a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
+  a.stream = stream;
+  const hipError_t e = drla_launch(&a);
+  if (e != hipSuccess) return fail(DRLA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return DRLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_host) {
+  int64_t nc = 0;
+  if (check_problem(p, cu_seqlens_host, &nc) != DRLA_OK) return 0;
+  drla_layout L;
+  layout_of(p, nc, cu_seqlens_host != nullptr, &L);
+  return L.total;
+}
+
+drla_status drla_workspace_layout(const drla_problem* p, const int32_t* cu_seqlens_host, drla_layout* out) {
+  int64_t nc = 0;
+  if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
+  drla_status st = check_problem(p, cu_seqlens_host, &nc);
+  if (st != DRLA_OK) return st;
+  layout_of(p, nc, cu_seqlens_host != nullptr, out);
+  return DRLA_OK;
+}
+
+drla_status gdn_prefill(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
+                        const float* g, const float* h0, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return run(false, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+             workspace_bytes, stream);
+}
+
+drla_status kda_prefill(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
+                        const float* g, const float* h0, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return run(true, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+             workspace_bytes, stream);
+}
+
+const char* drla_status_str(drla_status s) {
+  switch (s) {
+    case DRLA_OK: return "ok";
+    case DRLA_ERR_NULL: return "null pointer";
+    case DRLA_ERR_SHAPE: return "bad shape";
+    case DRLA_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case DRLA_ERR_ALIGN: return "misaligned pointer";
+    case DRLA_ERR_SEQLENS: return "bad cu_seqlens";
+    case DRLA_ERR_WORKSPACE: return "workspace too small";
+    case DRLA_ERR_ALIAS: return "overlapping buffers";
+    case DRLA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* drla_last_error(void) { return g_last_error.c_str(); }
+
+int drla_version(void) { return 1; }
+
+}  // extern "C"

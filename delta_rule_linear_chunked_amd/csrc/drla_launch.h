@@ -1,0 +1,32 @@
+// Internal interface between the C ABI layer (drla_api.cpp) and the kernels
+// (drla_kernels.hip).  Not part of the public ABI.
+#ifndef DRLA_LAUNCH_H
+#define DRLA_LAUNCH_H
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define DRLA_CHUNK_TOKENS 64
+
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const float* h0;
+  const int32_t* cu_dev;  // NULL for a dense batch
+  void* o;
+  float* ht;
+  void* workspace;
+  size_t off_sched, off_w, off_kt, off_u, off_vp, off_h, off_gamma;
+  int64_t total_tokens;
+  int64_t n_chunks;
+  int32_t n_seqs, h_qk, h_v, dk, dv;
+  int32_t kda, f32;
+  void* stream;
+} drla_launch_args;
+
+hipError_t drla_launch(const drla_launch_args* a);
+
+#endif

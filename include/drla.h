@@ -1,0 +1,141 @@
+/*
+ * drla -- chunked prefill of delta-rule linear attention on MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no framework types.  Device pointers are
+ * HIP device memory; host pointers are ordinary host memory.
+ *
+ * What is computed.  For every sequence and value head, the token-by-token
+ * gated delta rule that "Empowering Hybrid Attention Models on NPUs"
+ * describes in Section 2.1 (the state S_{t-1} is updated with K_t and V_t,
+ * then the output is read from the updated state S_t with Q_t), with the
+ * state stored key-major, S in R^{dk x dv}:
+ *
+ *   GDN (scalar gate per token and head, Section 1 and Section 2.1):
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *   KDA (per-channel gate, Section 1; its cumulative gate is per key
+ *        channel, Section 7.5):
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *   both: o_t = S_t^T q_t
+ *
+ * evaluated chunkwise (64 tokens) in the Map-Reduce-Map form of Section 2.1:
+ * a chunk-parallel prep kernel (operators #1-#4: Gate, KKT, Solve, W/U), a
+ * sequential state scan (operator #5: H) and a chunk-parallel output kernel
+ * (operator #6: O).  Results equal the recurrence up to rounding.
+ *
+ * Layouts (row-major, token-major, sequences packed back to back):
+ *   q, k        [T, h_qk, dk]    io dtype
+ *   v           [T, h_v,  dv]    io dtype
+ *   beta        [T, h_v]         fp32, used as given (typically in (0,1))
+ *   g           GDN: [T, h_v]; KDA: [T, h_v, dk]   fp32 log-decay (<= 0)
+ *   h0, ht      [N, h_v, dk, dv] fp32 (key-major state per sequence, head)
+ *   o           [T, h_v, dv]     io dtype
+ *   cu_seqlens  [N+1] int32, cu[0] = 0, non-decreasing, cu[N] = T.
+ * v-head h reads q/k head h / (h_v / h_qk) (contiguous groups).  Without
+ * cu_seqlens the T tokens are N equal-length sequences (a dense batch).
+ * Chunks start at every sequence start; a sequence's last chunk may be short.
+ *
+ * Ownership.  The caller owns every buffer, including the workspace (size
+ * from drla_workspace_bytes).  The library allocates no device memory, keeps
+ * no state between calls except the thread-local last-error text, and never
+ * synchronises: a call enqueues its kernels on `stream` (a hipStream_t; NULL
+ * = the default stream) and returns.  The workspace must not be used by
+ * another call until this call's kernels have finished on `stream`.
+ *
+ * Errors.  Every argument check happens before anything is enqueued; on an
+ * error nothing is launched and nothing is written.  A launch failure returns
+ * DRLA_ERR_HIP.  drla_last_error() gives a message for the last failing call
+ * on this host thread.  Device faults surface at the caller's next
+ * synchronisation, as for any kernel.
+ */
+#ifndef DRLA_H
+#define DRLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRLA_CHUNK 64
+
+typedef enum {
+  DRLA_OK = 0,
+  DRLA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  DRLA_ERR_SHAPE = 2,       /* negative/zero sizes, h_v % h_qk != 0, T % N    */
+  DRLA_ERR_UNSUPPORTED = 3, /* dk or dv not in {64, 128}; unknown io dtype    */
+  DRLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned        */
+  DRLA_ERR_SEQLENS = 5,     /* cu_seqlens malformed, or only one of the pair  */
+  DRLA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required        */
+  DRLA_ERR_ALIAS = 7,       /* an output overlaps an input (ht == h0 allowed) */
+  DRLA_ERR_HIP = 8          /* a HIP launch or runtime call failed            */
+} drla_status;
+
+typedef enum { DRLA_BF16 = 0, DRLA_F32 = 1 } drla_dtype;
+
+typedef struct {
+  int32_t n_seqs;       /* N >= 1                                          */
+  int32_t h_qk;         /* query/key heads                                  */
+  int32_t h_v;          /* value heads; multiple of h_qk                    */
+  int32_t dk;           /* key dim, 64 or 128                               */
+  int32_t dv;           /* value dim, 64 or 128                             */
+  int32_t io_dtype;     /* drla_dtype of q, k, v and o                      */
+  int64_t total_tokens; /* T >= 0                                           */
+} drla_problem;
+
+/* Workspace bytes a call on `p` needs.  `cu_seqlens_host` is the host copy
+ * of cu_seqlens (NULL for a dense batch).  Returns 0 if `p` or the lengths
+ * are invalid (the prefill call then reports why). */
+size_t drla_workspace_bytes(const drla_problem* p,
+                            const int32_t* cu_seqlens_host);
+
+/* Gated DeltaNet chunked prefill (scalar gate g [T, h_v]).
+ *   q, k, v, beta, g      device inputs, layouts above
+ *   h0                    device [N,h_v,dk,dv] fp32 initial state, or NULL (zeros)
+ *   cu_seqlens_dev/_host  the same [N+1] array on device and host, or both NULL
+ *   o                     device output [T,h_v,dv] in io dtype
+ *   ht                    device output [N,h_v,dk,dv] fp32 final state, or NULL;
+ *                         may be exactly h0 (in-place state update)
+ *   workspace, ws_bytes   device scratch of at least drla_workspace_bytes(p, cu_host)
+ *   stream                hipStream_t
+ * All device pointers must be 16-byte aligned. */
+drla_status gdn_prefill(const drla_problem* p, const void* q, const void* k,
+                        const void* v, const float* beta, const float* g,
+                        const float* h0, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, void* o, float* ht,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kimi Delta Attention chunked prefill: identical to gdn_prefill except that
+ * g is per key channel, [T, h_v, dk] fp32. */
+drla_status kda_prefill(const drla_problem* p, const void* q, const void* k,
+                        const void* v, const float* beta, const float* g,
+                        const float* h0, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, void* o, float* ht,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Byte offsets of the per-chunk intermediates inside the workspace after a
+ * call, for inspection by tests.  Each is stored per (v-head, chunk) in the
+ * MFMA fragment order the kernels use (documented in drla_kernels.hip):
+ *   w: W = T diag(beta e^b) K        (64 x dk)    kt: e^{b_n - b} (.) K (64 x dk)
+ *   u: U = T diag(beta) V            (64 x dv)    vp: V' = U - W S     (64 x dv)
+ *   h: S entering the chunk          (dk x dv)    gamma: e^{b_n} (1 or dk floats)
+ * Elements are io dtype except gamma (fp32, room for dk floats per
+ * (v-head, chunk); GDN uses one).  n_chunks is the total chunk count over
+ * all sequences.  The layout is the same for GDN and KDA.  Returns DRLA_OK
+ * or a validation error. */
+typedef struct {
+  int64_t n_chunks;
+  size_t sched, w, kt, u, vp, h, gamma, total;
+} drla_layout;
+drla_status drla_workspace_layout(const drla_problem* p,
+                                  const int32_t* cu_seqlens_host,
+                                  drla_layout* out);
+
+const char* drla_status_str(drla_status s);
+const char* drla_last_error(void);
+int drla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DRLA_H */

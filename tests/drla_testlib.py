@@ -1,0 +1,92 @@
+"""Shared helpers for the tests: tensors from the seeded generator, error
+metrics, and decoding of the workspace's fragment order.  No arithmetic of
+the method lives here."""
+import numpy as np
+
+# Max-norm relative error bounds per io dtype, for o and the final state.
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def rel_err(x, y):
+    """max|x - y| / max|y| (y = oracle)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.abs(y).max() if y.size else 0.0
+    if den == 0.0:
+        return float(np.abs(x).max()) if x.size else 0.0
+    return float(np.abs(x - y).max() / den)
+
+
+def nmse(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    d = float((y * y).sum())
+    return float(((x - y) ** 2).sum() / d) if d > 0 else float((x * x).sum())
+
+
+def to_device(x, device="cuda"):
+    """Generator output (numpy) -> device tensors in the io dtype."""
+    import torch
+    io = torch.bfloat16 if x["io"] == "bf16" else torch.float32
+    d = {}
+    for name in ("q", "k", "v"):
+        d[name] = torch.from_numpy(np.ascontiguousarray(x[name])).to(device=device, dtype=io)
+    for name in ("beta", "g"):
+        d[name] = torch.from_numpy(np.ascontiguousarray(x[name])).to(device=device)
+    d["h0"] = None if x["h0"] is None else torch.from_numpy(x["h0"]).to(device=device)
+    if x["varlen"]:
+        d["cu"] = torch.from_numpy(x["cu_seqlens"]).to(device=device)
+        d["cu_host"] = [int(c) for c in x["cu_seqlens"]]
+    else:
+        d["cu"] = None
+        d["cu_host"] = None
+    return d
+
+
+def run_oracle(x, heads=None, threads=None):
+    """fp64 oracle on the same (bf16-rounded) inputs; optionally only the
+    listed v-heads (returns arrays for those heads only)."""
+    import oracle
+    q, k, v, beta, g, h0 = x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"]
+    if heads is not None:
+        grp = x["h_v"] // x["h_qk"]
+        hk = [h // grp for h in heads]
+        q, k = q[:, hk], k[:, hk]
+        v, beta, g = v[:, heads], beta[:, heads], g[:, heads]
+        h0 = None if h0 is None else h0[:, heads]
+    cu = x["cu_seqlens"] if x["varlen"] else None
+    return oracle.recurrence(q, k, v, beta, g, h0, cu, kda=x["kind"] == "kda",
+                             threads=threads)
+
+
+def kmap(g, j):
+    return 4 * g + j if j < 4 else 16 + 4 * g + (j - 4)
+
+
+def _slot_index():
+    """(lane, j) -> (outer offset 0..15, inner offset 0..31) of an operand block."""
+    outer = np.zeros((64, 8), dtype=np.int64)
+    inner = np.zeros((64, 8), dtype=np.int64)
+    for lane in range(64):
+        for j in range(8):
+            outer[lane, j] = lane % 16
+            inner[lane, j] = kmap(lane // 16, j)
+    return outer, inner
+
+
+def decode_blocks(raw, n_outer, n_inner, order):
+    """Decode one (v-head, chunk) region stored as operand blocks.
+
+    raw      flat array of n_outer*n_inner elements
+    order    "outer_major": block index = tile*(n_inner/32) + p
+    returns  dense [n_outer, n_inner] (outer index, inner index)
+    """
+    assert order == "outer_major"
+    to, ti = _slot_index()
+    nb_in = n_inner // 32
+    dense = np.zeros((n_outer, n_inner), dtype=np.float64)
+    blocks = np.asarray(raw, dtype=np.float64).reshape(-1, 64, 8)
+    for b in range(blocks.shape[0]):
+        tile, p = divmod(b, nb_in)
+        dense[16 * tile + to, 32 * p + ti] = blocks[b]
+    return dense

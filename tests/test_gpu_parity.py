@@ -1,0 +1,253 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bar: max|x - y| / max|y| <= 2e-2 for bf16 inputs and <= 1e-4 for fp32
+inputs, on o and on the final state, x = GPU, y = oracle on the same
+(bf16-rounded) inputs."""
+import numpy as np
+import pytest
+
+import workloads as W
+from drla_testlib import TOL, decode_blocks, nmse, rel_err, run_oracle, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def drla():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import delta_rule_linear_chunked_amd as m
+    m.load_library()
+    return m
+
+
+def _call(drla, x, d, **kw):
+    fn = drla.kda_prefill if x["kind"] == "kda" else drla.gdn_prefill
+    o, ht = fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
+               cu_seqlens_host=d["cu_host"], **kw)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def _check(tag, x, o, ht, o_ref, ht_ref):
+    tol = TOL[x["io"]]
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"{tag}: rel_err o={eo:.3e} ht={eh:.3e} nmse o={nmse(o, o_ref):.2e} "
+          f"ht={nmse(ht, ht_ref):.2e} (tol {tol:g})", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    assert eo <= tol, f"{tag}: o error {eo}"
+    assert eh <= tol, f"{tag}: final-state error {eh}"
+
+
+def _case(kind, io, dk, dv, lens=(200,), h_qk=2, h_v=2, h0_std=0.05, seed=11,
+          g_lo=None, g_hi=None):
+    if g_lo is None:
+        g_lo, g_hi = (0.01, 0.2) if kind == "gdn" else (0.005, 0.15)
+    s = W.small_spec(kind, lens=lens, h_qk=h_qk, h_v=h_v, dk=dk, dv=dv, io=io,
+                     g_lo=g_lo, g_hi=g_hi, h0_std=h0_std, seed=seed)
+    return W.make_inputs(s)
+
+
+# ---- small shapes: several tiles and a ragged tail -------------------------
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_small_shapes(drla, kind, io, dk, dv):
+    print(f"case kind={kind} io={io} dk={dk} dv={dv} T=200", flush=True)
+    x = _case(kind, io, dk, dv)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"{kind}/{io}/{dk}x{dv}", x, _np(o), _np(ht), o_ref, ht_ref)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_varlen_grouped_ragged(drla, kind, io):
+    """Packed sequences of lengths 1, 63, 64, 65, 130, 0, 7 with grouped heads
+    (4 v-heads share 2 q/k heads)."""
+    print(f"case varlen kind={kind} io={io}", flush=True)
+    x = _case(kind, io, 128, 128, lens=(1, 63, 64, 65, 130, 0, 7), h_qk=2, h_v=4)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"varlen {kind}/{io}", x, _np(o), _np(ht), o_ref, ht_ref)
+    # the zero-length sequence returns its initial state unchanged
+    np.testing.assert_array_equal(_np(ht)[5], x["h0"][5])
+
+
+def test_dense_batch_equals_packed(drla):
+    """A [B, T, H, d] dense batch is B sequences of T tokens."""
+    x = _case("gdn", "bf16", 128, 128, lens=(96, 96, 96), h_qk=2, h_v=2, h0_std=0.02)
+    d = to_device(x)
+    o1, h1 = _call(drla, x, d)
+    B = 3
+    o2, h2 = drla.gdn_prefill(d["q"].view(B, 96, 2, 128), d["k"].view(B, 96, 2, 128),
+                              d["v"].view(B, 96, 2, 128), d["beta"].view(B, 96, 2),
+                              d["g"].view(B, 96, 2), d["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(-1), o2.reshape(-1)) and torch.equal(h1, h2)
+
+
+# ---- edge cases ------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_empty_input_returns_initial_state(drla, kind):
+    x = _case(kind, "bf16", 128, 128, lens=(0,))
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    assert o.shape[0] == 0
+    np.testing.assert_array_equal(_np(ht), x["h0"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 64, 65])
+def test_short_sequences(drla, T):
+    x = _case("kda", "f32", 64, 64, lens=(T,))
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"T={T}", x, _np(o), _np(ht), o_ref, ht_ref)
+
+
+def test_in_place_state_update(drla):
+    """ht may be the same buffer as h0."""
+    x = _case("gdn", "bf16", 128, 128, lens=(150,))
+    d = to_device(x)
+    o_ref, ht_ref = run_oracle(x)
+    h = d["h0"].clone()
+    o, ht = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], h,
+                             final_state=h)
+    torch.cuda.synchronize()
+    assert ht.data_ptr() == h.data_ptr()
+    _check("in-place", x, _np(o), _np(h), o_ref, ht_ref)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_beta_zero_pure_decay(drla, kind):
+    x = _case(kind, "f32", 128, 64, lens=(130,), h0_std=0.3)
+    x["beta"][:] = 0.0
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"beta0 {kind}", x, _np(o), _np(ht), o_ref, ht_ref)
+
+
+def test_deterministic_and_guard_bands(drla):
+    """Bitwise identical across runs; nothing written outside o and ht."""
+    x = _case("kda", "bf16", 128, 128, lens=(77, 190), h_qk=1, h_v=2)
+    d = to_device(x)
+    T, H, dv = x["v"].shape
+    pad = 4096
+    obuf = torch.full((T * H * dv + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    hbuf = torch.full((2 * H * 128 * 128 + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+    o_view = obuf[pad:pad + T * H * dv].view(T, H, dv)
+    h_view = hbuf[pad:pad + 2 * H * 128 * 128].view(2, H, 128, 128)
+    runs = []
+    for _ in range(3):
+        o, ht = drla.kda_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
+                                 cu_seqlens_host=d["cu_host"], out=o_view, final_state=h_view)
+        torch.cuda.synchronize()
+        runs.append((o.clone(), ht.clone()))
+    for o, ht in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(ht, runs[0][1])
+    assert torch.isnan(obuf[:pad]).all() and torch.isnan(obuf[-pad:]).all()
+    assert torch.isnan(hbuf[:pad]).all() and torch.isnan(hbuf[-pad:]).all()
+    o_ref, ht_ref = run_oracle(x)
+    _check("guard", x, _np(runs[0][0]), _np(runs[0][1]), o_ref, ht_ref)
+
+
+# ---- per-kernel intermediates against the chunkwise oracle ---------------
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
+def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
+    """W, K~, U (prep), V', h (scan) and gamma against the fp64 chunkwise
+    form's intermediates on the same inputs, for every chunk (odd and even)."""
+    import oracle
+    print(f"case intermediates kind={kind} io={io} dk={dk} dv={dv}", flush=True)
+    x = _case(kind, io, dk, dv, lens=(250,), h_qk=1, h_v=2, h0_std=0.1)
+    d = to_device(x)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    lay = drla.workspace_layout(x["q"].shape, x["v"].shape, dt)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    fn = drla.kda_prefill if kind == "kda" else drla.gdn_prefill
+    fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], workspace=ws)
+    torch.cuda.synchronize()
+    _, _, inter = oracle.chunked(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"],
+                                 kda=kind == "kda", intermediates=True)
+    nc = lay["n_chunks"]
+    es = 4 if io == "f32" else 2
+    wse = ws.view(dt).float().cpu().numpy()
+    wsg = ws.view(torch.float32).cpu().numpy()
+
+    def region(off, per, h, c):
+        base = off // es + (h * nc + c) * per
+        return wse[base:base + per]
+    worst = {}
+    for h in range(2):
+        for c in range(nc):
+            it = inter[h][c]
+            n = it["W"].shape[0]
+            W_ = decode_blocks(region(lay["w"], 64 * dk, h, c), 64, dk, "outer_major")[:n]
+            Kt = decode_blocks(region(lay["kt"], 64 * dk, h, c), dk, 64, "outer_major").T[:n]
+            U_ = decode_blocks(region(lay["u"], 64 * dv, h, c), dv, 64, "outer_major").T[:n]
+            Vp = decode_blocks(region(lay["vp"], 64 * dv, h, c), dv, 64, "outer_major").T[:n]
+            Hc = decode_blocks(region(lay["h"], dk * dv, h, c), dv, dk, "outer_major").T
+            for name, got, want in (("W", W_, it["W"]), ("K~", Kt, it["Kt"]), ("U", U_, it["U"]),
+                                    ("V'", Vp, it["Vp"]), ("h", Hc, it["h"])):
+                worst[name] = max(worst.get(name, 0.0), rel_err(got, want))
+            # KDA: dk floats per (head, chunk); GDN: one float at index h*nc + c
+            per = dk if kind == "kda" else 1
+            gb = lay["gamma"] // 4 + (h * nc + c) * per
+            gam = wsg[gb:gb + per]
+            worst["gamma"] = max(worst.get("gamma", 0.0), rel_err(gam, np.atleast_1d(it["gamma"])))
+    print(kind, io, dk, dv, {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+    tol = TOL[io]
+    for name, e in worst.items():
+        assert e <= tol, f"{name}: {e}"
+
+
+# ---- the five named workloads ----------------------------------------------
+
+def _workload(drla, name, heads=None):
+    spec = W.WORKLOADS[name]
+    print(f"workload {name}: lens={spec.lens[:8]} h_qk={spec.h_qk} h_v={spec.h_v} "
+          f"d={spec.dk} io={spec.io} heads={heads}", flush=True)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o, ht = _np(o), _np(ht)
+    del d
+    o_ref, ht_ref = run_oracle(x, heads=heads)
+    if heads is not None:
+        o, ht = o[:, heads], ht[:, heads]
+    _check(name, x, o, ht, o_ref, ht_ref)
+
+
+def test_workload_gdn_tiny(drla):
+    _workload(drla, "gdn_tiny")
+
+
+def test_workload_gdn_prefill(drla):
+    _workload(drla, "gdn_prefill")
+
+
+def test_workload_kda_prefill(drla):
+    _workload(drla, "kda_prefill")
+
+
+def test_workload_gdn_varlen(drla):
+    _workload(drla, "gdn_varlen")
+
+
+def test_workload_gdn_long_sampled_heads(drla):
+    """65,536 tokens x 32 heads on the GPU; the oracle recomputes three heads
+    (first, middle, last) over the whole sequence."""
+    _workload(drla, "gdn_long", heads=[0, 17, 31])

@@ -1,0 +1,120 @@
+"""CPU tests of the C ABI library: it loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU (the validation
+path makes no HIP call, so it runs without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "drla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from delta_rule_linear_chunked_amd import _lib
+    if not os.path.exists(_lib.lib_path()):
+        from delta_rule_linear_chunked_amd import build
+        build.build()
+    return _lib.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert {"gdn_prefill", "kda_prefill", "drla_workspace_bytes", "drla_workspace_layout",
+            "drla_status_str", "drla_last_error", "drla_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.drla_version() == 1
+
+
+def _prob(n_seqs=1, h_qk=2, h_v=4, dk=128, dv=128, io=0, T=256):
+    from delta_rule_linear_chunked_amd._lib import Problem
+    return Problem(n_seqs, h_qk, h_v, dk, dv, io, T)
+
+
+def _call(lib, p, q=16, ws=16, cu_dev=None, cu_host=None, h0=None, ht=None, o=1 << 20,
+          kda=False, ws_bytes=1 << 40):
+    # Fake, aligned, non-overlapping "device" addresses: validation only
+    # compares and checks them; it never dereferences them.
+    base = 1 << 40
+    args = [ctypes.byref(p), base + q * 0 + 0x1000000 if q else None, base + 0x2000000,
+            base + 0x3000000, base + 0x4000000, base + 0x5000000, h0, cu_dev,
+            cu_host, base + o + 0x6000000 if o else None, ht,
+            base + 0x70000000 if ws else None, ws_bytes, None]
+    fn = lib.kda_prefill if kda else lib.gdn_prefill
+    return fn(*args)
+
+
+def _i32(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), arr
+
+
+def test_validation_errors(lib):
+    assert lib.gdn_prefill(None, None, None, None, None, None, None, None, None, None,
+                           None, None, 0, None) == 1
+    assert _call(lib, _prob(h_v=3)) == 2               # h_v % h_qk
+    assert _call(lib, _prob(dk=96)) == 3               # unsupported dk
+    assert _call(lib, _prob(io=7)) == 3                # unknown dtype
+    assert _call(lib, _prob(n_seqs=3, T=256)) == 2     # T % N for a dense batch
+    assert _call(lib, _prob(), q=0) == 1               # null q
+    assert _call(lib, _prob(), ws=0) == 6              # no workspace
+    assert _call(lib, _prob(), ws_bytes=10) == 6       # workspace too small
+    # misaligned pointer
+    p = _prob()
+    assert lib.gdn_prefill(ctypes.byref(p), (1 << 40) + 2, 1 << 41, 1 << 42, 1 << 43,
+                           1 << 44, None, None, None, 1 << 45, None, 1 << 46, 1 << 40, None) == 4
+    # output overlapping an input
+    assert lib.gdn_prefill(ctypes.byref(p), 1 << 40, 1 << 41, 1 << 42, 1 << 43,
+                           1 << 44, None, None, None, 1 << 40, None, 1 << 46, 1 << 40, None) == 7
+    msg = lib.drla_last_error().decode()
+    assert "overlap" in msg
+
+
+def test_cu_seqlens_validation(lib):
+    p = _prob(n_seqs=3, T=100)
+    dev = ctypes.cast(ctypes.c_void_p(1 << 47), ctypes.POINTER(ctypes.c_int32))
+    good, _g = _i32([0, 30, 30, 100])
+    assert _call(lib, p, cu_dev=dev, cu_host=None) == 5          # only one of the pair
+    bad0, _b0 = _i32([1, 30, 40, 100])
+    assert _call(lib, p, cu_dev=dev, cu_host=bad0) == 5
+    dec, _d = _i32([0, 40, 30, 100])
+    assert _call(lib, p, cu_dev=dev, cu_host=dec) == 5
+    end, _e = _i32([0, 30, 40, 99])
+    assert _call(lib, p, cu_dev=dev, cu_host=end) == 5
+    # the valid one gets past validation and fails only for the workspace size
+    assert _call(lib, p, cu_dev=dev, cu_host=good, ws_bytes=1) == 6
+
+
+def test_workspace_bytes_and_layout(lib):
+    from delta_rule_linear_chunked_amd._lib import Layout
+    p = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=0, T=4096)
+    n = lib.drla_workspace_bytes(ctypes.byref(p), None)
+    lay = Layout()
+    assert lib.drla_workspace_layout(ctypes.byref(p), None, ctypes.byref(lay)) == 0
+    assert lay.total == n and lay.n_chunks == 64
+    per = 64 * 16
+    # W, K~, U, V' are 64 x 128 bf16 and h is 128 x 128 bf16 per (head, chunk)
+    assert lay.kt - lay.w == per * 64 * 128 * 2
+    assert lay.h - lay.vp == per * 64 * 128 * 2
+    assert lay.gamma - lay.h == per * 128 * 128 * 2
+    cu, _c = _i32([0, 1, 65, 65, 200])
+    p2 = _prob(n_seqs=4, T=200)
+    lay2 = Layout()
+    assert lib.drla_workspace_layout(ctypes.byref(p2), cu, ctypes.byref(lay2)) == 0
+    assert lay2.n_chunks == 1 + 1 + 0 + 3
+    assert lib.drla_workspace_bytes(ctypes.byref(_prob(dk=80)), None) == 0
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.drla_status_str(s)
