@@ -1,0 +1,262 @@
+"""Throughput of chunked delta-rule prefill on one MI355X.
+
+One step = one full prefill call (prep, scan and output kernels) over the
+workload's inputs, already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline]
+
+Workloads (seeded, synthetic): gdn_prefill (default: 1 x 4096 tokens,
+16 heads, dk = dv = 128, bf16), kda_prefill, gdn_varlen, gdn_long, gdn_tiny.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN/KDA chunked-prefill tokens/s at H16 d128 T4096; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
+CHUNK = 64
+
+
+def kernel_costs(spec, n_tokens, n_seqs):
+    """Algorithmic bytes and flops per launch of each kernel (what the kernel
+    must read and write given the three-kernel split, and the MFMA work it
+    must do counting full 64-token chunk tiles), for this workload."""
+    es = 2 if spec.io == "bf16" else 4
+    dk, dv, hv, hqk = spec.dk, spec.dv, spec.h_v, spec.h_qk
+    kda = spec.kind == "kda"
+    th = n_tokens * hv                         # token-heads (v-heads)
+    tq = n_tokens * hqk                        # token-heads (q/k heads)
+    n_chunks = sum((L + CHUNK - 1) // CHUNK for L in spec_lens(spec))
+    ch = n_chunks * hv                         # (chunk, v-head) units
+    g_bytes = (dk if kda else 1) * 4
+    gam = (dk if kda else 1) * 4
+    state = n_seqs * hv * dk * dv * 4
+    prep_b = tq * dk * es + th * dv * es + th * 4 + th * g_bytes \
+        + th * (2 * dk + dv) * es + ch * gam
+    scan_b = th * (2 * dk + dv) * es + ch * gam + th * dv * es + ch * dk * dv * es \
+        + (state if spec.h0_std > 0 else 0) + state
+    out_b = 2 * tq * dk * es + th * dv * es + ch * dk * dv * es + th * g_bytes + th * dv * es
+    C = CHUNK
+    prep_f = ch * 2 * (C * C * dk + C * C * dk + C * C * dv)
+    scan_f = ch * 2 * (2 * C * dk * dv)
+    out_f = ch * 2 * (C * C * dk + C * dk * dv + C * C * dv)
+    return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f), "output": (out_b, out_f)}
+
+
+def spec_lens(spec):
+    return spec.lens
+
+
+class Hip:
+    """Raw HIP events through libamdhip64 (the library records them on the
+    stream its kernels run on)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per dispatch from committed rocprofv3 counter summaries
+    (profiles/<kernel>_<workload>_traffic.json), or None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        return d.get("hbm_bytes_per_dispatch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(x, spec, n_tokens, budget_s=10.0):
+    """The fp64 oracle on this host's cores over the whole workload,
+    repeated until about `budget_s` of wall time."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    units = spec.n_seqs * spec.h_v
+    used = min(cores, units)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.recurrence(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"],
+                          x["cu_seqlens"] if x["varlen"] else None,
+                          kda=spec.kind == "kda", threads=cores)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps == 1 and t_total > budget_s:
+            break
+    return {"value": round(n_tokens * reps / t_total, 1), "unit": "tokens/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"whole {spec.name} workload ({n_tokens} tokens x {spec.h_v} heads), "
+                      f"fp64 token recurrence, {reps} run(s) in {t_total:.1f} s, "
+                      f"threads over {units} (sequence, head) units on {cores} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gdn_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the prefill kernels "
+              "shard by (sequence, head) with no collective, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import delta_rule_linear_chunked_amd as drla
+    import workloads as W
+
+    spec = W.WORKLOADS[args.workload]
+    x = W.make_inputs(spec)
+    n_tokens = int(x["cu_seqlens"][-1])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    io = torch.bfloat16 if spec.io == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev, io) for n in ("q", "k", "v"))
+    beta = torch.from_numpy(x["beta"]).to(dev)
+    g = torch.from_numpy(x["g"]).to(dev)
+    h0 = None if x["h0"] is None else torch.from_numpy(x["h0"]).to(dev)
+    cu = torch.from_numpy(x["cu_seqlens"]).to(dev) if x["varlen"] else None
+    cu_host = [int(c) for c in x["cu_seqlens"]] if x["varlen"] else None
+    n_seqs = spec.n_seqs
+    o = torch.empty((n_tokens, spec.h_v, spec.dv), dtype=io, device=dev)
+    ht = torch.empty((n_seqs, spec.h_v, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(drla.workspace_bytes(x["q"].shape, x["v"].shape, io, n_seqs, cu_host), 1),
+                     dtype=torch.uint8, device=dev)
+    fn = drla.kda_prefill if spec.kind == "kda" else drla.gdn_prefill
+
+    def step(events=None):
+        fn(q, k, v, beta, g, h0, cu, cu_seqlens_host=cu_host, workspace=ws, out=o,
+           final_state=ht, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = Hip()
+    e0, e1 = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
+    for _ in range(args.steps):
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = hip.elapsed_ms(e0, e1)
+    ms_step = ms_total / args.steps
+
+    # per-kernel durations, live, with events at the stage boundaries
+    stage = {"prep": 0.0, "scan": 0.0, "output": 0.0}
+    evs = [hip.event() for _ in range(4)]
+    for _ in range(args.steps):
+        step(evs)
+        torch.cuda.synchronize()
+        stage["prep"] += hip.elapsed_ms(evs[0], evs[1])
+        stage["scan"] += hip.elapsed_ms(evs[1], evs[2])
+        stage["output"] += hip.elapsed_ms(evs[2], evs[3])
+    for key in stage:
+        stage[key] /= args.steps
+    for e in evs + [e0, e1]:
+        hip.destroy(e)
+
+    costs = kernel_costs(spec, n_tokens, n_seqs)
+    dom = max(stage, key=stage.get)
+    bytes_, flops = costs[dom]
+    t_s = stage[dom] * 1e-3
+    intensity = flops / bytes_
+    ridge = (BF16_PEAK_TFLOPS if spec.io == "bf16" else F32_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        ach = bytes_ / t_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops / t_s / 1e12
+        peak = BF16_PEAK_TFLOPS if spec.io == "bf16" else F32_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom, spec.name)
+    roof["kernel_ms"] = {kk: round(vv, 5) for kk, vv in stage.items()}
+    roof["algorithmic_bytes_per_launch"] = int(bytes_)
+    roof["algorithmic_flops_per_launch"] = int(flops)
+
+    total_bytes = sum(b for b, _ in costs.values())
+    total_flops = sum(f for _, f in costs.values())
+    # whole-call algorithmic I/O (q, k, v, beta, g, h0 in; o, ht out)
+    es = 2 if spec.io == "bf16" else 4
+    io_bytes = n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * 4
+                           + spec.h_v * (spec.dk if spec.kind == "kda" else 1) * 4) \
+        + (2 if spec.h0_std > 0 else 1) * n_seqs * spec.h_v * spec.dk * spec.dv * 4
+    line = {
+        "metric": METRIC,
+        "value": round(n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.io,
+        "data": "synthetic (seeded; q,k L2-normalised, v ~ N(0,1), beta = sigmoid(N(0,1)), "
+                "log-gates uniform)",
+        "config": {"workload": spec.name, "kind": spec.kind, "n_seqs": n_seqs,
+                   "total_tokens": n_tokens, "h_qk": spec.h_qk, "h_v": spec.h_v,
+                   "dk": spec.dk, "dv": spec.dv, "chunk": CHUNK, "io": spec.io},
+        "roofline": roof,
+        "path": {"algorithmic_io_bytes": int(io_bytes),
+                 "io_roofline_frac": round(io_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "kernel_bytes": int(total_bytes), "kernel_flops": int(total_flops),
+                 "mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                 "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, spec, n_tokens, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

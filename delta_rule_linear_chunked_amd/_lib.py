@@ -62,6 +62,10 @@ def load_library():
             f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp,
                           ctypes.c_size_t, vp]
             f.restype = ctypes.c_int
+        lib.drla_prefill_staged.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, vp,
+                                            i32p, vp, vp, vp, ctypes.c_size_t, vp,
+                                            ctypes.POINTER(ctypes.c_void_p)]
+        lib.drla_prefill_staged.restype = ctypes.c_int
         lib.drla_workspace_bytes.argtypes = [pp, i32p]
         lib.drla_workspace_bytes.restype = ctypes.c_size_t
         lib.drla_workspace_layout.argtypes = [pp, i32p, ctypes.POINTER(Layout)]
@@ -136,7 +140,7 @@ def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
 
 def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
              cu_seqlens_host=None, output_final_state=True, workspace=None,
-             out=None, final_state=None):
+             out=None, final_state=None, stage_events=None):
     lib = load_library()
     if q.dim() == 4:
         # dense batch [B, T, H, d]: B equal-length sequences
@@ -184,13 +188,18 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    fn = lib.kda_prefill if kda else lib.gdn_prefill
-    st = fn(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+    args = (ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
             beta.data_ptr(), g.data_ptr(),
             None if initial_state is None else initial_state.data_ptr(),
             None if cu_seqlens is None else cu_seqlens.data_ptr(),
             _i32p(cu_host), o.data_ptr(), None if ht is None else ht.data_ptr(),
             workspace.data_ptr(), workspace.numel(), stream)
+    if stage_events is not None:
+        evs = (ctypes.c_void_p * 4)(*stage_events)
+        st = lib.drla_prefill_staged(int(kda), *args, evs)
+    else:
+        fn = lib.kda_prefill if kda else lib.gdn_prefill
+        st = fn(*args)
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return o, ht

@@ -99,7 +99,8 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, drla_layout* L) {
 
 drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, const void* v,
                 const float* beta, const float* g, const float* h0, const int32_t* cu_dev,
-                const int32_t* cu_host, void* o, float* ht, void* ws, size_t ws_bytes, void* stream) {
+                const int32_t* cu_host, void* o, float* ht, void* ws, size_t ws_bytes, void* stream,
+                void* const* stage_events) {
   int64_t nc = 0;
   if (!p) return fail(DRLA_ERR_NULL, "problem is NULL");
   if ((cu_dev == nullptr) != (cu_host == nullptr))
@@ -167,6 +168,7 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
   a.kda = kda ? 1 : 0;
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
   a.stream = stream;
+  a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
   if (e != hipSuccess) return fail(DRLA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
@@ -199,7 +201,7 @@ drla_status gdn_prefill(const drla_problem* p, const void* q, const void* k, con
                         const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return run(false, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
-             workspace_bytes, stream);
+             workspace_bytes, stream, nullptr);
 }
 
 drla_status kda_prefill(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
@@ -207,7 +209,16 @@ drla_status kda_prefill(const drla_problem* p, const void* q, const void* k, con
                         const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return run(true, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
-             workspace_bytes, stream);
+             workspace_bytes, stream, nullptr);
+}
+
+drla_status drla_prefill_staged(int kda, const drla_problem* p, const void* q, const void* k, const void* v,
+                                const float* beta, const float* g, const float* h0,
+                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, void* o,
+                                float* ht, void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* stage_events) {
+  return run(kda != 0, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+             workspace_bytes, stream, stage_events);
 }
 
 const char* drla_status_str(drla_status s) {

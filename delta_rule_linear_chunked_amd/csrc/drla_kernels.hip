@@ -706,17 +706,26 @@ __global__ __launch_bounds__(256) void output_kernel(Params P) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool KDA, typename ET>
 static hipError_t launch_all(const Params& P, int n_seqs, const int32_t* cu_dev, int32_t* sched,
-                             hipStream_t st) {
+                             hipStream_t st, void* const* ev) {
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord((hipEvent_t)ev[i], st);
+  };
+  mark(0);
   if (P.s.chunk_seq && n_seqs > 0) {
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu_dev, n_seqs, P.nc, sched,
                        sched + P.nc, sched + 2 * P.nc);
   }
   const int64_t nblk = P.nc * P.h_v;
   if (nblk > 0) hipLaunchKernelGGL((prep_kernel<DK, DV, KDA, ET>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  mark(1);
   const int64_t nscan = (int64_t)n_seqs * P.h_v * (DV / 16);
   if (nscan > 0) hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET>), dim3((unsigned)nscan), dim3(64), 0, st, P);
+  mark(2);
   if (nblk > 0) hipLaunchKernelGGL((output_kernel<DK, DV, KDA, ET>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-  return hipGetLastError();
+  mark(3);
+  const hipError_t le = hipGetLastError();
+  return e != hipSuccess ? e : le;
 }
 
 }  // namespace drla
@@ -759,7 +768,7 @@ hipError_t drla_launch(const drla_launch_args* a) {
   const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (a->f32 ? 8 : 0);
 #define DRLA_CASE(K, DK_, DV_, KDA_, ET_) \
   case K:                                 \
-    return launch_all<DK_, DV_, KDA_, ET_>(P, a->n_seqs, a->cu_dev, sched, st);
+    return launch_all<DK_, DV_, KDA_, ET_>(P, a->n_seqs, a->cu_dev, sched, st, a->stage_events);
   switch (key) {
     DRLA_CASE(0, 64, 64, false, bf16)
     DRLA_CASE(1, 128, 64, false, bf16)

@@ -25,6 +25,7 @@ typedef struct {
   int32_t n_seqs, h_qk, h_v, dk, dv;
   int32_t kda, f32;
   void* stream;
+  void* const* stage_events;  // NULL, or 4 hipEvent_t recorded at stage boundaries
 } drla_launch_args;
 
 hipError_t drla_launch(const drla_launch_args* a);

@@ -113,6 +113,22 @@ drla_status kda_prefill(const drla_problem* p, const void* q, const void* k,
                         const int32_t* cu_seqlens_host, void* o, float* ht,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* gdn_prefill (kda == 0) or kda_prefill (kda != 0), additionally recording
+ * four caller-created hipEvent_t on `stream` (passed as void*): stage_events[0]
+ * before the first kernel, [1] after the prep kernel (operators #1-#4 of
+ * Section 2.1), [2] after the state scan (#5), [3] after the output kernel
+ * (#6), so that a benchmark can time each kernel on the stream it runs on.
+ * stage_events may be NULL (then identical to the plain call).  A failing
+ * event record returns DRLA_ERR_HIP. */
+drla_status drla_prefill_staged(int kda, const drla_problem* p, const void* q,
+                                const void* k, const void* v, const float* beta,
+                                const float* g, const float* h0,
+                                const int32_t* cu_seqlens_dev,
+                                const int32_t* cu_seqlens_host, void* o,
+                                float* ht, void* workspace,
+                                size_t workspace_bytes, void* stream,
+                                void* const* stage_events);
+
 /* Byte offsets of the per-chunk intermediates inside the workspace after a
  * call, for inspection by tests.  Each is stored per (v-head, chunk) in the
  * MFMA fragment order the kernels use (documented in drla_kernels.hip):
