@@ -6,6 +6,7 @@ every step of the computation runs in the library's HIP kernels.  If the
 library is not built the calls raise; there is no other code path.
 """
 from ._lib import (  # noqa: F401
+    KEEP_INTERMEDIATES,
     DrlaError,
     gdn_prefill,
     kda_prefill,
@@ -16,4 +17,4 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["gdn_prefill", "kda_prefill", "workspace_bytes", "workspace_layout",
-           "load_library", "lib_path", "DrlaError"]
+           "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES"]

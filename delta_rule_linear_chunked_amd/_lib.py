@@ -37,7 +37,11 @@ class Problem(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64)] + [
-        (n, ctypes.c_size_t) for n in ("sched", "w", "kt", "u", "vp", "h", "gamma", "total")]
+        (n, ctypes.c_size_t) for n in ("sched", "tb", "pm", "kt", "kw", "qw", "gam", "vp", "h",
+                                       "total")]
+
+
+KEEP_INTERMEDIATES = 1
 
 
 def lib_path() -> str:
@@ -62,13 +66,14 @@ def load_library():
             f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp,
                           ctypes.c_size_t, vp]
             f.restype = ctypes.c_int
-        lib.drla_prefill_staged.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, vp,
-                                            i32p, vp, vp, vp, ctypes.c_size_t, vp,
-                                            ctypes.POINTER(ctypes.c_void_p)]
-        lib.drla_prefill_staged.restype = ctypes.c_int
+        lib.drla_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp,
+                                        vp, i32p, vp, vp, vp, ctypes.c_size_t, vp,
+                                        ctypes.POINTER(ctypes.c_void_p)]
+        lib.drla_prefill_ex.restype = ctypes.c_int
         lib.drla_workspace_bytes.argtypes = [pp, i32p]
         lib.drla_workspace_bytes.restype = ctypes.c_size_t
-        lib.drla_workspace_layout.argtypes = [pp, i32p, ctypes.POINTER(Layout)]
+        lib.drla_workspace_layout.argtypes = [ctypes.c_int, pp, i32p, ctypes.c_int,
+                                              ctypes.POINTER(Layout)]
         lib.drla_workspace_layout.restype = ctypes.c_int
         lib.drla_status_str.argtypes = [ctypes.c_int]
         lib.drla_status_str.restype = ctypes.c_char_p
@@ -124,7 +129,10 @@ def workspace_bytes(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
 
 
 def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
-                     cu_seqlens_host: Optional[Sequence[int]] = None) -> dict:
+                     cu_seqlens_host: Optional[Sequence[int]] = None, kda: bool = False,
+                     flags: int = 0) -> dict:
+    """Workspace regions (byte offsets) of a drla_prefill_ex call with the
+    same gate kind, shapes, lengths and flags."""
     lib = load_library()
     cu = None if cu_seqlens_host is None else torch.tensor(list(cu_seqlens_host), dtype=torch.int32)
     if cu is not None:
@@ -132,7 +140,8 @@ def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
     p = Problem(n_seqs, q_shape[1], v_shape[1], q_shape[2], v_shape[2],
                 BF16 if io_dtype == torch.bfloat16 else F32, q_shape[0])
     out = Layout()
-    st = lib.drla_workspace_layout(ctypes.byref(p), _i32p(cu), ctypes.byref(out))
+    st = lib.drla_workspace_layout(int(kda), ctypes.byref(p), _i32p(cu), int(flags),
+                                   ctypes.byref(out))
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return {n: getattr(out, n) for n, _ in Layout._fields_}
@@ -140,7 +149,7 @@ def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
 
 def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
              cu_seqlens_host=None, output_final_state=True, workspace=None,
-             out=None, final_state=None, stage_events=None):
+             out=None, final_state=None, stage_events=None, flags=0):
     lib = load_library()
     if q.dim() == 4:
         # dense batch [B, T, H, d]: B equal-length sequences
@@ -184,7 +193,15 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
     if output_final_state:
         ht = final_state if final_state is not None else \
             torch.empty((n_seqs, h_v, dk, dv), dtype=torch.float32, device=dev)
-    need = int(lib.drla_workspace_bytes(ctypes.byref(prob), _i32p(cu_host)))
+    if flags:
+        lay = Layout()
+        st = lib.drla_workspace_layout(int(kda), ctypes.byref(prob), _i32p(cu_host), int(flags),
+                                       ctypes.byref(lay))
+        if st != 0:
+            raise DrlaError(st, lib.drla_last_error().decode())
+        need = int(lay.total)
+    else:
+        need = int(lib.drla_workspace_bytes(ctypes.byref(prob), _i32p(cu_host)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -194,9 +211,9 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
             None if cu_seqlens is None else cu_seqlens.data_ptr(),
             _i32p(cu_host), o.data_ptr(), None if ht is None else ht.data_ptr(),
             workspace.data_ptr(), workspace.numel(), stream)
-    if stage_events is not None:
-        evs = (ctypes.c_void_p * 4)(*stage_events)
-        st = lib.drla_prefill_staged(int(kda), *args, evs)
+    if stage_events is not None or flags:
+        evs = None if stage_events is None else (ctypes.c_void_p * 3)(*stage_events)
+        st = lib.drla_prefill_ex(int(kda), int(flags), *args, evs)
     else:
         fn = lib.kda_prefill if kda else lib.gdn_prefill
         st = fn(*args)

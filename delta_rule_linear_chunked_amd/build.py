@@ -6,6 +6,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -29,14 +30,15 @@ def hipcc() -> str:
 
 
 def sources():
-    return [os.path.join(CSRC, f) for f in ("drla_kernels.hip", "drla_api.cpp")]
+    return [os.path.join(CSRC, f) for f in
+            ("drla_prep.hip", "drla_scan.hip", "drla_launch.hip", "drla_api.cpp")]
 
 
 def build(verbose: bool = False, extra=()) -> str:
     """Compile every source and link libdrla.so.  Always recompiles."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
+    cmds, objs = [], []
     for src in sources():
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         cmd = [cc, *HIPFLAGS, *extra, "-c", src, "-o", obj]
@@ -44,8 +46,12 @@ def build(verbose: bool = False, extra=()) -> str:
             cmd = [cc, "-x", "hip", *HIPFLAGS, *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        cmds.append(cmd)
         objs.append(obj)
+    # one compiler process per source, in parallel
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        for f in [ex.submit(subprocess.check_call, c) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:

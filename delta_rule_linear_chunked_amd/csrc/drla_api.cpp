@@ -75,29 +75,35 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
   return DRLA_OK;
 }
 
-void layout_of(const drla_problem* p, int64_t nc, bool varlen, drla_layout* L) {
+void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int flags, drla_layout* L) {
   const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
   const size_t ncH = (size_t)nc * p->h_v;
+  const size_t frag = 64 * 8 * es;  // one operand fragment
+  const bool keep = (flags & DRLA_KEEP_INTERMEDIATES) != 0;
   size_t off = 0;
   L->n_chunks = nc;
   L->sched = off;
   off = align_up(off + (varlen ? (2 * (size_t)nc + p->n_seqs + 1) * 4 : 0));
-  L->w = off;
-  off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  L->tb = off;
+  off = align_up(off + ncH * 8 * frag);
+  L->pm = off;
+  off = align_up(off + ncH * 8 * frag);
   L->kt = off;
   off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
-  L->u = off;
-  off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
-  L->vp = off;
-  off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
-  L->h = off;
-  off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
-  L->gamma = off;
-  off = align_up(off + ncH * p->dk * 4);
+  L->kw = kda ? off : 0;
+  if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  L->qw = kda ? off : 0;
+  if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  L->gam = kda ? off : 0;
+  if (kda) off = align_up(off + ncH * p->dk * 4);
+  L->vp = keep ? off : 0;
+  if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
+  L->h = keep ? off : 0;
+  if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
   L->total = off;
 }
 
-drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, const void* v,
+drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const void* k, const void* v,
                 const float* beta, const float* g, const float* h0, const int32_t* cu_dev,
                 const int32_t* cu_host, void* o, float* ht, void* ws, size_t ws_bytes, void* stream,
                 void* const* stage_events) {
@@ -107,6 +113,7 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
     return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
   drla_status st = check_problem(p, cu_host, &nc);
   if (st != DRLA_OK) return st;
+  if (flags & ~DRLA_KEEP_INTERMEDIATES) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   const int64_t T = p->total_tokens;
   if (T > 0 && (!q || !k || !v || !beta || !g || !o))
     return fail(DRLA_ERR_NULL, "q, k, v, beta, g and o must be non-NULL");
@@ -114,7 +121,7 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
   drla_layout L;
-  layout_of(p, nc, cu_dev != nullptr, &L);
+  layout_of(p, nc, cu_dev != nullptr, kda, flags, &L);
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(DRLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : 0);
   const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
@@ -152,12 +159,14 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
   a.ht = ht;
   a.workspace = ws;
   a.off_sched = L.sched;
-  a.off_w = L.w;
+  a.off_tb = L.tb;
+  a.off_pm = L.pm;
   a.off_kt = L.kt;
-  a.off_u = L.u;
+  a.off_kw = L.kw;
+  a.off_qw = L.qw;
+  a.off_gam = L.gam;
   a.off_vp = L.vp;
   a.off_h = L.h;
-  a.off_gamma = L.gamma;
   a.total_tokens = T;
   a.n_chunks = nc;
   a.n_seqs = p->n_seqs;
@@ -167,6 +176,7 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
   a.dv = p->dv;
   a.kda = kda ? 1 : 0;
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
+  a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
@@ -180,19 +190,22 @@ drla_status run(bool kda, const drla_problem* p, const void* q, const void* k, c
 extern "C" {
 
 size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_host) {
+  // The KDA layout is the larger one; GDN calls use a prefix of it.
   int64_t nc = 0;
   if (check_problem(p, cu_seqlens_host, &nc) != DRLA_OK) return 0;
   drla_layout L;
-  layout_of(p, nc, cu_seqlens_host != nullptr, &L);
+  layout_of(p, nc, cu_seqlens_host != nullptr, true, 0, &L);
   return L.total;
 }
 
-drla_status drla_workspace_layout(const drla_problem* p, const int32_t* cu_seqlens_host, drla_layout* out) {
+drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t* cu_seqlens_host, int flags,
+                                  drla_layout* out) {
   int64_t nc = 0;
   if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
   drla_status st = check_problem(p, cu_seqlens_host, &nc);
   if (st != DRLA_OK) return st;
-  layout_of(p, nc, cu_seqlens_host != nullptr, out);
+  if (flags & ~DRLA_KEEP_INTERMEDIATES) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  layout_of(p, nc, cu_seqlens_host != nullptr, kda != 0, flags, out);
   return DRLA_OK;
 }
 
@@ -200,7 +213,7 @@ drla_status gdn_prefill(const drla_problem* p, const void* q, const void* k, con
                         const float* g, const float* h0, const int32_t* cu_seqlens_dev,
                         const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return run(false, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+  return run(false, 0, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
              workspace_bytes, stream, nullptr);
 }
 
@@ -208,16 +221,16 @@ drla_status kda_prefill(const drla_problem* p, const void* q, const void* k, con
                         const float* g, const float* h0, const int32_t* cu_seqlens_dev,
                         const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return run(true, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+  return run(true, 0, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
              workspace_bytes, stream, nullptr);
 }
 
-drla_status drla_prefill_staged(int kda, const drla_problem* p, const void* q, const void* k, const void* v,
-                                const float* beta, const float* g, const float* h0,
-                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, void* o,
-                                float* ht, void* workspace, size_t workspace_bytes, void* stream,
-                                void* const* stage_events) {
-  return run(kda != 0, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
+drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const void* q, const void* k,
+                            const void* v, const float* beta, const float* g, const float* h0,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, void* o,
+                            float* ht, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* stage_events) {
+  return run(kda != 0, flags, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
              workspace_bytes, stream, stage_events);
 }
 
@@ -238,6 +251,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 1; }
+int drla_version(void) { return 2; }
 
 }  // extern "C"

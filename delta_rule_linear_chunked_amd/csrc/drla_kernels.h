@@ -1,0 +1,56 @@
+// Kernel parameter blocks and per-variant launchers (internal).
+#ifndef DRLA_KERNELS_H
+#define DRLA_KERNELS_H
+
+#include "drla_common.h"
+
+namespace drla {
+
+struct PrepParams {
+  const void* q;
+  const void* k;
+  const float* beta;
+  const float* g;
+  void* tb;    // Tb = T diag(beta): 8 fragments per (head, chunk)
+  void* pm;    // P: 8 fragments per (head, chunk)
+  void* kt;    // K~^T: dk/8 fragments per (head, chunk)
+  void* kw;    // KDA: K e^{B}, dk/8 fragments
+  void* qw;    // KDA: Q e^{B}, dk/8 fragments
+  float* gam;  // KDA: e^{b_n}, dk floats
+  Sched s;
+  int32_t h_qk, h_v, grp;
+  int64_t nc;
+};
+
+struct ScanParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* h0;
+  void* o;
+  float* ht;
+  const void* tb;
+  const void* pm;
+  const void* kt;
+  const void* kw;
+  const void* qw;
+  const float* gam;
+  void* insp_vp;  // optional: V' per (head, chunk), fragments (dv tile, token block)
+  void* insp_h;   // optional: state entering each chunk, fragments (dv tile, dk block)
+  Sched s;
+  int32_t h_qk, h_v, grp;
+  int64_t nc;
+};
+
+hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st);
+
+template <int DK, bool KDA, typename ET>
+hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st);
+
+template <int DK, int DV, bool KDA, typename ET>
+hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
+
+}  // namespace drla
+
+#endif

@@ -1,5 +1,5 @@
-// Internal interface between the C ABI layer (drla_api.cpp) and the kernels
-// (drla_kernels.hip).  Not part of the public ABI.
+// Internal interface between the C ABI layer (drla_api.cpp) and the kernel
+// launcher (drla_launch.hip).  Not part of the public ABI.
 #ifndef DRLA_LAUNCH_H
 #define DRLA_LAUNCH_H
 #include <hip/hip_runtime.h>
@@ -19,13 +19,14 @@ typedef struct {
   void* o;
   float* ht;
   void* workspace;
-  size_t off_sched, off_w, off_kt, off_u, off_vp, off_h, off_gamma;
+  // byte offsets into the workspace; vp/h only used when inspect != 0
+  size_t off_sched, off_tb, off_pm, off_kt, off_kw, off_qw, off_gam, off_vp, off_h;
   int64_t total_tokens;
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;
-  int32_t kda, f32;
+  int32_t kda, f32, inspect;
   void* stream;
-  void* const* stage_events;  // NULL, or 4 hipEvent_t recorded at stage boundaries
+  void* const* stage_events;  // NULL, or 3 hipEvent_t recorded at kernel boundaries
 } drla_launch_args;
 
 hipError_t drla_launch(const drla_launch_args* a);

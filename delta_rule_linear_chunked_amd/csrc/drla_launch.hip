@@ -1,0 +1,111 @@
+// Kernel launcher: picks the (dk, dv, gate, dtype) variant and enqueues
+// schedule (packed input only) -> prep -> scan on the caller's stream.
+#include "drla_common.h"
+#include "drla_kernels.h"
+
+namespace drla {
+
+template <int DK, int DV, bool KDA, typename ET>
+static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
+  hipStream_t st = (hipStream_t)a->stream;
+  void* const* ev = a->stage_events;
+  char* ws = (char*)a->workspace;
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord((hipEvent_t)ev[i], st);
+  };
+  const int grp = a->h_v / a->h_qk;
+  const int64_t nc = a->n_chunks;
+
+  PrepParams pp = {};
+  pp.q = a->q;
+  pp.k = a->k;
+  pp.beta = a->beta;
+  pp.g = a->g;
+  pp.tb = ws + a->off_tb;
+  pp.pm = ws + a->off_pm;
+  pp.kt = ws + a->off_kt;
+  pp.kw = KDA ? ws + a->off_kw : nullptr;
+  pp.qw = KDA ? ws + a->off_qw : nullptr;
+  pp.gam = KDA ? (float*)(ws + a->off_gam) : nullptr;
+  pp.s = s;
+  pp.h_qk = a->h_qk;
+  pp.h_v = a->h_v;
+  pp.grp = grp;
+  pp.nc = nc;
+
+  ScanParams sp = {};
+  sp.q = a->q;
+  sp.k = a->k;
+  sp.v = a->v;
+  sp.g = a->g;
+  sp.h0 = a->h0;
+  sp.o = a->o;
+  sp.ht = a->ht;
+  sp.tb = pp.tb;
+  sp.pm = pp.pm;
+  sp.kt = pp.kt;
+  sp.kw = pp.kw;
+  sp.qw = pp.qw;
+  sp.gam = pp.gam;
+  sp.insp_vp = a->inspect ? ws + a->off_vp : nullptr;
+  sp.insp_h = a->inspect ? ws + a->off_h : nullptr;
+  sp.s = s;
+  sp.h_qk = a->h_qk;
+  sp.h_v = a->h_v;
+  sp.grp = grp;
+  sp.nc = nc;
+
+  mark(0);
+  if (e == hipSuccess && s.chunk_seq && a->n_seqs > 0)
+    e = launch_schedule(a->cu_dev, a->n_seqs, nc, (int32_t*)(ws + a->off_sched), st);
+  if (e == hipSuccess) e = launch_prep<DK, KDA, ET>(pp, nc * a->h_v, st);
+  mark(1);
+  if (e == hipSuccess)
+    e = launch_scan<DK, DV, KDA, ET>(sp, (int64_t)a->n_seqs * a->h_v * (DV / 16), a->inspect != 0, st);
+  mark(2);
+  return e;
+}
+
+}  // namespace drla
+
+hipError_t drla_launch(const drla_launch_args* a) {
+  using namespace drla;
+  Sched s = {};
+  int32_t* sched = (int32_t*)((char*)a->workspace + a->off_sched);
+  if (a->cu_dev) {
+    s.chunk_seq = sched;
+    s.chunk_start = sched + a->n_chunks;
+    s.seq_chunk0 = sched + 2 * a->n_chunks;
+    s.cu = a->cu_dev;
+  } else {
+    s.seq_len = a->n_seqs > 0 ? a->total_tokens / a->n_seqs : 0;
+    s.cps = (int32_t)((s.seq_len + C - 1) / C);
+  }
+  s.n_seqs = a->n_seqs;
+  const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (a->f32 ? 8 : 0);
+#define DRLA_CASE(K, DK_, DV_, KDA_, ET_) \
+  case K:                                 \
+    return launch_all<DK_, DV_, KDA_, ET_>(a, s);
+  switch (key) {
+    DRLA_CASE(0, 64, 64, false, bf16)
+    DRLA_CASE(1, 128, 64, false, bf16)
+    DRLA_CASE(2, 64, 128, false, bf16)
+    DRLA_CASE(3, 128, 128, false, bf16)
+    DRLA_CASE(4, 64, 64, true, bf16)
+    DRLA_CASE(5, 128, 64, true, bf16)
+    DRLA_CASE(6, 64, 128, true, bf16)
+    DRLA_CASE(7, 128, 128, true, bf16)
+    DRLA_CASE(8, 64, 64, false, float)
+    DRLA_CASE(9, 128, 64, false, float)
+    DRLA_CASE(10, 64, 128, false, float)
+    DRLA_CASE(11, 128, 128, false, float)
+    DRLA_CASE(12, 64, 64, true, float)
+    DRLA_CASE(13, 128, 64, true, float)
+    DRLA_CASE(14, 64, 128, true, float)
+    DRLA_CASE(15, 128, 128, true, float)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DRLA_CASE
+}

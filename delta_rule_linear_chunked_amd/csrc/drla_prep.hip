@@ -1,0 +1,393 @@
+// Chunk-parallel preparation for delta-rule chunked prefill (gfx950).
+//
+// "Empowering Hybrid Attention Models on NPUs", Section 2.1 splits chunked
+// prefill into chunk-independent Map operators (#1 Gate, #2 KKT, #3 Solve,
+// #4 W/U), a sequence-dependent Reduce (#5 H) and a chunk-independent output
+// Map (#6 O); Section 5 factors the inverse out of W ("operator rewriting")
+// so that the products with K, S and Q no longer wait for the inversion.
+// This kernel does the chunk-independent part once per (chunk, value head):
+//
+//   #1 Gate   b_r = sum_{i<=r} g_i in the chunk (per key channel for KDA)
+//   #2 KKT    A = strict_lower(diag(beta) (K K^T (.) D)),  D_ri = e^{b_r-b_i}
+//             (KDA: (K e^{B}) (K e^{-B})^T, the decay per key channel)
+//   #3 Solve  T = (I + A)^{-1}: 16x16 diagonal blocks by forward
+//             substitution, the rest by two rounds of blocked products
+//   #4 factor Tb = T diag(beta): W = Tb diag(e^b) K and U = Tb V are never
+//             formed; the scan applies Tb to V - diag(e^b) K S instead
+//             (Section 5's rewriting: V' = U - W S = Tb (V - diag(e^b) K S)).
+//
+// It also emits the chunk-local operands of the output Map, so that the
+// sequential kernel only multiplies:
+//   P   = lower_incl(Q K^T (.) D)                 (KDA: (Q e^{B})(K e^{-B})^T)
+//   K~^T with K~ = diag(e^{b_n - b}) K            (KDA: K (.) e^{b_n - B})
+//   KDA only: K e^{B}, Q e^{B} and gamma = e^{b_n} per key channel.
+// All are written in MFMA fragment order (drla_common.h).
+#include "drla_common.h"
+#include "drla_kernels.h"
+
+namespace drla {
+
+// Chunk table for packed input: one workgroup, prefix sum of the
+// per-sequence chunk counts.  Entries past `nc` are never written.
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_seqs, int64_t nc,
+                                                        int32_t* chunk_seq, int32_t* chunk_start,
+                                                        int32_t* seq_chunk0) {
+  __shared__ int32_t sc[256];
+  const int t = threadIdx.x;
+  int64_t carry = 0;
+  for (int base = 0; base < n_seqs; base += 256) {
+    const int s = base + t;
+    int cnt = 0;
+    int64_t st = 0;
+    if (s < n_seqs) {
+      st = cu[s];
+      const int64_t L = (int64_t)cu[s + 1] - st;
+      cnt = L > 0 ? (int)((L + C - 1) / C) : 0;
+    }
+    sc[t] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = t >= off ? sc[t - off] : 0;
+      __syncthreads();
+      sc[t] += add;
+      __syncthreads();
+    }
+    const int64_t excl = carry + sc[t] - cnt;
+    if (s < n_seqs) {
+      seq_chunk0[s] = (int32_t)excl;
+      for (int j = 0; j < cnt; ++j) {
+        const int64_t idx = excl + j;
+        if (idx < nc) {
+          chunk_seq[idx] = s;
+          chunk_start[idx] = (int32_t)(st + (int64_t)C * j);
+        }
+      }
+    }
+    carry += sc[255];
+    __syncthreads();
+  }
+  if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
+}
+
+// One workgroup (4 waves) per (chunk, value head).
+template <int DK, bool KDA, typename ET>
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
+  typedef typename VT<ET>::v8 V8;
+  typedef typename VT<ET>::v16b V16;
+  constexpr int PE = VT<ET>::per16;
+  constexpr int KB = DK / 32;
+  constexpr int KP = DK + 16 / (int)sizeof(ET);  // padded row: 16-byte aligned, 4-bank skew
+  constexpr int TP = C + 4;
+  constexpr int MID = C / 2 - 1;                      // KDA: reference row of the factored decay
+  __shared__ __attribute__((aligned(16))) ET Ks[C][KP];
+  __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
+  __shared__ __attribute__((aligned(16))) float Ts[C][TP];  // T
+  __shared__ __attribute__((aligned(16))) float Tt[C][TP];  // T transposed
+  __shared__ float bs[C];
+  __shared__ float betas[C];
+  __shared__ float Bs[KDA ? C : 1][KDA ? DK + 4 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int64_t bid = blockIdx.x;
+  const int h = (int)(bid / P.nc);
+  const int64_t c = bid - (int64_t)h * P.nc;
+  int seq, len;
+  int64_t t0;
+  chunk_of(P.s, c, seq, t0, len);
+  const int hk = h / P.grp;
+  const int64_t ch = (int64_t)h * P.nc + c;
+  const ET* kg = (const ET*)P.k;
+  const ET* qg = (const ET*)P.q;
+
+  // #1 Gate.  Tokens past the sequence end get beta = g = 0: they write
+  // nothing and do not decay.
+  if (tid < C) {
+    float be = 0.f, gg = 0.f;
+    if (tid < len) {
+      be = P.beta[(t0 + tid) * P.h_v + h];
+      if (!KDA) gg = P.g[(t0 + tid) * P.h_v + h];
+    }
+    betas[tid] = be;
+    if (!KDA) {
+      float x = gg;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      bs[tid] = x;
+    }
+  }
+  if (KDA) {
+    for (int d = tid; d < DK; d += 256) {
+      float run = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < C; ++r) {
+        run += r < len ? P.g[((t0 + r) * P.h_v + h) * DK + d] : 0.f;
+        Bs[r][d] = run;
+      }
+    }
+  }
+  // K rows of the chunk into LDS (zero rows past the end).
+  {
+    constexpr int KV = DK / PE;
+    for (int idx = tid; idx < C * KV; idx += 256) {
+      const int r = idx / KV, cv = idx - r * KV;
+      V16 x = {};
+      if (r < len) x = *(const V16*)(kg + ((t0 + r) * P.h_qk + hk) * DK + cv * PE);
+      *(V16*)&Ks[r][cv * PE] = x;
+    }
+  }
+  // Upper off-diagonal 16x16 blocks of T are zero.
+  for (int idx = tid; idx < 6 * 256; idx += 256) {
+    const int blk = idx >> 8, e = idx & 255;
+    const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+    const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+    const int r = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
+    Ts[r][j] = 0.f;
+    Tt[j][r] = 0.f;
+  }
+  __syncthreads();
+
+  // K row fragment of token tile t, inner block p.  KDA: scaled by
+  // e^{s (B - B_mid)} per element (s = +1 for the row side of a product,
+  // -1 for the column side); the reference row keeps the exponents small.
+  auto kfrag = [&](int t, int p, float s) -> V8 {
+    const int r = 16 * t + c16;
+    V8 x = row_slots<ET>(&Ks[r][32 * p], g4);
+    if (KDA) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 32 * p + kmap(g4, j);
+        x[j] = (ET)(to_f(x[j]) * __expf(s * (Bs[r][d] - Bs[MID][d])));
+      }
+    }
+    return x;
+  };
+
+  // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w), five
+  // 16x16 tiles per wave.
+  {
+    const int rt = wv;
+    V8 ar[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) ar[p] = kfrag(rt, p, 1.f);
+    for (int it = 0; it <= rt; ++it) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < KB; ++p) acc = mma(ar[p], kfrag(it, p, -1.f), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g4 + e, i = 16 * it + c16;
+        float a = 0.f;
+        if (i < r) {
+          a = betas[r] * acc[e];
+          if (!KDA) a *= __expf(bs[r] - bs[i]);
+        }
+        As[r][i] = a;
+      }
+    }
+    // P^T tiles (jt, pr) = K_jt Q_pr^T; tiles jt = 2p, 2p+1 form fragment
+    // (pr, p) of P (outer = query token, inner = key token).
+    const int pr = 3 - wv;
+    const int rq = 16 * pr + c16;
+    V8 qf[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      V8 x = {};
+      if (rq < len) x = row_slots<ET>(qg + ((t0 + rq) * P.h_qk + hk) * DK + 32 * p, g4);
+      if (KDA) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = 32 * p + kmap(g4, j);
+          x[j] = (ET)(to_f(x[j]) * __expf(Bs[rq][d] - Bs[MID][d]));
+        }
+      }
+      qf[p] = x;
+    }
+    floatx4 pt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      pt[jt] = zero4();
+      if (jt <= pr) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < KB; ++p) acc = mma(kfrag(jt, p, -1.f), qf[p], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g4 + e;
+          float x = 0.f;
+          if (j <= rq) x = KDA ? acc[e] : acc[e] * __expf(bs[rq] - bs[j]);
+          pt[jt][e] = x;
+        }
+      }
+    }
+    V8* pg = (V8*)P.pm + ch * (8 * 64);
+    pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(pt[0], pt[1]);
+    pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(pt[2], pt[3]);
+  }
+  __syncthreads();
+
+  if (wv == 0) {
+    // #3 Solve, level 0: the four 16x16 diagonal blocks of T by forward
+    // substitution, one column per lane (block lane/16, column lane%16).
+    const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
+      t[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      Ts[o + r][o + cc] = t[r];
+      Tt[o + cc][o + r] = t[r];
+    }
+  } else {
+    // Meanwhile: K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16
+    // key channels of state tile mt in the scan's row order, inner = token
+    // block p), and the KDA operands.
+    constexpr int NF = (DK / 16) * 2;
+    V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
+    for (int f = wv - 1; f < NF; f += 3) {
+      const int mt = f >> 1, p = f & 1;
+      const int d = state_row(mt, c16);
+      V8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * p + kmap(g4, j);
+        const float sc = KDA ? __expf(Bs[C - 1][d] - Bs[i][d]) : __expf(bs[C - 1] - bs[i]);
+        x[j] = (ET)(to_f(Ks[i][d]) * sc);
+      }
+      ktg[f * 64 + lane] = x;
+    }
+    if (KDA) {
+      // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
+      // with contiguous key channels 32p + 8g + j, the scan's state order
+      V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
+      V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
+      for (int f = wv - 1; f < 4 * KB; f += 3) {
+        const int nt = f / KB, p = f - nt * KB;
+        const int r = 16 * nt + c16;
+        V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
+        V8 xq = {};
+        if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + hk) * DK + 32 * p + 8 * g4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
+          xk[j] = (ET)(to_f(xk[j]) * e);
+          xq[j] = (ET)(to_f(xq[j]) * e);
+        }
+        kwg[f * 64 + lane] = xk;
+        qwg[f * 64 + lane] = xq;
+      }
+      for (int d = tid - 64; d < DK; d += 192) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
+    }
+  }
+  __syncthreads();
+
+  // #3 Solve, level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
+  // (16-wide contractions, zero-padded to the 32-wide fragment).
+  if (wv < 2) {
+    const int b0 = 16 * (2 * wv), b1 = b0 + 16;
+    V8 a = {}, tb = {}, tl = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * g4 + j;
+      a[j] = (ET)As[b1 + c16][b0 + k];
+      tb[j] = (ET)Tt[b0 + c16][b0 + k];
+      tl[j] = (ET)Ts[b1 + c16][b1 + k];
+    }
+    const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
+    V8 yb = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
+    const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
+      Tt[b0 + c16][b1 + 4 * g4 + e] = -t[e];
+    }
+  }
+  __syncthreads();
+
+  // Level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
+  // and T2 are the finished 32x32 diagonal halves.
+  if (wv < 2) {
+    const int jt = wv;
+    floatx4 z[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r = 32 + 16 * m + c16;
+      V8 a, tb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = kmap(g4, j);
+        a[j] = (ET)As[r][k];
+        tb[j] = (ET)Tt[16 * jt + c16][k];
+      }
+      z[m] = mma(a, tb, zero4());
+    }
+    const V8 zb = pack<ET>(z[0], z[1]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r = 32 + 16 * m + c16;
+      V8 tl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
+      const floatx4 t = mma(tl, zb, zero4());
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
+        Tt[16 * jt + c16][32 + 16 * m + 4 * g4 + e] = -t[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
+  // block p), eight per (chunk, head); the ones above the diagonal are zero.
+  {
+    const int nt = wv;
+    V8* tg = (V8*)P.tb + ch * (8 * 64);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      V8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * p + kmap(g4, j);
+        x[j] = (ET)(Ts[16 * nt + c16][i] * betas[i]);
+      }
+      tg[(nt * 2 + p) * 64 + lane] = x;
+    }
+  }
+}
+
+template <int DK, bool KDA, typename ET>
+hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
+  if (nblk > 0) hipLaunchKernelGGL((prep_kernel<DK, KDA, ET>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu, n_seqs, nc, sched, sched + nc,
+                     sched + 2 * nc);
+  return hipGetLastError();
+}
+
+#define DRLA_PREP_INST(DK_, KDA_, ET_) \
+  template hipError_t launch_prep<DK_, KDA_, ET_>(const PrepParams&, int64_t, hipStream_t);
+DRLA_PREP_INST(64, false, bf16)
+DRLA_PREP_INST(128, false, bf16)
+DRLA_PREP_INST(64, true, bf16)
+DRLA_PREP_INST(128, true, bf16)
+DRLA_PREP_INST(64, false, float)
+DRLA_PREP_INST(128, false, float)
+DRLA_PREP_INST(64, true, float)
+DRLA_PREP_INST(128, true, float)
+#undef DRLA_PREP_INST
+
+}  // namespace drla

@@ -1,0 +1,312 @@
+// Sequential state scan fused with the output Map (gfx950).
+//
+// Operator #5 (H) of the Map-Reduce-Map split in "Empowering Hybrid
+// Attention Models on NPUs", Section 2.1, is the only sequence-dependent
+// step; operator #6 (O) needs only the state entering the chunk and the
+// intermediate v_c (Section 5).  Following Section 5's chunk-first order
+// (read the state, produce the output, then update the state in place), one
+// workgroup walks the chunks of one (sequence, value head, 16 state columns)
+// with the state in registers and produces the chunk's output on the way:
+//
+//   X   = diag(e^b) K S                    (KDA: (K e^{B}) S)
+//   V'  = Tb (V - X)                       (= U - W S of Section 5's rewriting)
+//   O   = diag(e^b) Q S + P V'             (KDA: (Q e^{B}) S + P V')
+//   S  <- e^{b_n} S + K~^T V'              (KDA: Diag(e^{b_n}) S + K~^T V')
+//
+// Tb, P and K~^T come from the prep kernel.  The state columns are
+// independent (the column split of Section 4, "Computation Splitting"), so
+// workgroups for different column blocks never communicate; the 16 columns
+// are the width of one MFMA tile.
+//
+// Inside the workgroup wave w owns token tile w (16 tokens) for X, V', O,
+// and rows [16 (dk/64) w, ...) of the state for its update.  Per chunk the
+// waves exchange the state (as bf16/fp32 fragments) and R = V - X through
+// LDS, with two barriers.
+#include "drla_common.h"
+#include "drla_kernels.h"
+
+namespace drla {
+
+// Operands of one chunk for wave w.  Every load is unconditional: the
+// chunk's rows of q, k, v and g are read through buffer resources limited to
+// its valid tokens, so rows past the end of a short chunk read as zero, and
+// no load sits behind a branch (a branch would make the compiler wait for
+// all outstanding loads, including the next chunk's).
+template <int DK, bool KDA, typename ET>
+struct ScanOps {
+  typedef typename VT<ET>::v4 V4;
+  typedef typename VT<ET>::v8 V8;
+  static constexpr int KB = DK / 32;
+  static constexpr int MT = DK / 64;  // state row tiles per wave
+  V8 kr[KB];       // K rows of token tile w, key channels 32p + 8g + j (KDA: K e^{B})
+  V8 qr[KB];       // Q rows, same order (KDA: Q e^{B})
+  V8 kt[MT][2];    // K~^T fragments of this wave's state rows
+  V8 tb[6];        // Tb fragments (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  V8 pb[2];        // P fragments (w, 0), (w, 1)
+  V4 vv;           // V at token 16w + c, columns 16 nb + 4g + e
+  floatx4 gm[MT];  // KDA: e^{b_n} of this lane's state rows
+  float gl;        // GDN: g of token `lane` (zero past the end)
+  rsrc_t orsrc;    // this chunk's rows of o
+};
+
+struct ScanCtx {
+  int64_t ts;    // first token of the sequence
+  int64_t te;    // one past its last token
+  int64_t c0;    // workspace index of its first chunk
+  int h, hk, nb, w, lane;
+};
+
+template <int DK, int DV, bool KDA, typename ET>
+__device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanParams& P, const ScanCtx& x,
+                                          int64_t i) {
+  typedef typename VT<ET>::v4 V4;
+  typedef typename VT<ET>::v8 V8;
+  constexpr int KB = DK / 32, MT = DK / 64, es = sizeof(ET);
+  const int lane = x.lane, w = x.w, g4 = lane >> 4, c16 = lane & 15;
+  const int64_t t0 = x.ts + (int64_t)C * i;
+  const int64_t left = x.te - t0;
+  const uint32_t len = (uint32_t)(left < C ? left : C);
+  const int64_t ch = (int64_t)x.h * P.nc + x.c0 + i;
+  const int rw = 16 * w + c16;  // this lane's token in the chunk
+  if (KDA) {
+    const V8* kw = (const V8*)P.kw + ch * (int64_t)(C * DK / 8);
+    const V8* qw = (const V8*)P.qw + ch * (int64_t)(C * DK / 8);
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      o.kr[p] = kw[(w * KB + p) * 64 + lane];
+      o.qr[p] = qw[(w * KB + p) * 64 + lane];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      o.gm[m] = *(const floatx4*)(P.gam + ch * DK + state_row(w * MT + m, 4 * g4));
+  } else {
+    const size_t qrow = (size_t)P.h_qk * DK;
+    const rsrc_t kr = make_rsrc((const ET*)P.k + t0 * qrow, len * qrow * es);
+    const rsrc_t qr = make_rsrc((const ET*)P.q + t0 * qrow, len * qrow * es);
+    const uint32_t off = (uint32_t)(((size_t)rw * P.h_qk + x.hk) * DK + 8 * g4) * es;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      o.kr[p] = bload<V8>(kr, off + 32 * p * es);
+      o.qr[p] = bload<V8>(qr, off + 32 * p * es);
+    }
+    const rsrc_t gr = make_rsrc(P.g + t0 * P.h_v, len * P.h_v * 4);
+    o.gl = bload<float>(gr, ((uint32_t)lane * P.h_v + x.h) * 4);
+  }
+  const V8* kt = (const V8*)P.kt + ch * (int64_t)(C * DK / 8);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) o.kt[m][p] = kt[((w * MT + m) * 2 + p) * 64 + lane];
+  const V8* tb = (const V8*)P.tb + ch * (8 * 64);
+  o.tb[0] = tb[0 * 64 + lane];
+  o.tb[1] = tb[2 * 64 + lane];
+  o.tb[2] = tb[4 * 64 + lane];
+  o.tb[3] = tb[5 * 64 + lane];
+  o.tb[4] = tb[6 * 64 + lane];
+  o.tb[5] = tb[7 * 64 + lane];
+  const V8* pm = (const V8*)P.pm + ch * (8 * 64);
+  o.pb[0] = pm[(2 * w) * 64 + lane];
+  o.pb[1] = pm[(2 * w + 1) * 64 + lane];  // zero for w < 2
+  const size_t vrow = (size_t)P.h_v * DV;
+  const rsrc_t vr = make_rsrc((const ET*)P.v + t0 * vrow, len * vrow * es);
+  o.vv = bload<V4>(vr, (uint32_t)(((size_t)rw * P.h_v + x.h) * DV + 16 * x.nb + 4 * g4) * es);
+  o.orsrc = make_rsrc((ET*)P.o + t0 * vrow, len * vrow * es);
+}
+
+template <int DK, int DV, bool KDA, typename ET, bool INSPECT>
+__global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
+  typedef typename VT<ET>::v4 V4;
+  typedef typename VT<ET>::v8 V8;
+  constexpr int KB = DK / 32, MT = DK / 64, NB = DV / 16, es = sizeof(ET);
+  __shared__ V8 Sf[KB][64];  // state entering the chunk, as fragments (inner = key channel)
+  __shared__ V8 Rf[2][64];   // R = V - X, as B fragments (inner = token)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  // Consecutive workgroups go to different XCDs; renumber so that the NB
+  // column blocks of one (sequence, head), which read the same K, Q and prep
+  // operands, run on one XCD and share its L2.
+  int b = blockIdx.x;
+  const int G = gridDim.x;
+  if (G % 8 == 0) b = (b % 8) * (G / 8) + b / 8;
+  const int unit = b / NB, nb = b - unit * NB;
+  const int seq = unit / P.h_v, h = unit - seq * P.h_v;
+
+  ScanCtx x;
+  x.h = h;
+  x.hk = h / P.grp;
+  x.nb = nb;
+  x.w = w;
+  x.lane = lane;
+  int64_t n;  // chunks of this sequence
+  if (P.s.chunk_seq) {
+    x.ts = P.s.cu[seq];
+    x.te = P.s.cu[seq + 1];
+    int64_t c1;
+    seq_chunks(P.s, seq, P.nc, x.c0, c1);
+    n = x.te > x.ts ? (x.te - x.ts + C - 1) / C : 0;
+    if (n > c1 - x.c0) n = c1 - x.c0;  // device lengths disagree with the table
+  } else {
+    x.ts = (int64_t)seq * P.s.seq_len;
+    x.te = x.ts + P.s.seq_len;
+    x.c0 = (int64_t)seq * P.s.cps;
+    n = P.s.cps;
+  }
+  const int col = 16 * nb + c16;
+  const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
+
+  // this wave's state rows: tiles w*MT + m, element e is key channel
+  // state_row(mt, 4g + e), column col
+  floatx4 S[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[m][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(w * MT + m, 4 * g4 + e) * DV + col] : 0.f;
+  auto put_state = [&]() {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mt = w * MT + m;
+      ((V4*)&Sf[mt >> 1][lane])[mt & 1] = pack4<ET>(S[m]);
+    }
+  };
+  put_state();
+
+  // R element (token 16w + c, column 4g + e) belongs to fragment w/2, lane
+  // 16 (c/4) + 4g + e, slot 4 (w%2) + c%4
+  ET* const rdst = (ET*)&Rf[w >> 1][16 * (c16 >> 2) + 4 * g4] + 4 * (w & 1) + (c16 & 3);
+  const uint32_t ooff = (uint32_t)(((size_t)(16 * w + c16) * P.h_v + h) * DV + 16 * nb + 4 * g4) * es;
+
+  auto step = [&](const ScanOps<DK, KDA, ET>& op, int64_t i) {
+    // GDN: b = in-chunk cumulative log-decay of token `lane`
+    float eb = 1.f, gam = 1.f;
+    if (!KDA) {
+      float y = op.gl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(y, off);
+        if (lane >= off) y += t;
+      }
+      gam = __expf(__shfl(y, 63));
+      eb = __expf(__shfl(y, 16 * w + c16));  // e^{b} of this lane's token
+    }
+    lds_barrier();  // the state entering this chunk is in Sf
+    V8 sf[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) sf[p] = Sf[p][lane];
+    if (INSPECT && w == 0) {
+      V8* hp = (V8*)P.insp_h + ((int64_t)h * P.nc + x.c0 + i) * (int64_t)(DK * DV / 8);
+#pragma unroll
+      for (int p = 0; p < KB; ++p) hp[(nb * KB + p) * 64 + lane] = sf[p];
+    }
+    // X^T and the state part of O^T for token tile w: lane holds
+    // [column 4g + e][token 16w + c]
+    floatx4 xt = zero4(), o = zero4();
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      xt = mma(sf[p], op.kr[p], xt);
+      o = mma(sf[p], op.qr[p], o);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(op.vv[e]) - eb * xt[e]);
+    lds_barrier();  // R of all token tiles is in Rf
+    const V8 rf0 = Rf[0][lane], rf1 = Rf[1][lane];
+    floatx4 vt[4];
+    vt[0] = mma(op.tb[0], rf0, zero4());
+    vt[1] = mma(op.tb[1], rf0, zero4());
+    vt[2] = mma(op.tb[3], rf1, mma(op.tb[2], rf0, zero4()));
+    vt[3] = mma(op.tb[5], rf1, mma(op.tb[4], rf0, zero4()));
+    // V' as the A operand of O^T and the B operand of the update (K~ already
+    // carries e^{b_n - b})
+    V8 vf[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) vf[p] = pack<ET>(vt[2 * p], vt[2 * p + 1]);
+    if (INSPECT && w == 0) {
+      V8* vp = (V8*)P.insp_vp + ((int64_t)h * P.nc + x.c0 + i) * (int64_t)(C * DV / 8);
+      vp[(nb * 2 + 0) * 64 + lane] = vf[0];
+      vp[(nb * 2 + 1) * 64 + lane] = vf[1];
+    }
+    // S <- gamma S + K~^T V'
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (KDA)
+        S[m] *= op.gm[m];
+      else
+        S[m] *= gam;
+      S[m] = mma(op.kt[m][0], vf[0], S[m]);
+      S[m] = mma(op.kt[m][1], vf[1], S[m]);
+    }
+    put_state();
+    // O^T tile: columns are tokens 16w + c; rows past the end are dropped
+    o *= eb;
+    o = mma(vf[0], op.pb[0], o);
+    if (w >= 2) o = mma(vf[1], op.pb[1], o);
+    bstore(op.orsrc, ooff, pack4<ET>(o));
+  };
+
+  // Two operand sets: the next chunk's operands load while this chunk
+  // computes.  The fp32 variant's operands are twice as large; it loads one
+  // chunk at a time.
+  if (n > 0) {
+    constexpr bool kPingPong = sizeof(ET) == 2;
+    if (kPingPong) {
+      ScanOps<DK, KDA, ET> bufa, bufb;
+      scan_load<DK, DV, KDA, ET>(bufa, P, x, 0);
+      for (int64_t i = 0; i < n; i += 2) {
+        scan_load<DK, DV, KDA, ET>(bufb, P, x, i + 1 < n ? i + 1 : n - 1);
+        step(bufa, i);
+        if (i + 1 >= n) break;
+        scan_load<DK, DV, KDA, ET>(bufa, P, x, i + 2 < n ? i + 2 : n - 1);
+        step(bufb, i + 1);
+      }
+    } else {
+      ScanOps<DK, KDA, ET> buf;
+      for (int64_t i = 0; i < n; ++i) {
+        scan_load<DK, DV, KDA, ET>(buf, P, x, i);
+        step(buf, i);
+      }
+    }
+  }
+  if (P.ht) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        P.ht[sbase + (int64_t)state_row(w * MT + m, 4 * g4 + e) * DV + col] = S[m][e];
+  }
+}
+
+template <int DK, int DV, bool KDA, typename ET>
+hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
+  if (nblk > 0) {
+    if (inspect)
+      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else
+      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace drla
+
+namespace drla {
+#define DRLA_SCAN_INST(DK_, DV_, KDA_, ET_) \
+  template hipError_t launch_scan<DK_, DV_, KDA_, ET_>(const ScanParams&, int64_t, bool, hipStream_t);
+DRLA_SCAN_INST(64, 64, false, bf16)
+DRLA_SCAN_INST(128, 64, false, bf16)
+DRLA_SCAN_INST(64, 128, false, bf16)
+DRLA_SCAN_INST(128, 128, false, bf16)
+DRLA_SCAN_INST(64, 64, true, bf16)
+DRLA_SCAN_INST(128, 64, true, bf16)
+DRLA_SCAN_INST(64, 128, true, bf16)
+DRLA_SCAN_INST(128, 128, true, bf16)
+DRLA_SCAN_INST(64, 64, false, float)
+DRLA_SCAN_INST(128, 64, false, float)
+DRLA_SCAN_INST(64, 128, false, float)
+DRLA_SCAN_INST(128, 128, false, float)
+DRLA_SCAN_INST(64, 64, true, float)
+DRLA_SCAN_INST(128, 64, true, float)
+DRLA_SCAN_INST(64, 128, true, float)
+DRLA_SCAN_INST(128, 128, true, float)
+#undef DRLA_SCAN_INST
+}  // namespace drla

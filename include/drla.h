@@ -18,9 +18,12 @@
  *   both: o_t = S_t^T q_t
  *
  * evaluated chunkwise (64 tokens) in the Map-Reduce-Map form of Section 2.1:
- * a chunk-parallel prep kernel (operators #1-#4: Gate, KKT, Solve, W/U), a
- * sequential state scan (operator #5: H) and a chunk-parallel output kernel
- * (operator #6: O).  Results equal the recurrence up to rounding.
+ * a chunk-parallel prep kernel (operators #1-#3 Gate, KKT, Solve, and the
+ * factor T diag(beta) that operator #4 W/U is built from, kept unexpanded
+ * as in Section 5's operator rewriting) and one kernel that runs the
+ * sequential state scan (#5 H) and the output (#6 O) chunk by chunk, state
+ * first-read, then output, then in-place update (Section 5, "cross-chunk
+ * reordering").  Results equal the recurrence up to rounding.
  *
  * Layouts (row-major, token-major, sequences packed back to back):
  *   q, k        [T, h_qk, dk]    io dtype
@@ -83,9 +86,10 @@ typedef struct {
   int64_t total_tokens; /* T >= 0                                           */
 } drla_problem;
 
-/* Workspace bytes a call on `p` needs.  `cu_seqlens_host` is the host copy
- * of cu_seqlens (NULL for a dense batch).  Returns 0 if `p` or the lengths
- * are invalid (the prefill call then reports why). */
+/* Workspace bytes a gdn_prefill or kda_prefill call on `p` needs (the
+ * larger of the two; a GDN call uses less).  `cu_seqlens_host` is the host
+ * copy of cu_seqlens (NULL for a dense batch).  Returns 0 if `p` or the
+ * lengths are invalid (the prefill call then reports why). */
 size_t drla_workspace_bytes(const drla_problem* p,
                             const int32_t* cu_seqlens_host);
 
@@ -113,38 +117,57 @@ drla_status kda_prefill(const drla_problem* p, const void* q, const void* k,
                         const int32_t* cu_seqlens_host, void* o, float* ht,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* gdn_prefill (kda == 0) or kda_prefill (kda != 0), additionally recording
- * four caller-created hipEvent_t on `stream` (passed as void*): stage_events[0]
- * before the first kernel, [1] after the prep kernel (operators #1-#4 of
- * Section 2.1), [2] after the state scan (#5), [3] after the output kernel
- * (#6), so that a benchmark can time each kernel on the stream it runs on.
- * stage_events may be NULL (then identical to the plain call).  A failing
- * event record returns DRLA_ERR_HIP. */
-drla_status drla_prefill_staged(int kda, const drla_problem* p, const void* q,
-                                const void* k, const void* v, const float* beta,
-                                const float* g, const float* h0,
-                                const int32_t* cu_seqlens_dev,
-                                const int32_t* cu_seqlens_host, void* o,
-                                float* ht, void* workspace,
-                                size_t workspace_bytes, void* stream,
-                                void* const* stage_events);
+/* Flags of drla_prefill_ex. */
+#define DRLA_KEEP_INTERMEDIATES 1 /* also write V' and the per-chunk state (tests) */
 
-/* Byte offsets of the per-chunk intermediates inside the workspace after a
- * call, for inspection by tests.  Each is stored per (v-head, chunk) in the
- * MFMA fragment order the kernels use (documented in drla_kernels.hip):
- *   w: W = T diag(beta e^b) K        (64 x dk)    kt: e^{b_n - b} (.) K (64 x dk)
- *   u: U = T diag(beta) V            (64 x dv)    vp: V' = U - W S     (64 x dv)
- *   h: S entering the chunk          (dk x dv)    gamma: e^{b_n} (1 or dk floats)
- * Elements are io dtype except gamma (fp32, room for dk floats per
- * (v-head, chunk); GDN uses one).  n_chunks is the total chunk count over
- * all sequences.  The layout is the same for GDN and KDA.  Returns DRLA_OK
- * or a validation error. */
+/* gdn_prefill (kda == 0) or kda_prefill (kda != 0) with options.
+ *   flags         0 or DRLA_KEEP_INTERMEDIATES.  With the flag the kernels
+ *                 also store, per (value head, chunk), V' = U - W S (the
+ *                 "v_c" intermediate of Section 5) and the state entering the
+ *                 chunk, at the offsets drla_workspace_layout reports for the
+ *                 same flags; the workspace must then be that layout's total.
+ *   stage_events  NULL, or three caller-created hipEvent_t (passed as void*)
+ *                 recorded on `stream`: [0] before the first kernel, [1]
+ *                 after the prep kernel (operators #1-#4 of Section 2.1), [2]
+ *                 after the scan/output kernel (#5, #6), so that a benchmark
+ *                 can time each kernel on the stream it runs on.  A failing
+ *                 event record returns DRLA_ERR_HIP.
+ * Other arguments and errors as for gdn_prefill. */
+drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const void* q,
+                            const void* k, const void* v, const float* beta,
+                            const float* g, const float* h0,
+                            const int32_t* cu_seqlens_dev,
+                            const int32_t* cu_seqlens_host, void* o, float* ht,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* stage_events);
+
+/* Byte offsets of the regions of the workspace of a call of drla_prefill_ex
+ * with the same kda, problem, lengths and flags, for inspection by tests.
+ * Each is stored per (value head, chunk), chunk index fastest, as MFMA
+ * operand fragments: a fragment covers 16 "outer" x 32 "inner" indices and
+ * is 64 lanes x 8 contiguous elements; lane l = 16 g + c (g < 4, c < 16)
+ * holds outer index c at inner indices 4g + j (j < 4) and 12 + 4g + j
+ * (4 <= j < 8).
+ *   tb:  T diag(beta), T = (I + A)^{-1}; 8 fragments (outer token tile 0..3,
+ *        inner token block 0..1, index tile*2 + block)
+ *   pm:  P = lower_incl(Q K^T (.) D) (the intra-chunk output weights), 8
+ *        fragments in the same order
+ *   kt:  K~^T, K~ = e^{b_n - b} (.) K; dk/8 fragments (outer key-channel
+ *        tile, inner token block, index tile*2 + block)
+ *   kw, qw (KDA only): K (.) e^{B}, Q (.) e^{B}; dk/8 fragments (outer token
+ *        tile, inner key block, index tile*(dk/32) + block)
+ *   gam (KDA only): e^{b_n} per key channel, dk floats
+ *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
+ *        inner token block, index tile*2 + block) and the state entering the
+ *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
+ * Elements are io dtype except gam (fp32).  n_chunks is the total chunk
+ * count over all sequences.  Returns DRLA_OK or a validation error. */
 typedef struct {
   int64_t n_chunks;
-  size_t sched, w, kt, u, vp, h, gamma, total;
+  size_t sched, tb, pm, kt, kw, qw, gam, vp, h, total;
 } drla_layout;
-drla_status drla_workspace_layout(const drla_problem* p,
-                                  const int32_t* cu_seqlens_host,
+drla_status drla_workspace_layout(int kda, const drla_problem* p,
+                                  const int32_t* cu_seqlens_host, int flags,
                                   drla_layout* out);
 
 const char* drla_status_str(drla_status s);

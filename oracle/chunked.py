@@ -67,13 +67,15 @@ def _chunk(Qc, Kc, Vc, bc, gc, S, kda):
     # #5 H (read): V' from the incoming state
     Vp = U - W @ S
     # #6 O
-    O = Qw @ S + np.where(lower_incl, QK, 0.0) @ Vp
+    P = np.where(lower_incl, QK, 0.0)
+    O = Qw @ S + P @ Vp
     # #5 H (update)
     if kda:
         S_next = gamma[:, None] * S + Kt.T @ Vp
     else:
         S_next = gamma * S + Kt.T @ Vp
-    inter = dict(b=B, A=A, T=T, W=W, U=U, Vp=Vp, Kt=Kt, gamma=gamma, h=S.copy())
+    inter = dict(b=B, A=A, T=T, Tb=T * bc[None, :], P=P, Kw=Kw, Qw=Qw, W=W, U=U, Vp=Vp,
+                 Kt=Kt, gamma=gamma, h=S.copy())
     return O, S_next, inter
 
 
@@ -81,8 +83,9 @@ def chunked(q, k, v, beta, g, h0=None, cu_seqlens=None, kda=False,
             chunk: int = 64, intermediates: bool = False):
     """fp64 chunkwise evaluation.  Same layouts and return values as
     ``oracle.recurrence``; with ``intermediates=True`` also returns a list,
-    per (sequence, v-head), of per-chunk dicts (b, A, T, W, U, Vp, Kt,
-    gamma, h = state entering the chunk).  Chunks start at each sequence
+    per (sequence, v-head), of per-chunk dicts (b, A, T, Tb = T diag(beta),
+    P = lower_incl(Q K^T (.) D), Kw = e^b (.) K, Qw = e^b (.) Q, W, U, Vp,
+    Kt, gamma, h = state entering the chunk).  Chunks start at each sequence
     start; the last chunk of a sequence may be shorter."""
     q, k, v, beta, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, beta, g))
     T, h_qk, dk = q.shape

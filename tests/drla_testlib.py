@@ -60,29 +60,38 @@ def run_oracle(x, heads=None, threads=None):
 
 
 def kmap(g, j):
+    """Inner index of slot j in lane group g (the fragment order of the
+    library's workspace: 4 + 4 at a distance of 16)."""
     return 4 * g + j if j < 4 else 16 + 4 * g + (j - 4)
 
 
-def _slot_index():
-    """(lane, j) -> (outer offset 0..15, inner offset 0..31) of an operand block."""
+def kmap_contiguous(g, j):
+    """Inner index of slot j in lane group g for fragments whose inner index
+    is a key channel (8 contiguous channels per lane)."""
+    return 8 * g + j
+
+
+def _slot_index(inner_map):
+    """(lane, j) -> (outer offset 0..15, inner offset 0..31) of a fragment."""
     outer = np.zeros((64, 8), dtype=np.int64)
     inner = np.zeros((64, 8), dtype=np.int64)
     for lane in range(64):
         for j in range(8):
             outer[lane, j] = lane % 16
-            inner[lane, j] = kmap(lane // 16, j)
+            inner[lane, j] = inner_map(lane // 16, j)
     return outer, inner
 
 
-def decode_blocks(raw, n_outer, n_inner, order):
-    """Decode one (v-head, chunk) region stored as operand blocks.
+def decode_blocks(raw, n_outer, n_inner, order, inner_map=kmap):
+    """Decode one (v-head, chunk) region stored as fragments.
 
-    raw      flat array of n_outer*n_inner elements
-    order    "outer_major": block index = tile*(n_inner/32) + p
-    returns  dense [n_outer, n_inner] (outer index, inner index)
+    raw        flat array of n_outer*n_inner elements
+    order      "outer_major": fragment index = tile*(n_inner/32) + p
+    inner_map  slot -> inner index map (kmap or kmap_contiguous)
+    returns    dense [n_outer, n_inner] (outer index, inner index)
     """
     assert order == "outer_major"
-    to, ti = _slot_index()
+    to, ti = _slot_index(inner_map)
     nb_in = n_inner // 32
     dense = np.zeros((n_outer, n_inner), dtype=np.float64)
     blocks = np.asarray(raw, dtype=np.float64).reshape(-1, 64, 8)
@@ -90,3 +99,8 @@ def decode_blocks(raw, n_outer, n_inner, order):
         tile, p = divmod(b, nb_in)
         dense[16 * tile + to, 32 * p + ti] = blocks[b]
     return dense
+
+
+def state_row(mt, rho):
+    """Key channel held by row rho of state tile mt in the scan kernel."""
+    return 32 * (mt >> 1) + 8 * (rho >> 2) + 4 * (mt & 1) + (rho & 3)

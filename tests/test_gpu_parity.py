@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from drla_testlib import TOL, decode_blocks, nmse, rel_err, run_oracle, to_device
+from drla_testlib import (TOL, decode_blocks, kmap_contiguous, nmse, rel_err, run_oracle,
+                          state_row, to_device)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -168,20 +169,24 @@ def test_deterministic_and_guard_bands(drla):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
 def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
-    """W, K~, U (prep), V', h (scan) and gamma against the fp64 chunkwise
-    form's intermediates on the same inputs, for every chunk (odd and even)."""
+    """Prep outputs (T diag(beta), P, K~^T; KDA: K e^B, Q e^B, e^{b_n}) and
+    the scan's V' and per-chunk state, against the fp64 chunkwise form's
+    intermediates on the same inputs, for every chunk (the last one short)."""
     import oracle
     print(f"case intermediates kind={kind} io={io} dk={dk} dv={dv}", flush=True)
     x = _case(kind, io, dk, dv, lens=(250,), h_qk=1, h_v=2, h0_std=0.1)
     d = to_device(x)
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    lay = drla.workspace_layout(x["q"].shape, x["v"].shape, dt)
+    kda = kind == "kda"
+    lay = drla.workspace_layout(x["q"].shape, x["v"].shape, dt, kda=kda,
+                                flags=drla.KEEP_INTERMEDIATES)
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
-    fn = drla.kda_prefill if kind == "kda" else drla.gdn_prefill
-    fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], workspace=ws)
+    fn = drla.kda_prefill if kda else drla.gdn_prefill
+    fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], workspace=ws,
+       flags=drla.KEEP_INTERMEDIATES)
     torch.cuda.synchronize()
     _, _, inter = oracle.chunked(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"],
-                                 kda=kind == "kda", intermediates=True)
+                                 kda=kda, intermediates=True)
     nc = lay["n_chunks"]
     es = 4 if io == "f32" else 2
     wse = ws.view(dt).float().cpu().numpy()
@@ -190,24 +195,44 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
     def region(off, per, h, c):
         base = off // es + (h * nc + c) * per
         return wse[base:base + per]
+
+    def pad(a, shape):
+        out = np.zeros(shape)
+        out[tuple(slice(0, n) for n in a.shape)] = a
+        return out
+    # position of key channel d among the decoded K~^T rows
+    krow = np.array([state_row(r // 16, r % 16) for r in range(dk)])
+    krow_inv = np.argsort(krow)
     worst = {}
     for h in range(2):
         for c in range(nc):
             it = inter[h][c]
             n = it["W"].shape[0]
-            W_ = decode_blocks(region(lay["w"], 64 * dk, h, c), 64, dk, "outer_major")[:n]
-            Kt = decode_blocks(region(lay["kt"], 64 * dk, h, c), dk, 64, "outer_major").T[:n]
-            U_ = decode_blocks(region(lay["u"], 64 * dv, h, c), dv, 64, "outer_major").T[:n]
-            Vp = decode_blocks(region(lay["vp"], 64 * dv, h, c), dv, 64, "outer_major").T[:n]
-            Hc = decode_blocks(region(lay["h"], dk * dv, h, c), dv, dk, "outer_major").T
-            for name, got, want in (("W", W_, it["W"]), ("K~", Kt, it["Kt"]), ("U", U_, it["U"]),
-                                    ("V'", Vp, it["Vp"]), ("h", Hc, it["h"])):
-                worst[name] = max(worst.get(name, 0.0), rel_err(got, want))
-            # KDA: dk floats per (head, chunk); GDN: one float at index h*nc + c
-            per = dk if kind == "kda" else 1
-            gb = lay["gamma"] // 4 + (h * nc + c) * per
-            gam = wsg[gb:gb + per]
-            worst["gamma"] = max(worst.get("gamma", 0.0), rel_err(gam, np.atleast_1d(it["gamma"])))
+            got = {
+                "Tb": decode_blocks(region(lay["tb"], 64 * 64, h, c), 64, 64, "outer_major"),
+                "P": decode_blocks(region(lay["pm"], 64 * 64, h, c), 64, 64, "outer_major"),
+                # K~^T rows are the scan's state rows: tile mt row rho is key
+                # channel state_row(mt, rho)
+                "K~": decode_blocks(region(lay["kt"], 64 * dk, h, c), dk, 64,
+                                    "outer_major")[krow_inv].T,
+                "V'": decode_blocks(region(lay["vp"], 64 * dv, h, c), dv, 64, "outer_major").T[:n],
+                "h": decode_blocks(region(lay["h"], dk * dv, h, c), dv, dk, "outer_major",
+                                   kmap_contiguous).T,
+            }
+            want = {"Tb": pad(it["Tb"], (64, 64)), "P": pad(it["P"], (64, 64)),
+                    "K~": pad(it["Kt"], (64, dk)), "V'": it["Vp"], "h": it["h"]}
+            if kda:
+                got["Kw"] = decode_blocks(region(lay["kw"], 64 * dk, h, c), 64, dk, "outer_major",
+                                          kmap_contiguous)
+                got["Qw"] = decode_blocks(region(lay["qw"], 64 * dk, h, c), 64, dk, "outer_major",
+                                          kmap_contiguous)
+                want["Kw"] = pad(it["Kw"], (64, dk))
+                want["Qw"] = pad(it["Qw"], (64, dk))
+                gb = lay["gam"] // 4 + (h * nc + c) * dk
+                got["gamma"] = wsg[gb:gb + dk]
+                want["gamma"] = it["gamma"]
+            for name in got:
+                worst[name] = max(worst.get(name, 0.0), rel_err(got[name], want[name]))
     print(kind, io, dk, dv, {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     tol = TOL[io]
     for name, e in worst.items():

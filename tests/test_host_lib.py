@@ -29,11 +29,12 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert {"gdn_prefill", "kda_prefill", "drla_workspace_bytes", "drla_workspace_layout",
-            "drla_status_str", "drla_last_error", "drla_version"} <= set(names)
+    assert {"gdn_prefill", "kda_prefill", "drla_prefill_ex", "drla_workspace_bytes",
+            "drla_workspace_layout", "drla_status_str", "drla_last_error",
+            "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 1
+    assert lib.drla_version() == 2
 
 
 def _prob(n_seqs=1, h_qk=2, h_v=4, dk=128, dv=128, io=0, T=256):
@@ -100,18 +101,33 @@ def test_workspace_bytes_and_layout(lib):
     p = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=0, T=4096)
     n = lib.drla_workspace_bytes(ctypes.byref(p), None)
     lay = Layout()
-    assert lib.drla_workspace_layout(ctypes.byref(p), None, ctypes.byref(lay)) == 0
+    assert lib.drla_workspace_layout(1, ctypes.byref(p), None, 0, ctypes.byref(lay)) == 0
     assert lay.total == n and lay.n_chunks == 64
-    per = 64 * 16
-    # W, K~, U, V' are 64 x 128 bf16 and h is 128 x 128 bf16 per (head, chunk)
-    assert lay.kt - lay.w == per * 64 * 128 * 2
-    assert lay.h - lay.vp == per * 64 * 128 * 2
-    assert lay.gamma - lay.h == per * 128 * 128 * 2
+    per = 64 * 16                       # (chunk, head) pairs
+    frag = 64 * 8 * 2                   # one bf16 fragment
+    assert lay.pm - lay.tb == per * 8 * frag
+    assert lay.kt - lay.pm == per * 8 * frag
+    assert lay.kw - lay.kt == per * 64 * 128 * 2
+    assert lay.qw - lay.kw == per * 64 * 128 * 2
+    assert lay.gam - lay.qw == per * 64 * 128 * 2
+    assert lay.total - lay.gam == per * 128 * 4
+    assert lay.vp == 0 and lay.h == 0
+    # GDN needs no KDA operands: its workspace is the prefix up to gam
+    gl = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
+    assert gl.kw == 0 and gl.total == lay.kw < n
+    # with the inspection flag V' and h follow
+    kl = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
+    assert kl.vp == gl.total and kl.h - kl.vp == per * 64 * 128 * 2
+    assert kl.total - kl.h == per * 128 * 128 * 2
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 3
     cu, _c = _i32([0, 1, 65, 65, 200])
     p2 = _prob(n_seqs=4, T=200)
     lay2 = Layout()
-    assert lib.drla_workspace_layout(ctypes.byref(p2), cu, ctypes.byref(lay2)) == 0
+    assert lib.drla_workspace_layout(0, ctypes.byref(p2), cu, 0, ctypes.byref(lay2)) == 0
     assert lay2.n_chunks == 1 + 1 + 0 + 3
+    assert lay2.tb >= (2 * 5 + 4 + 1) * 4      # chunk table first
     assert lib.drla_workspace_bytes(ctypes.byref(_prob(dk=80)), None) == 0
 
 
