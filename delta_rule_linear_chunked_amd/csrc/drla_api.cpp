@@ -94,8 +94,8 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
   L->qw = kda ? off : 0;
   if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
-  L->gam = kda ? off : 0;
-  if (kda) off = align_up(off + ncH * p->dk * 4);
+  L->gam = off;
+  off = align_up(off + ncH * (kda ? p->dk : DRLA_CHUNK) * 4);
   L->vp = keep ? off : 0;
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;

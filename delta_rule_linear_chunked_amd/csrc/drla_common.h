@@ -127,6 +127,20 @@ template <> __device__ __forceinline__ floatx8 bload<floatx8>(rsrc_t r, uint32_t
   const floatx4 lo = bload<floatx4>(r, off), hi = bload<floatx4>(r, off + 16);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// Fragment `f` (64 lanes x 16 or 32 bytes) of a fragment array through a
+// buffer resource: the per-lane offset is loop-invariant and the fragment
+// offset is a scalar, so no per-load address arithmetic lands in VGPRs.
+template <typename V>
+__device__ __forceinline__ V fload(rsrc_t r, uint32_t lane_off, int f) {
+  if constexpr (sizeof(V) == 16) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, f * 64 * 16, 0));
+  } else {
+    const floatx4 lo = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, f * 64 * 32, 0));
+    const floatx4 hi = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + 16, f * 64 * 32, 0));
+    return __builtin_bit_cast(V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, bf16x4 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
 }

@@ -16,7 +16,7 @@ struct PrepParams {
   void* kt;    // K~^T: dk/8 fragments per (head, chunk)
   void* kw;    // KDA: K e^{B}, dk/8 fragments
   void* qw;    // KDA: Q e^{B}, dk/8 fragments
-  float* gam;  // KDA: e^{b_n}, dk floats
+  float* gam;  // GDN: e^{b_r}, 64 floats; KDA: e^{b_n} per key channel, dk floats
   Sched s;
   int32_t h_qk, h_v, grp;
   int64_t nc;

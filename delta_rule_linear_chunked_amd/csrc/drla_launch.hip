@@ -27,7 +27,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   pp.kt = ws + a->off_kt;
   pp.kw = KDA ? ws + a->off_kw : nullptr;
   pp.qw = KDA ? ws + a->off_qw : nullptr;
-  pp.gam = KDA ? (float*)(ws + a->off_gam) : nullptr;
+  pp.gam = (float*)(ws + a->off_gam);
   pp.s = s;
   pp.h_qk = a->h_qk;
   pp.h_v = a->h_v;

@@ -20,7 +20,8 @@
 // sequential kernel only multiplies:
 //   P   = lower_incl(Q K^T (.) D)                 (KDA: (Q e^{B})(K e^{-B})^T)
 //   K~^T with K~ = diag(e^{b_n - b}) K            (KDA: K (.) e^{b_n - B})
-//   KDA only: K e^{B}, Q e^{B} and gamma = e^{b_n} per key channel.
+//   the decay factors: GDN e^{b_r} per token row (row 63 is e^{b_n});
+//   KDA e^{b_n} per key channel, and K e^{B}, Q e^{B}.
 // All are written in MFMA fragment order (drla_common.h).
 #include "drla_common.h"
 #include "drla_kernels.h"
@@ -285,6 +286,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
         qwg[f * 64 + lane] = xq;
       }
       for (int d = tid - 64; d < DK; d += 192) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
+    } else if (tid >= 64 && tid < 128) {
+      // GDN: e^{b_r} of every row; row 63 holds e^{b_n} (rows past the end
+      // carry the last b)
+      P.gam[ch * C + (tid - 64)] = __expf(bs[tid - 64]);
     }
   }
   __syncthreads();

@@ -45,7 +45,8 @@ struct ScanOps {
   V8 pb[2];        // P fragments (w, 0), (w, 1)
   V4 vv;           // V at token 16w + c, columns 16 nb + 4g + e
   floatx4 gm[MT];  // KDA: e^{b_n} of this lane's state rows
-  float gl;        // GDN: g of token `lane` (zero past the end)
+  float eb;        // GDN: e^{b} of token 16w + c
+  float gam;       // GDN: e^{b_n}
   rsrc_t orsrc;    // this chunk's rows of o
 };
 
@@ -58,7 +59,7 @@ struct ScanCtx {
 
 template <int DK, int DV, bool KDA, typename ET>
 __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanParams& P, const ScanCtx& x,
-                                          int64_t i) {
+                                          int i) {
   typedef typename VT<ET>::v4 V4;
   typedef typename VT<ET>::v8 V8;
   constexpr int KB = DK / 32, MT = DK / 64, es = sizeof(ET);
@@ -68,17 +69,18 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
   const uint32_t len = (uint32_t)(left < C ? left : C);
   const int64_t ch = (int64_t)x.h * P.nc + x.c0 + i;
   const int rw = 16 * w + c16;  // this lane's token in the chunk
+  const uint32_t loff = (uint32_t)lane * sizeof(V8);  // lane's slot in a fragment
   if (KDA) {
-    const V8* kw = (const V8*)P.kw + ch * (int64_t)(C * DK / 8);
-    const V8* qw = (const V8*)P.qw + ch * (int64_t)(C * DK / 8);
+    const rsrc_t kw = make_rsrc((const V8*)P.kw + ch * (C * DK / 8), C * DK * es);
+    const rsrc_t qw = make_rsrc((const V8*)P.qw + ch * (C * DK / 8), C * DK * es);
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
-      o.kr[p] = kw[(w * KB + p) * 64 + lane];
-      o.qr[p] = qw[(w * KB + p) * 64 + lane];
+      o.kr[p] = fload<V8>(kw, loff, w * KB + p);
+      o.qr[p] = fload<V8>(qw, loff, w * KB + p);
     }
+    const rsrc_t gr = make_rsrc(P.gam + ch * DK, DK * 4);
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      o.gm[m] = *(const floatx4*)(P.gam + ch * DK + state_row(w * MT + m, 4 * g4));
+    for (int m = 0; m < MT; ++m) o.gm[m] = bload<floatx4>(gr, state_row(w * MT + m, 4 * g4) * 4);
   } else {
     const size_t qrow = (size_t)P.h_qk * DK;
     const rsrc_t kr = make_rsrc((const ET*)P.k + t0 * qrow, len * qrow * es);
@@ -89,24 +91,29 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
       o.kr[p] = bload<V8>(kr, off + 32 * p * es);
       o.qr[p] = bload<V8>(qr, off + 32 * p * es);
     }
-    const rsrc_t gr = make_rsrc(P.g + t0 * P.h_v, len * P.h_v * 4);
-    o.gl = bload<float>(gr, ((uint32_t)lane * P.h_v + x.h) * 4);
+    const rsrc_t gr = make_rsrc(P.gam + ch * C, C * 4);
+    // e^{b_n} is the same for every lane; an opaque per-lane offset keeps
+    // it a vector value, so no scalar copy has to wait for the load
+    uint32_t last = (C - 1) * 4;
+    asm("" : "+v"(last));
+    o.eb = bload<float>(gr, rw * 4);
+    o.gam = bload<float>(gr, last);
   }
-  const V8* kt = (const V8*)P.kt + ch * (int64_t)(C * DK / 8);
+  const rsrc_t ktr = make_rsrc((const V8*)P.kt + ch * (C * DK / 8), C * DK * es);
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) o.kt[m][p] = kt[((w * MT + m) * 2 + p) * 64 + lane];
-  const V8* tb = (const V8*)P.tb + ch * (8 * 64);
-  o.tb[0] = tb[0 * 64 + lane];
-  o.tb[1] = tb[2 * 64 + lane];
-  o.tb[2] = tb[4 * 64 + lane];
-  o.tb[3] = tb[5 * 64 + lane];
-  o.tb[4] = tb[6 * 64 + lane];
-  o.tb[5] = tb[7 * 64 + lane];
-  const V8* pm = (const V8*)P.pm + ch * (8 * 64);
-  o.pb[0] = pm[(2 * w) * 64 + lane];
-  o.pb[1] = pm[(2 * w + 1) * 64 + lane];  // zero for w < 2
+    for (int p = 0; p < 2; ++p) o.kt[m][p] = fload<V8>(ktr, loff, (w * MT + m) * 2 + p);
+  const rsrc_t tbr = make_rsrc((const V8*)P.tb + ch * (8 * 64), 8 * 64 * sizeof(V8));
+  o.tb[0] = fload<V8>(tbr, loff, 0);
+  o.tb[1] = fload<V8>(tbr, loff, 2);
+  o.tb[2] = fload<V8>(tbr, loff, 4);
+  o.tb[3] = fload<V8>(tbr, loff, 5);
+  o.tb[4] = fload<V8>(tbr, loff, 6);
+  o.tb[5] = fload<V8>(tbr, loff, 7);
+  const rsrc_t pmr = make_rsrc((const V8*)P.pm + ch * (8 * 64), 8 * 64 * sizeof(V8));
+  o.pb[0] = fload<V8>(pmr, loff, 2 * w);
+  o.pb[1] = fload<V8>(pmr, loff, 2 * w + 1);  // zero for w < 2
   const size_t vrow = (size_t)P.h_v * DV;
   const rsrc_t vr = make_rsrc((const ET*)P.v + t0 * vrow, len * vrow * es);
   o.vv = bload<V4>(vr, (uint32_t)(((size_t)rw * P.h_v + x.h) * DV + 16 * x.nb + 4 * g4) * es);
@@ -121,7 +128,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   __shared__ V8 Sf[KB][64];  // state entering the chunk, as fragments (inner = key channel)
   __shared__ V8 Rf[2][64];   // R = V - X, as B fragments (inner = token)
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g4 = lane >> 4, c16 = lane & 15;
   // Consecutive workgroups go to different XCDs; renumber so that the NB
   // column blocks of one (sequence, head), which read the same K, Q and prep
@@ -177,19 +185,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   ET* const rdst = (ET*)&Rf[w >> 1][16 * (c16 >> 2) + 4 * g4] + 4 * (w & 1) + (c16 & 3);
   const uint32_t ooff = (uint32_t)(((size_t)(16 * w + c16) * P.h_v + h) * DV + 16 * nb + 4 * g4) * es;
 
-  auto step = [&](const ScanOps<DK, KDA, ET>& op, int64_t i) {
-    // GDN: b = in-chunk cumulative log-decay of token `lane`
-    float eb = 1.f, gam = 1.f;
-    if (!KDA) {
-      float y = op.gl;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(y, off);
-        if (lane >= off) y += t;
-      }
-      gam = __expf(__shfl(y, 63));
-      eb = __expf(__shfl(y, 16 * w + c16));  // e^{b} of this lane's token
-    }
+  auto step = [&](const ScanOps<DK, KDA, ET>& op, int i) {
+    // GDN decay factors (from prep): e^{b} of this lane's token, e^{b_n}
+    const float eb = KDA ? 1.f : op.eb, gam = KDA ? 1.f : op.gam;
     lds_barrier();  // the state entering this chunk is in Sf
     V8 sf[KB];
 #pragma unroll
@@ -250,18 +248,30 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   if (n > 0) {
     constexpr bool kPingPong = sizeof(ET) == 2;
     if (kPingPong) {
+      // The scheduling barriers keep the memory operations in program order
+      // -- next chunk's loads, this chunk's products, this chunk's store --
+      // so that waiting for this chunk's operands never waits for the loads
+      // just issued (loads and stores share one in-order counter).
+      // Chunk counters are 32-bit and wave-uniform so that the loop control
+      // stays on the scalar unit.
+      const int nn = __builtin_amdgcn_readfirstlane((int)n);
       ScanOps<DK, KDA, ET> bufa, bufb;
       scan_load<DK, DV, KDA, ET>(bufa, P, x, 0);
-      for (int64_t i = 0; i < n; i += 2) {
-        scan_load<DK, DV, KDA, ET>(bufb, P, x, i + 1 < n ? i + 1 : n - 1);
+      for (int i = 0; i < nn; i += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        scan_load<DK, DV, KDA, ET>(bufb, P, x, min(i + 1, nn - 1));
+        __builtin_amdgcn_sched_barrier(0);
         step(bufa, i);
-        if (i + 1 >= n) break;
-        scan_load<DK, DV, KDA, ET>(bufa, P, x, i + 2 < n ? i + 2 : n - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 >= nn) break;
+        scan_load<DK, DV, KDA, ET>(bufa, P, x, min(i + 2, nn - 1));
+        __builtin_amdgcn_sched_barrier(0);
         step(bufb, i + 1);
       }
     } else {
+      const int nn = __builtin_amdgcn_readfirstlane((int)n);
       ScanOps<DK, KDA, ET> buf;
-      for (int64_t i = 0; i < n; ++i) {
+      for (int i = 0; i < nn; ++i) {
         scan_load<DK, DV, KDA, ET>(buf, P, x, i);
         step(buf, i);
       }

@@ -156,7 +156,8 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *        tile, inner token block, index tile*2 + block)
  *   kw, qw (KDA only): K (.) e^{B}, Q (.) e^{B}; dk/8 fragments (outer token
  *        tile, inner key block, index tile*(dk/32) + block)
- *   gam (KDA only): e^{b_n} per key channel, dk floats
+ *   gam: decay factors, fp32: GDN e^{b_r} for the 64 token rows (row 63 is
+ *        e^{b_n}); KDA e^{b_n} per key channel, dk floats
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)

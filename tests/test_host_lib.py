@@ -112,10 +112,11 @@ def test_workspace_bytes_and_layout(lib):
     assert lay.gam - lay.qw == per * 64 * 128 * 2
     assert lay.total - lay.gam == per * 128 * 4
     assert lay.vp == 0 and lay.h == 0
-    # GDN needs no KDA operands: its workspace is the prefix up to gam
+    # GDN needs no KDA operands; its decay factors are 64 floats per chunk
     gl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
-    assert gl.kw == 0 and gl.total == lay.kw < n
+    assert gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kw
+    assert gl.total - gl.gam == per * 64 * 4 and gl.total < n
     # with the inspection flag V' and h follow
     kl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
