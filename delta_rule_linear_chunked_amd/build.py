@@ -31,7 +31,8 @@ def hipcc() -> str:
 
 def sources():
     return [os.path.join(CSRC, f) for f in
-            ("drla_prep.hip", "drla_scan.hip", "drla_launch.hip", "drla_api.cpp")]
+            ("drla_prep.hip", "drla_scan.hip", "drla_scan_lds.hip", "drla_launch.hip",
+             "drla_api.cpp")]
 
 
 def build(verbose: bool = False, extra=()) -> str:

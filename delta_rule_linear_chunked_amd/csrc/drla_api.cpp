@@ -88,14 +88,17 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   off = align_up(off + ncH * 8 * frag);
   L->pm = off;
   off = align_up(off + ncH * 8 * frag);
-  L->kt = off;
-  off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
+  // K~^T is only needed by the register-fed scan (KDA, fp32 inputs); the
+  // LDS-fed GDN scan transposes K itself
+  const bool need_kt = kda || p->io_dtype != DRLA_BF16;
+  L->kt = need_kt ? off : 0;
+  if (need_kt) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
   L->kw = kda ? off : 0;
   if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
   L->qw = kda ? off : 0;
   if (kda) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
   L->gam = off;
-  off = align_up(off + ncH * (kda ? p->dk : DRLA_CHUNK) * 4);
+  off = align_up(off + ncH * (kda ? p->dk : 2 * DRLA_CHUNK) * 4);
   L->vp = keep ? off : 0;
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;

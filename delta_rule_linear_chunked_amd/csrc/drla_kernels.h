@@ -13,10 +13,10 @@ struct PrepParams {
   const float* g;
   void* tb;    // Tb = T diag(beta): 8 fragments per (head, chunk)
   void* pm;    // P: 8 fragments per (head, chunk)
-  void* kt;    // K~^T: dk/8 fragments per (head, chunk)
+  void* kt;    // K~^T: dk/8 fragments per (head, chunk), or null (not needed)
   void* kw;    // KDA: K e^{B}, dk/8 fragments
   void* qw;    // KDA: Q e^{B}, dk/8 fragments
-  float* gam;  // GDN: e^{b_r}, 64 floats; KDA: e^{b_n} per key channel, dk floats
+  float* gam;  // GDN: e^{b_r} then e^{b_n - b_r}, 128 floats; KDA: e^{b_n} per key channel
   Sched s;
   int32_t h_qk, h_v, grp;
   int64_t nc;
@@ -50,6 +50,10 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st);
 
 template <int DK, int DV, bool KDA, typename ET>
 hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
+
+// GDN with bf16 inputs: the LDS-fed scan (drla_scan_lds.hip)
+template <int DK, int DV>
+hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
 
 }  // namespace drla
 

@@ -24,7 +24,9 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   pp.g = a->g;
   pp.tb = ws + a->off_tb;
   pp.pm = ws + a->off_pm;
-  pp.kt = ws + a->off_kt;
+  // the LDS-fed scan (GDN, bf16) transposes K itself and needs no K~^T
+  constexpr bool kLdsScan = !KDA && sizeof(ET) == 2;
+  pp.kt = kLdsScan ? nullptr : ws + a->off_kt;
   pp.kw = KDA ? ws + a->off_kw : nullptr;
   pp.qw = KDA ? ws + a->off_qw : nullptr;
   pp.gam = (float*)(ws + a->off_gam);
@@ -61,8 +63,13 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     e = launch_schedule(a->cu_dev, a->n_seqs, nc, (int32_t*)(ws + a->off_sched), st);
   if (e == hipSuccess) e = launch_prep<DK, KDA, ET>(pp, nc * a->h_v, st);
   mark(1);
-  if (e == hipSuccess)
-    e = launch_scan<DK, DV, KDA, ET>(sp, (int64_t)a->n_seqs * a->h_v * (DV / 16), a->inspect != 0, st);
+  const int64_t nscan = (int64_t)a->n_seqs * a->h_v * (DV / 16);
+  if (e == hipSuccess) {
+    if constexpr (kLdsScan)
+      e = launch_scan_lds<DK, DV>(sp, nscan, a->inspect != 0, st);
+    else
+      e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
+  }
   mark(2);
   return e;
 }

@@ -19,8 +19,9 @@
 // It also emits the chunk-local operands of the output Map, so that the
 // sequential kernel only multiplies:
 //   P   = lower_incl(Q K^T (.) D)                 (KDA: (Q e^{B})(K e^{-B})^T)
-//   K~^T with K~ = diag(e^{b_n - b}) K            (KDA: K (.) e^{b_n - B})
-//   the decay factors: GDN e^{b_r} per token row (row 63 is e^{b_n});
+//   K~^T with K~ = diag(e^{b_n - b}) K            (KDA: K (.) e^{b_n - B});
+//        not needed (null) when the scan transposes K itself
+//   the decay factors: GDN e^{b_r} and e^{b_n - b_r} per token row;
 //   KDA e^{b_n} per key channel, and K e^{B}, Q e^{B}.
 // All are written in MFMA fragment order (drla_common.h).
 #include "drla_common.h"
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     // block p), and the KDA operands.
     constexpr int NF = (DK / 16) * 2;
     V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
-    for (int f = wv - 1; f < NF; f += 3) {
+    for (int f = wv - 1; P.kt && f < NF; f += 3) {
       const int mt = f >> 1, p = f & 1;
       const int d = state_row(mt, c16);
       V8 x;
@@ -287,9 +288,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       }
       for (int d = tid - 64; d < DK; d += 192) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
     } else if (tid >= 64 && tid < 128) {
-      // GDN: e^{b_r} of every row; row 63 holds e^{b_n} (rows past the end
-      // carry the last b)
-      P.gam[ch * C + (tid - 64)] = __expf(bs[tid - 64]);
+      // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
+      // holds e^{b_n} (rows past the end carry the last b)
+      const int r = tid - 64;
+      P.gam[ch * (2 * C) + r] = __expf(bs[r]);
+      P.gam[ch * (2 * C) + C + r] = __expf(bs[C - 1] - bs[r]);
     }
   }
   __syncthreads();

@@ -91,7 +91,7 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
       o.kr[p] = bload<V8>(kr, off + 32 * p * es);
       o.qr[p] = bload<V8>(qr, off + 32 * p * es);
     }
-    const rsrc_t gr = make_rsrc(P.gam + ch * C, C * 4);
+    const rsrc_t gr = make_rsrc(P.gam + ch * (2 * C), C * 4);
     // e^{b_n} is the same for every lane; an opaque per-lane offset keeps
     // it a vector value, so no scalar copy has to wait for the load
     uint32_t last = (C - 1) * 4;

@@ -1,0 +1,339 @@
+// Sequential state scan fused with the output Map, LDS-fed (GDN, bf16).
+//
+// Same computation as drla_scan.hip -- operators #5 (H) and #6 (O) of the
+// Map-Reduce-Map split in "Empowering Hybrid Attention Models on NPUs",
+// Section 2.1, in the chunk-first order of its Section 5 -- organised so
+// that every byte a workgroup needs crosses the CU's load path once:
+//
+//   wave 0    (state)   the state recurrence of the chunk, with the 16 state
+//                       columns in registers:
+//                         X   = diag(e^b) K S
+//                         V'  = Tb (V - X)
+//                         S  <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
+//   waves 1,2 (loaders) copy the operands of chunk t+2 (K and Q rows, Tb,
+//                       P, this block's 16 columns of V, the decay factors)
+//                       into a three-slot LDS ring with LDS-direct loads,
+//                       and touch chunk t+PF so that it sits in L2 when its
+//                       copy is issued
+//   wave 3    (output)  O = diag(e^b) Q S + P V' for the chunk, and its store
+//
+// K^T is never stored: the state wave reads K rows from LDS with the
+// transposing ds_read_b64_tr_b16 (within a 16-lane group, lane i receives
+// element i%4 of the four-element segments addressed by lanes 4j + i/4,
+// j = 0..3).  Two workgroup barriers per chunk: after V' is in LDS (the
+// output wave needs it) and at the end (next state published, ring slot
+// released, next chunk's operands landed).
+//
+// Only the loader waves issue loads, so their wait counts are exact: every
+// chunk they issue exactly kIssued copies and kTouched touches.
+#include "drla_common.h"
+#include "drla_kernels.h"
+
+namespace drla {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing LDS read (see above); `p` must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 ds_read_tr(const void* p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// LDS-direct loads: lane l's 16 (4) bytes from `g` land at lds + 16 l (4 l).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and nothing else.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+template <int DK>
+struct LdsSlot {
+  static constexpr int RB = DK * 2;                       // bytes per K/Q row
+  __attribute__((aligned(16))) unsigned char k[C * RB];  // K rows, 16-byte chunks swizzled
+  __attribute__((aligned(16))) unsigned char q[C * RB];  // Q rows, same
+  bf16x8 tb[6][64];                                       // Tb fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+  bf16x8 pm[6][64];                                       // P fragments, same order
+  __attribute__((aligned(16))) bf16 v[C][16];             // V, this block's 16 columns
+  __attribute__((aligned(16))) float eb[C];               // e^{b_r}
+  __attribute__((aligned(16))) float ebn[C];              // e^{b_n - b_r}
+};
+
+// Byte offset of 16-byte chunk j of row r in a swizzled K/Q tile (the chunk
+// index is XORed with the row so that a fragment's 16 rows hit 16 banks).
+template <int DK>
+__device__ __forceinline__ int swz(int r, int j) {
+  constexpr int NCH = DK / 8;
+  return r * (DK * 2) + ((j ^ (r & (NCH - 1))) << 4);
+}
+
+template <int DK, int DV, bool INSPECT>
+__global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
+  constexpr int KB = DK / 32, KT = DK / 16, NB = DV / 16;
+  constexpr int NS = 3;                       // ring slots
+  constexpr int PF = 6;                       // L2 touch distance, chunks
+  constexpr int NCH = DK / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 1024 / (DK * 2);        // rows per 1 KiB copy
+  constexpr int kIssued = C / RPI + 6 + 2;    // copies per loader wave and chunk
+  constexpr int kTouched = (DK * 2 > 128 ? 2 : 1) + 2;  // touches per loader wave and chunk
+  __shared__ LdsSlot<DK> slot[NS];
+  __shared__ bf16x8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
+  __shared__ bf16x8 vbuf[2][64];      // V' of the chunk, A fragments (inner = token)
+  __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, c16 = lane & 15;
+  int b = blockIdx.x;
+  const int G = gridDim.x;
+  if (G % 8 == 0) b = (b % 8) * (G / 8) + b / 8;  // column blocks of a head on one XCD
+  const int unit = b / NB, nb = b - unit * NB;
+  const int seq = unit / P.h_v, h = unit - seq * P.h_v;
+  const int hk = h / P.grp;
+
+  int64_t ts, te, c0, nch;
+  if (P.s.chunk_seq) {
+    ts = P.s.cu[seq];
+    te = P.s.cu[seq + 1];
+    int64_t c1;
+    seq_chunks(P.s, seq, P.nc, c0, c1);
+    nch = te > ts ? (te - ts + C - 1) / C : 0;
+    if (nch > c1 - c0) nch = c1 - c0;  // device lengths disagree with the table
+  } else {
+    ts = (int64_t)seq * P.s.seq_len;
+    te = ts + P.s.seq_len;
+    c0 = (int64_t)seq * P.s.cps;
+    nch = P.s.cps;
+  }
+  const int n = __builtin_amdgcn_readfirstlane((int)nch);
+  const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
+  const int col = 16 * nb + c16;
+  const bf16* kg = (const bf16*)P.k;
+  const bf16* qg = (const bf16*)P.q;
+  const bf16* vg = (const bf16*)P.v;
+
+  // ---- loaders: copy chunk i into ring slot i % NS ------------------------
+  // wave 1: K rows, Tb, decay factors; wave 2: Q rows, P, V.  Rows past the
+  // end of a short chunk repeat its last row: their Tb columns and rows are
+  // zero (beta = 0 there), so they reach no result.
+  auto issue = [&](int i) {
+    LdsSlot<DK>& sl = slot[i % NS];
+    const int64_t t0 = ts + (int64_t)C * i;
+    const int last = (int)((te - t0 < C ? te - t0 : C) - 1);
+    const int64_t ch = (int64_t)h * P.nc + c0 + i;
+    const bf16* src = w == 1 ? kg : qg;
+    unsigned char* dst = w == 1 ? sl.k : sl.q;
+#pragma unroll
+    for (int u = 0; u < C / RPI; ++u) {
+      const int r = u * RPI + lane / NCH;
+      const int j = (lane % NCH) ^ (r & (NCH - 1));
+      const int rr = r < last ? r : last;
+      lds_dma16(src + ((t0 + rr) * P.h_qk + hk) * DK + 8 * j, dst + u * 1024);
+    }
+    const bf16x8* fr = (const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64) + lane;
+    bf16x8(*fdst)[64] = w == 1 ? sl.tb : sl.pm;
+    lds_dma16(fr + 0 * 64, &fdst[0][0]);
+    lds_dma16(fr + 2 * 64, &fdst[1][0]);
+    lds_dma16(fr + 4 * 64, &fdst[2][0]);
+    lds_dma16(fr + 5 * 64, &fdst[3][0]);
+    lds_dma16(fr + 6 * 64, &fdst[4][0]);
+    lds_dma16(fr + 7 * 64, &fdst[5][0]);
+    if (w == 1) {
+      const float* gm = P.gam + ch * (2 * C);
+      lds_dma4(gm + lane, sl.eb);
+      lds_dma4(gm + C + lane, sl.ebn);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 32 * u + (lane >> 1);
+        const int rr = r < last ? r : last;
+        lds_dma16(vg + ((t0 + rr) * P.h_v + h) * DV + 16 * nb + 8 * (lane & 1), &sl.v[32 * u][0]);
+      }
+    }
+  };
+  // touch chunk i's operands, one 128-byte line per lane
+  auto prefetch = [&](int i) {
+    const int64_t t0 = ts + (int64_t)C * i;
+    const int last = (int)((te - t0 < C ? te - t0 : C) - 1);
+    const int64_t ch = (int64_t)h * P.nc + c0 + i;
+    const int r = lane < last ? lane : last;
+    const unsigned char* row = (const unsigned char*)((w == 1 ? kg : qg) + ((t0 + r) * P.h_qk + hk) * DK);
+    lds_dma4(row, touch);
+    if (DK * 2 > 128) lds_dma4(row + 128, touch);
+    const unsigned char* fr = (const unsigned char*)((const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64));
+    lds_dma4(fr + 128 * lane, touch);
+    if (w == 1)
+      lds_dma4((const unsigned char*)(P.gam + ch * (2 * C)) + 128 * (lane & 3), touch);
+    else
+      lds_dma4(vg + ((t0 + r) * P.h_v + h) * DV + 16 * nb, touch);
+  };
+
+  // ---- prologue ------------------------------------------------------------
+  floatx4 S[KT];  // state wave: tile mt, element e is key channel state_row(mt, 4g + e)
+  if (w == 0) {
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[mt][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] : 0.f;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) sbuf[0][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+  } else if (w < 3 && n > 0) {
+    issue(0);
+    issue(n > 1 ? 1 : 0);
+    // touches for chunks 2..3 (the loop touches chunk t + PF); at most 63
+    // operations can be outstanding, so the prologue touches fewer
+#pragma unroll
+    for (int i = 2; i < 4; ++i) prefetch(i < n ? i : n - 1);
+    // chunk 0 has landed once at most the later copies and touches are pending
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + 2 * kTouched));
+  }
+  lds_barrier();
+
+  const uint32_t orow = (uint32_t)(((size_t)c16 * P.h_v + h) * DV + 16 * nb + 4 * g4) * 2;
+  const uint32_t ostep = (uint32_t)(16 * P.h_v * DV * 2);  // 16 tokens
+
+  for (int t = 0; t < n; ++t) {
+    const LdsSlot<DK>& sl = slot[t % NS];
+    const int64_t t0 = ts + (int64_t)C * t;
+    const int64_t ch = (int64_t)h * P.nc + c0 + t;
+    if (w == 0) {
+      // ---------------- state wave ----------------
+      bf16x8 sf[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+      if (INSPECT) {
+        bf16x8* hp = (bf16x8*)P.insp_h + ch * (int64_t)(DK * DV / 8);
+#pragma unroll
+        for (int p = 0; p < KB; ++p) hp[(nb * KB + p) * 64 + lane] = sf[p];
+      }
+      // X = K S for the four token tiles: lane holds [16 nt + 4g + e][c]
+      floatx4 x[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = zero4();
+#pragma unroll
+        for (int p = 0; p < KB; ++p)
+          x[nt] = mma(*(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4)), sf[p], x[nt]);
+      }
+      // R = V - diag(e^b) X; V[16 nt + 4g + e][c] comes from the transposing
+      // read (lane 4e' + q of the group addresses row 16 nt + 4g + e',
+      // columns 4q..4q+3)
+      floatx4 rr[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x4 vv = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
+        const floatx4 eb = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[nt][e] = to_f(vv[e]) - eb[e] * x[nt][e];
+      }
+      const bf16x8 rf0 = pack<bf16>(rr[0], rr[1]), rf1 = pack<bf16>(rr[2], rr[3]);
+      // V' = Tb R
+      floatx4 vt[4];
+      vt[0] = mma(sl.tb[0][lane], rf0, zero4());
+      vt[1] = mma(sl.tb[1][lane], rf0, zero4());
+      vt[2] = mma(sl.tb[3][lane], rf1, mma(sl.tb[2][lane], rf0, zero4()));
+      vt[3] = mma(sl.tb[5][lane], rf1, mma(sl.tb[4][lane], rf0, zero4()));
+      const bf16x8 vf0 = pack<bf16>(vt[0], vt[1]), vf1 = pack<bf16>(vt[2], vt[3]);
+      vbuf[0][lane] = vf0;
+      vbuf[1][lane] = vf1;
+      if (INSPECT) {
+        bf16x8* vp = (bf16x8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
+        vp[(nb * 2 + 0) * 64 + lane] = vf0;
+        vp[(nb * 2 + 1) * 64 + lane] = vf1;
+      }
+      lds_barrier();  // (mid) V' is in LDS
+      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
+      floatx4 vs[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
+      const bf16x8 vs0 = pack<bf16>(vs[0], vs[1]), vs1 = pack<bf16>(vs[2], vs[3]);
+      const float gam = sl.eb[C - 1];
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) {
+        // K^T fragment (outer = key channel state_row(mt, c), inner = token):
+        // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
+        // upper half), channels state_row(mt, 4q) .. +3
+        const int d = state_row(mt, 4 * (c16 & 3));
+        const int joff = d & 7;
+        floatx4 acc = S[mt] * gam;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
+          const bf16x4 lo = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * joff);
+          const bf16x4 hi = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * joff);
+          acc = mma(cat<bf16>(lo, hi), p == 0 ? vs0 : vs1, acc);
+        }
+        S[mt] = acc;
+      }
+#pragma unroll
+      for (int p = 0; p < KB; ++p) sbuf[(t + 1) & 1][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+    } else if (w == 3) {
+      // ---------------- output wave ----------------
+      bf16x8 sf[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) sf[p] = sbuf[t & 1][p][lane];
+      // state part of O^T: lane holds [column 4g + e][token 16 nt + c]
+      floatx4 o[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        o[nt] = zero4();
+#pragma unroll
+        for (int p = 0; p < KB; ++p)
+          o[nt] = mma(sf[p], *(const bf16x8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4)), o[nt]);
+        o[nt] *= sl.eb[16 * nt + c16];
+      }
+      lds_barrier();  // (mid) V' is in LDS
+      const bf16x8 vf0 = vbuf[0][lane], vf1 = vbuf[1][lane];
+      o[0] = mma(vf0, sl.pm[0][lane], o[0]);
+      o[1] = mma(vf0, sl.pm[1][lane], o[1]);
+      o[2] = mma(vf1, sl.pm[3][lane], mma(vf0, sl.pm[2][lane], o[2]));
+      o[3] = mma(vf1, sl.pm[5][lane], mma(vf0, sl.pm[4][lane], o[3]));
+      const int64_t left = te - t0;
+      const uint32_t len = (uint32_t)(left < C ? left : C);
+      const rsrc_t orr = make_rsrc((bf16*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<bf16>(o[nt]));  // rows past the end dropped
+    } else {
+      // ---------------- loader waves ----------------
+      issue(t + 2 < n ? t + 2 : n - 1);
+      prefetch(t + PF < n ? t + PF : n - 1);
+      lds_barrier();  // (mid)
+      // everything issued before this chunk -- in particular chunk t+1's
+      // copy -- has landed
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + kTouched));
+    }
+    lds_barrier();  // (end) next state in sbuf, slot t % NS free, chunk t+1 landed
+  }
+  if (w == 0 && P.ht) {
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        P.ht[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = S[mt][e];
+  }
+  if (w == 1 || w == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+template <int DK, int DV>
+hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
+  if (nblk > 0) {
+    if (inspect)
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_scan_lds<64, 64>(const ScanParams&, int64_t, bool, hipStream_t);
+template hipError_t launch_scan_lds<128, 64>(const ScanParams&, int64_t, bool, hipStream_t);
+template hipError_t launch_scan_lds<64, 128>(const ScanParams&, int64_t, bool, hipStream_t);
+template hipError_t launch_scan_lds<128, 128>(const ScanParams&, int64_t, bool, hipStream_t);
+
+}  // namespace drla

@@ -153,11 +153,13 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   pm:  P = lower_incl(Q K^T (.) D) (the intra-chunk output weights), 8
  *        fragments in the same order
  *   kt:  K~^T, K~ = e^{b_n - b} (.) K; dk/8 fragments (outer key-channel
- *        tile, inner token block, index tile*2 + block)
+ *        tile, inner token block, index tile*2 + block); only for KDA and
+ *        fp32 inputs (else 0: that scan transposes K on chip)
  *   kw, qw (KDA only): K (.) e^{B}, Q (.) e^{B}; dk/8 fragments (outer token
  *        tile, inner key block, index tile*(dk/32) + block)
  *   gam: decay factors, fp32: GDN e^{b_r} for the 64 token rows (row 63 is
- *        e^{b_n}); KDA e^{b_n} per key channel, dk floats
+ *        e^{b_n}) then e^{b_n - b_r}, 128 floats; KDA e^{b_n} per key
+ *        channel, dk floats
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)

@@ -211,16 +211,19 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
             got = {
                 "Tb": decode_blocks(region(lay["tb"], 64 * 64, h, c), 64, 64, "outer_major"),
                 "P": decode_blocks(region(lay["pm"], 64 * 64, h, c), 64, 64, "outer_major"),
-                # K~^T rows are the scan's state rows: tile mt row rho is key
-                # channel state_row(mt, rho)
-                "K~": decode_blocks(region(lay["kt"], 64 * dk, h, c), dk, 64,
-                                    "outer_major")[krow_inv].T,
                 "V'": decode_blocks(region(lay["vp"], 64 * dv, h, c), dv, 64, "outer_major").T[:n],
                 "h": decode_blocks(region(lay["h"], dk * dv, h, c), dv, dk, "outer_major",
                                    kmap_contiguous).T,
             }
             want = {"Tb": pad(it["Tb"], (64, 64)), "P": pad(it["P"], (64, 64)),
-                    "K~": pad(it["Kt"], (64, dk)), "V'": it["Vp"], "h": it["h"]}
+                    "V'": it["Vp"], "h": it["h"]}
+            if lay["kt"]:
+                # K~^T (written for the register-fed scan only): its rows are
+                # the scan's state rows, tile mt row rho = key channel
+                # state_row(mt, rho)
+                got["K~"] = decode_blocks(region(lay["kt"], 64 * dk, h, c), dk, 64,
+                                          "outer_major")[krow_inv].T
+                want["K~"] = pad(it["Kt"], (64, dk))
             if kda:
                 got["Kw"] = decode_blocks(region(lay["kw"], 64 * dk, h, c), 64, dk, "outer_major",
                                           kmap_contiguous)

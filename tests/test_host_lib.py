@@ -112,11 +112,17 @@ def test_workspace_bytes_and_layout(lib):
     assert lay.gam - lay.qw == per * 64 * 128 * 2
     assert lay.total - lay.gam == per * 128 * 4
     assert lay.vp == 0 and lay.h == 0
-    # GDN needs no KDA operands; its decay factors are 64 floats per chunk
+    # GDN with bf16 inputs needs neither K~^T nor the KDA operands; its decay
+    # factors are 2 x 64 floats per chunk
     gl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
-    assert gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kw
-    assert gl.total - gl.gam == per * 64 * 4 and gl.total < n
+    assert gl.kt == 0 and gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kt
+    assert gl.total - gl.gam == per * 128 * 4 and gl.total < n
+    # fp32 inputs keep K~^T for the register-fed scan
+    pf = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=1, T=4096)
+    fl = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(pf), None, 0, ctypes.byref(fl)) == 0
+    assert fl.gam - fl.kt == per * 64 * 128 * 4
     # with the inspection flag V' and h follow
     kl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
