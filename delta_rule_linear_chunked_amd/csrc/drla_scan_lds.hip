@@ -204,6 +204,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     const int64_t ch = (int64_t)h * P.nc + c0 + t;
     if (w == 0) {
       // ---------------- state wave ----------------
+      // Each phase first issues all of its LDS reads, then its products, so
+      // that the LDS latency is paid once per phase rather than per product.
       bf16x8 sf[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
@@ -212,33 +214,47 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
         for (int p = 0; p < KB; ++p) hp[(nb * KB + p) * 64 + lane] = sf[p];
       }
+      bf16x8 kr[4][KB];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) kr[nt][p] = *(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+      // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
+      // group addresses row 16 nt + 4g + e', columns 4q..4q+3
+      bf16x4 vv[4];
+      floatx4 ebv[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        vv[nt] = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
+        ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
+      }
+      bf16x8 tbf[6];
+#pragma unroll
+      for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
+      __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles: lane holds [16 nt + 4g + e][c]
       floatx4 x[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        x[nt] = zero4();
+      for (int nt = 0; nt < 4; ++nt) x[nt] = zero4();
 #pragma unroll
-        for (int p = 0; p < KB; ++p)
-          x[nt] = mma(*(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4)), sf[p], x[nt]);
-      }
-      // R = V - diag(e^b) X; V[16 nt + 4g + e][c] comes from the transposing
-      // read (lane 4e' + q of the group addresses row 16 nt + 4g + e',
-      // columns 4q..4q+3)
+      for (int p = 0; p < KB; ++p)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) x[nt] = mma(kr[nt][p], sf[p], x[nt]);
+      // R = V - diag(e^b) X, as B fragments (inner = token)
       floatx4 rr[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x4 vv = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
-        const floatx4 eb = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[nt][e] = to_f(vv[e]) - eb[e] * x[nt][e];
-      }
+        for (int e = 0; e < 4; ++e) rr[nt][e] = to_f(vv[nt][e]) - ebv[nt][e] * x[nt][e];
       const bf16x8 rf0 = pack<bf16>(rr[0], rr[1]), rf1 = pack<bf16>(rr[2], rr[3]);
       // V' = Tb R
       floatx4 vt[4];
-      vt[0] = mma(sl.tb[0][lane], rf0, zero4());
-      vt[1] = mma(sl.tb[1][lane], rf0, zero4());
-      vt[2] = mma(sl.tb[3][lane], rf1, mma(sl.tb[2][lane], rf0, zero4()));
-      vt[3] = mma(sl.tb[5][lane], rf1, mma(sl.tb[4][lane], rf0, zero4()));
+      vt[0] = mma(tbf[0], rf0, zero4());
+      vt[1] = mma(tbf[1], rf0, zero4());
+      vt[2] = mma(tbf[2], rf0, zero4());
+      vt[3] = mma(tbf[4], rf0, zero4());
+      vt[2] = mma(tbf[3], rf1, vt[2]);
+      vt[3] = mma(tbf[5], rf1, vt[3]);
       const bf16x8 vf0 = pack<bf16>(vt[0], vt[1]), vf1 = pack<bf16>(vt[2], vt[3]);
       vbuf[0][lane] = vf0;
       vbuf[1][lane] = vf1;
@@ -248,29 +264,37 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         vp[(nb * 2 + 1) * 64 + lane] = vf1;
       }
       lds_barrier();  // (mid) V' is in LDS
-      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
-      floatx4 vs[4];
+      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V').  K^T fragment (outer =
+      // key channel state_row(mt, c), inner = token): lane 4e' + q of group
+      // g addresses token 32p + 4g + e' (+16 for the upper half), channels
+      // state_row(mt, 4q) .. +3
+      floatx4 env[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
-      const bf16x8 vs0 = pack<bf16>(vs[0], vs[1]), vs1 = pack<bf16>(vs[2], vs[3]);
+      for (int nt = 0; nt < 4; ++nt) env[nt] = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
       const float gam = sl.eb[C - 1];
+      bf16x4 kt[KT][2][2];
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt) {
-        // K^T fragment (outer = key channel state_row(mt, c), inner = token):
-        // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
-        // upper half), channels state_row(mt, 4q) .. +3
         const int d = state_row(mt, 4 * (c16 & 3));
-        const int joff = d & 7;
-        floatx4 acc = S[mt] * gam;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
-          const bf16x4 lo = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * joff);
-          const bf16x4 hi = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * joff);
-          acc = mma(cat<bf16>(lo, hi), p == 0 ? vs0 : vs1, acc);
+          kt[mt][p][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          kt[mt][p][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
         }
-        S[mt] = acc;
       }
+      __builtin_amdgcn_sched_barrier(0);
+      floatx4 vs[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * env[nt];
+      const bf16x8 vs0 = pack<bf16>(vs[0], vs[1]), vs1 = pack<bf16>(vs[2], vs[3]);
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) S[mt] *= gam;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+          S[mt] = mma(cat<bf16>(kt[mt][p][0], kt[mt][p][1]), p == 0 ? vs0 : vs1, S[mt]);
 #pragma unroll
       for (int p = 0; p < KB; ++p) sbuf[(t + 1) & 1][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
     } else if (w == 3) {
@@ -278,22 +302,36 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       bf16x8 sf[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) sf[p] = sbuf[t & 1][p][lane];
+      bf16x8 qr[4][KB];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) qr[nt][p] = *(const bf16x8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
+      float ebt[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) ebt[nt] = sl.eb[16 * nt + c16];
+      bf16x8 pmf[6];
+#pragma unroll
+      for (int f = 0; f < 6; ++f) pmf[f] = sl.pm[f][lane];
+      __builtin_amdgcn_sched_barrier(0);
       // state part of O^T: lane holds [column 4g + e][token 16 nt + c]
       floatx4 o[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        o[nt] = zero4();
+      for (int nt = 0; nt < 4; ++nt) o[nt] = zero4();
 #pragma unroll
-        for (int p = 0; p < KB; ++p)
-          o[nt] = mma(sf[p], *(const bf16x8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4)), o[nt]);
-        o[nt] *= sl.eb[16 * nt + c16];
-      }
+      for (int p = 0; p < KB; ++p)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) o[nt] = mma(sf[p], qr[nt][p], o[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
       lds_barrier();  // (mid) V' is in LDS
       const bf16x8 vf0 = vbuf[0][lane], vf1 = vbuf[1][lane];
-      o[0] = mma(vf0, sl.pm[0][lane], o[0]);
-      o[1] = mma(vf0, sl.pm[1][lane], o[1]);
-      o[2] = mma(vf1, sl.pm[3][lane], mma(vf0, sl.pm[2][lane], o[2]));
-      o[3] = mma(vf1, sl.pm[5][lane], mma(vf0, sl.pm[4][lane], o[3]));
+      o[0] = mma(vf0, pmf[0], o[0]);
+      o[1] = mma(vf0, pmf[1], o[1]);
+      o[2] = mma(vf0, pmf[2], o[2]);
+      o[3] = mma(vf0, pmf[4], o[3]);
+      o[2] = mma(vf1, pmf[3], o[2]);
+      o[3] = mma(vf1, pmf[5], o[3]);
       const int64_t left = te - t0;
       const uint32_t len = (uint32_t)(left < C ? left : C);
       const rsrc_t orr = make_rsrc((bf16*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
