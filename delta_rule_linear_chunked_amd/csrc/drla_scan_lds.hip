@@ -20,9 +20,9 @@
 // K^T is never stored: the state wave reads K rows from LDS with the
 // transposing ds_read_b64_tr_b16 (within a 16-lane group, lane i receives
 // element i%4 of the four-element segments addressed by lanes 4j + i/4,
-// j = 0..3).  Two workgroup barriers per chunk: after V' is in LDS (the
-// output wave needs it) and at the end (next state published, ring slot
-// released, next chunk's operands landed).
+// j = 0..3).  One workgroup barrier per chunk (next state and V' published,
+// ring slot released, next chunk's operands landed); the output wave adds
+// the P V' term of a chunk one chunk later, keeping P in registers.
 //
 // Only the loader waves issue loads, so their wait counts are exact: every
 // chunk they issue exactly kIssued copies and kTouched touches.
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int kTouched = (DK * 2 > 128 ? 2 : 1) + 2;  // touches per loader wave and chunk
   __shared__ LdsSlot<DK> slot[NS];
   __shared__ bf16x8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
-  __shared__ bf16x8 vbuf[2][64];      // V' of the chunk, A fragments (inner = token)
+  __shared__ bf16x8 vbuf[2][2][64];   // V' of the last two chunks, A fragments (inner = token)
   __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -197,6 +197,26 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 
   const uint32_t orow = (uint32_t)(((size_t)c16 * P.h_v + h) * DV + 16 * nb + 4 * g4) * 2;
   const uint32_t ostep = (uint32_t)(16 * P.h_v * DV * 2);  // 16 tokens
+  // output wave: add P V' of chunk i (first token t0i) to the partial O^T
+  // and store it; rows past the end of the sequence are dropped
+  floatx4 o[4];
+  bf16x8 pmf[6];
+  auto finish_output = [&](int64_t t0i, int i) {
+    const bf16x8 vf0 = vbuf[i & 1][0][lane], vf1 = vbuf[i & 1][1][lane];
+    o[0] = mma(vf0, pmf[0], o[0]);
+    o[1] = mma(vf0, pmf[1], o[1]);
+    o[2] = mma(vf0, pmf[2], o[2]);
+    o[3] = mma(vf0, pmf[4], o[3]);
+    o[2] = mma(vf1, pmf[3], o[2]);
+    o[3] = mma(vf1, pmf[5], o[3]);
+    const int64_t left = te - t0i;
+    const uint32_t len = (uint32_t)(left < C ? left : C);
+    const rsrc_t orr = make_rsrc((bf16*)P.o + t0i * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<bf16>(o[nt]));
+  };
+
+  int64_t t0prev = 0;  // output wave: first token of the chunk in o
 
   for (int t = 0; t < n; ++t) {
     const LdsSlot<DK>& sl = slot[t % NS];
@@ -204,8 +224,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     const int64_t ch = (int64_t)h * P.nc + c0 + t;
     if (w == 0) {
       // ---------------- state wave ----------------
-      // Each phase first issues all of its LDS reads, then its products, so
-      // that the LDS latency is paid once per phase rather than per product.
+      // All LDS reads of the chunk are issued first, then the products, so
+      // that the LDS latency is paid once per chunk.
       bf16x8 sf[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
@@ -222,15 +242,31 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
       // group addresses row 16 nt + 4g + e', columns 4q..4q+3
       bf16x4 vv[4];
-      floatx4 ebv[4];
+      floatx4 ebv[4], env[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         vv[nt] = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
         ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
+        env[nt] = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
       }
       bf16x8 tbf[6];
 #pragma unroll
       for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
+      const float gam = sl.eb[C - 1];
+      // K^T fragments (outer = key channel state_row(mt, c), inner = token):
+      // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
+      // upper half), channels state_row(mt, 4q) .. +3
+      bf16x4 kt[KT][2][2];
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) {
+        const int d = state_row(mt, 4 * (c16 & 3));
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
+          kt[mt][p][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          kt[mt][p][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles: lane holds [16 nt + 4g + e][c]
       floatx4 x[4];
@@ -256,34 +292,14 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       vt[2] = mma(tbf[3], rf1, vt[2]);
       vt[3] = mma(tbf[5], rf1, vt[3]);
       const bf16x8 vf0 = pack<bf16>(vt[0], vt[1]), vf1 = pack<bf16>(vt[2], vt[3]);
-      vbuf[0][lane] = vf0;
-      vbuf[1][lane] = vf1;
+      vbuf[t & 1][0][lane] = vf0;
+      vbuf[t & 1][1][lane] = vf1;
       if (INSPECT) {
         bf16x8* vp = (bf16x8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
         vp[(nb * 2 + 0) * 64 + lane] = vf0;
         vp[(nb * 2 + 1) * 64 + lane] = vf1;
       }
-      lds_barrier();  // (mid) V' is in LDS
-      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V').  K^T fragment (outer =
-      // key channel state_row(mt, c), inner = token): lane 4e' + q of group
-      // g addresses token 32p + 4g + e' (+16 for the upper half), channels
-      // state_row(mt, 4q) .. +3
-      floatx4 env[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) env[nt] = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
-      const float gam = sl.eb[C - 1];
-      bf16x4 kt[KT][2][2];
-#pragma unroll
-      for (int mt = 0; mt < KT; ++mt) {
-        const int d = state_row(mt, 4 * (c16 & 3));
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
-          kt[mt][p][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
-          kt[mt][p][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
       floatx4 vs[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * env[nt];
@@ -299,6 +315,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int p = 0; p < KB; ++p) sbuf[(t + 1) & 1][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
     } else if (w == 3) {
       // ---------------- output wave ----------------
+      // finish the previous chunk: its V' was published at the last barrier
+      if (t > 0) finish_output(t0prev, t - 1);
+      // state part of this chunk's O^T: lane holds [column 4g + e][token 16 nt + c]
       bf16x8 sf[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) sf[p] = sbuf[t & 1][p][lane];
@@ -310,12 +329,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       float ebt[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) ebt[nt] = sl.eb[16 * nt + c16];
-      bf16x8 pmf[6];
 #pragma unroll
-      for (int f = 0; f < 6; ++f) pmf[f] = sl.pm[f][lane];
+      for (int f = 0; f < 6; ++f) pmf[f] = sl.pm[f][lane];  // kept for the next step
       __builtin_amdgcn_sched_barrier(0);
-      // state part of O^T: lane holds [column 4g + e][token 16 nt + c]
-      floatx4 o[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) o[nt] = zero4();
 #pragma unroll
@@ -324,30 +340,18 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         for (int nt = 0; nt < 4; ++nt) o[nt] = mma(sf[p], qr[nt][p], o[nt]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
-      lds_barrier();  // (mid) V' is in LDS
-      const bf16x8 vf0 = vbuf[0][lane], vf1 = vbuf[1][lane];
-      o[0] = mma(vf0, pmf[0], o[0]);
-      o[1] = mma(vf0, pmf[1], o[1]);
-      o[2] = mma(vf0, pmf[2], o[2]);
-      o[3] = mma(vf0, pmf[4], o[3]);
-      o[2] = mma(vf1, pmf[3], o[2]);
-      o[3] = mma(vf1, pmf[5], o[3]);
-      const int64_t left = te - t0;
-      const uint32_t len = (uint32_t)(left < C ? left : C);
-      const rsrc_t orr = make_rsrc((bf16*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<bf16>(o[nt]));  // rows past the end dropped
+      t0prev = t0;
     } else {
       // ---------------- loader waves ----------------
       issue(t + 2 < n ? t + 2 : n - 1);
       prefetch(t + PF < n ? t + PF : n - 1);
-      lds_barrier();  // (mid)
       // everything issued before this chunk -- in particular chunk t+1's
       // copy -- has landed
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + kTouched));
     }
-    lds_barrier();  // (end) next state in sbuf, slot t % NS free, chunk t+1 landed
+    lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
   }
+  if (w == 3 && n > 0) finish_output(t0prev, n - 1);
   if (w == 0 && P.ht) {
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
