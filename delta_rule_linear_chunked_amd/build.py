@@ -16,9 +16,12 @@ LIB = os.path.join(BUILD, "libdrla.so")
 
 ARCH = "gfx950"
 # Packed fp32 vector ops are kept off: hipcc would otherwise form
-# v_pk_{add,mul,fma}_f32 from float2 code.
+# v_pk_{add,mul,fma}_f32 from float2 code.  MFMA accumulators are kept in
+# VGPRs: the scans scale and convert them with vector ALU code every chunk,
+# which in the AGPR form costs a copy in and out of the AGPR file.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -40,12 +40,16 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const void* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// LDS-direct loads: lane l's 16 (4) bytes from `g` land at lds + 16 l (4 l).
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+// LDS-direct buffer loads: lane l's 16 (4) bytes at byte offset voff + soff
+// of the buffer land at lds + 16 l (4 l).  Callers keep soff = 0 and put the
+// whole offset in voff, which the hardware range check covers: a read past
+// the buffer's size returns zero.  The instruction offset stays 0 (it would
+// move the LDS side too).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt immediate that waits for at most n outstanding vector memory
@@ -118,63 +122,81 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   const bf16* vg = (const bf16*)P.v;
 
   // ---- loaders: copy chunk i into ring slot i % NS ------------------------
-  // wave 1: K rows, Tb, decay factors; wave 2: Q rows, P, V.  Rows past the
-  // end of a short chunk repeat its last row: their Tb columns and rows are
-  // zero (beta = 0 there), so they reach no result.
+  // wave 1: K rows, Tb, decay factors; wave 2: Q rows, P, V.  Each copy goes
+  // through a buffer descriptor that starts at the chunk and ends at its last
+  // valid token, so rows past the end of a short chunk read zero (their Tb
+  // rows and columns are zero as well: beta = 0 there).  The per-lane byte
+  // offsets are the same for every chunk.
+  constexpr int NP = NCH > RPI ? NCH / RPI : 1;  // swizzle patterns of the row copies
+  const uint32_t kstride = (uint32_t)P.h_qk * DK * 2;  // bytes between tokens of q, k
+  const uint32_t vstride = (uint32_t)P.h_v * DV * 2;   // bytes between tokens of v
+  uint32_t roff[NP];
+#pragma unroll
+  for (int v = 0; v < NP; ++v) {
+    const int r = v * RPI + lane / NCH;
+    roff[v] = (uint32_t)r * kstride + 16u * (uint32_t)((lane % NCH) ^ (r & (NCH - 1)));
+  }
+  const uint32_t voff = (uint32_t)(lane >> 1) * vstride + 16u * (uint32_t)(lane & 1);
+  auto chunk_len = [&](int i) -> uint32_t {
+    const int64_t left = te - (ts + (int64_t)C * i);
+    return (uint32_t)(left < C ? left : C);
+  };
+  auto row_rsrc = [&](int i) -> rsrc_t {
+    const bf16* src = (w == 1 ? kg : qg) + ((ts + (int64_t)C * i) * P.h_qk + hk) * DK;
+    return make_rsrc(src, (chunk_len(i) - 1) * kstride + DK * 2);
+  };
+  auto v_rsrc = [&](int i) -> rsrc_t {
+    const bf16* src = vg + ((ts + (int64_t)C * i) * P.h_v + h) * DV + 16 * nb;
+    return make_rsrc(src, (chunk_len(i) - 1) * vstride + 32);
+  };
+  auto frag_rsrc = [&](int i) -> rsrc_t {
+    const int64_t ch = (int64_t)h * P.nc + c0 + i;
+    return make_rsrc((const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64), 8 * 1024);
+  };
+  auto gam_rsrc = [&](int i) -> rsrc_t {
+    const int64_t ch = (int64_t)h * P.nc + c0 + i;
+    return make_rsrc(P.gam + ch * (2 * C), 2 * C * 4);
+  };
   auto issue = [&](int i) {
     LdsSlot<DK>& sl = slot[i % NS];
-    const int64_t t0 = ts + (int64_t)C * i;
-    const int last = (int)((te - t0 < C ? te - t0 : C) - 1);
-    const int64_t ch = (int64_t)h * P.nc + c0 + i;
-    const bf16* src = w == 1 ? kg : qg;
+    const rsrc_t rr = row_rsrc(i);
     unsigned char* dst = w == 1 ? sl.k : sl.q;
 #pragma unroll
-    for (int u = 0; u < C / RPI; ++u) {
-      const int r = u * RPI + lane / NCH;
-      const int j = (lane % NCH) ^ (r & (NCH - 1));
-      const int rr = r < last ? r : last;
-      lds_dma16(src + ((t0 + rr) * P.h_qk + hk) * DK + 8 * j, dst + u * 1024);
-    }
-    const bf16x8* fr = (const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64) + lane;
+    for (int u = 0; u < C / RPI; ++u) lds_dma16(rr, roff[u % NP] + (uint32_t)(u / NP) * (NP * RPI) * kstride, 0, dst + u * 1024);
+    const rsrc_t fr = frag_rsrc(i);
     bf16x8(*fdst)[64] = w == 1 ? sl.tb : sl.pm;
-    lds_dma16(fr + 0 * 64, &fdst[0][0]);
-    lds_dma16(fr + 2 * 64, &fdst[1][0]);
-    lds_dma16(fr + 4 * 64, &fdst[2][0]);
-    lds_dma16(fr + 5 * 64, &fdst[3][0]);
-    lds_dma16(fr + 6 * 64, &fdst[4][0]);
-    lds_dma16(fr + 7 * 64, &fdst[5][0]);
+    const uint32_t lo = 16u * lane;
+    lds_dma16(fr, lo + 0 * 1024, 0, &fdst[0][0]);
+    lds_dma16(fr, lo + 2 * 1024, 0, &fdst[1][0]);
+    lds_dma16(fr, lo + 4 * 1024, 0, &fdst[2][0]);
+    lds_dma16(fr, lo + 5 * 1024, 0, &fdst[3][0]);
+    lds_dma16(fr, lo + 6 * 1024, 0, &fdst[4][0]);
+    lds_dma16(fr, lo + 7 * 1024, 0, &fdst[5][0]);
     if (w == 1) {
-      const float* gm = P.gam + ch * (2 * C);
-      lds_dma4(gm + lane, sl.eb);
-      lds_dma4(gm + C + lane, sl.ebn);
+      const rsrc_t gr = gam_rsrc(i);
+      lds_dma4(gr, 4u * lane, 0, sl.eb);
+      lds_dma4(gr, 4u * lane + 4 * C, 0, sl.ebn);
     } else {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = 32 * u + (lane >> 1);
-        const int rr = r < last ? r : last;
-        lds_dma16(vg + ((t0 + rr) * P.h_v + h) * DV + 16 * nb + 8 * (lane & 1), &sl.v[32 * u][0]);
-      }
+      const rsrc_t vr = v_rsrc(i);
+      lds_dma16(vr, voff, 0, &sl.v[0][0]);
+      lds_dma16(vr, voff + 32 * vstride, 0, &sl.v[32][0]);
     }
   };
   // touch chunk i's operands, one 128-byte line per lane
   auto prefetch = [&](int i) {
-    const int64_t t0 = ts + (int64_t)C * i;
-    const int last = (int)((te - t0 < C ? te - t0 : C) - 1);
-    const int64_t ch = (int64_t)h * P.nc + c0 + i;
-    const int r = lane < last ? lane : last;
-    const unsigned char* row = (const unsigned char*)((w == 1 ? kg : qg) + ((t0 + r) * P.h_qk + hk) * DK);
-    lds_dma4(row, touch);
-    if (DK * 2 > 128) lds_dma4(row + 128, touch);
-    const unsigned char* fr = (const unsigned char*)((const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64));
-    lds_dma4(fr + 128 * lane, touch);
+    const rsrc_t rr = row_rsrc(i);
+    lds_dma4(rr, (uint32_t)lane * kstride, 0, touch);
+    if (DK * 2 > 128) lds_dma4(rr, (uint32_t)lane * kstride + 128, 0, touch);
+    lds_dma4(frag_rsrc(i), 128u * lane, 0, touch);
     if (w == 1)
-      lds_dma4((const unsigned char*)(P.gam + ch * (2 * C)) + 128 * (lane & 3), touch);
+      lds_dma4(gam_rsrc(i), 128u * (lane & 3), 0, touch);
     else
-      lds_dma4(vg + ((t0 + r) * P.h_v + h) * DV + 16 * nb, touch);
+      lds_dma4(v_rsrc(i), (uint32_t)lane * vstride, 0, touch);
   };
 
   // ---- prologue ------------------------------------------------------------
   floatx4 S[KT];  // state wave: tile mt, element e is key channel state_row(mt, 4g + e)
+  bf16x8 sf[KB];   // state wave: S as bf16 B fragments (inner = key channel)
   if (w == 0) {
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
@@ -182,7 +204,10 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int e = 0; e < 4; ++e)
         S[mt][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] : 0.f;
 #pragma unroll
-    for (int p = 0; p < KB; ++p) sbuf[0][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+    for (int p = 0; p < KB; ++p) {
+      sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+      sbuf[0][p][lane] = sf[p];
+    }
   } else if (w < 3 && n > 0) {
     issue(0);
     issue(n > 1 ? 1 : 0);
@@ -224,21 +249,22 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     const int64_t ch = (int64_t)h * P.nc + c0 + t;
     if (w == 0) {
       // ---------------- state wave ----------------
-      // All LDS reads of the chunk are issued first, then the products, so
-      // that the LDS latency is paid once per chunk.
-      bf16x8 sf[KB];
-#pragma unroll
-      for (int p = 0; p < KB; ++p) sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+      // Nothing of this wave is in flight here; saying so lets the compiler
+      // count the LDS reads below exactly (it cannot see through the
+      // loaders' LDS-direct loads on the other branch).
+      __builtin_amdgcn_s_waitcnt(0);
+      // LDS reads in the order they are consumed: the operands of R and V'
+      // and the K rows of X first, then (while X runs) the K^T fragments of
+      // the update.  `sf` holds the state entering the chunk (packed at the
+      // end of the last chunk).
       if (INSPECT) {
         bf16x8* hp = (bf16x8*)P.insp_h + ch * (int64_t)(DK * DV / 8);
 #pragma unroll
         for (int p = 0; p < KB; ++p) hp[(nb * KB + p) * 64 + lane] = sf[p];
       }
-      bf16x8 kr[4][KB];
+      bf16x8 tbf[6];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int p = 0; p < KB; ++p) kr[nt][p] = *(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+      for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
       // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
       // group addresses row 16 nt + 4g + e', columns 4q..4q+3
       bf16x4 vv[4];
@@ -249,24 +275,12 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
         env[nt] = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
       }
-      bf16x8 tbf[6];
-#pragma unroll
-      for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
       const float gam = sl.eb[C - 1];
-      // K^T fragments (outer = key channel state_row(mt, c), inner = token):
-      // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
-      // upper half), channels state_row(mt, 4q) .. +3
-      bf16x4 kt[KT][2][2];
+      bf16x8 kr[KB][4];
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt) {
-        const int d = state_row(mt, 4 * (c16 & 3));
+      for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
-          kt[mt][p][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
-          kt[mt][p][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
-        }
-      }
+        for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
       __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles: lane holds [16 nt + 4g + e][c]
       floatx4 x[4];
@@ -275,7 +289,23 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
       for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) x[nt] = mma(kr[nt][p], sf[p], x[nt]);
+        for (int nt = 0; nt < 4; ++nt) x[nt] = mma(kr[p][nt], sf[p], x[nt]);
+      __builtin_amdgcn_sched_barrier(0);
+      // K^T fragments (outer = key channel state_row(mt, c), inner = token):
+      // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
+      // upper half), channels state_row(mt, 4q) .. +3
+      bf16x4 kt[2][KT][2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) {
+          const int d = state_row(mt, 4 * (c16 & 3));
+          kt[p][mt][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          kt[p][mt][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // R = V - diag(e^b) X, as B fragments (inner = token)
       floatx4 rr[4];
 #pragma unroll
@@ -310,17 +340,20 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
-          S[mt] = mma(cat<bf16>(kt[mt][p][0], kt[mt][p][1]), p == 0 ? vs0 : vs1, S[mt]);
+          S[mt] = mma(cat<bf16>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1, S[mt]);
 #pragma unroll
-      for (int p = 0; p < KB; ++p) sbuf[(t + 1) & 1][p][lane] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+      for (int p = 0; p < KB; ++p) {
+        sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+        sbuf[(t + 1) & 1][p][lane] = sf[p];
+      }
     } else if (w == 3) {
       // ---------------- output wave ----------------
       // finish the previous chunk: its V' was published at the last barrier
       if (t > 0) finish_output(t0prev, t - 1);
       // state part of this chunk's O^T: lane holds [column 4g + e][token 16 nt + c]
-      bf16x8 sf[KB];
+      bf16x8 so[KB];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) sf[p] = sbuf[t & 1][p][lane];
+      for (int p = 0; p < KB; ++p) so[p] = sbuf[t & 1][p][lane];
       bf16x8 qr[4][KB];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
@@ -337,7 +370,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
       for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) o[nt] = mma(sf[p], qr[nt][p], o[nt]);
+        for (int nt = 0; nt < 4; ++nt) o[nt] = mma(so[p], qr[nt][p], o[nt]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
       t0prev = t0;
@@ -345,9 +378,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // ---------------- loader waves ----------------
       issue(t + 2 < n ? t + 2 : n - 1);
       prefetch(t + PF < n ? t + PF : n - 1);
-      // everything issued before this chunk -- in particular chunk t+1's
-      // copy -- has landed
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + kTouched));
+      // chunk t+1's copy has landed; the touches issued after it (chunks
+      // t+5 and t+6, often HBM misses) and chunk t+2's copy may be pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + 2 * kTouched));
     }
     lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
   }
