@@ -155,6 +155,10 @@ def main():
     ap.add_argument("--workload", default="gdn_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the bench, run a plain elementwise copy of MIB MiB (bf16 negate: "
+                         "reads and writes MIB MiB) five times, the reference dispatch that scales "
+                         "the HBM byte counters of a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the prefill kernels "
@@ -273,6 +277,15 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, spec, n_tokens, args.cpu_budget)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {n * 2} bytes read and {n * 2} bytes written per dispatch",
+              file=sys.stderr)
     print(json.dumps(line), flush=True)
 
 
