@@ -71,8 +71,12 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
   if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
 }
 
-// One workgroup (4 waves) per (chunk, value head).
-template <int DK, bool KDA, typename ET>
+// One workgroup (4 waves) per (chunk, value head).  KT: write K~^T (the
+// register-fed scans need it; the LDS-fed one transposes K itself).
+//
+// LDS is reused across phases: K (and KDA's gate table) live until the
+// chunk operands are written, T from the solve on, in the same bytes.
+template <int DK, bool KDA, typename ET, bool KT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   typedef typename VT<ET>::v8 V8;
   typedef typename VT<ET>::v16b V16;
@@ -80,14 +84,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   constexpr int KB = DK / 32;
   constexpr int KP = DK + 16 / (int)sizeof(ET);  // padded row: 16-byte aligned, 4-bank skew
   constexpr int TP = C + 4;
-  constexpr int MID = C / 2 - 1;                      // KDA: reference row of the factored decay
-  __shared__ __attribute__((aligned(16))) ET Ks[C][KP];
+  constexpr int MID = C / 2 - 1;                 // KDA: reference row of the factored decay
+  constexpr int BP = DK + 4;
+  constexpr int NPART = 256 / DK;                // KDA gate: row parts per channel
+  constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
+  constexpr int BS_BYTES = KDA ? C * BP * 4 : 0;
+  constexpr int TS_BYTES = C * TP * 4;
+  constexpr int U_BYTES = KS_BYTES + BS_BYTES > TS_BYTES ? KS_BYTES + BS_BYTES : TS_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
   __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
-  __shared__ __attribute__((aligned(16))) float Ts[C][TP];  // T
-  __shared__ __attribute__((aligned(16))) float Tt[C][TP];  // T transposed
   __shared__ float bs[C];
   __shared__ float betas[C];
-  __shared__ float Bs[KDA ? C : 1][KDA ? DK + 4 : 1];
+  __shared__ float Btot[KDA ? NPART : 1][KDA ? DK : 1];
+  ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
+  float(*Bs)[BP] = (float(*)[BP])(un + KS_BYTES);  // KDA: B per row and key channel (phases 0-1)
+  float(*Ts)[TP] = (float(*)[TP])un;             // T (phase 2 on)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -102,6 +113,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   const ET* kg = (const ET*)P.k;
   const ET* qg = (const ET*)P.q;
 
+  // ---- phase 0: loads ---------------------------------------------------------
+  // Q rows of this wave's P tile (row tile 3 - w) go to registers first, so
+  // that their latency overlaps the gate and K loads.
+  const int pr = 3 - wv;
+  const int rq = 16 * pr + c16;
+  V8 qf[KB];
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    V8 x = {};
+    if (rq < len) x = row_slots<ET>(qg + ((t0 + rq) * P.h_qk + hk) * DK + 32 * p, g4);
+    qf[p] = x;
+  }
   // #1 Gate.  Tokens past the sequence end get beta = g = 0: they write
   // nothing and do not decay.
   if (tid < C) {
@@ -122,14 +145,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     }
   }
   if (KDA) {
-    for (int d = tid; d < DK; d += 256) {
-      float run = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < C; ++r) {
-        run += r < len ? P.g[((t0 + r) * P.h_v + h) * DK + d] : 0.f;
-        Bs[r][d] = run;
-      }
+    // per key channel d, NPART runs of C / NPART rows: all loads in flight
+    // at once, a prefix sum in registers, the run offsets added below
+    constexpr int RPP = C / NPART;
+    const int d = tid % DK, part = tid / DK;
+    float gv[RPP];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      const int r = part * RPP + i;
+      gv[i] = r < len ? P.g[((t0 + r) * P.h_v + h) * DK + d] : 0.f;
     }
+#pragma unroll
+    for (int i = 1; i < RPP; ++i) gv[i] += gv[i - 1];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] = gv[i];
+    Btot[part][d] = gv[RPP - 1];
   }
   // K rows of the chunk into LDS (zero rows past the end).
   {
@@ -141,28 +171,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       *(V16*)&Ks[r][cv * PE] = x;
     }
   }
-  // Upper off-diagonal 16x16 blocks of T are zero.
-  for (int idx = tid; idx < 6 * 256; idx += 256) {
-    const int blk = idx >> 8, e = idx & 255;
-    const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-    const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-    const int r = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
-    Ts[r][j] = 0.f;
-    Tt[j][r] = 0.f;
-  }
   __syncthreads();
+  if (KDA && NPART > 1) {
+    constexpr int RPP = C / NPART;
+    const int d = tid % DK, part = tid / DK;
+    float off = 0.f;
+    for (int q2 = 0; q2 < part; ++q2) off += Btot[q2][d];
+    if (part > 0) {
+#pragma unroll
+      for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] += off;
+    }
+    __syncthreads();
+  }
 
+  // ---- phase 1: products and the chunk operands --------------------------------
   // K row fragment of token tile t, inner block p.  KDA: scaled by
   // e^{s (B - B_mid)} per element (s = +1 for the row side of a product,
   // -1 for the column side); the reference row keeps the exponents small.
-  auto kfrag = [&](int t, int p, float s) -> V8 {
+  auto kfrag = [&](int t, int p, float sg) -> V8 {
     const int r = 16 * t + c16;
     V8 x = row_slots<ET>(&Ks[r][32 * p], g4);
     if (KDA) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int d = 32 * p + kmap(g4, j);
-        x[j] = (ET)(to_f(x[j]) * __expf(s * (Bs[r][d] - Bs[MID][d])));
+        x[j] = (ET)(to_f(x[j]) * __expf(sg * (Bs[r][d] - Bs[MID][d])));
       }
     }
     return x;
@@ -192,21 +225,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     }
     // P^T tiles (jt, pr) = K_jt Q_pr^T; tiles jt = 2p, 2p+1 form fragment
     // (pr, p) of P (outer = query token, inner = key token).
-    const int pr = 3 - wv;
-    const int rq = 16 * pr + c16;
-    V8 qf[KB];
+    if (KDA) {
 #pragma unroll
-    for (int p = 0; p < KB; ++p) {
-      V8 x = {};
-      if (rq < len) x = row_slots<ET>(qg + ((t0 + rq) * P.h_qk + hk) * DK + 32 * p, g4);
-      if (KDA) {
+      for (int p = 0; p < KB; ++p)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int d = 32 * p + kmap(g4, j);
-          x[j] = (ET)(to_f(x[j]) * __expf(Bs[rq][d] - Bs[MID][d]));
+          qf[p][j] = (ET)(to_f(qf[p][j]) * __expf(Bs[rq][d] - Bs[MID][d]));
         }
-      }
-      qf[p] = x;
     }
     floatx4 pt[4];
 #pragma unroll
@@ -229,32 +255,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(pt[0], pt[1]);
     pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(pt[2], pt[3]);
   }
-  __syncthreads();
-
-  if (wv == 0) {
-    // #3 Solve, level 0: the four 16x16 diagonal blocks of T by forward
-    // substitution, one column per lane (block lane/16, column lane%16).
-    const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
-      t[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      Ts[o + r][o + cc] = t[r];
-      Tt[o + cc][o + r] = t[r];
-    }
-  } else {
-    // Meanwhile: K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16
-    // key channels of state tile mt in the scan's row order, inner = token
-    // block p), and the KDA operands.
+  // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
+  // of state tile mt in the scan's row order, inner = token block p).
+  if (KT) {
     constexpr int NF = (DK / 16) * 2;
     V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
-    for (int f = wv - 1; P.kt && f < NF; f += 3) {
+    for (int f = wv; f < NF; f += 4) {
       const int mt = f >> 1, p = f & 1;
       const int d = state_row(mt, c16);
       V8 x;
@@ -266,39 +272,64 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       }
       ktg[f * 64 + lane] = x;
     }
-    if (KDA) {
-      // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
-      // with contiguous key channels 32p + 8g + j, the scan's state order
-      V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
-      V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
-      for (int f = wv - 1; f < 4 * KB; f += 3) {
-        const int nt = f / KB, p = f - nt * KB;
-        const int r = 16 * nt + c16;
-        V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
-        V8 xq = {};
-        if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + hk) * DK + 32 * p + 8 * g4);
+  }
+  if (KDA) {
+    // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
+    // with contiguous key channels 32p + 8g + j, the scan's state order
+    V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
+    V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
+    for (int f = wv; f < 4 * KB; f += 4) {
+      const int nt = f / KB, p = f - nt * KB;
+      const int r = 16 * nt + c16;
+      V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
+      V8 xq = {};
+      if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + hk) * DK + 32 * p + 8 * g4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
-          xk[j] = (ET)(to_f(xk[j]) * e);
-          xq[j] = (ET)(to_f(xq[j]) * e);
-        }
-        kwg[f * 64 + lane] = xk;
-        qwg[f * 64 + lane] = xq;
+      for (int j = 0; j < 8; ++j) {
+        const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
+        xk[j] = (ET)(to_f(xk[j]) * e);
+        xq[j] = (ET)(to_f(xq[j]) * e);
       }
-      for (int d = tid - 64; d < DK; d += 192) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
-    } else if (tid >= 64 && tid < 128) {
-      // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
-      // holds e^{b_n} (rows past the end carry the last b)
-      const int r = tid - 64;
-      P.gam[ch * (2 * C) + r] = __expf(bs[r]);
-      P.gam[ch * (2 * C) + C + r] = __expf(bs[C - 1] - bs[r]);
+      kwg[f * 64 + lane] = xk;
+      qwg[f * 64 + lane] = xq;
+    }
+    for (int d = tid; d < DK; d += 256) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
+  } else if (tid < C) {
+    // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
+    // holds e^{b_n} (rows past the end carry the last b)
+    P.gam[ch * (2 * C) + tid] = __expf(bs[tid]);
+    P.gam[ch * (2 * C) + C + tid] = __expf(bs[C - 1] - bs[tid]);
+  }
+  __syncthreads();  // K and the gate table are dead from here; T takes their bytes
+
+  // ---- phase 2: #3 Solve --------------------------------------------------------
+  if (wv == 0) {
+    // level 0: the four 16x16 diagonal blocks of T by forward substitution,
+    // one column per lane (block lane/16, column lane%16)
+    const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
+      t[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
+  } else {
+    // the upper off-diagonal 16x16 blocks of T are zero
+    for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
+      const int blk = idx >> 8, e = idx & 255;
+      const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+      const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      Ts[16 * bi + (e >> 4)][16 * bj + (e & 15)] = 0.f;
     }
   }
   __syncthreads();
 
-  // #3 Solve, level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
-  // (16-wide contractions, zero-padded to the 32-wide fragment).
+  // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (16-wide
+  // contractions, zero-padded to the 32-wide fragment)
   if (wv < 2) {
     const int b0 = 16 * (2 * wv), b1 = b0 + 16;
     V8 a = {}, tb = {}, tl = {};
@@ -306,7 +337,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     for (int j = 0; j < 4; ++j) {
       const int k = 4 * g4 + j;
       a[j] = (ET)As[b1 + c16][b0 + k];
-      tb[j] = (ET)Tt[b0 + c16][b0 + k];
+      tb[j] = (ET)Ts[b0 + k][b0 + c16];
       tl[j] = (ET)Ts[b1 + c16][b1 + k];
     }
     const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
@@ -315,15 +346,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
     const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
-      Tt[b0 + c16][b1 + 4 * g4 + e] = -t[e];
-    }
+    for (int e = 0; e < 4; ++e) Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
   }
   __syncthreads();
 
-  // Level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
-  // and T2 are the finished 32x32 diagonal halves.
+  // level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
+  // and T2 are the finished 32x32 diagonal halves
   if (wv < 2) {
     const int jt = wv;
     floatx4 z[2];
@@ -335,7 +363,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       for (int j = 0; j < 8; ++j) {
         const int k = kmap(g4, j);
         a[j] = (ET)As[r][k];
-        tb[j] = (ET)Tt[16 * jt + c16][k];
+        tb[j] = (ET)Ts[k][16 * jt + c16];
       }
       z[m] = mma(a, tb, zero4());
     }
@@ -348,10 +376,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
       const floatx4 t = mma(tl, zb, zero4());
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
-        Tt[16 * jt + c16][32 + 16 * m + 4 * g4 + e] = -t[e];
-      }
+      for (int e = 0; e < 4; ++e) Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
     }
   }
   __syncthreads();
@@ -376,7 +401,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
 
 template <int DK, bool KDA, typename ET>
 hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  if (nblk > 0) hipLaunchKernelGGL((prep_kernel<DK, KDA, ET>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  if (nblk > 0) {
+    if constexpr (KDA)
+      hipLaunchKernelGGL((prep_kernel<DK, true, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else if (P.kt)
+      hipLaunchKernelGGL((prep_kernel<DK, false, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else
+      hipLaunchKernelGGL((prep_kernel<DK, false, ET, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  }
   return hipGetLastError();
 }
 
