@@ -71,13 +71,16 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
   if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
 }
 
-// One workgroup (4 waves) per (chunk, value head).  KT: write K~^T (the
+// A persistent grid of 256-thread workgroups walks the (chunk, value head)
+// units.  PF: while a workgroup computes one unit, the loads of its next
+// unit are in flight (K, Q, beta, g into registers); KDA goes without, its
+// gate table would take too many registers.  KT: write K~^T (the
 // register-fed scans need it; the LDS-fed one transposes K itself).
 //
 // LDS is reused across phases: K (and KDA's gate table) live until the
 // chunk operands are written, T from the solve on, in the same bytes.
-template <int DK, bool KDA, typename ET, bool KT>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
+template <int DK, bool KDA, typename ET, bool KT, bool PF>
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits) {
   typedef typename VT<ET>::v8 V8;
   typedef typename VT<ET>::v16b V16;
   constexpr int PE = VT<ET>::per16;
@@ -87,6 +90,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   constexpr int MID = C / 2 - 1;                 // KDA: reference row of the factored decay
   constexpr int BP = DK + 4;
   constexpr int NPART = 256 / DK;                // KDA gate: row parts per channel
+  constexpr int RPP = C / NPART;
+  constexpr int KV = DK / PE;                    // 16-byte pieces per K row
+  constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
   constexpr int BS_BYTES = KDA ? C * BP * 4 : 0;
   constexpr int TS_BYTES = C * TP * 4;
@@ -102,314 +108,387 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int64_t bid = blockIdx.x;
-  const int h = (int)(bid / P.nc);
-  const int64_t c = bid - (int64_t)h * P.nc;
-  int seq, len;
-  int64_t t0;
-  chunk_of(P.s, c, seq, t0, len);
-  const int hk = h / P.grp;
-  const int64_t ch = (int64_t)h * P.nc + c;
   const ET* kg = (const ET*)P.k;
   const ET* qg = (const ET*)P.q;
-
-  // ---- phase 0: loads ---------------------------------------------------------
-  // Q rows of this wave's P tile (row tile 3 - w) go to registers first, so
-  // that their latency overlaps the gate and K loads.
-  const int pr = 3 - wv;
+  const int pr = 3 - wv;  // this wave's row tile of P
   const int rq = 16 * pr + c16;
-  V8 qf[KB];
-#pragma unroll
-  for (int p = 0; p < KB; ++p) {
-    V8 x = {};
-    if (rq < len) x = row_slots<ET>(qg + ((t0 + rq) * P.h_qk + hk) * DK + 32 * p, g4);
-    qf[p] = x;
-  }
-  // #1 Gate.  Tokens past the sequence end get beta = g = 0: they write
-  // nothing and do not decay.
-  if (tid < C) {
-    float be = 0.f, gg = 0.f;
-    if (tid < len) {
-      be = P.beta[(t0 + tid) * P.h_v + h];
-      if (!KDA) gg = P.g[(t0 + tid) * P.h_v + h];
-    }
-    betas[tid] = be;
-    if (!KDA) {
-      float x = gg;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      bs[tid] = x;
-    }
-  }
-  if (KDA) {
-    // per key channel d, NPART runs of C / NPART rows: all loads in flight
-    // at once, a prefix sum in registers, the run offsets added below
-    constexpr int RPP = C / NPART;
-    const int d = tid % DK, part = tid / DK;
-    float gv[RPP];
-#pragma unroll
-    for (int i = 0; i < RPP; ++i) {
-      const int r = part * RPP + i;
-      gv[i] = r < len ? P.g[((t0 + r) * P.h_v + h) * DK + d] : 0.f;
-    }
-#pragma unroll
-    for (int i = 1; i < RPP; ++i) gv[i] += gv[i - 1];
-#pragma unroll
-    for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] = gv[i];
-    Btot[part][d] = gv[RPP - 1];
-  }
-  // K rows of the chunk into LDS (zero rows past the end).
-  {
-    constexpr int KV = DK / PE;
-    for (int idx = tid; idx < C * KV; idx += 256) {
-      const int r = idx / KV, cv = idx - r * KV;
-      V16 x = {};
-      if (r < len) x = *(const V16*)(kg + ((t0 + r) * P.h_qk + hk) * DK + cv * PE);
-      *(V16*)&Ks[r][cv * PE] = x;
-    }
-  }
-  __syncthreads();
-  if (KDA && NPART > 1) {
-    constexpr int RPP = C / NPART;
-    const int d = tid % DK, part = tid / DK;
-    float off = 0.f;
-    for (int q2 = 0; q2 < part; ++q2) off += Btot[q2][d];
-    if (part > 0) {
-#pragma unroll
-      for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] += off;
-    }
-    __syncthreads();
-  }
 
-  // ---- phase 1: products and the chunk operands --------------------------------
-  // K row fragment of token tile t, inner block p.  KDA: scaled by
-  // e^{s (B - B_mid)} per element (s = +1 for the row side of a product,
-  // -1 for the column side); the reference row keeps the exponents small.
-  auto kfrag = [&](int t, int p, float sg) -> V8 {
-    const int r = 16 * t + c16;
-    V8 x = row_slots<ET>(&Ks[r][32 * p], g4);
-    if (KDA) {
+  struct Unit {
+    int h, hk, len;
+    int64_t t0, ch;
+  };
+  auto unit_of = [&](int64_t u) {
+    Unit U;
+    U.h = (int)(u / P.nc);
+    const int64_t c = u - (int64_t)U.h * P.nc;
+    int seq;
+    chunk_of(P.s, c, seq, U.t0, U.len);
+    U.hk = U.h / P.grp;
+    U.ch = (int64_t)U.h * P.nc + c;
+    return U;
+  };
+  // a unit's inputs in registers; tokens past the sequence end read as zero
+  // (beta = g = 0: they write nothing and do not decay)
+  V16 kpre[NKV];
+  V8 qpre[KB];
+  float bpre = 0.f, gpre = 0.f;
+  float gvpre[KDA ? RPP : 1];
+  auto load = [&](const Unit& U) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 32 * p + kmap(g4, j);
-        x[j] = (ET)(to_f(x[j]) * __expf(sg * (Bs[r][d] - Bs[MID][d])));
+    for (int i = 0; i < NKV; ++i) {
+      const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
+      V16 x = {};
+      if (r < U.len) x = *(const V16*)(kg + ((U.t0 + r) * P.h_qk + U.hk) * DK + cv * PE);
+      kpre[i] = x;
+    }
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      V8 x = {};
+      if (rq < U.len) x = row_slots<ET>(qg + ((U.t0 + rq) * P.h_qk + U.hk) * DK + 32 * p, g4);
+      qpre[p] = x;
+    }
+    if (tid < C) {
+      bpre = tid < U.len ? P.beta[(U.t0 + tid) * P.h_v + U.h] : 0.f;
+      if (!KDA) gpre = tid < U.len ? P.g[(U.t0 + tid) * P.h_v + U.h] : 0.f;
+    }
+    if (KDA) {
+      const int d = tid % DK, part = tid / DK;
+#pragma unroll
+      for (int i = 0; i < RPP; ++i) {
+        const int r = part * RPP + i;
+        gvpre[i] = r < U.len ? P.g[((U.t0 + r) * P.h_v + U.h) * DK + d] : 0.f;
       }
     }
-    return x;
   };
 
-  // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w), five
-  // 16x16 tiles per wave.
-  {
-    const int rt = wv;
-    V8 ar[KB];
+  // PF: a persistent grid; otherwise one unit per workgroup
+  int64_t u = blockIdx.x;
+  Unit U = unit_of(u);
+  load(U);
+  for (;;) {
+    const int h = U.h, len = U.len;
+    const int64_t t0 = U.t0, ch = U.ch;
+
+    // ---- phase 0: stage the unit, start loading the next one -------------------
+    V8 qf[KB];
 #pragma unroll
-    for (int p = 0; p < KB; ++p) ar[p] = kfrag(rt, p, 1.f);
-    for (int it = 0; it <= rt; ++it) {
-      floatx4 acc = zero4();
+    for (int p = 0; p < KB; ++p) qf[p] = qpre[p];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) acc = mma(ar[p], kfrag(it, p, -1.f), acc);
+    for (int i = 0; i < NKV; ++i) {
+      const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
+      *(V16*)&Ks[r][cv * PE] = kpre[i];
+    }
+    // #1 Gate: in-chunk prefix sums of the log-decay
+    if (tid < C) {
+      betas[tid] = bpre;
+      if (!KDA) {
+        float x = gpre;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, i = 16 * it + c16;
-        float a = 0.f;
-        if (i < r) {
-          a = betas[r] * acc[e];
-          if (!KDA) a *= __expf(bs[r] - bs[i]);
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off);
+          if (lane >= off) x += y;
         }
-        As[r][i] = a;
+        bs[tid] = x;
       }
     }
-    // P^T tiles (jt, pr) = K_jt Q_pr^T; tiles jt = 2p, 2p+1 form fragment
-    // (pr, p) of P (outer = query token, inner = key token).
     if (KDA) {
+      // per key channel d, NPART runs of RPP rows: a prefix sum in registers,
+      // the run offsets added after the barrier
+      const int d = tid % DK, part = tid / DK;
+      float run = 0.f;
 #pragma unroll
-      for (int p = 0; p < KB; ++p)
+      for (int i = 0; i < RPP; ++i) {
+        run += gvpre[i];
+        Bs[part * RPP + i][d] = run;
+      }
+      Btot[part][d] = run;
+    }
+    const int64_t unext = u + gridDim.x;
+    Unit Un = U;
+    if (unext < nunits) {
+      Un = unit_of(unext);
+      if (PF) load(Un);
+    }
+    __syncthreads();
+    if (KDA && NPART > 1) {
+      const int d = tid % DK, part = tid / DK;
+      float off = 0.f;
+      for (int q2 = 0; q2 < part; ++q2) off += Btot[q2][d];
+      if (part > 0) {
+#pragma unroll
+        for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] += off;
+      }
+      __syncthreads();
+    }
+
+    // ---- phase 1: products and the chunk operands --------------------------------
+    // K row fragment of token tile t, inner block p.  KDA: scaled by
+    // e^{s (B - B_mid)} per element (s = +1 for the row side of a product,
+    // -1 for the column side); the reference row keeps the exponents small.
+    auto kfrag = [&](int t, int p, float sg) -> V8 {
+      const int r = 16 * t + c16;
+      V8 x = row_slots<ET>(&Ks[r][32 * p], g4);
+      if (KDA) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int d = 32 * p + kmap(g4, j);
-          qf[p][j] = (ET)(to_f(qf[p][j]) * __expf(Bs[rq][d] - Bs[MID][d]));
+          x[j] = (ET)(to_f(x[j]) * __expf(sg * (Bs[r][d] - Bs[MID][d])));
         }
-    }
-    floatx4 pt[4];
+      }
+      return x;
+    };
+
+    // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w).  Every
+    // wave multiplies its row tile with all four column tiles (the products
+    // past the diagonal are dropped), so all K fragments are read from LDS
+    // at once and no branch splits the reads from the products.
+    {
+      const int rt = wv;
+      V8 ar[KB], kc[4][KB];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      pt[jt] = zero4();
-      if (jt <= pr) {
-        floatx4 acc = zero4();
+      for (int p = 0; p < KB; ++p) ar[p] = kfrag(rt, p, 1.f);
 #pragma unroll
-        for (int p = 0; p < KB; ++p) acc = mma(kfrag(jt, p, -1.f), qf[p], acc);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) kc[t][p] = kfrag(t, p, -1.f);
+      if (KDA) {
+#pragma unroll
+        for (int p = 0; p < KB; ++p)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int d = 32 * p + kmap(g4, j);
+            qf[p][j] = (ET)(to_f(qf[p][j]) * __expf(Bs[rq][d] - Bs[MID][d]));
+          }
+      }
+      floatx4 acc[4], pt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] = zero4();
+        pt[t] = zero4();
+      }
+#pragma unroll
+      for (int p = 0; p < KB; ++p)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[t] = mma(ar[p], kc[t][p], acc[t]);  // A tile (rt, t)
+          pt[t] = mma(kc[t][p], qf[p], pt[t]);    // P^T tile (t, pr) = K_t Q_pr^T
+        }
+      // A: strictly lower part, scaled by beta_r (and e^{b_r - b_i} for GDN);
+      // tiles past the diagonal are never read
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t > rt) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = 16 * jt + 4 * g4 + e;
+          const int r = 16 * rt + 4 * g4 + e, i = 16 * t + c16;
           float x = 0.f;
-          if (j <= rq) x = KDA ? acc[e] : acc[e] * __expf(bs[rq] - bs[j]);
-          pt[jt][e] = x;
+          if (i < r) {
+            x = betas[r] * acc[t][e];
+            if (!KDA) x *= __expf(bs[r] - bs[i]);
+          }
+          As[r][i] = x;
         }
       }
-    }
-    V8* pg = (V8*)P.pm + ch * (8 * 64);
-    pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(pt[0], pt[1]);
-    pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(pt[2], pt[3]);
-  }
-  // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
-  // of state tile mt in the scan's row order, inner = token block p).
-  if (KT) {
-    constexpr int NF = (DK / 16) * 2;
-    V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
-    for (int f = wv; f < NF; f += 4) {
-      const int mt = f >> 1, p = f & 1;
-      const int d = state_row(mt, c16);
-      V8 x;
+      // P: tiles jt = 2p, 2p+1 of P^T form fragment (pr, p) of P (outer =
+      // query token, inner = key token); inclusive lower part only
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = 32 * p + kmap(g4, j);
-        const float sc = KDA ? __expf(Bs[C - 1][d] - Bs[i][d]) : __expf(bs[C - 1] - bs[i]);
-        x[j] = (ET)(to_f(Ks[i][d]) * sc);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * t + 4 * g4 + e;
+          float x = 0.f;
+          if (j <= rq) x = KDA ? pt[t][e] : pt[t][e] * __expf(bs[rq] - bs[j]);
+          pt[t][e] = x;
+        }
+      V8* pg = (V8*)P.pm + ch * (8 * 64);
+      pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(pt[0], pt[1]);
+      pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(pt[2], pt[3]);
+    }
+    // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
+    // of state tile mt in the scan's row order, inner = token block p).
+    if (KT) {
+      constexpr int NF = (DK / 16) * 2;
+      V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
+      for (int f = wv; f < NF; f += 4) {
+        const int mt = f >> 1, p = f & 1;
+        const int d = state_row(mt, c16);
+        V8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 32 * p + kmap(g4, j);
+          const float sc = KDA ? __expf(Bs[C - 1][d] - Bs[i][d]) : __expf(bs[C - 1] - bs[i]);
+          x[j] = (ET)(to_f(Ks[i][d]) * sc);
+        }
+        ktg[f * 64 + lane] = x;
       }
-      ktg[f * 64 + lane] = x;
     }
-  }
-  if (KDA) {
-    // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
-    // with contiguous key channels 32p + 8g + j, the scan's state order
-    V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
-    V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
-    for (int f = wv; f < 4 * KB; f += 4) {
-      const int nt = f / KB, p = f - nt * KB;
-      const int r = 16 * nt + c16;
-      V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
-      V8 xq = {};
-      if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + hk) * DK + 32 * p + 8 * g4);
+    if (KDA) {
+      // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
+      // with contiguous key channels 32p + 8g + j, the scan's state order
+      V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
+      V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
+      for (int f = wv; f < 4 * KB; f += 4) {
+        const int nt = f / KB, p = f - nt * KB;
+        const int r = 16 * nt + c16;
+        V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
+        V8 xq = {};
+        if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + U.hk) * DK + 32 * p + 8 * g4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
-        xk[j] = (ET)(to_f(xk[j]) * e);
-        xq[j] = (ET)(to_f(xq[j]) * e);
+        for (int j = 0; j < 8; ++j) {
+          const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
+          xk[j] = (ET)(to_f(xk[j]) * e);
+          xq[j] = (ET)(to_f(xq[j]) * e);
+        }
+        kwg[f * 64 + lane] = xk;
+        qwg[f * 64 + lane] = xq;
       }
-      kwg[f * 64 + lane] = xk;
-      qwg[f * 64 + lane] = xq;
+      for (int d = tid; d < DK; d += 256) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
+    } else if (tid < C) {
+      // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
+      // holds e^{b_n} (rows past the end carry the last b)
+      P.gam[ch * (2 * C) + tid] = __expf(bs[tid]);
+      P.gam[ch * (2 * C) + C + tid] = __expf(bs[C - 1] - bs[tid]);
     }
-    for (int d = tid; d < DK; d += 256) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
-  } else if (tid < C) {
-    // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
-    // holds e^{b_n} (rows past the end carry the last b)
-    P.gam[ch * (2 * C) + tid] = __expf(bs[tid]);
-    P.gam[ch * (2 * C) + C + tid] = __expf(bs[C - 1] - bs[tid]);
-  }
-  __syncthreads();  // K and the gate table are dead from here; T takes their bytes
+    __syncthreads();  // K and the gate table are dead from here; T takes their bytes
 
-  // ---- phase 2: #3 Solve --------------------------------------------------------
-  if (wv == 0) {
-    // level 0: the four 16x16 diagonal blocks of T by forward substitution,
-    // one column per lane (block lane/16, column lane%16)
-    const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
-    float t[16];
+    // ---- phase 2: #3 Solve --------------------------------------------------------
+    if (wv == 0) {
+      // level 0: the four 16x16 diagonal blocks of T by forward substitution,
+      // one column per lane (block lane/16, column lane%16)
+      const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
+      float t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == cc) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
-      t[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
-  } else {
-    // the upper off-diagonal 16x16 blocks of T are zero
-    for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
-      const int blk = idx >> 8, e = idx & 255;
-      const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-      const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-      Ts[16 * bi + (e >> 4)][16 * bj + (e & 15)] = 0.f;
-    }
-  }
-  __syncthreads();
-
-  // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (16-wide
-  // contractions, zero-padded to the 32-wide fragment)
-  if (wv < 2) {
-    const int b0 = 16 * (2 * wv), b1 = b0 + 16;
-    V8 a = {}, tb = {}, tl = {};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 4 * g4 + j;
-      a[j] = (ET)As[b1 + c16][b0 + k];
-      tb[j] = (ET)Ts[b0 + k][b0 + c16];
-      tl[j] = (ET)Ts[b1 + c16][b1 + k];
-    }
-    const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
-    V8 yb = {};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
-    const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
-  }
-  __syncthreads();
-
-  // level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
-  // and T2 are the finished 32x32 diagonal halves
-  if (wv < 2) {
-    const int jt = wv;
-    floatx4 z[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = 32 + 16 * m + c16;
-      V8 a, tb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = kmap(g4, j);
-        a[j] = (ET)As[r][k];
-        tb[j] = (ET)Ts[k][16 * jt + c16];
+        for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
+        t[r] = acc;
       }
-      z[m] = mma(a, tb, zero4());
-    }
-    const V8 zb = pack<ET>(z[0], z[1]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = 32 + 16 * m + c16;
-      V8 tl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
-      const floatx4 t = mma(tl, zb, zero4());
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
-    }
-  }
-  __syncthreads();
-
-  // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
-  // block p), eight per (chunk, head); the ones above the diagonal are zero.
-  {
-    const int nt = wv;
-    V8* tg = (V8*)P.tb + ch * (8 * 64);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      V8 x;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = 32 * p + kmap(g4, j);
-        x[j] = (ET)(Ts[16 * nt + c16][i] * betas[i]);
+      for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
+    } else {
+      // the upper off-diagonal 16x16 blocks of T are zero
+      for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        Ts[16 * bi + (e >> 4)][16 * bj + (e & 15)] = 0.f;
       }
-      tg[(nt * 2 + p) * 64 + lane] = x;
     }
+    __syncthreads();
+
+    // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (16-wide
+    // contractions, zero-padded to the 32-wide fragment)
+    if (wv < 2) {
+      const int b0 = 16 * (2 * wv), b1 = b0 + 16;
+      V8 a = {}, tb = {}, tl = {};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * g4 + j;
+        a[j] = (ET)As[b1 + c16][b0 + k];
+        tb[j] = (ET)Ts[b0 + k][b0 + c16];
+        tl[j] = (ET)Ts[b1 + c16][b1 + k];
+      }
+      const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
+      V8 yb = {};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
+      const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
+    }
+    __syncthreads();
+
+    // level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
+    // and T2 are the finished 32x32 diagonal halves
+    if (wv < 2) {
+      const int jt = wv;
+      floatx4 z[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r = 32 + 16 * m + c16;
+        V8 a, tb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = kmap(g4, j);
+          a[j] = (ET)As[r][k];
+          tb[j] = (ET)Ts[k][16 * jt + c16];
+        }
+        z[m] = mma(a, tb, zero4());
+      }
+      const V8 zb = pack<ET>(z[0], z[1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r = 32 + 16 * m + c16;
+        V8 tl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
+        const floatx4 t = mma(tl, zb, zero4());
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
+      }
+    }
+    __syncthreads();
+
+    // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
+    // block p), eight per (chunk, head); the ones above the diagonal are zero.
+    {
+      const int nt = wv;
+      V8* tg = (V8*)P.tb + ch * (8 * 64);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        V8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 32 * p + kmap(g4, j);
+          x[j] = (ET)(Ts[16 * nt + c16][i] * betas[i]);
+        }
+        tg[(nt * 2 + p) * 64 + lane] = x;
+      }
+    }
+    if (!PF) break;
+    u += gridDim.x;
+    if (u >= nunits) break;
+    __syncthreads();  // T is read; the next unit's K takes its bytes
+    U = Un;
   }
+}
+
+// Workgroups of `kern` that fit on the chip at once (cached per device).
+template <typename K>
+static int64_t resident_groups(K kern, int lds_bytes) {
+  static int64_t cached[16] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds_bytes) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    cached[dev] = (int64_t)per_cu * cus;
+  }
+  return cached[dev];
+}
+
+template <int DK, bool KDA, typename ET, bool KT>
+static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
+  auto kern = prep_kernel<DK, KDA, ET, KT, !KDA>;
+  const int64_t fit = KDA ? nblk : resident_groups(kern, 0);
+  const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, nblk);
+  return hipGetLastError();
 }
 
 template <int DK, bool KDA, typename ET>
 hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  if (nblk > 0) {
-    if constexpr (KDA)
-      hipLaunchKernelGGL((prep_kernel<DK, true, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-    else if (P.kt)
-      hipLaunchKernelGGL((prep_kernel<DK, false, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-    else
-      hipLaunchKernelGGL((prep_kernel<DK, false, ET, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-  }
-  return hipGetLastError();
+  if (nblk <= 0) return hipGetLastError();
+  if constexpr (KDA)
+    return launch_prep_v<DK, true, ET, true>(P, nblk, st);
+  else if (P.kt)
+    return launch_prep_v<DK, false, ET, true>(P, nblk, st);
+  else
+    return launch_prep_v<DK, false, ET, false>(P, nblk, st);
 }
 
 hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st) {
