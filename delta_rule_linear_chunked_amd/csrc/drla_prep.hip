@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   Unit U = unit_of(u);
   load(U);
   for (;;) {
-    const int h = U.h, len = U.len;
+    const int len = U.len;
     const int64_t t0 = U.t0, ch = U.ch;
 
     // ---- phase 0: stage the unit, start loading the next one -------------------
