@@ -12,9 +12,9 @@
 //                         S  <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
 //   waves 1,2 (loaders) copy the operands of chunk t+2 (K and Q rows, Tb,
 //                       P, this block's 16 columns of V, the decay factors)
-//                       into a three-slot LDS ring with LDS-direct loads,
-//                       and touch chunk t+PF so that it sits in L2 when its
-//                       copy is issued
+//                       into a three-slot LDS ring with LDS-direct loads;
+//                       wave 1 also touches this block's share of chunk
+//                       t+PF so that it sits in L2 when its copy is issued
 //   wave 3    (output)  O = diag(e^b) Q S + P V' for the chunk, and its store
 //
 // K^T is never stored: the state wave reads K rows from LDS with the
@@ -25,7 +25,7 @@
 // the P V' term of a chunk one chunk later, keeping P in registers.
 //
 // Only the loader waves issue loads, so their wait counts are exact: every
-// chunk they issue exactly kIssued copies and kTouched touches.
+// chunk each issues exactly kIssued copies, and wave 1 kTouched touches.
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int NCH = DK / 8;                 // 16-byte chunks per row
   constexpr int RPI = 1024 / (DK * 2);        // rows per 1 KiB copy
   constexpr int kIssued = C / RPI + 6 + 2;    // copies per loader wave and chunk
-  constexpr int kTouched = (DK * 2 > 128 ? 2 : 1) + 2;  // touches per loader wave and chunk
+  constexpr int kTouched = 2;                 // touches per chunk (loader wave 1)
   __shared__ LdsSlot<DK> slot[NS];
   __shared__ bf16x8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
   __shared__ bf16x8 vbuf[2][2][64];   // V' of the last two chunks, A fragments (inner = token)
@@ -182,16 +182,34 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       lds_dma16(vr, voff + 32 * vstride, 0, &sl.v[32][0]);
     }
   };
-  // touch chunk i's operands, one 128-byte line per lane
-  auto prefetch = [&](int i) {
-    const rsrc_t rr = row_rsrc(i);
-    lds_dma4(rr, (uint32_t)lane * kstride, 0, touch);
-    if (DK * 2 > 128) lds_dma4(rr, (uint32_t)lane * kstride + 128, 0, touch);
-    lds_dma4(frag_rsrc(i), 128u * lane, 0, touch);
-    if (w == 1)
+  // L2 touches: the eight (four) column blocks of a head share their
+  // XCD's L2, so each touches its own share of a chunk's 128-byte lines --
+  // K rows, Q rows, Tb, P, the head's V rows, the decay factors -- two
+  // touch loads per chunk, issued by loader wave 1 only.
+  constexpr int KL = DK * 2 / 128, VL = DV * 2 / 128;  // lines per K/Q row, per V row
+  constexpr int NG = 2 * KL + 2 + VL + 1;                // line groups of a chunk
+  static_assert(NG <= 2 * NB, "two touch loads per column block cover a chunk");
+  auto touch_group = [&](int gi, int i) {
+    const int64_t tc = ts + (int64_t)C * i;
+    const uint32_t lrow = (chunk_len(i) - 1);
+    if (gi < 2 * KL) {  // K or Q rows, line gi % KL
+      const bf16* src = (gi < KL ? kg : qg) + (tc * P.h_qk + hk) * DK;
+      lds_dma4(make_rsrc(src, lrow * kstride + DK * 2), (uint32_t)lane * kstride + 128u * (uint32_t)(gi % KL), 0, touch);
+    } else if (gi < 2 * KL + 2) {  // Tb or P fragments
+      const int64_t ch = (int64_t)h * P.nc + c0 + i;
+      const bf16x8* fr = (const bf16x8*)(gi == 2 * KL ? P.tb : P.pm) + ch * (8 * 64);
+      lds_dma4(make_rsrc(fr, 8 * 1024), 128u * lane, 0, touch);
+    } else if (gi < 2 * KL + 2 + VL) {  // the head's V rows, line gi - 2 KL - 2
+      const bf16* src = vg + (tc * P.h_v + h) * DV;
+      lds_dma4(make_rsrc(src, lrow * vstride + DV * 2), (uint32_t)lane * vstride + 128u * (uint32_t)(gi - 2 * KL - 2), 0,
+               touch);
+    } else {  // decay factors
       lds_dma4(gam_rsrc(i), 128u * (lane & 3), 0, touch);
-    else
-      lds_dma4(v_rsrc(i), (uint32_t)lane * vstride, 0, touch);
+    }
+  };
+  auto prefetch = [&](int i) {
+    touch_group(nb, i);
+    touch_group(nb + NB < NG ? nb + NB : NG - 1, i);
   };
 
   // ---- prologue ------------------------------------------------------------
@@ -211,12 +229,15 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   } else if (w < 3 && n > 0) {
     issue(0);
     issue(n > 1 ? 1 : 0);
-    // touches for chunks 2..3 (the loop touches chunk t + PF); at most 63
-    // operations can be outstanding, so the prologue touches fewer
+    if (w == 1) {
+      // touches for chunks 2..5 (the loop touches chunk t + PF)
 #pragma unroll
-    for (int i = 2; i < 4; ++i) prefetch(i < n ? i : n - 1);
-    // chunk 0 has landed once at most the later copies and touches are pending
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + 2 * kTouched));
+      for (int i = 2; i < PF; ++i) prefetch(i < n ? i : n - 1);
+      // chunk 0 has landed once at most the later copies and touches are pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + (PF - 2) * kTouched));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
+    }
   }
   lds_barrier();
 
@@ -243,11 +264,12 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 
   int64_t t0prev = 0;  // output wave: first token of the chunk in o
 
-  for (int t = 0; t < n; ++t) {
-    const LdsSlot<DK>& sl = slot[t % NS];
-    const int64_t t0 = ts + (int64_t)C * t;
-    const int64_t ch = (int64_t)h * P.nc + c0 + t;
-    if (w == 0) {
+  // Each role runs its own loop (one barrier per chunk in each), so that
+  // the registers one role keeps across chunks are free in the others.
+  if (w == 0) {
+    for (int t = 0; t < n; ++t) {
+      const LdsSlot<DK>& sl = slot[t % NS];
+      const int64_t ch = (int64_t)h * P.nc + c0 + t;
       // ---------------- state wave ----------------
       // Nothing of this wave is in flight here; saying so lets the compiler
       // count the LDS reads below exactly (it cannot see through the
@@ -346,7 +368,19 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
         sbuf[(t + 1) & 1][p][lane] = sf[p];
       }
-    } else if (w == 3) {
+      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+    }
+    if (P.ht) {
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          P.ht[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = S[mt][e];
+    }
+  } else if (w == 3) {
+    for (int t = 0; t < n; ++t) {
+      const LdsSlot<DK>& sl = slot[t % NS];
+      const int64_t t0 = ts + (int64_t)C * t;
       // ---------------- output wave ----------------
       // finish the previous chunk: its V' was published at the last barrier
       if (t > 0) finish_output(t0prev, t - 1);
@@ -374,25 +408,25 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
       t0prev = t0;
-    } else {
+      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+    }
+    if (n > 0) finish_output(t0prev, n - 1);
+  } else {
+    for (int t = 0; t < n; ++t) {
       // ---------------- loader waves ----------------
       issue(t + 2 < n ? t + 2 : n - 1);
-      prefetch(t + PF < n ? t + PF : n - 1);
-      // chunk t+1's copy has landed; the touches issued after it (chunks
-      // t+5 and t+6, often HBM misses) and chunk t+2's copy may be pending
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + 2 * kTouched));
+      // chunk t+1's copy has landed; chunk t+2's copy and the touches issued
+      // after t+1's copy (chunks t+5 and t+6, often HBM misses) may be pending
+      if (w == 1) {
+        prefetch(t + PF < n ? t + PF : n - 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued + 2 * kTouched));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
+      }
+      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
     }
-    lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
-  if (w == 3 && n > 0) finish_output(t0prev, n - 1);
-  if (w == 0 && P.ht) {
-#pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        P.ht[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = S[mt][e];
-  }
-  if (w == 1 || w == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 template <int DK, int DV>
