@@ -304,36 +304,47 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
       __builtin_amdgcn_sched_barrier(0);
-      // X = K S for the four token tiles: lane holds [16 nt + 4g + e][c]
+      // X = K S for the four token tiles (lane holds [16 nt + 4g + e][c]),
+      // interleaved with work that does not depend on it: the K^T reads of
+      // the update (outer = key channel state_row(mt, c), inner = token;
+      // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
+      // upper half), channels state_row(mt, 4q) .. +3), V to floats and the
+      // decay of the state.  Step i issues one product, two reads and three
+      // vector operations.
       floatx4 x[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) x[nt] = zero4();
-#pragma unroll
-      for (int p = 0; p < KB; ++p)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) x[nt] = mma(kr[p][nt], sf[p], x[nt]);
-      __builtin_amdgcn_sched_barrier(0);
-      // K^T fragments (outer = key channel state_row(mt, c), inner = token):
-      // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
-      // upper half), channels state_row(mt, 4q) .. +3
       bf16x4 kt[2][KT][2];
+      floatx4 vfl[4];
+      static_assert(2 * 2 * KT == 2 * 4 * KB, "two K^T reads per product");
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int r0 = 32 * p + 4 * g4 + (c16 >> 2);
+      for (int i = 0; i < 4 * KB; ++i) {
+        x[i % 4] = mma(kr[i / 4][i % 4], sf[i / 4], x[i % 4]);
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt) {
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
+          const int r0 = 32 * p + 4 * g4 + (c16 >> 2) + 16 * hf;
           const int d = state_row(mt, 4 * (c16 & 3));
-          kt[p][mt][0] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
-          kt[p][mt][1] = ds_read_tr(sl.k + swz<DK>(r0 + 16, d >> 3) + 2 * (d & 7));
+          kt[p][mt][hf] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
         }
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj) {
+          const int j = 3 * i + jj;
+          if (j < 4 * KT) {
+            S[j / 4][j % 4] *= gam;
+          } else if (j < 4 * KT + 16) {
+            const int q2 = j - 4 * KT;
+            vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
       // R = V - diag(e^b) X, as B fragments (inner = token)
       floatx4 rr[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[nt][e] = to_f(vv[nt][e]) - ebv[nt][e] * x[nt][e];
+        for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - ebv[nt][e] * x[nt][e];
       const bf16x8 rf0 = pack<bf16>(rr[0], rr[1]), rf1 = pack<bf16>(rr[2], rr[3]);
       // V' = Tb R
       floatx4 vt[4];
@@ -356,8 +367,6 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * env[nt];
       const bf16x8 vs0 = pack<bf16>(vs[0], vs[1]), vs1 = pack<bf16>(vs[2], vs[3]);
-#pragma unroll
-      for (int mt = 0; mt < KT; ++mt) S[mt] *= gam;
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
