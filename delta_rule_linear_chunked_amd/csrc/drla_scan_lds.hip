@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // the update (outer = key channel state_row(mt, c), inner = token;
       // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
       // upper half), channels state_row(mt, 4q) .. +3), V to floats and the
-      // decay of the state.  Step i issues one product, two reads and three
+      // decay of the state.  Step i issues one product, two reads and NV
       // vector operations.
       floatx4 x[4];
 #pragma unroll
@@ -317,6 +317,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       bf16x4 kt[2][KT][2];
       floatx4 vfl[4];
       static_assert(2 * 2 * KT == 2 * 4 * KB, "two K^T reads per product");
+      constexpr int NV = (4 * KT + 16 + 4 * KB - 1) / (4 * KB);  // vector operations per product
 #pragma unroll
       for (int i = 0; i < 4 * KB; ++i) {
         x[i % 4] = mma(kr[i / 4][i % 4], sf[i / 4], x[i % 4]);
@@ -328,8 +329,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
           kt[p][mt][hf] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
         }
 #pragma unroll
-        for (int jj = 0; jj < 3; ++jj) {
-          const int j = 3 * i + jj;
+        for (int jj = 0; jj < NV; ++jj) {
+          const int j = NV * i + jj;
           if (j < 4 * KT) {
             S[j / 4][j % 4] *= gam;
           } else if (j < 4 * KT + 16) {
