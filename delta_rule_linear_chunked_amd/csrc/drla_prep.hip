@@ -73,11 +73,17 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
 
 // A persistent grid of 256-thread workgroups walks the (chunk, value head)
 // units.  PF: while a workgroup computes one unit, the loads of its next
-// unit are in flight (K, Q, beta, g into registers); KDA goes without, its
-// gate table would take too many registers.  KT: write K~^T (the
+// unit are in flight (K, Q, beta, g into registers).  KT: write K~^T (the
 // register-fed scans need it; the LDS-fed one transposes K itself).
 //
-// LDS is reused across phases: K (and KDA's gate table) live until the
+// KDA: every thread owns one key channel d and C / NPART rows of the chunk;
+// it forms the cumulative gate B of its rows in registers and scales its
+// elements of K and Q once -- K e^{B - B_m}, K e^{B_m - B}, Q e^{B - B_m},
+// with the reference B_m = B of row C/2 - 1 keeping the exponents small --
+// so the products and the chunk operands only multiply by per-channel
+// constants (e^{B_m}, e^{B_n - B_m}).
+//
+// LDS is reused across phases: K (and KDA's scaled tiles) live until the
 // chunk operands are written, T from the solve on, in the same bytes.
 template <int DK, bool KDA, typename ET, bool KT, bool PF>
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits) {
@@ -87,23 +93,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   constexpr int KB = DK / 32;
   constexpr int KP = DK + 16 / (int)sizeof(ET);  // padded row: 16-byte aligned, 4-bank skew
   constexpr int TP = C + 4;
-  constexpr int MID = C / 2 - 1;                 // KDA: reference row of the factored decay
-  constexpr int BP = DK + 4;
   constexpr int NPART = 256 / DK;                // KDA gate: row parts per channel
   constexpr int RPP = C / NPART;
   constexpr int KV = DK / PE;                    // 16-byte pieces per K row
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
-  constexpr int BS_BYTES = KDA ? C * BP * 4 : 0;
   constexpr int TS_BYTES = C * TP * 4;
-  constexpr int U_BYTES = KS_BYTES + BS_BYTES > TS_BYTES ? KS_BYTES + BS_BYTES : TS_BYTES;
+  constexpr int NT = KDA ? 3 : 1;                // K-sized tiles: KDA K e^{B-B_m}, K e^{B_m-B}, Q e^{B-B_m}
+  constexpr int U_BYTES = NT * KS_BYTES > TS_BYTES ? NT * KS_BYTES : TS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
   __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
   __shared__ float bs[C];
   __shared__ float betas[C];
   __shared__ float Btot[KDA ? NPART : 1][KDA ? DK : 1];
-  ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
-  float(*Bs)[BP] = (float(*)[BP])(un + KS_BYTES);  // KDA: B per row and key channel (phases 0-1)
+  __shared__ float cnl[KDA ? DK : 1];            // KDA: e^{B_n - B_m} per key channel
+  __shared__ float ebm[KDA ? DK : 1];            // KDA: e^{B_m} per key channel
+  ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows; KDA: K e^{B - B_m} (phases 0-1)
+  ET(*Kn)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: K e^{B_m - B}
+  ET(*Qs)[KP] = (ET(*)[KP])(un + 2 * KS_BYTES);  // KDA: Q rows, then Q e^{B - B_m}
   float(*Ts)[TP] = (float(*)[TP])un;             // T (phase 2 on)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -130,7 +137,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   // a unit's inputs in registers; tokens past the sequence end read as zero
   // (beta = g = 0: they write nothing and do not decay)
   V16 kpre[NKV];
-  V8 qpre[KB];
+  V16 qvpre[KDA ? NKV : 1];  // KDA: Q rows, staged like K
+  V8 qpre[KDA ? 1 : KB];     // GDN: Q fragments of this wave's P tile
   float bpre = 0.f, gpre = 0.f;
   float gvpre[KDA ? RPP : 1];
   auto load = [&](const Unit& U) {
@@ -141,11 +149,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       if (r < U.len) x = *(const V16*)(kg + ((U.t0 + r) * P.h_qk + U.hk) * DK + cv * PE);
       kpre[i] = x;
     }
+    if (KDA) {
 #pragma unroll
-    for (int p = 0; p < KB; ++p) {
-      V8 x = {};
-      if (rq < U.len) x = row_slots<ET>(qg + ((U.t0 + rq) * P.h_qk + U.hk) * DK + 32 * p, g4);
-      qpre[p] = x;
+      for (int i = 0; i < NKV; ++i) {
+        const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
+        V16 x = {};
+        if (r < U.len) x = *(const V16*)(qg + ((U.t0 + r) * P.h_qk + U.hk) * DK + cv * PE);
+        qvpre[i] = x;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        V8 x = {};
+        if (rq < U.len) x = row_slots<ET>(qg + ((U.t0 + rq) * P.h_qk + U.hk) * DK + 32 * p, g4);
+        qpre[p] = x;
+      }
     }
     if (tid < C) {
       bpre = tid < U.len ? P.beta[(U.t0 + tid) * P.h_v + U.h] : 0.f;
@@ -166,17 +184,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   Unit U = unit_of(u);
   load(U);
   for (;;) {
-    const int len = U.len;
-    const int64_t t0 = U.t0, ch = U.ch;
+    [[maybe_unused]] const int len = U.len;
+    [[maybe_unused]] const int64_t t0 = U.t0;
+    const int64_t ch = U.ch;
 
     // ---- phase 0: stage the unit, start loading the next one -------------------
     V8 qf[KB];
+    if (!KDA) {
 #pragma unroll
-    for (int p = 0; p < KB; ++p) qf[p] = qpre[p];
+      for (int p = 0; p < KB; ++p) qf[p] = qpre[KDA ? 0 : p];
+    }
 #pragma unroll
     for (int i = 0; i < NKV; ++i) {
       const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
       *(V16*)&Ks[r][cv * PE] = kpre[i];
+      if (KDA) *(V16*)&Qs[r][cv * PE] = qvpre[i];
     }
     // #1 Gate: in-chunk prefix sums of the log-decay
     if (tid < C) {
@@ -191,15 +213,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         bs[tid] = x;
       }
     }
+    // KDA: per key channel d, NPART runs of RPP rows; prefix sums in
+    // registers, the run offsets added after the barrier
+    float bv[KDA ? RPP : 1];
     if (KDA) {
-      // per key channel d, NPART runs of RPP rows: a prefix sum in registers,
-      // the run offsets added after the barrier
       const int d = tid % DK, part = tid / DK;
       float run = 0.f;
 #pragma unroll
       for (int i = 0; i < RPP; ++i) {
         run += gvpre[i];
-        Bs[part * RPP + i][d] = run;
+        bv[i] = run;
       }
       Btot[part][d] = run;
     }
@@ -210,32 +233,43 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       if (PF) load(Un);
     }
     __syncthreads();
-    if (KDA && NPART > 1) {
+    if (KDA) {
+      // B of this thread's rows, the reference B_m (row C/2 - 1: the end of
+      // the first NPART/2 runs) and B_n; then the scaled elements
       const int d = tid % DK, part = tid / DK;
-      float off = 0.f;
-      for (int q2 = 0; q2 < part; ++q2) off += Btot[q2][d];
-      if (part > 0) {
+      float off = 0.f, bm = 0.f, bn = 0.f;
 #pragma unroll
-        for (int i = 0; i < RPP; ++i) Bs[part * RPP + i][d] += off;
+      for (int q2 = 0; q2 < NPART; ++q2) {
+        const float tq = Btot[q2][d];
+        if (q2 < part) off += tq;
+        if (q2 < NPART / 2) bm += tq;
+        bn += tq;
+      }
+#pragma unroll
+      for (int i = 0; i < RPP; ++i) {
+        const int r = part * RPP + i;
+        const float x = bv[i] + off - bm;
+        const float e = __expf(x), ei = __expf(-x);
+        const float kv = to_f(Ks[r][d]);
+        Ks[r][d] = (ET)(kv * e);
+        Kn[r][d] = (ET)(kv * ei);
+        Qs[r][d] = (ET)(to_f(Qs[r][d]) * e);
+      }
+      if (part == 0) {
+        cnl[d] = __expf(bn - bm);
+        ebm[d] = __expf(bm);
+        P.gam[ch * DK + d] = __expf(bn);
       }
       __syncthreads();
     }
 
     // ---- phase 1: products and the chunk operands --------------------------------
-    // K row fragment of token tile t, inner block p.  KDA: scaled by
-    // e^{s (B - B_mid)} per element (s = +1 for the row side of a product,
-    // -1 for the column side); the reference row keeps the exponents small.
+    // K row fragment of token tile t, inner block p.  KDA: K e^{B - B_m}
+    // for the row side of a product (sg > 0), K e^{B_m - B} for the column
+    // side.
     auto kfrag = [&](int t, int p, float sg) -> V8 {
       const int r = 16 * t + c16;
-      V8 x = row_slots<ET>(&Ks[r][32 * p], g4);
-      if (KDA) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int d = 32 * p + kmap(g4, j);
-          x[j] = (ET)(to_f(x[j]) * __expf(sg * (Bs[r][d] - Bs[MID][d])));
-        }
-      }
-      return x;
+      return row_slots<ET>(KDA && sg < 0.f ? &Kn[r][32 * p] : &Ks[r][32 * p], g4);
     };
 
     // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w).  Every
@@ -253,12 +287,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         for (int p = 0; p < KB; ++p) kc[t][p] = kfrag(t, p, -1.f);
       if (KDA) {
 #pragma unroll
-        for (int p = 0; p < KB; ++p)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int d = 32 * p + kmap(g4, j);
-            qf[p][j] = (ET)(to_f(qf[p][j]) * __expf(Bs[rq][d] - Bs[MID][d]));
-          }
+        for (int p = 0; p < KB; ++p) qf[p] = row_slots<ET>(&Qs[rq][32 * p], g4);
       }
       floatx4 acc[4], pt[4];
 #pragma unroll
@@ -316,8 +345,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 32 * p + kmap(g4, j);
-          const float sc = KDA ? __expf(Bs[C - 1][d] - Bs[i][d]) : __expf(bs[C - 1] - bs[i]);
-          x[j] = (ET)(to_f(Ks[i][d]) * sc);
+          x[j] = KDA ? (ET)(to_f(Kn[i][d]) * cnl[d]) : (ET)(to_f(Ks[i][d]) * __expf(bs[C - 1] - bs[i]));
         }
         ktg[f * 64 + lane] = x;
       }
@@ -331,18 +359,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         const int nt = f / KB, p = f - nt * KB;
         const int r = 16 * nt + c16;
         V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
-        V8 xq = {};
-        if (r < len) xq = *(const V8*)(qg + ((t0 + r) * P.h_qk + U.hk) * DK + 32 * p + 8 * g4);
+        V8 xq = *(const V8*)&Qs[r][32 * p + 8 * g4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float e = __expf(Bs[r][32 * p + 8 * g4 + j]);
+          const float e = ebm[32 * p + 8 * g4 + j];
           xk[j] = (ET)(to_f(xk[j]) * e);
           xq[j] = (ET)(to_f(xq[j]) * e);
         }
         kwg[f * 64 + lane] = xk;
         qwg[f * 64 + lane] = xq;
       }
-      for (int d = tid; d < DK; d += 256) P.gam[ch * DK + d] = __expf(Bs[C - 1][d]);
     } else if (tid < C) {
       // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
       // holds e^{b_n} (rows past the end carry the last b)
