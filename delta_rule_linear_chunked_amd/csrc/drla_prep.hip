@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   constexpr int TP = C + 4;
   constexpr int NPART = 256 / DK;                // KDA gate: row parts per channel
   constexpr int RPP = C / NPART;
+  constexpr bool LF = !KDA && !KT;               // operands for the LDS-fed scan
   constexpr int KV = DK / PE;                    // 16-byte pieces per K row
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
@@ -272,6 +273,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       return row_slots<ET>(KDA && sg < 0.f ? &Kn[r][32 * p] : &Ks[r][32 * p], g4);
     };
 
+    // P of this wave's row tile as B fragments of P^T (kept for the LDS-fed
+    // scan's form, which stores P Tb instead of P)
+    V8 pfr[2];
     // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w).  Every
     // wave multiplies its row tile with all four column tiles (the products
     // past the diagonal are dropped), so all K fragments are read from LDS
@@ -329,9 +333,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
           if (j <= rq) x = KDA ? pt[t][e] : pt[t][e] * __expf(bs[rq] - bs[j]);
           pt[t][e] = x;
         }
-      V8* pg = (V8*)P.pm + ch * (8 * 64);
-      pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(pt[0], pt[1]);
-      pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(pt[2], pt[3]);
+      pfr[0] = pack<ET>(pt[0], pt[1]);
+      pfr[1] = pack<ET>(pt[2], pt[3]);
+      if (!LF) {
+        V8* pg = (V8*)P.pm + ch * (8 * 64);
+        pg[(pr * 2 + 0) * 64 + lane] = pfr[0];
+        pg[(pr * 2 + 1) * 64 + lane] = pfr[1];
+      }
     }
     // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
     // of state tile mt in the scan's row order, inner = token block p).
@@ -458,8 +466,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 
     // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
     // block p), eight per (chunk, head); the ones above the diagonal are zero.
+    // LF: diag(e^{b_n - b}) Tb instead (the scan then forms e^{b_n - b} (.) V'
+    // directly), and Tb^T staged in the bytes of A for P Tb below.
     {
-      const int nt = wv;
+      const int nt = wv, r = 16 * nt + c16;
+      const float en = LF ? __expf(bs[C - 1] - bs[r]) : 1.f;
       V8* tg = (V8*)P.tb + ch * (8 * 64);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -467,10 +478,32 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 32 * p + kmap(g4, j);
-          x[j] = (ET)(Ts[16 * nt + c16][i] * betas[i]);
+          const float tb = Ts[r][i] * betas[i];
+          if (LF) As[i][r] = tb;
+          x[j] = (ET)(tb * en);
         }
         tg[(nt * 2 + p) * 64 + lane] = x;
       }
+    }
+    if (LF) {
+      // P Tb for the output Map (the scan multiplies it with R = V - e^b X):
+      // tiles (it, pr) of (P Tb)^T = Tb^T P^T, packed in pairs into fragment
+      // (pr, p) with P's layout (outer = query token, inner = token)
+      __syncthreads();
+      floatx4 ptt[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        ptt[it] = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const floatx4 lo = *(const floatx4*)&As[16 * it + c16][32 * p + 4 * g4];
+          const floatx4 hi = *(const floatx4*)&As[16 * it + c16][32 * p + 16 + 4 * g4];
+          ptt[it] = mma(pack<ET>(lo, hi), pfr[p], ptt[it]);
+        }
+      }
+      V8* pg = (V8*)P.pm + ch * (8 * 64);
+      pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(ptt[0], ptt[1]);
+      pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(ptt[2], ptt[3]);
     }
     if (!PF) break;
     u += gridDim.x;

@@ -7,22 +7,27 @@
 //
 //   wave 0    (state)   the state recurrence of the chunk, with the 16 state
 //                       columns in registers:
-//                         X   = diag(e^b) K S
-//                         V'  = Tb (V - X)
-//                         S  <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
-//   waves 1,2 (loaders) copy the operands of chunk t+2 (K and Q rows, Tb,
-//                       P, this block's 16 columns of V, the decay factors)
+//                         R   = V - diag(e^b) K S
+//                         V~  = Tv R        = diag(e^{b_n - b}) V'
+//                         S  <- e^{b_n} S + K^T V~
+//                       where Tv = diag(e^{b_n - b}) Tb and V' = Tb R
+//   waves 1,2 (loaders) copy the operands of chunk t+2 (K and Q rows, Tv,
+//                       P Tb, this block's 16 columns of V, the decay factors)
 //                       into a three-slot LDS ring with LDS-direct loads;
 //                       wave 1 also touches this block's share of chunk
 //                       t+PF so that it sits in L2 when its copy is issued
-//   wave 3    (output)  O = diag(e^b) Q S + P V' for the chunk, and its store
+//   wave 3    (output)  O = diag(e^b) Q S + (P Tb) R for the chunk (= P V'),
+//                       and its store
 //
 // K^T is never stored: the state wave reads K rows from LDS with the
 // transposing ds_read_b64_tr_b16 (within a 16-lane group, lane i receives
 // element i%4 of the four-element segments addressed by lanes 4j + i/4,
-// j = 0..3).  One workgroup barrier per chunk (next state and V' published,
+// j = 0..3).  One workgroup barrier per chunk (next state and R published,
 // ring slot released, next chunk's operands landed); the output wave adds
-// the P V' term of a chunk one chunk later, keeping P in registers.
+// the (P Tb) R term of a chunk one chunk later, keeping P Tb in registers.
+// Folding the row decay into Tv and Tb into P removes the decay factors of
+// V' and the scaling of V' from the state wave's serial chain; all three
+// factors have entries of magnitude at most those of Tb and P.
 //
 // Only the loader waves issue loads, so their wait counts are exact: every
 // chunk each issues exactly kIssued copies, and wave 1 kTouched touches.
@@ -61,8 +66,8 @@ struct LdsSlot {
   static constexpr int RB = DK * 2;                       // bytes per K/Q row
   __attribute__((aligned(16))) unsigned char k[C * RB];  // K rows, 16-byte chunks swizzled
   __attribute__((aligned(16))) unsigned char q[C * RB];  // Q rows, same
-  bf16x8 tb[6][64];                                       // Tb fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
-  bf16x8 pm[6][64];                                       // P fragments, same order
+  bf16x8 tb[6][64];                                       // Tv fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+  bf16x8 pm[6][64];                                       // P Tb fragments, same order
   __attribute__((aligned(16))) bf16 v[C][16];             // V, this block's 16 columns
   __attribute__((aligned(16))) float eb[C];               // e^{b_r}
   __attribute__((aligned(16))) float ebn[C];              // e^{b_n - b_r}
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int kTouched = 2;                 // touches per chunk (loader wave 1)
   __shared__ LdsSlot<DK> slot[NS];
   __shared__ bf16x8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
-  __shared__ bf16x8 vbuf[2][2][64];   // V' of the last two chunks, A fragments (inner = token)
+  __shared__ bf16x8 vbuf[2][2][64];   // R of the last two chunks, A fragments (inner = token)
   __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 
   const uint32_t orow = (uint32_t)(((size_t)c16 * P.h_v + h) * DV + 16 * nb + 4 * g4) * 2;
   const uint32_t ostep = (uint32_t)(16 * P.h_v * DV * 2);  // 16 tokens
-  // output wave: add P V' of chunk i (first token t0i) to the partial O^T
+  // output wave: add (P Tb) R of chunk i (first token t0i) to the partial O^T
   // and store it; rows past the end of the sequence are dropped
   floatx4 o[4];
   bf16x8 pmf[6];
@@ -290,12 +295,11 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
       // group addresses row 16 nt + 4g + e', columns 4q..4q+3
       bf16x4 vv[4];
-      floatx4 ebv[4], env[4];
+      floatx4 ebv[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         vv[nt] = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
         ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
-        env[nt] = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
       }
       const float gam = sl.eb[C - 1];
       bf16x8 kr[KB][4];
@@ -347,7 +351,10 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - ebv[nt][e] * x[nt][e];
       const bf16x8 rf0 = pack<bf16>(rr[0], rr[1]), rf1 = pack<bf16>(rr[2], rr[3]);
-      // V' = Tb R
+      // R goes to the output wave, which multiplies it with P Tb
+      vbuf[t & 1][0][lane] = rf0;
+      vbuf[t & 1][1][lane] = rf1;
+      // diag(e^{b_n - b}) V' = (diag(e^{b_n - b}) Tb) R
       floatx4 vt[4];
       vt[0] = mma(tbf[0], rf0, zero4());
       vt[1] = mma(tbf[1], rf0, zero4());
@@ -355,19 +362,21 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       vt[3] = mma(tbf[4], rf0, zero4());
       vt[2] = mma(tbf[3], rf1, vt[2]);
       vt[3] = mma(tbf[5], rf1, vt[3]);
-      const bf16x8 vf0 = pack<bf16>(vt[0], vt[1]), vf1 = pack<bf16>(vt[2], vt[3]);
-      vbuf[t & 1][0][lane] = vf0;
-      vbuf[t & 1][1][lane] = vf1;
+      const bf16x8 vs0 = pack<bf16>(vt[0], vt[1]), vs1 = pack<bf16>(vt[2], vt[3]);
       if (INSPECT) {
+        // V' itself, for the intermediate checks
+        floatx4 vq[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const floatx4 env = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vq[nt][e] = vt[nt][e] / env[e];
+        }
         bf16x8* vp = (bf16x8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
-        vp[(nb * 2 + 0) * 64 + lane] = vf0;
-        vp[(nb * 2 + 1) * 64 + lane] = vf1;
+        vp[(nb * 2 + 0) * 64 + lane] = pack<bf16>(vq[0], vq[1]);
+        vp[(nb * 2 + 1) * 64 + lane] = pack<bf16>(vq[2], vq[3]);
       }
       // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
-      floatx4 vs[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vs[nt] = vt[nt] * env[nt];
-      const bf16x8 vs0 = pack<bf16>(vs[0], vs[1]), vs1 = pack<bf16>(vs[2], vs[3]);
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
         sbuf[(t + 1) & 1][p][lane] = sf[p];
       }
-      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+      lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
     if (P.ht) {
 #pragma unroll
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       const LdsSlot<DK>& sl = slot[t % NS];
       const int64_t t0 = ts + (int64_t)C * t;
       // ---------------- output wave ----------------
-      // finish the previous chunk: its V' was published at the last barrier
+      // finish the previous chunk: its R was published at the last barrier
       if (t > 0) finish_output(t0prev, t - 1);
       // state part of this chunk's O^T: lane holds [column 4g + e][token 16 nt + c]
       bf16x8 so[KB];
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
       t0prev = t0;
-      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+      lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
     if (n > 0) finish_output(t0prev, n - 1);
   } else {
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
       }
-      lds_barrier();  // next state and this V' published, slot t % NS free, chunk t+1 landed
+      lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }

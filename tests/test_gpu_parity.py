@@ -169,8 +169,9 @@ def test_deterministic_and_guard_bands(drla):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
 def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
-    """Prep outputs (T diag(beta), P, K~^T; KDA: K e^B, Q e^B, e^{b_n}) and
-    the scan's V' and per-chunk state, against the fp64 chunkwise form's
+    """Prep outputs (T diag(beta), P, K~^T; KDA: K e^B, Q e^B, e^{b_n}; for
+    the LDS-fed GDN scan diag(e^{b_n - b}) T diag(beta) and P T diag(beta))
+    and the scan's V' and per-chunk state, against the fp64 chunkwise form's
     intermediates on the same inputs, for every chunk (the last one short)."""
     import oracle
     print(f"case intermediates kind={kind} io={io} dk={dk} dv={dv}", flush=True)
@@ -217,6 +218,11 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
             }
             want = {"Tb": pad(it["Tb"], (64, 64)), "P": pad(it["P"], (64, 64)),
                     "V'": it["Vp"], "h": it["h"]}
+            if not kda and io == "bf16":
+                # the LDS-fed scan's operands: diag(e^{b_n - b}) Tb and P Tb
+                env = np.exp(it["b"][-1] - it["b"])
+                want["Tb"] = pad(env[:, None] * it["Tb"], (64, 64))
+                want["P"] = pad(it["P"] @ it["Tb"], (64, 64))
             if lay["kt"]:
                 # K~^T (written for the register-fed scan only): its rows are
                 # the scan's state rows, tile mt row rho = key channel
