@@ -71,6 +71,10 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
   if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
 }
 
+// Position of element e (0..31) of a 32-element block in fragment order:
+// element kmap(g, j) at 8g + j.
+__device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
+
 // A persistent grid of 256-thread workgroups walks the (chunk, value head)
 // units.  PF: while a workgroup computes one unit, the loads of its next
 // unit are in flight (K, Q, beta, g into registers).  KT: write K~^T (the
@@ -198,7 +202,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 #pragma unroll
     for (int i = 0; i < NKV; ++i) {
       const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
-      *(V16*)&Ks[r][cv * PE] = kpre[i];
+      if (LF) {
+        // fragment order within each 32-element block: the 8 elements one
+        // lane of group g takes (4g..4g+3, 16+4g..16+4g+3) sit at 8g..8g+7
+        const int e0 = (cv * PE) & 31, base = (cv * PE) - e0;
+        typedef typename VT<ET>::v4 V4;
+        const V16 x = kpre[i];
+        const V4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+        *(V4*)&Ks[r][base + kpos(e0)] = lo;
+        *(V4*)&Ks[r][base + kpos(e0 + 4)] = hi;
+      } else {
+        *(V16*)&Ks[r][cv * PE] = kpre[i];
+      }
       if (KDA) *(V16*)&Qs[r][cv * PE] = qvpre[i];
     }
     // #1 Gate: in-chunk prefix sums of the log-decay
@@ -270,6 +285,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
     // side.
     auto kfrag = [&](int t, int p, float sg) -> V8 {
       const int r = 16 * t + c16;
+      if (LF) return *(const V8*)&Ks[r][32 * p + 8 * g4];
       return row_slots<ET>(KDA && sg < 0.f ? &Kn[r][32 * p] : &Ks[r][32 * p], g4);
     };
 
@@ -389,14 +405,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
     if (wv == 0) {
       // level 0: the four 16x16 diagonal blocks of T by forward substitution,
       // one column per lane (block lane/16, column lane%16)
+      // (rows of A read four at a time, four partial sums per row)
       const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
       float t[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float acc = (r == cc) ? 1.f : 0.f;
+        float acc[4] = {(r == cc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= As[o + r][o + i] * t[i];
-        t[r] = acc;
+        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+          const floatx4 a = *(const floatx4*)&As[o + r][o + 4 * i4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * i4 + e < r) acc[e] -= a[e] * t[4 * i4 + e];
+        }
+        t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
