@@ -535,15 +535,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   }
 }
 
-// Workgroups of `kern` that fit on the chip at once (cached per device).
-template <typename K>
-static int64_t resident_groups(K kern, int lds_bytes) {
+// Workgroups of one prep kernel variant that fit on the chip at once (cached
+// per variant and device: the variants differ in registers and LDS).
+template <int DK, bool KDA, typename ET, bool KT>
+static int64_t resident_groups() {
+  auto kern = prep_kernel<DK, KDA, ET, KT, !KDA>;
   static int64_t cached[16] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds_bytes) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -555,7 +557,7 @@ static int64_t resident_groups(K kern, int lds_bytes) {
 template <int DK, bool KDA, typename ET, bool KT>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
   auto kern = prep_kernel<DK, KDA, ET, KT, !KDA>;
-  const int64_t fit = KDA ? nblk : resident_groups(kern, 0);
+  const int64_t fit = KDA ? nblk : resident_groups<DK, KDA, ET, KT>();
   const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, nblk);
   return hipGetLastError();
