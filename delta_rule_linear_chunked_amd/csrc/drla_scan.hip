@@ -21,7 +21,9 @@
 // Inside the workgroup wave w owns token tile w (16 tokens) for X, V', O,
 // and rows [16 (dk/64) w, ...) of the state for its update.  Per chunk the
 // waves exchange the state (as bf16/fp32 fragments) and R = V - X through
-// LDS, with two barriers.
+// LDS, with two barriers.  Every wave needs all six Tb fragments; each loads
+// at most two of them and the set is shared through LDS, so the chunk's
+// operands cross the CU's load path once.
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -41,7 +43,7 @@ struct ScanOps {
   V8 kr[KB];       // K rows of token tile w, key channels 32p + 8g + j (KDA: K e^{B})
   V8 qr[KB];       // Q rows, same order (KDA: Q e^{B})
   V8 kt[MT][2];    // K~^T fragments of this wave's state rows
-  V8 tb[6];        // Tb fragments (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  V8 tb[2];        // this wave's share of the Tb fragments (see tb_frag)
   V8 pb[2];        // P fragments (w, 0), (w, 1)
   V4 vv;           // V at token 16w + c, columns 16 nb + 4g + e
   floatx4 gm[MT];  // KDA: e^{b_n} of this lane's state rows
@@ -56,6 +58,12 @@ struct ScanCtx {
   int64_t c0;    // workspace index of its first chunk
   int h, hk, nb, w, lane;
 };
+
+// The six nonzero Tb fragments (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) sit at
+// these indices of the eight in the workspace; wave w loads shares 2w, 2w+1
+// (wave 3 repeats the last one, so no load depends on the wave).
+__device__ __forceinline__ int tb_frag(int j) { return j < 2 ? 2 * j : j + 2; }
+__device__ __forceinline__ int tb_share(int w, int s) { return min(2 * w + s, 5); }
 
 template <int DK, int DV, bool KDA, typename ET>
 __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanParams& P, const ScanCtx& x,
@@ -105,12 +113,8 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
 #pragma unroll
     for (int p = 0; p < 2; ++p) o.kt[m][p] = fload<V8>(ktr, loff, (w * MT + m) * 2 + p);
   const rsrc_t tbr = make_rsrc((const V8*)P.tb + ch * (8 * 64), 8 * 64 * sizeof(V8));
-  o.tb[0] = fload<V8>(tbr, loff, 0);
-  o.tb[1] = fload<V8>(tbr, loff, 2);
-  o.tb[2] = fload<V8>(tbr, loff, 4);
-  o.tb[3] = fload<V8>(tbr, loff, 5);
-  o.tb[4] = fload<V8>(tbr, loff, 6);
-  o.tb[5] = fload<V8>(tbr, loff, 7);
+  o.tb[0] = fload<V8>(tbr, loff, tb_frag(tb_share(w, 0)));
+  o.tb[1] = fload<V8>(tbr, loff, tb_frag(tb_share(w, 1)));
   const rsrc_t pmr = make_rsrc((const V8*)P.pm + ch * (8 * 64), 8 * 64 * sizeof(V8));
   o.pb[0] = fload<V8>(pmr, loff, 2 * w);
   o.pb[1] = fload<V8>(pmr, loff, 2 * w + 1);  // zero for w < 2
@@ -125,8 +129,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   typedef typename VT<ET>::v4 V4;
   typedef typename VT<ET>::v8 V8;
   constexpr int KB = DK / 32, MT = DK / 64, NB = DV / 16, es = sizeof(ET);
-  __shared__ V8 Sf[KB][64];  // state entering the chunk, as fragments (inner = key channel)
-  __shared__ V8 Rf[2][64];   // R = V - X, as B fragments (inner = token)
+  __shared__ V8 Sf[KB][64];     // state entering the chunk, as fragments (inner = key channel)
+  __shared__ V8 Rf[2][64];      // R = V - X, as B fragments (inner = token)
+  __shared__ V8 Tbs[2][6][64];  // Tb fragments of chunks i (slot i % 2)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -185,13 +190,24 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   ET* const rdst = (ET*)&Rf[w >> 1][16 * (c16 >> 2) + 4 * g4] + 4 * (w & 1) + (c16 & 3);
   const uint32_t ooff = (uint32_t)(((size_t)(16 * w + c16) * P.h_v + h) * DV + 16 * nb + 4 * g4) * es;
 
+  // this wave's Tb fragments of chunk i into the shared set; slot i % 2 was
+  // last read in chunk i - 2, which every wave has finished once it is past
+  // the first barrier of chunk i - 1
+  auto put_tb = [&](const ScanOps<DK, KDA, ET>& op, int i) {
+    Tbs[i & 1][tb_share(w, 0)][lane] = op.tb[0];
+    Tbs[i & 1][tb_share(w, 1)][lane] = op.tb[1];
+  };
+
   auto step = [&](const ScanOps<DK, KDA, ET>& op, int i) {
     // GDN decay factors (from prep): e^{b} of this lane's token, e^{b_n}
     const float eb = KDA ? 1.f : op.eb, gam = KDA ? 1.f : op.gam;
-    lds_barrier();  // the state entering this chunk is in Sf
+    lds_barrier();  // the state entering this chunk is in Sf, its Tb in Tbs
     V8 sf[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) sf[p] = Sf[p][lane];
+    V8 tb[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) tb[f] = Tbs[i & 1][f][lane];
     if (INSPECT && w == 0) {
       V8* hp = (V8*)P.insp_h + ((int64_t)h * P.nc + x.c0 + i) * (int64_t)(DK * DV / 8);
 #pragma unroll
@@ -210,10 +226,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
     lds_barrier();  // R of all token tiles is in Rf
     const V8 rf0 = Rf[0][lane], rf1 = Rf[1][lane];
     floatx4 vt[4];
-    vt[0] = mma(op.tb[0], rf0, zero4());
-    vt[1] = mma(op.tb[1], rf0, zero4());
-    vt[2] = mma(op.tb[3], rf1, mma(op.tb[2], rf0, zero4()));
-    vt[3] = mma(op.tb[5], rf1, mma(op.tb[4], rf0, zero4()));
+    vt[0] = mma(tb[0], rf0, zero4());
+    vt[1] = mma(tb[1], rf0, zero4());
+    vt[2] = mma(tb[3], rf1, mma(tb[2], rf0, zero4()));
+    vt[3] = mma(tb[5], rf1, mma(tb[4], rf0, zero4()));
     // V' as the A operand of O^T and the B operand of the update (K~ already
     // carries e^{b_n - b})
     V8 vf[2];
@@ -257,6 +273,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
       const int nn = __builtin_amdgcn_readfirstlane((int)n);
       ScanOps<DK, KDA, ET> bufa, bufb;
       scan_load<DK, DV, KDA, ET>(bufa, P, x, 0);
+      put_tb(bufa, 0);
       for (int i = 0; i < nn; i += 2) {
         __builtin_amdgcn_sched_barrier(0);
         scan_load<DK, DV, KDA, ET>(bufb, P, x, min(i + 1, nn - 1));
@@ -264,15 +281,19 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
         step(bufa, i);
         __builtin_amdgcn_sched_barrier(0);
         if (i + 1 >= nn) break;
+        put_tb(bufb, i + 1);
         scan_load<DK, DV, KDA, ET>(bufa, P, x, min(i + 2, nn - 1));
         __builtin_amdgcn_sched_barrier(0);
         step(bufb, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        put_tb(bufa, i + 2);
       }
     } else {
       const int nn = __builtin_amdgcn_readfirstlane((int)n);
       ScanOps<DK, KDA, ET> buf;
       for (int i = 0; i < nn; ++i) {
         scan_load<DK, DV, KDA, ET>(buf, P, x, i);
+        put_tb(buf, i);
         step(buf, i);
       }
     }
