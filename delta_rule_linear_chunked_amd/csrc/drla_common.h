@@ -141,6 +141,23 @@ __device__ __forceinline__ V fload(rsrc_t r, uint32_t lane_off, int f) {
   }
 }
 
+// LDS-direct buffer loads: lane l's 16 (4) bytes at byte offset voff + soff
+// of the buffer land at lds + 16 l (4 l).  Callers keep soff = 0 and put the
+// whole offset in voff, which the hardware range check covers: a read past
+// the buffer's size returns zero.  The instruction offset stays 0 (it would
+// move the LDS side too).  They count in vmcnt only.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and nothing else.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, bf16x4 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
 }

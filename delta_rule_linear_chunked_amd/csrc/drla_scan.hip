@@ -24,6 +24,11 @@
 // LDS, with two barriers.  Every wave needs all six Tb fragments; each loads
 // at most two of them and the set is shared through LDS, so the chunk's
 // operands cross the CU's load path once.
+//
+// KDA with bf16 inputs (RING): the operand stream into registers bounds the
+// kernel, so only each wave's own token tile of K e^B and Q e^B goes to
+// registers; K~^T, Tb, P, V and e^{b_n} come through a three-slot LDS ring
+// that two more waves fill with LDS-direct loads two chunks ahead.
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -65,9 +70,23 @@ struct ScanCtx {
 __device__ __forceinline__ int tb_frag(int j) { return j < 2 ? 2 * j : j + 2; }
 __device__ __forceinline__ int tb_share(int w, int s) { return min(2 * w + s, 5); }
 
+// One slot of the RING variant's operand ring (bf16).
+template <int DK>
+struct RingSlot {
+  bf16x8 kt[DK / 8][64];                         // K~^T fragments, index tile*2 + block
+  bf16x8 tb[6][64];                              // Tb fragments, tb_frag order
+  bf16x8 pm[6][64];                              // P fragments, same order
+  __attribute__((aligned(16))) bf16 v[C][16];    // V, this block's 16 columns
+  __attribute__((aligned(16))) float gam[256];   // e^{b_n} per key channel (dk used)
+};
+
+template <bool KDA, typename ET>
+constexpr bool ring_variant() { return KDA && sizeof(ET) == 2; }
+
 template <int DK, int DV, bool KDA, typename ET>
 __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanParams& P, const ScanCtx& x,
                                           int i) {
+  constexpr bool RING = ring_variant<KDA, ET>();
   typedef typename VT<ET>::v4 V4;
   typedef typename VT<ET>::v8 V8;
   constexpr int KB = DK / 32, MT = DK / 64, es = sizeof(ET);
@@ -86,9 +105,11 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
       o.kr[p] = fload<V8>(kw, loff, w * KB + p);
       o.qr[p] = fload<V8>(qw, loff, w * KB + p);
     }
-    const rsrc_t gr = make_rsrc(P.gam + ch * DK, DK * 4);
+    if constexpr (!RING) {
+      const rsrc_t gr = make_rsrc(P.gam + ch * DK, DK * 4);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) o.gm[m] = bload<floatx4>(gr, state_row(w * MT + m, 4 * g4) * 4);
+      for (int m = 0; m < MT; ++m) o.gm[m] = bload<floatx4>(gr, state_row(w * MT + m, 4 * g4) * 4);
+    }
   } else {
     const size_t qrow = (size_t)P.h_qk * DK;
     const rsrc_t kr = make_rsrc((const ET*)P.k + t0 * qrow, len * qrow * es);
@@ -107,6 +128,9 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
     o.eb = bload<float>(gr, rw * 4);
     o.gam = bload<float>(gr, last);
   }
+  const size_t vrow = (size_t)P.h_v * DV;
+  o.orsrc = make_rsrc((ET*)P.o + t0 * vrow, len * vrow * es);
+  if constexpr (RING) return;
   const rsrc_t ktr = make_rsrc((const V8*)P.kt + ch * (C * DK / 8), C * DK * es);
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -118,20 +142,22 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
   const rsrc_t pmr = make_rsrc((const V8*)P.pm + ch * (8 * 64), 8 * 64 * sizeof(V8));
   o.pb[0] = fload<V8>(pmr, loff, 2 * w);
   o.pb[1] = fload<V8>(pmr, loff, 2 * w + 1);  // zero for w < 2
-  const size_t vrow = (size_t)P.h_v * DV;
   const rsrc_t vr = make_rsrc((const ET*)P.v + t0 * vrow, len * vrow * es);
   o.vv = bload<V4>(vr, (uint32_t)(((size_t)rw * P.h_v + x.h) * DV + 16 * x.nb + 4 * g4) * es);
-  o.orsrc = make_rsrc((ET*)P.o + t0 * vrow, len * vrow * es);
 }
 
 template <int DK, int DV, bool KDA, typename ET, bool INSPECT>
-__global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
+__global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_kernel(ScanParams P) {
   typedef typename VT<ET>::v4 V4;
   typedef typename VT<ET>::v8 V8;
   constexpr int KB = DK / 32, MT = DK / 64, NB = DV / 16, es = sizeof(ET);
-  __shared__ V8 Sf[KB][64];     // state entering the chunk, as fragments (inner = key channel)
-  __shared__ V8 Rf[2][64];      // R = V - X, as B fragments (inner = token)
-  __shared__ V8 Tbs[2][6][64];  // Tb fragments of chunks i (slot i % 2)
+  constexpr bool RING = ring_variant<KDA, ET>();
+  constexpr int NS = 3;                          // RING: slots
+  __shared__ V8 Sf[KB][64];                      // state entering the chunk, as fragments (inner = key channel)
+  __shared__ V8 Rf[2][64];                       // R = V - X, as B fragments (inner = token)
+  __shared__ V8 Tbs[RING ? 1 : 2][6][64];        // Tb fragments of chunk i (slot i % 2)
+  __shared__ __attribute__((aligned(16))) unsigned char ring_raw[RING ? NS * sizeof(RingSlot<DK>) : 16];
+  RingSlot<DK>* const ring = (RingSlot<DK>*)ring_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -168,6 +194,69 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   const int col = 16 * nb + c16;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
 
+  if constexpr (RING) {
+    if (w >= 4) {
+      // ---------------- loader waves (RING) ----------------
+      // wave 4: K~^T and e^{b_n}; wave 5: Tb, P and this block's 16
+      // columns of V.  Chunk i goes to slot i % NS two chunks ahead; every
+      // copy reads through a descriptor that ends at the chunk's data (V:
+      // at its last valid token, so rows past it read zero).
+      constexpr int K4 = DK / 8 + 1, K5 = 6 + 6 + 2;  // copies per chunk
+      const int nn = __builtin_amdgcn_readfirstlane((int)n);
+      const uint32_t vstride = (uint32_t)(P.h_v * DV * es);
+      const uint32_t voff = (uint32_t)(lane >> 1) * vstride + 16u * (uint32_t)(lane & 1);
+      const uint32_t lo = 16u * (uint32_t)lane;
+      auto issue = [&](int i) {
+        RingSlot<DK>& sl = ring[i % NS];
+        const int64_t ch = (int64_t)h * P.nc + x.c0 + i;
+        if (w == 4) {
+          const rsrc_t kr = make_rsrc((const V8*)P.kt + ch * (C * DK / 8), C * DK * es);
+#pragma unroll
+          for (int f = 0; f < DK / 8; ++f) lds_dma16(kr, lo + 1024u * f, 0, &sl.kt[f][0]);
+          lds_dma16(make_rsrc(P.gam + ch * DK, DK * 4), lo, 0, sl.gam);
+        } else {
+          const rsrc_t tr = make_rsrc((const V8*)P.tb + ch * (8 * 64), 8 * 64 * sizeof(V8));
+          const rsrc_t pr = make_rsrc((const V8*)P.pm + ch * (8 * 64), 8 * 64 * sizeof(V8));
+#pragma unroll
+          for (int j = 0; j < 6; ++j) lds_dma16(tr, lo + 1024u * tb_frag(j), 0, &sl.tb[j][0]);
+#pragma unroll
+          for (int j = 0; j < 6; ++j) lds_dma16(pr, lo + 1024u * tb_frag(j), 0, &sl.pm[j][0]);
+          const int64_t t0 = x.ts + (int64_t)C * i;
+          const int64_t left = x.te - t0;
+          const uint32_t len = (uint32_t)(left < C ? left : C);
+          const rsrc_t vr = make_rsrc((const ET*)P.v + (t0 * P.h_v + h) * DV + 16 * nb, (len - 1) * vstride + 32);
+          lds_dma16(vr, voff, 0, &sl.v[0][0]);
+          lds_dma16(vr, voff + 32 * vstride, 0, &sl.v[32][0]);
+        }
+      };
+      // wait until at most one chunk's copies (issued after the one
+      // waited for) are in flight, or none
+      auto wait_all_but_one = [&](bool one) {
+        if (!one)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        else if (w == 4)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(K4));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(K5));
+      };
+      if (nn > 0) {
+        issue(0);
+        if (nn > 1) issue(1);
+        wait_all_but_one(nn > 1);  // chunk 0 has landed
+      }
+      // as many barriers as the compute waves: two per chunk
+      for (int t = 0; t < nn; ++t) {
+        lds_barrier();  // chunk t under way; slot (t + 2) % NS was last read in chunk t - 1
+        const bool more = t + 2 < nn;
+        if (more) issue(t + 2);
+        lds_barrier();
+        wait_all_but_one(more);  // chunk t + 1 has landed before the next chunk starts
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      return;
+    }
+  }
+
   // this wave's state rows: tiles w*MT + m, element e is key channel
   // state_row(mt, 4g + e), column col
   floatx4 S[MT];
@@ -194,20 +283,51 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
   // last read in chunk i - 2, which every wave has finished once it is past
   // the first barrier of chunk i - 1
   auto put_tb = [&](const ScanOps<DK, KDA, ET>& op, int i) {
-    Tbs[i & 1][tb_share(w, 0)][lane] = op.tb[0];
-    Tbs[i & 1][tb_share(w, 1)][lane] = op.tb[1];
+    if constexpr (!RING) {
+      Tbs[i & 1][tb_share(w, 0)][lane] = op.tb[0];
+      Tbs[i & 1][tb_share(w, 1)][lane] = op.tb[1];
+    }
   };
 
   auto step = [&](const ScanOps<DK, KDA, ET>& op, int i) {
     // GDN decay factors (from prep): e^{b} of this lane's token, e^{b_n}
     const float eb = KDA ? 1.f : op.eb, gam = KDA ? 1.f : op.gam;
-    lds_barrier();  // the state entering this chunk is in Sf, its Tb in Tbs
+    lds_barrier();  // the state entering this chunk is in Sf, its Tb in Tbs (RING: chunk i in its slot)
     V8 sf[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) sf[p] = Sf[p][lane];
-    V8 tb[6];
+    // operands shared through LDS (RING: all but K e^B and Q e^B)
+    V8 tb[6], kt[MT][2], pb[2];
+    V4 vv;
+    floatx4 gm[MT];
+    if constexpr (RING) {
+      const RingSlot<DK>& sl = ring[i % NS];
+      vv = *(const V4*)&sl.v[16 * w + c16][4 * g4];
 #pragma unroll
-    for (int f = 0; f < 6; ++f) tb[f] = Tbs[i & 1][f][lane];
+      for (int f = 0; f < 6; ++f) tb[f] = sl.tb[f][lane];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        kt[m][0] = sl.kt[(w * MT + m) * 2][lane];
+        kt[m][1] = sl.kt[(w * MT + m) * 2 + 1][lane];
+        gm[m] = *(const floatx4*)&sl.gam[state_row(w * MT + m, 4 * g4)];
+      }
+      // P fragments (w, 0) and (w, 1) in tb_frag order; (w, 1) is zero and
+      // unused for w < 2
+      pb[0] = sl.pm[w < 2 ? w : 2 * w - 2][lane];
+      pb[1] = sl.pm[w < 2 ? 0 : 2 * w - 1][lane];
+    } else {
+#pragma unroll
+      for (int f = 0; f < 6; ++f) tb[f] = Tbs[i & 1][f][lane];
+      vv = op.vv;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        kt[m][0] = op.kt[m][0];
+        kt[m][1] = op.kt[m][1];
+        gm[m] = op.gm[m];
+      }
+      pb[0] = op.pb[0];
+      pb[1] = op.pb[1];
+    }
     if (INSPECT && w == 0) {
       V8* hp = (V8*)P.insp_h + ((int64_t)h * P.nc + x.c0 + i) * (int64_t)(DK * DV / 8);
 #pragma unroll
@@ -222,7 +342,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
       o = mma(sf[p], op.qr[p], o);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(op.vv[e]) - eb * xt[e]);
+    for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(vv[e]) - eb * xt[e]);
     lds_barrier();  // R of all token tiles is in Rf
     const V8 rf0 = Rf[0][lane], rf1 = Rf[1][lane];
     floatx4 vt[4];
@@ -244,17 +364,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (KDA)
-        S[m] *= op.gm[m];
+        S[m] *= gm[m];
       else
         S[m] *= gam;
-      S[m] = mma(op.kt[m][0], vf[0], S[m]);
-      S[m] = mma(op.kt[m][1], vf[1], S[m]);
+      S[m] = mma(kt[m][0], vf[0], S[m]);
+      S[m] = mma(kt[m][1], vf[1], S[m]);
     }
     put_state();
     // O^T tile: columns are tokens 16w + c; rows past the end are dropped
     o *= eb;
-    o = mma(vf[0], op.pb[0], o);
-    if (w >= 2) o = mma(vf[1], op.pb[1], o);
+    o = mma(vf[0], pb[0], o);
+    if (w >= 2) o = mma(vf[1], pb[1], o);
     bstore(op.orsrc, ooff, pack4<ET>(o));
   };
 
@@ -271,6 +391,29 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
       // Chunk counters are 32-bit and wave-uniform so that the loop control
       // stays on the scalar unit.
       const int nn = __builtin_amdgcn_readfirstlane((int)n);
+      if constexpr (RING) {
+        // only K e^B and Q e^B go to registers: three sets, loaded two
+        // chunks ahead, cover the load latency
+        ScanOps<DK, KDA, ET> bufa, bufb, bufc;
+        scan_load<DK, DV, KDA, ET>(bufa, P, x, 0);
+        scan_load<DK, DV, KDA, ET>(bufb, P, x, min(1, nn - 1));
+        for (int i = 0; i < nn; i += 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          scan_load<DK, DV, KDA, ET>(bufc, P, x, min(i + 2, nn - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          step(bufa, i);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 1 >= nn) break;
+          scan_load<DK, DV, KDA, ET>(bufa, P, x, min(i + 3, nn - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          step(bufb, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 2 >= nn) break;
+          scan_load<DK, DV, KDA, ET>(bufb, P, x, min(i + 4, nn - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          step(bufc, i + 2);
+        }
+      } else {
       ScanOps<DK, KDA, ET> bufa, bufb;
       scan_load<DK, DV, KDA, ET>(bufa, P, x, 0);
       put_tb(bufa, 0);
@@ -287,6 +430,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
         step(bufb, i + 1);
         __builtin_amdgcn_sched_barrier(0);
         put_tb(bufa, i + 2);
+      }
       }
     } else {
       const int nn = __builtin_amdgcn_readfirstlane((int)n);
@@ -310,10 +454,11 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams P) {
 template <int DK, int DV, bool KDA, typename ET>
 hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
   if (nblk > 0) {
+    constexpr unsigned threads = ring_variant<KDA, ET>() ? 384 : 256;
     if (inspect)
-      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, true>), dim3((unsigned)nblk), dim3(threads), 0, st, P);
     else
-      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((scan_kernel<DK, DV, KDA, ET, false>), dim3((unsigned)nblk), dim3(threads), 0, st, P);
   }
   return hipGetLastError();
 }

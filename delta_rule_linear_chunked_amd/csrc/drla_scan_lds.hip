@@ -37,7 +37,6 @@
 namespace drla {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Transposing LDS read (see above); `p` must be 8-byte aligned.
 __device__ __forceinline__ bf16x4 ds_read_tr(const void* p) {
@@ -45,21 +44,6 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const void* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// LDS-direct buffer loads: lane l's 16 (4) bytes at byte offset voff + soff
-// of the buffer land at lds + 16 l (4 l).  Callers keep soff = 0 and put the
-// whole offset in voff, which the hardware range check covers: a read past
-// the buffer's size returns zero.  The instruction offset stays 0 (it would
-// move the LDS side too).
-__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
-}
-
-// s_waitcnt immediate that waits for at most n outstanding vector memory
-// operations (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and nothing else.
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
 template <int DK>
 struct LdsSlot {
