@@ -296,25 +296,17 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
     V8 sf[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) sf[p] = Sf[p][lane];
-    // operands shared through LDS (RING: all but K e^B and Q e^B)
+    // operands shared through LDS (RING: all but K e^B and Q e^B).  RING
+    // reads V first and the operands of the second half (Tb, K~^T, P, the
+    // decay) only once the products of X and O are issued: one wave issues
+    // an LDS read every ~23 cycles, so reading them all up front would hold
+    // the products back.
     V8 tb[6], kt[MT][2], pb[2];
     V4 vv;
     floatx4 gm[MT];
+    const RingSlot<DK>& sl = ring[RING ? i % NS : 0];
     if constexpr (RING) {
-      const RingSlot<DK>& sl = ring[i % NS];
       vv = *(const V4*)&sl.v[16 * w + c16][4 * g4];
-#pragma unroll
-      for (int f = 0; f < 6; ++f) tb[f] = sl.tb[f][lane];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        kt[m][0] = sl.kt[(w * MT + m) * 2][lane];
-        kt[m][1] = sl.kt[(w * MT + m) * 2 + 1][lane];
-        gm[m] = *(const floatx4*)&sl.gam[state_row(w * MT + m, 4 * g4)];
-      }
-      // P fragments (w, 0) and (w, 1) in tb_frag order; (w, 1) is zero and
-      // unused for w < 2
-      pb[0] = sl.pm[w < 2 ? w : 2 * w - 2][lane];
-      pb[1] = sl.pm[w < 2 ? 0 : 2 * w - 1][lane];
     } else {
 #pragma unroll
       for (int f = 0; f < 6; ++f) tb[f] = Tbs[i & 1][f][lane];
@@ -340,6 +332,22 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
     for (int p = 0; p < KB; ++p) {
       xt = mma(sf[p], op.kr[p], xt);
       o = mma(sf[p], op.qr[p], o);
+    }
+    if constexpr (RING) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < 6; ++f) tb[f] = sl.tb[f][lane];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        kt[m][0] = sl.kt[(w * MT + m) * 2][lane];
+        kt[m][1] = sl.kt[(w * MT + m) * 2 + 1][lane];
+        gm[m] = *(const floatx4*)&sl.gam[state_row(w * MT + m, 4 * g4)];
+      }
+      // P fragments (w, 0) and (w, 1) in tb_frag order; (w, 1) is zero and
+      // unused for w < 2
+      pb[0] = sl.pm[w < 2 ? w : 2 * w - 2][lane];
+      pb[1] = sl.pm[w < 2 ? 0 : 2 * w - 1][lane];
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(vv[e]) - eb * xt[e]);
