@@ -139,6 +139,64 @@ def test_beta_zero_pure_decay(drla, kind):
     _check(f"beta0 {kind}", x, _np(o), _np(ht), o_ref, ht_ref)
 
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_split_invariance(drla, kind, io):
+    """One call on [0, T) against [0, t) then [t, T) from the first part's
+    final state, t inside a chunk: both within the bar of the oracle and of
+    each other (the chunk boundaries, hence the rounding, differ)."""
+    print(f"case split-invariance kind={kind} io={io}", flush=True)
+    T, t = 300, 130
+    x = _case(kind, io, 128, 128, lens=(T,), h_qk=2, h_v=2, h0_std=0.05)
+    d = to_device(x)
+    fn = drla.kda_prefill if kind == "kda" else drla.gdn_prefill
+    o, ht = fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    part = lambda a, lo, hi: a[lo:hi].contiguous()
+    o1, h1 = fn(*(part(d[n], 0, t) for n in ("q", "k", "v", "beta", "g")), d["h0"])
+    o2, h2 = fn(*(part(d[n], t, T) for n in ("q", "k", "v", "beta", "g")), h1)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = run_oracle(x)
+    o12 = np.concatenate([_np(o1), _np(o2)])
+    _check(f"split {kind}/{io}", x, o12, _np(h2), o_ref, ht_ref)
+    _check(f"whole {kind}/{io}", x, _np(o), _np(ht), o_ref, ht_ref)
+    tol = TOL[io]
+    assert rel_err(o12, _np(o)) <= tol and rel_err(_np(h2), _np(ht)) <= tol
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_kda_with_uniform_gate_equals_gdn(drla, io):
+    """KDA whose per-channel gate repeats one value over the key channels
+    computes GDN."""
+    print(f"case kda-uniform io={io}", flush=True)
+    x = _case("gdn", io, 128, 64, lens=(70, 200), h_qk=1, h_v=2, h0_std=0.05)
+    d = to_device(x)
+    o_g, h_g = _call(drla, x, d)
+    gk = d["g"][:, :, None].expand(-1, -1, 128).contiguous()
+    o_k, h_k = drla.kda_prefill(d["q"], d["k"], d["v"], d["beta"], gk, d["h0"], d["cu"],
+                                cu_seqlens_host=d["cu_host"])
+    torch.cuda.synchronize()
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"kda-uniform {io}", x, _np(o_k), _np(h_k), o_ref, ht_ref)
+    tol = TOL[io]
+    assert rel_err(_np(o_k), _np(o_g)) <= tol and rel_err(_np(h_k), _np(h_g)) <= tol
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_grouped_heads_equal_repeated_dense(drla, kind):
+    """Value head h reads q/k head h // (h_v / h_qk): the grouped call equals
+    the call with q and k repeated to h_v heads, bit for bit."""
+    print(f"case grouped kind={kind}", flush=True)
+    x = _case(kind, "bf16", 128, 128, lens=(150, 64), h_qk=2, h_v=4, h0_std=0.02)
+    d = to_device(x)
+    o1, h1 = _call(drla, x, d)
+    rq = d["q"].repeat_interleave(2, dim=1).contiguous()
+    rk = d["k"].repeat_interleave(2, dim=1).contiguous()
+    fn = drla.kda_prefill if kind == "kda" else drla.gdn_prefill
+    o2, h2 = fn(rq, rk, d["v"], d["beta"], d["g"], d["h0"], d["cu"], cu_seqlens_host=d["cu_host"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
 def test_deterministic_and_guard_bands(drla):
     """Bitwise identical across runs; nothing written outside o and ht."""
     x = _case("kda", "bf16", 128, 128, lens=(77, 190), h_qk=1, h_v=2)
