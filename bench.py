@@ -8,6 +8,8 @@ workload's inputs, already resident in HBM.  Prints one JSON line.
 
 Workloads (seeded, synthetic): gdn_prefill (default: 1 x 4096 tokens,
 16 heads, dk = dv = 128, bf16), kda_prefill, gdn_varlen, gdn_long, gdn_tiny.
+gdn_decode / kda_decode time one decode step instead (256 sequences, one
+token each, from a nonzero state), under their own metric.
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN/KDA chunked-prefill tokens/s at H16 d128 T4096; % of MFMA/HBM roofline"
+DECODE_METRIC = "GDN/KDA decode-step tokens/s (one token per sequence); % of HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
@@ -147,6 +150,92 @@ def cpu_baseline(x, spec, n_tokens, budget_s=10.0):
                       f"threads over {units} (sequence, head) units on {cores} host cores"}
 
 
+def copy_calibration(torch, dev, mib):
+    """A plain elementwise copy of `mib` MiB (bf16 negate: reads and writes
+    mib MiB), five times: the reference dispatch that scales the HBM byte
+    counters of a rocprofv3 --pmc run."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"copy calibration: {n * 2} bytes read and {n * 2} bytes written per dispatch",
+          file=sys.stderr)
+
+
+def decode_bench(args, spec, x, torch, drla):
+    """One decode step per timed step: every sequence's next token from the
+    fixed state h0 (read) to a separate new state (written)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    io = torch.bfloat16 if spec.io == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev, io) for n in ("q", "k", "v"))
+    beta = torch.from_numpy(x["beta"]).to(dev)
+    g = torch.from_numpy(x["g"]).to(dev)
+    h0 = torch.from_numpy(x["h0"]).to(dev)
+    N = spec.n_seqs
+    o = torch.empty((N, spec.h_v, spec.dv), dtype=io, device=dev)
+    ht = torch.empty_like(h0)
+    fn = drla.kda_decode if spec.kind == "kda" else drla.gdn_decode
+
+    def step():
+        fn(q, k, v, beta, g, h0, out=o, final_state=ht)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = Hip()
+    e0, e1 = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
+    for _ in range(args.steps):
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = hip.elapsed_ms(e0, e1) / args.steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    es = 2 if spec.io == "bf16" else 4
+    kda = spec.kind == "kda"
+    # algorithmic bytes: q, k, v, beta, g, h0 in; o, new state out
+    bytes_ = N * (2 * spec.h_qk * spec.dk * es + 2 * spec.h_v * spec.dv * es + spec.h_v * 4
+                  + spec.h_v * (spec.dk if kda else 1) * 4) + 2 * N * spec.h_v * spec.dk * spec.dv * 4
+    ach = bytes_ / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": DECODE_METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.io,
+        "data": "synthetic (seeded; q,k L2-normalised, v ~ N(0,1), beta = sigmoid(N(0,1)), "
+                "log-gates uniform, state N(0, 0.02))",
+        "config": {"workload": spec.name, "kind": spec.kind, "n_seqs": N, "tokens_per_seq": 1,
+                   "h_qk": spec.h_qk, "h_v": spec.h_v, "dk": spec.dk, "dv": spec.dv,
+                   "io": spec.io},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "decode",
+                     "traffic": load_traffic("decode", spec.name),
+                     "kernel_ms": {"decode": round(ms_step, 5)},
+                     "algorithmic_bytes_per_launch": int(bytes_)},
+        "path": {"host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, spec, N, args.cpu_budget)
+    copy_calibration(torch, dev, args.copy_calibration)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,8 +260,10 @@ def main():
     import delta_rule_linear_chunked_amd as drla
     import workloads as W
 
-    spec = W.WORKLOADS[args.workload]
+    spec = W.spec_by_name(args.workload)
     x = W.make_inputs(spec)
+    if args.workload in W.DECODE_WORKLOADS:
+        return decode_bench(args, spec, x, torch, drla)
     n_tokens = int(x["cu_seqlens"][-1])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -277,15 +368,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, spec, n_tokens, args.cpu_budget)
-    if args.copy_calibration > 0:
-        n = args.copy_calibration * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        print(f"copy calibration: {n * 2} bytes read and {n * 2} bytes written per dispatch",
-              file=sys.stderr)
+    copy_calibration(torch, dev, args.copy_calibration)
     print(json.dumps(line), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Chunked prefill of delta-rule linear attention (GDN, KDA) on MI355X.
+"""Chunked prefill (and the single-token decode step) of delta-rule linear
+attention (GDN, KDA) on MI355X.
 
 Python binding of the C ABI in ``include/drla.h`` (``libdrla.so``): argument
 marshalling only.  PyTorch provides device memory and the current stream;
@@ -8,7 +9,9 @@ library is not built the calls raise; there is no other code path.
 from ._lib import (  # noqa: F401
     KEEP_INTERMEDIATES,
     DrlaError,
+    gdn_decode,
     gdn_prefill,
+    kda_decode,
     kda_prefill,
     lib_path,
     load_library,
@@ -16,5 +19,5 @@ from ._lib import (  # noqa: F401
     workspace_layout,
 )
 
-__all__ = ["gdn_prefill", "kda_prefill", "workspace_bytes", "workspace_layout",
+__all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "workspace_bytes", "workspace_layout",
            "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES"]

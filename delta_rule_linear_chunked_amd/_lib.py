@@ -66,6 +66,10 @@ def load_library():
             f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp,
                           ctypes.c_size_t, vp]
             f.restype = ctypes.c_int
+        for name in ("gdn_decode", "kda_decode"):
+            f = getattr(lib, name)
+            f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            f.restype = ctypes.c_int
         lib.drla_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp,
                                         vp, i32p, vp, vp, vp, ctypes.c_size_t, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
@@ -233,3 +237,55 @@ def gdn_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
 def kda_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
     """Kimi Delta Attention chunked prefill; g is per key channel [T,h_v,dk]."""
     return _prefill(True, q, k, v, beta, g, initial_state, cu_seqlens, **kw)
+
+
+def _decode(kda: bool, q, k, v, beta, g, state=None, out=None, final_state=None,
+            in_place=False):
+    lib = load_library()
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [N, h_qk, dk] and v [N, h_v, dv]")
+    N, h_v, dk, dv = q.shape[0], v.shape[1], q.shape[2], v.shape[2]
+    for name, x in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g)):
+        if not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("beta and g must be float32")
+    want_g = (N, h_v, dk) if kda else (N, h_v)
+    if tuple(beta.shape) != (N, h_v) or tuple(g.shape) != want_g:
+        raise ValueError(f"beta must be {(N, h_v)} and g {want_g}")
+    if state is not None and (state.dtype != torch.float32 or not state.is_contiguous()
+                              or tuple(state.shape) != (N, h_v, dk, dv)):
+        raise ValueError(f"state must be contiguous float32 {(N, h_v, dk, dv)}")
+    prob = _problem(q, v, N, N)
+    dev = q.device
+    o = out if out is not None else torch.empty((N, h_v, dv), dtype=q.dtype, device=dev)
+    if in_place:
+        if state is None:
+            raise ValueError("in_place needs a state")
+        ht = state
+    else:
+        ht = final_state if final_state is not None else \
+            torch.empty((N, h_v, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    fn = lib.kda_decode if kda else lib.gdn_decode
+    st = fn(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+            g.data_ptr(), None if state is None else state.data_ptr(), o.data_ptr(),
+            ht.data_ptr(), stream)
+    if st != 0:
+        raise DrlaError(st, lib.drla_last_error().decode())
+    return o, ht
+
+
+def gdn_decode(q, k, v, beta, g, state=None, **kw):
+    """One Gated DeltaNet decode step: row n of q, k [N, h_qk, dk], v
+    [N, h_v, dv], beta, g [N, h_v] is sequence n's next token; state
+    [N, h_v, dk, dv] fp32 (None: zeros).  Returns (o [N, h_v, dv], new
+    state); with in_place=True the state tensor is updated and returned."""
+    return _decode(False, q, k, v, beta, g, state, **kw)
+
+
+def kda_decode(q, k, v, beta, g, state=None, **kw):
+    """One Kimi Delta Attention decode step; g is per key channel [N, h_v, dk]."""
+    return _decode(True, q, k, v, beta, g, state, **kw)

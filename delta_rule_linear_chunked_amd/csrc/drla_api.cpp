@@ -188,9 +188,73 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   return DRLA_OK;
 }
 
+drla_status run_decode(bool kda, const drla_problem* p, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, void* o, float* ht, void* stream) {
+  int64_t nc = 0;
+  drla_status st = check_problem(p, nullptr, &nc);
+  if (st != DRLA_OK) return st;
+  if (p->total_tokens != p->n_seqs)
+    return fail(DRLA_ERR_SHAPE, "decode: total_tokens (%lld) must equal n_seqs (%d), one token each",
+                (long long)p->total_tokens, p->n_seqs);
+  if (!q || !k || !v || !beta || !g || !o) return fail(DRLA_ERR_NULL, "q, k, v, beta, g and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, beta, g, h0, o, ht};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const int64_t N = p->n_seqs;
+  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t nq = (size_t)N * p->h_qk * p->dk * es, nv = (size_t)N * p->h_v * p->dv * es;
+  const size_t nb = (size_t)N * p->h_v * 4, ng = kda ? nb * p->dk : nb;
+  const size_t ns = (size_t)N * p->h_v * p->dk * p->dv * 4;
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {beta, nb}, {g, ng}, {h0, ns}};
+  const Buf outs[] = {{o, nv}, {ht, ns}};
+  for (int i = 0; i < 2; ++i)
+    for (const Buf& b : ins) {
+      if (i == 1 && b.p == h0 && ht == h0) continue;  // in-place state update
+      if (overlap(outs[i].p, outs[i].n, b.p, b.n))
+        return fail(DRLA_ERR_ALIAS, "an output buffer overlaps an input buffer");
+    }
+  if (overlap(o, nv, ht, ns)) return fail(DRLA_ERR_ALIAS, "output buffers overlap");
+  drla_decode_args a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.o = o;
+  a.ht = ht;
+  a.n_seqs = p->n_seqs;
+  a.h_qk = p->h_qk;
+  a.h_v = p->h_v;
+  a.dk = p->dk;
+  a.dv = p->dv;
+  a.kda = kda ? 1 : 0;
+  a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
+  a.stream = stream;
+  const hipError_t e = drla_launch_decode(&a);
+  if (e != hipSuccess) return fail(DRLA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return DRLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+drla_status gdn_decode(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
+                       const float* g, const float* h0, void* o, float* ht, void* stream) {
+  return run_decode(false, p, q, k, v, beta, g, h0, o, ht, stream);
+}
+
+drla_status kda_decode(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
+                       const float* g, const float* h0, void* o, float* ht, void* stream) {
+  return run_decode(true, p, q, k, v, beta, g, h0, o, ht, stream);
+}
 
 size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_host) {
   // The KDA layout is the larger one; GDN calls use a prefix of it.
@@ -254,6 +318,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 2; }
+int drla_version(void) { return 3; }
 
 }  // extern "C"

@@ -43,6 +43,19 @@ struct ScanParams {
   int64_t nc;
 };
 
+// One decode step: every input row is one sequence's token.
+struct DecodeParams {
+  const void* q;   // [N, h_qk, dk]
+  const void* k;   // [N, h_qk, dk]
+  const void* v;   // [N, h_v, dv]
+  const float* beta;  // [N, h_v]
+  const float* g;     // [N, h_v] (KDA: [N, h_v, dk])
+  const float* h0;    // [N, h_v, dk, dv] or null
+  void* o;            // [N, h_v, dv]
+  float* ht;          // [N, h_v, dk, dv] or null; may be h0
+  int32_t h_qk, h_v;
+};
+
 hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st);
 
 template <int DK, bool KDA, typename ET>

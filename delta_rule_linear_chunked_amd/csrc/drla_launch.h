@@ -31,4 +31,20 @@ typedef struct {
 
 hipError_t drla_launch(const drla_launch_args* a);
 
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const float* h0;
+  void* o;
+  float* ht;
+  int32_t n_seqs, h_qk, h_v, dk, dv;
+  int32_t kda, f32;
+  void* stream;
+} drla_decode_args;
+
+hipError_t drla_launch_decode(const drla_decode_args* a);
+
 #endif

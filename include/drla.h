@@ -117,6 +117,32 @@ drla_status kda_prefill(const drla_problem* p, const void* q, const void* k,
                         const int32_t* cu_seqlens_host, void* o, float* ht,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of Gated DeltaNet: one token per sequence continuing
+ * from the state h0 -- the per-token recurrence of "Empowering Hybrid
+ * Attention Models on NPUs", Section 2.1, that the chunked prefill also
+ * computes (decay the state, x = S^T k, S += beta k (v - x)^T, o = S^T q).
+ *   p                     total_tokens must equal n_seqs (row n is sequence
+ *                         n's token); dk, dv, heads and io dtype as prefill
+ *   q, k                  device [N, h_qk, dk] in io dtype
+ *   v                     device [N, h_v, dv] in io dtype
+ *   beta, g               device [N, h_v] fp32 (g: log-decay)
+ *   h0                    device [N, h_v, dk, dv] fp32 state, or NULL (zeros)
+ *   o                     device output [N, h_v, dv] in io dtype
+ *   ht                    device output [N, h_v, dk, dv] fp32, or NULL; may
+ *                         be exactly h0 (the usual in-place step)
+ *   stream                hipStream_t
+ * No workspace; all device pointers 16-byte aligned; errors as prefill
+ * (checked before anything is enqueued). */
+drla_status gdn_decode(const drla_problem* p, const void* q, const void* k,
+                       const void* v, const float* beta, const float* g,
+                       const float* h0, void* o, float* ht, void* stream);
+
+/* Kimi Delta Attention decode step: as gdn_decode with g per key channel,
+ * [N, h_v, dk] fp32 (the state's key rows decay by e^{g}). */
+drla_status kda_decode(const drla_problem* p, const void* q, const void* k,
+                       const void* v, const float* beta, const float* g,
+                       const float* h0, void* o, float* ht, void* stream);
+
 /* Flags of drla_prefill_ex. */
 #define DRLA_KEEP_INTERMEDIATES 1 /* also write V' and the per-chunk state (tests) */
 

@@ -29,12 +29,12 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert {"gdn_prefill", "kda_prefill", "drla_prefill_ex", "drla_workspace_bytes",
-            "drla_workspace_layout", "drla_status_str", "drla_last_error",
+    assert {"gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "drla_prefill_ex",
+            "drla_workspace_bytes", "drla_workspace_layout", "drla_status_str", "drla_last_error",
             "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 2
+    assert lib.drla_version() == 3
 
 
 def _prob(n_seqs=1, h_qk=2, h_v=4, dk=128, dv=128, io=0, T=256):
@@ -79,6 +79,28 @@ def test_validation_errors(lib):
                            1 << 44, None, None, None, 1 << 40, None, 1 << 46, 1 << 40, None) == 7
     msg = lib.drla_last_error().decode()
     assert "overlap" in msg
+
+
+def test_decode_validation_errors(lib):
+    """The decode entry points check everything before enqueueing anything
+    (fake aligned addresses: never dereferenced on these paths)."""
+    b = 1 << 40
+    ins = [b + 0x1000000, b + 0x2000000, b + 0x3000000, b + 0x4000000, b + 0x5000000]
+
+    def call(p, q=ins[0], h0=None, o=b + 0x6000000, ht=b + 0x7000000, kda=False):
+        fn = lib.kda_decode if kda else lib.gdn_decode
+        return fn(ctypes.byref(p), q, *ins[1:], h0, o, ht, None)
+
+    assert lib.gdn_decode(None, *([None] * 9)) == 1
+    assert call(_prob(n_seqs=4, T=8)) == 2              # two tokens per sequence
+    assert call(_prob(n_seqs=4, T=4, h_v=3)) == 2       # h_v % h_qk
+    assert call(_prob(n_seqs=4, T=4, dk=96)) == 3       # unsupported dk
+    assert call(_prob(n_seqs=4, T=4), q=None) == 1      # null q
+    assert call(_prob(n_seqs=4, T=4), o=None) == 1      # null o
+    assert call(_prob(n_seqs=4, T=4), q=ins[0] + 8) == 4, "misaligned q"
+    assert call(_prob(n_seqs=4, T=4), o=ins[2], kda=True) == 7   # o over v
+    assert call(_prob(n_seqs=4, T=4), h0=b + 0x8000000, ht=b + 0x8000000 + 4096) == 7
+    assert "overlap" in lib.drla_last_error().decode()
 
 
 def test_cu_seqlens_validation(lib):

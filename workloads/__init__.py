@@ -79,9 +79,18 @@ WORKLOADS = {
                      0.001, 0.05, 0.02, seed=4),
 }
 
+# Decode steps (one token per sequence from a nonzero state): a serving
+# batch of 256 sequences at the prefill configs' head shape.
+DECODE_WORKLOADS = {
+    "gdn_decode": Spec("gdn_decode", "gdn", (1,) * 256, 16, 16, 128, 128, "bf16",
+                       0.01, 0.2, 0.02, varlen=True, seed=5),
+    "kda_decode": Spec("kda_decode", "kda", (1,) * 256, 16, 16, 128, 128, "bf16",
+                       0.005, 0.15, 0.02, varlen=True, seed=6),
+}
+
 
 def spec_by_name(name: str) -> Spec:
-    return WORKLOADS[name]
+    return WORKLOADS[name] if name in WORKLOADS else DECODE_WORKLOADS[name]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
