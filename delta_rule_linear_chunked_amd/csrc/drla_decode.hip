@@ -14,7 +14,8 @@
 // j = t % dv and a contiguous run of RPT rows, so every row of the state is
 // read and written as one coalesced line per wave.  The two column sums
 // (x, o) combine the row groups' partial sums through LDS.  Each state
-// element is read and written by the same thread, so ht may be h0.
+// element is read and written by the same thread, so ht may be h0.  The
+// state streams through once, so its loads and stores are non-temporal.
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
   float s[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
-    s[r] = P.h0 ? P.h0[sbase + (int64_t)(rg * RPT + r) * DV + j] : 0.f;
+    s[r] = P.h0 ? __builtin_nontemporal_load(&P.h0[sbase + (int64_t)(rg * RPT + r) * DV + j]) : 0.f;
 
   const ET* qg = (const ET*)P.q + ((int64_t)n * P.h_qk + hk) * DK;
   const ET* kg = (const ET*)P.k + ((int64_t)n * P.h_qk + hk) * DK;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
   }
   if (P.ht) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) P.ht[sbase + (int64_t)(rg * RPT + r) * DV + j] = s[r];
+    for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r], &P.ht[sbase + (int64_t)(rg * RPT + r) * DV + j]);
   }
   part[1][rg][j] = po;
   __syncthreads();
