@@ -9,7 +9,8 @@ workload's inputs, already resident in HBM.  Prints one JSON line.
 Workloads (seeded, synthetic): gdn_prefill (default: 1 x 4096 tokens,
 16 heads, dk = dv = 128, bf16), kda_prefill, gdn_varlen, gdn_long, gdn_tiny.
 gdn_decode / kda_decode time one decode step instead (256 sequences, one
-token each, from a nonzero state), under their own metric.
+token each, from a nonzero state), under their own metric; gdn_prefill_f16 /
+kda_prefill_f16 are the prefill configs with fp16 q, k, v.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN/KDA chunked-prefill tokens/s at H16 d128 T4096; % of MFMA/HBM roofline"
 DECODE_METRIC = "GDN/KDA decode-step tokens/s (one token per sequence); % of HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 (and fp16) MFMA, published
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
 CHUNK = 64
 
@@ -40,7 +41,7 @@ def kernel_costs(spec, n_tokens, n_seqs):
     the design.  Flops: the MFMA work of the kernel counting full 16x16
     tiles as issued (the strictly-upper tiles of the 64x64 chunk products are
     skipped)."""
-    es = 2 if spec.io == "bf16" else 4
+    es = 4 if spec.io == "f32" else 2
     dk, dv, hv, hqk = spec.dk, spec.dv, spec.h_v, spec.h_qk
     kda = spec.kind == "kda"
     th = n_tokens * hv                         # token x value head
@@ -171,7 +172,7 @@ def decode_bench(args, spec, x, torch, drla):
     fixed state h0 (read) to a separate new state (written)."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    io = torch.bfloat16 if spec.io == "bf16" else torch.float32
+    io = {"bf16": torch.bfloat16, "f16": torch.float16}.get(spec.io, torch.float32)
     q, k, v = (torch.from_numpy(x[n]).to(dev, io) for n in ("q", "k", "v"))
     beta = torch.from_numpy(x["beta"]).to(dev)
     g = torch.from_numpy(x["g"]).to(dev)
@@ -200,7 +201,7 @@ def decode_bench(args, spec, x, torch, drla):
     ms_step = hip.elapsed_ms(e0, e1) / args.steps
     hip.destroy(e0)
     hip.destroy(e1)
-    es = 2 if spec.io == "bf16" else 4
+    es = 4 if spec.io == "f32" else 2
     kda = spec.kind == "kda"
     # algorithmic bytes: q, k, v, beta, g, h0 in; o, new state out
     bytes_ = N * (2 * spec.h_qk * spec.dk * es + 2 * spec.h_v * spec.dv * es + spec.h_v * 4
@@ -267,7 +268,7 @@ def main():
     n_tokens = int(x["cu_seqlens"][-1])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    io = torch.bfloat16 if spec.io == "bf16" else torch.float32
+    io = {"bf16": torch.bfloat16, "f16": torch.float16}.get(spec.io, torch.float32)
     q, k, v = (torch.from_numpy(x[n]).to(dev, io) for n in ("q", "k", "v"))
     beta = torch.from_numpy(x["beta"]).to(dev)
     g = torch.from_numpy(x["g"]).to(dev)
@@ -320,14 +321,14 @@ def main():
     bytes_, flops = costs[dom]
     t_s = stage[dom] * 1e-3
     intensity = flops / bytes_
-    ridge = (BF16_PEAK_TFLOPS if spec.io == "bf16" else F32_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = (F32_PEAK_TFLOPS if spec.io == "f32" else BF16_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
         ach = bytes_ / t_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     else:
         ach = flops / t_s / 1e12
-        peak = BF16_PEAK_TFLOPS if spec.io == "bf16" else F32_PEAK_TFLOPS
+        peak = F32_PEAK_TFLOPS if spec.io == "f32" else BF16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4)}
     roof["kernel"] = dom
@@ -338,7 +339,7 @@ def main():
 
     total_flops = sum(f for _, f in costs.values())
     # whole-call algorithmic I/O (q, k, v, beta, g, h0 in; o, ht out)
-    es = 2 if spec.io == "bf16" else 4
+    es = 4 if spec.io == "f32" else 2
     io_bytes = n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * 4
                            + spec.h_v * (spec.dk if spec.kind == "kda" else 1) * 4) \
         + (2 if spec.h0_std > 0 else 1) * n_seqs * spec.h_v * spec.dk * spec.dv * 4

@@ -16,7 +16,7 @@ _LIB = os.path.join(_HERE, "_build", "libdrla.so")
 _lock = threading.Lock()
 _lib = None
 
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported size or dtype",
           4: "misaligned pointer", 5: "bad cu_seqlens", 6: "workspace too small",
           7: "overlapping buffers", 8: "HIP error"}
@@ -101,15 +101,17 @@ def _host_cu(cu_seqlens, cu_seqlens_host):
     return arr
 
 
+def _io_code(dtype):
+    codes = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}
+    if dtype not in codes:
+        raise ValueError(f"q/k/v dtype must be bfloat16, float16 or float32, got {dtype}")
+    return codes[dtype]
+
+
 def _problem(q, v, n_seqs, total):
     if q.dtype != v.dtype:
         raise ValueError("q, k and v must have the same dtype")
-    if q.dtype == torch.bfloat16:
-        io = BF16
-    elif q.dtype == torch.float32:
-        io = F32
-    else:
-        raise ValueError(f"q/k/v dtype must be bfloat16 or float32, got {q.dtype}")
+    io = _io_code(q.dtype)
     return Problem(n_seqs, q.shape[-2], v.shape[-2], q.shape[-1], v.shape[-1], io, total)
 
 
@@ -128,7 +130,7 @@ def workspace_bytes(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
     if cu is not None:
         n_seqs = len(cu) - 1
     p = Problem(n_seqs, q_shape[1], v_shape[1], q_shape[2], v_shape[2],
-                BF16 if io_dtype == torch.bfloat16 else F32, T)
+                _io_code(io_dtype), T)
     return int(lib.drla_workspace_bytes(ctypes.byref(p), _i32p(cu)))
 
 
@@ -142,7 +144,7 @@ def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
     if cu is not None:
         n_seqs = len(cu) - 1
     p = Problem(n_seqs, q_shape[1], v_shape[1], q_shape[2], v_shape[2],
-                BF16 if io_dtype == torch.bfloat16 else F32, q_shape[0])
+                _io_code(io_dtype), q_shape[0])
     out = Layout()
     st = lib.drla_workspace_layout(int(kda), ctypes.byref(p), _i32p(cu), int(flags),
                                    ctypes.byref(out))

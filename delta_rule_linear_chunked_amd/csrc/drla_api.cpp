@@ -50,7 +50,7 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
   if (p->total_tokens > INT32_MAX) return fail(DRLA_ERR_SHAPE, "total_tokens must fit in int32");
   if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
     return fail(DRLA_ERR_UNSUPPORTED, "dk, dv must be 64 or 128 (got %d, %d)", p->dk, p->dv);
-  if (p->io_dtype != DRLA_BF16 && p->io_dtype != DRLA_F32)
+  if (p->io_dtype != DRLA_BF16 && p->io_dtype != DRLA_F32 && p->io_dtype != DRLA_F16)
     return fail(DRLA_ERR_UNSUPPORTED, "unknown io dtype %d", p->io_dtype);
   int64_t nc = 0;
   if (cu_host) {
@@ -76,7 +76,7 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
 }
 
 void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int flags, drla_layout* L) {
-  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
   const size_t ncH = (size_t)nc * p->h_v;
   const size_t frag = 64 * 8 * es;  // one operand fragment
   const bool keep = (flags & DRLA_KEEP_INTERMEDIATES) != 0;
@@ -90,7 +90,7 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   off = align_up(off + ncH * 8 * frag);
   // K~^T is only needed by the register-fed scan (KDA, fp32 inputs); the
   // LDS-fed GDN scan transposes K itself
-  const bool need_kt = kda || p->io_dtype != DRLA_BF16;
+  const bool need_kt = kda || p->io_dtype == DRLA_F32;
   L->kt = need_kt ? off : 0;
   if (need_kt) off = align_up(off + ncH * DRLA_CHUNK * p->dk * es);
   L->kw = kda ? off : 0;
@@ -127,7 +127,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   layout_of(p, nc, cu_dev != nullptr, kda, flags, &L);
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(DRLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : 0);
-  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
   const size_t nq = (size_t)T * p->h_qk * p->dk * es, nv = (size_t)T * p->h_v * p->dv * es;
   const size_t nb = (size_t)T * p->h_v * 4, ng = kda ? nb * p->dk : nb;
   const size_t ns = (size_t)p->n_seqs * p->h_v * p->dk * p->dv * 4;
@@ -179,6 +179,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.dv = p->dv;
   a.kda = kda ? 1 : 0;
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
+  a.f16 = p->io_dtype == DRLA_F16 ? 1 : 0;
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
@@ -201,7 +202,7 @@ drla_status run_decode(bool kda, const drla_problem* p, const void* q, const voi
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
   const int64_t N = p->n_seqs;
-  const size_t es = p->io_dtype == DRLA_BF16 ? 2 : 4;
+  const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
   const size_t nq = (size_t)N * p->h_qk * p->dk * es, nv = (size_t)N * p->h_v * p->dv * es;
   const size_t nb = (size_t)N * p->h_v * 4, ng = kda ? nb * p->dk : nb;
   const size_t ns = (size_t)N * p->h_v * p->dk * p->dv * 4;
@@ -235,6 +236,7 @@ drla_status run_decode(bool kda, const drla_problem* p, const void* q, const voi
   a.dv = p->dv;
   a.kda = kda ? 1 : 0;
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
+  a.f16 = p->io_dtype == DRLA_F16 ? 1 : 0;
   a.stream = stream;
   const hipError_t e = drla_launch_decode(&a);
   if (e != hipSuccess) return fail(DRLA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));

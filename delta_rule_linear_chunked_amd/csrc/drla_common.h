@@ -27,6 +27,9 @@ namespace drla {
 typedef __bf16 bf16;
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 
@@ -39,6 +42,12 @@ template <> struct VT<bf16> {
   typedef bf16x8 v16b;  // one 16-byte vector
   static constexpr int per16 = 8;
 };
+template <> struct VT<f16> {
+  typedef f16x4 v4;
+  typedef f16x8 v8;
+  typedef f16x8 v16b;
+  static constexpr int per16 = 8;
+};
 template <> struct VT<float> {
   typedef floatx4 v4;
   typedef floatx8 v8;
@@ -46,10 +55,14 @@ template <> struct VT<float> {
   static constexpr int per16 = 4;
 };
 
-// D += A B over one 32-wide inner block (bf16: one v_mfma_f32_16x16x32_bf16;
-// fp32: eight v_mfma_f32_16x16x4_f32, slot j of every lane in step j).
+// D += A B over one 32-wide inner block (bf16, fp16: one
+// v_mfma_f32_16x16x32_bf16 / _f16; fp32: eight v_mfma_f32_16x16x4_f32, slot
+// j of every lane in step j).
 __device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma(const f16x8& a, const f16x8& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ floatx4 mma(const floatx8& a, const floatx8& b, floatx4 c) {
 #pragma unroll
@@ -120,6 +133,12 @@ template <> __device__ __forceinline__ bf16x4 bload<bf16x4>(rsrc_t r, uint32_t o
 template <> __device__ __forceinline__ bf16x8 bload<bf16x8>(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+template <> __device__ __forceinline__ f16x4 bload<f16x4>(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ f16x8 bload<f16x8>(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 template <> __device__ __forceinline__ floatx4 bload<floatx4>(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -158,6 +177,9 @@ __device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t voff, uint32_t soff,
 // operations (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and nothing else.
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, f16x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, bf16x4 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
 }

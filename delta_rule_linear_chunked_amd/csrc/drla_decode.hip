@@ -117,7 +117,8 @@ hipError_t drla_launch_decode(const drla_decode_args* a) {
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
   if (units == 0) return hipSuccess;
   hipStream_t st = (hipStream_t)a->stream;
-  const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (a->f32 ? 8 : 0);
+  const int io = a->f32 ? 1 : a->f16 ? 2 : 0;
+  const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (io << 3);
 #define DRLA_DEC_CASE(K, DK_, DV_, KDA_, ET_) \
   case K:                                   \
     return launch_decode_v<DK_, DV_, KDA_, ET_>(P, units, st);
@@ -138,6 +139,14 @@ hipError_t drla_launch_decode(const drla_decode_args* a) {
     DRLA_DEC_CASE(13, 128, 64, true, float)
     DRLA_DEC_CASE(14, 64, 128, true, float)
     DRLA_DEC_CASE(15, 128, 128, true, float)
+    DRLA_DEC_CASE(16, 64, 64, false, f16)
+    DRLA_DEC_CASE(17, 128, 64, false, f16)
+    DRLA_DEC_CASE(18, 64, 128, false, f16)
+    DRLA_DEC_CASE(19, 128, 128, false, f16)
+    DRLA_DEC_CASE(20, 64, 64, true, f16)
+    DRLA_DEC_CASE(21, 128, 64, true, f16)
+    DRLA_DEC_CASE(22, 64, 128, true, f16)
+    DRLA_DEC_CASE(23, 128, 128, true, f16)
   }
 #undef DRLA_DEC_CASE
   return hipErrorInvalidValue;

@@ -64,8 +64,8 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st);
 template <int DK, int DV, bool KDA, typename ET>
 hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
 
-// GDN with bf16 inputs: the LDS-fed scan (drla_scan_lds.hip)
-template <int DK, int DV>
+// GDN with 16-bit inputs (T = bf16 or f16): the LDS-fed scan (drla_scan_lds.hip)
+template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
 
 }  // namespace drla

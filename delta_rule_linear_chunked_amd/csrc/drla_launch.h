@@ -24,7 +24,7 @@ typedef struct {
   int64_t total_tokens;
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;
-  int32_t kda, f32, inspect;
+  int32_t kda, f32, f16, inspect;  // f32 / f16: io dtype (neither: bf16)
   void* stream;
   void* const* stage_events;  // NULL, or 3 hipEvent_t recorded at kernel boundaries
 } drla_launch_args;
@@ -41,7 +41,7 @@ typedef struct {
   void* o;
   float* ht;
   int32_t n_seqs, h_qk, h_v, dk, dv;
-  int32_t kda, f32;
+  int32_t kda, f32, f16;
   void* stream;
 } drla_decode_args;
 

@@ -24,7 +24,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   pp.g = a->g;
   pp.tb = ws + a->off_tb;
   pp.pm = ws + a->off_pm;
-  // the LDS-fed scan (GDN, bf16) transposes K itself and needs no K~^T
+  // the LDS-fed scan (GDN, 16-bit inputs) transposes K itself and needs no K~^T
   constexpr bool kLdsScan = !KDA && sizeof(ET) == 2;
   pp.kt = kLdsScan ? nullptr : ws + a->off_kt;
   pp.kw = KDA ? ws + a->off_kw : nullptr;
@@ -66,7 +66,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   const int64_t nscan = (int64_t)a->n_seqs * a->h_v * (DV / 16);
   if (e == hipSuccess) {
     if constexpr (kLdsScan)
-      e = launch_scan_lds<DK, DV>(sp, nscan, a->inspect != 0, st);
+      e = launch_scan_lds<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
     else
       e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
   }
@@ -90,7 +90,8 @@ hipError_t drla_launch(const drla_launch_args* a) {
     s.cps = (int32_t)((s.seq_len + C - 1) / C);
   }
   s.n_seqs = a->n_seqs;
-  const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (a->f32 ? 8 : 0);
+  const int io = a->f32 ? 1 : a->f16 ? 2 : 0;
+  const int key = (a->dk == 128 ? 1 : 0) | (a->dv == 128 ? 2 : 0) | (a->kda ? 4 : 0) | (io << 3);
 #define DRLA_CASE(K, DK_, DV_, KDA_, ET_) \
   case K:                                 \
     return launch_all<DK_, DV_, KDA_, ET_>(a, s);
@@ -111,6 +112,14 @@ hipError_t drla_launch(const drla_launch_args* a) {
     DRLA_CASE(13, 128, 64, true, float)
     DRLA_CASE(14, 64, 128, true, float)
     DRLA_CASE(15, 128, 128, true, float)
+    DRLA_CASE(16, 64, 64, false, f16)
+    DRLA_CASE(17, 128, 64, false, f16)
+    DRLA_CASE(18, 64, 128, false, f16)
+    DRLA_CASE(19, 128, 128, false, f16)
+    DRLA_CASE(20, 64, 64, true, f16)
+    DRLA_CASE(21, 128, 64, true, f16)
+    DRLA_CASE(22, 64, 128, true, f16)
+    DRLA_CASE(23, 128, 128, true, f16)
     default:
       return hipErrorInvalidValue;
   }

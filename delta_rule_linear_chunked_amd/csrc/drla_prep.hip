@@ -586,6 +586,10 @@ DRLA_PREP_INST(64, false, bf16)
 DRLA_PREP_INST(128, false, bf16)
 DRLA_PREP_INST(64, true, bf16)
 DRLA_PREP_INST(128, true, bf16)
+DRLA_PREP_INST(64, false, f16)
+DRLA_PREP_INST(128, false, f16)
+DRLA_PREP_INST(64, true, f16)
+DRLA_PREP_INST(128, true, f16)
 DRLA_PREP_INST(64, false, float)
 DRLA_PREP_INST(128, false, float)
 DRLA_PREP_INST(64, true, float)

@@ -20,12 +20,12 @@
 //
 // Inside the workgroup wave w owns token tile w (16 tokens) for X, V', O,
 // and rows [16 (dk/64) w, ...) of the state for its update.  Per chunk the
-// waves exchange the state (as bf16/fp32 fragments) and R = V - X through
+// waves exchange the state (as 16-bit/fp32 fragments) and R = V - X through
 // LDS, with two barriers.  Every wave needs all six Tb fragments; each loads
 // at most two of them and the set is shared through LDS, so the chunk's
 // operands cross the CU's load path once.
 //
-// KDA with bf16 inputs (RING): the operand stream into registers bounds the
+// KDA with 16-bit inputs (RING): the operand stream into registers bounds the
 // kernel, so only each wave's own token tile of K e^B and Q e^B goes to
 // registers; K~^T, Tb, P, V and e^{b_n} come through a three-slot LDS ring
 // that two more waves fill with LDS-direct loads two chunks ahead.
@@ -70,13 +70,14 @@ struct ScanCtx {
 __device__ __forceinline__ int tb_frag(int j) { return j < 2 ? 2 * j : j + 2; }
 __device__ __forceinline__ int tb_share(int w, int s) { return min(2 * w + s, 5); }
 
-// One slot of the RING variant's operand ring (bf16).
-template <int DK>
+// One slot of the RING variant's operand ring (16-bit ET).
+template <int DK, typename ET>
 struct RingSlot {
-  bf16x8 kt[DK / 8][64];                         // K~^T fragments, index tile*2 + block
-  bf16x8 tb[6][64];                              // Tb fragments, tb_frag order
-  bf16x8 pm[6][64];                              // P fragments, same order
-  __attribute__((aligned(16))) bf16 v[C][16];    // V, this block's 16 columns
+  typedef typename VT<ET>::v8 V8;
+  V8 kt[DK / 8][64];                             // K~^T fragments, index tile*2 + block
+  V8 tb[6][64];                                  // Tb fragments, tb_frag order
+  V8 pm[6][64];                                  // P fragments, same order
+  __attribute__((aligned(16))) ET v[C][16];      // V, this block's 16 columns
   __attribute__((aligned(16))) float gam[256];   // e^{b_n} per key channel (dk used)
 };
 
@@ -156,8 +157,8 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
   __shared__ V8 Sf[KB][64];                      // state entering the chunk, as fragments (inner = key channel)
   __shared__ V8 Rf[2][64];                       // R = V - X, as B fragments (inner = token)
   __shared__ V8 Tbs[RING ? 1 : 2][6][64];        // Tb fragments of chunk i (slot i % 2)
-  __shared__ __attribute__((aligned(16))) unsigned char ring_raw[RING ? NS * sizeof(RingSlot<DK>) : 16];
-  RingSlot<DK>* const ring = (RingSlot<DK>*)ring_raw;
+  __shared__ __attribute__((aligned(16))) unsigned char ring_raw[RING ? NS * sizeof(RingSlot<DK, ET>) : 16];
+  RingSlot<DK, ET>* const ring = (RingSlot<DK, ET>*)ring_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -207,7 +208,7 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
       const uint32_t voff = (uint32_t)(lane >> 1) * vstride + 16u * (uint32_t)(lane & 1);
       const uint32_t lo = 16u * (uint32_t)lane;
       auto issue = [&](int i) {
-        RingSlot<DK>& sl = ring[i % NS];
+        RingSlot<DK, ET>& sl = ring[i % NS];
         const int64_t ch = (int64_t)h * P.nc + x.c0 + i;
         if (w == 4) {
           const rsrc_t kr = make_rsrc((const V8*)P.kt + ch * (C * DK / 8), C * DK * es);
@@ -304,7 +305,7 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
     V8 tb[6], kt[MT][2], pb[2];
     V4 vv;
     floatx4 gm[MT];
-    const RingSlot<DK>& sl = ring[RING ? i % NS : 0];
+    const RingSlot<DK, ET>& sl = ring[RING ? i % NS : 0];
     if constexpr (RING) {
       vv = *(const V4*)&sl.v[16 * w + c16][4 * g4];
     } else {
@@ -484,6 +485,10 @@ DRLA_SCAN_INST(64, 64, true, bf16)
 DRLA_SCAN_INST(128, 64, true, bf16)
 DRLA_SCAN_INST(64, 128, true, bf16)
 DRLA_SCAN_INST(128, 128, true, bf16)
+DRLA_SCAN_INST(64, 64, true, f16)
+DRLA_SCAN_INST(128, 64, true, f16)
+DRLA_SCAN_INST(64, 128, true, f16)
+DRLA_SCAN_INST(128, 128, true, f16)
 DRLA_SCAN_INST(64, 64, false, float)
 DRLA_SCAN_INST(128, 64, false, float)
 DRLA_SCAN_INST(64, 128, false, float)

@@ -1,4 +1,5 @@
-// Sequential state scan fused with the output Map, LDS-fed (GDN, bf16).
+// Sequential state scan fused with the output Map, LDS-fed (GDN, 16-bit
+// inputs: bf16 or fp16).
 //
 // Same computation as drla_scan.hip -- operators #5 (H) and #6 (O) of the
 // Map-Reduce-Map split in "Empowering Hybrid Attention Models on NPUs",
@@ -38,21 +39,24 @@ namespace drla {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-// Transposing LDS read (see above); `p` must be 8-byte aligned.
-__device__ __forceinline__ bf16x4 ds_read_tr(const void* p) {
+// Transposing LDS read (see above) of 16-bit elements of type T; `p` must
+// be 8-byte aligned.
+template <typename T>
+__device__ __forceinline__ typename VT<T>::v4 ds_read_tr(const void* p) {
   const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(typename VT<T>::v4, v);
 }
 
 
-template <int DK>
+template <int DK, typename T>
 struct LdsSlot {
+  typedef typename VT<T>::v8 H8;
   static constexpr int RB = DK * 2;                       // bytes per K/Q row
   __attribute__((aligned(16))) unsigned char k[C * RB];  // K rows, 16-byte chunks swizzled
   __attribute__((aligned(16))) unsigned char q[C * RB];  // Q rows, same
-  bf16x8 tb[6][64];                                       // Tv fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
-  bf16x8 pm[6][64];                                       // P Tb fragments, same order
-  __attribute__((aligned(16))) bf16 v[C][16];             // V, this block's 16 columns
+  H8 tb[6][64];                                       // Tv fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+  H8 pm[6][64];                                       // P Tb fragments, same order
+  __attribute__((aligned(16))) T v[C][16];             // V, this block's 16 columns
   __attribute__((aligned(16))) float eb[C];               // e^{b_r}
   __attribute__((aligned(16))) float ebn[C];              // e^{b_n - b_r}
 };
@@ -65,8 +69,10 @@ __device__ __forceinline__ int swz(int r, int j) {
   return r * (DK * 2) + ((j ^ (r & (NCH - 1))) << 4);
 }
 
-template <int DK, int DV, bool INSPECT>
+template <int DK, int DV, bool INSPECT, typename T>
 __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
+  typedef typename VT<T>::v8 H8;
+  typedef typename VT<T>::v4 H4;
   constexpr int KB = DK / 32, KT = DK / 16, NB = DV / 16;
   constexpr int NS = 3;                       // ring slots
   constexpr int PF = 6;                       // L2 touch distance, chunks
@@ -74,9 +80,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int RPI = 1024 / (DK * 2);        // rows per 1 KiB copy
   constexpr int kIssued = C / RPI + 6 + 2;    // copies per loader wave and chunk
   constexpr int kTouched = 2;                 // touches per chunk (loader wave 1)
-  __shared__ LdsSlot<DK> slot[NS];
-  __shared__ bf16x8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
-  __shared__ bf16x8 vbuf[2][2][64];   // R of the last two chunks, A fragments (inner = token)
+  __shared__ LdsSlot<DK, T> slot[NS];
+  __shared__ H8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
+  __shared__ H8 vbuf[2][2][64];   // R of the last two chunks, A fragments (inner = token)
   __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -106,9 +112,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
   const int col = 16 * nb + c16;
-  const bf16* kg = (const bf16*)P.k;
-  const bf16* qg = (const bf16*)P.q;
-  const bf16* vg = (const bf16*)P.v;
+  const T* kg = (const T*)P.k;
+  const T* qg = (const T*)P.q;
+  const T* vg = (const T*)P.v;
 
   // ---- loaders: copy chunk i into ring slot i % NS ------------------------
   // wave 1: K rows, Tb, decay factors; wave 2: Q rows, P, V.  Each copy goes
@@ -131,29 +137,29 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     return (uint32_t)(left < C ? left : C);
   };
   auto row_rsrc = [&](int i) -> rsrc_t {
-    const bf16* src = (w == 1 ? kg : qg) + ((ts + (int64_t)C * i) * P.h_qk + hk) * DK;
+    const T* src = (w == 1 ? kg : qg) + ((ts + (int64_t)C * i) * P.h_qk + hk) * DK;
     return make_rsrc(src, (chunk_len(i) - 1) * kstride + DK * 2);
   };
   auto v_rsrc = [&](int i) -> rsrc_t {
-    const bf16* src = vg + ((ts + (int64_t)C * i) * P.h_v + h) * DV + 16 * nb;
+    const T* src = vg + ((ts + (int64_t)C * i) * P.h_v + h) * DV + 16 * nb;
     return make_rsrc(src, (chunk_len(i) - 1) * vstride + 32);
   };
   auto frag_rsrc = [&](int i) -> rsrc_t {
     const int64_t ch = (int64_t)h * P.nc + c0 + i;
-    return make_rsrc((const bf16x8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64), 8 * 1024);
+    return make_rsrc((const H8*)(w == 1 ? P.tb : P.pm) + ch * (8 * 64), 8 * 1024);
   };
   auto gam_rsrc = [&](int i) -> rsrc_t {
     const int64_t ch = (int64_t)h * P.nc + c0 + i;
     return make_rsrc(P.gam + ch * (2 * C), 2 * C * 4);
   };
   auto issue = [&](int i) {
-    LdsSlot<DK>& sl = slot[i % NS];
+    LdsSlot<DK, T>& sl = slot[i % NS];
     const rsrc_t rr = row_rsrc(i);
     unsigned char* dst = w == 1 ? sl.k : sl.q;
 #pragma unroll
     for (int u = 0; u < C / RPI; ++u) lds_dma16(rr, roff[u % NP] + (uint32_t)(u / NP) * (NP * RPI) * kstride, 0, dst + u * 1024);
     const rsrc_t fr = frag_rsrc(i);
-    bf16x8(*fdst)[64] = w == 1 ? sl.tb : sl.pm;
+    H8(*fdst)[64] = w == 1 ? sl.tb : sl.pm;
     const uint32_t lo = 16u * lane;
     lds_dma16(fr, lo + 0 * 1024, 0, &fdst[0][0]);
     lds_dma16(fr, lo + 2 * 1024, 0, &fdst[1][0]);
@@ -182,14 +188,14 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     const int64_t tc = ts + (int64_t)C * i;
     const uint32_t lrow = (chunk_len(i) - 1);
     if (gi < 2 * KL) {  // K or Q rows, line gi % KL
-      const bf16* src = (gi < KL ? kg : qg) + (tc * P.h_qk + hk) * DK;
+      const T* src = (gi < KL ? kg : qg) + (tc * P.h_qk + hk) * DK;
       lds_dma4(make_rsrc(src, lrow * kstride + DK * 2), (uint32_t)lane * kstride + 128u * (uint32_t)(gi % KL), 0, touch);
     } else if (gi < 2 * KL + 2) {  // Tb or P fragments
       const int64_t ch = (int64_t)h * P.nc + c0 + i;
-      const bf16x8* fr = (const bf16x8*)(gi == 2 * KL ? P.tb : P.pm) + ch * (8 * 64);
+      const H8* fr = (const H8*)(gi == 2 * KL ? P.tb : P.pm) + ch * (8 * 64);
       lds_dma4(make_rsrc(fr, 8 * 1024), 128u * lane, 0, touch);
     } else if (gi < 2 * KL + 2 + VL) {  // the head's V rows, line gi - 2 KL - 2
-      const bf16* src = vg + (tc * P.h_v + h) * DV;
+      const T* src = vg + (tc * P.h_v + h) * DV;
       lds_dma4(make_rsrc(src, lrow * vstride + DV * 2), (uint32_t)lane * vstride + 128u * (uint32_t)(gi - 2 * KL - 2), 0,
                touch);
     } else {  // decay factors
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 
   // ---- prologue ------------------------------------------------------------
   floatx4 S[KT];  // state wave: tile mt, element e is key channel state_row(mt, 4g + e)
-  bf16x8 sf[KB];   // state wave: S as bf16 B fragments (inner = key channel)
+  H8 sf[KB];   // state wave: S as 16-bit B fragments (inner = key channel)
   if (w == 0) {
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         S[mt][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] : 0.f;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
-      sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+      sf[p] = pack<T>(S[2 * p], S[2 * p + 1]);
       sbuf[0][p][lane] = sf[p];
     }
   } else if (w < 3 && n > 0) {
@@ -235,9 +241,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   // output wave: add (P Tb) R of chunk i (first token t0i) to the partial O^T
   // and store it; rows past the end of the sequence are dropped
   floatx4 o[4];
-  bf16x8 pmf[6];
+  H8 pmf[6];
   auto finish_output = [&](int64_t t0i, int i) {
-    const bf16x8 vf0 = vbuf[i & 1][0][lane], vf1 = vbuf[i & 1][1][lane];
+    const H8 vf0 = vbuf[i & 1][0][lane], vf1 = vbuf[i & 1][1][lane];
     o[0] = mma(vf0, pmf[0], o[0]);
     o[1] = mma(vf0, pmf[1], o[1]);
     o[2] = mma(vf0, pmf[2], o[2]);
@@ -246,9 +252,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     o[3] = mma(vf1, pmf[5], o[3]);
     const int64_t left = te - t0i;
     const uint32_t len = (uint32_t)(left < C ? left : C);
-    const rsrc_t orr = make_rsrc((bf16*)P.o + t0i * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+    const rsrc_t orr = make_rsrc((T*)P.o + t0i * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<bf16>(o[nt]));
+    for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<T>(o[nt]));
   };
 
   int64_t t0prev = 0;  // output wave: first token of the chunk in o
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   // the registers one role keeps across chunks are free in the others.
   if (w == 0) {
     for (int t = 0; t < n; ++t) {
-      const LdsSlot<DK>& sl = slot[t % NS];
+      const LdsSlot<DK, T>& sl = slot[t % NS];
       const int64_t ch = (int64_t)h * P.nc + c0 + t;
       // ---------------- state wave ----------------
       // Nothing of this wave is in flight here; saying so lets the compiler
@@ -269,28 +275,28 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // the update.  `sf` holds the state entering the chunk (packed at the
       // end of the last chunk).
       if (INSPECT) {
-        bf16x8* hp = (bf16x8*)P.insp_h + ch * (int64_t)(DK * DV / 8);
+        H8* hp = (H8*)P.insp_h + ch * (int64_t)(DK * DV / 8);
 #pragma unroll
         for (int p = 0; p < KB; ++p) hp[(nb * KB + p) * 64 + lane] = sf[p];
       }
-      bf16x8 tbf[6];
+      H8 tbf[6];
 #pragma unroll
       for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
       // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
       // group addresses row 16 nt + 4g + e', columns 4q..4q+3
-      bf16x4 vv[4];
+      H4 vv[4];
       floatx4 ebv[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        vv[nt] = ds_read_tr(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
+        vv[nt] = ds_read_tr<T>(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
         ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
       }
       const float gam = sl.eb[C - 1];
-      bf16x8 kr[KB][4];
+      H8 kr[KB][4];
 #pragma unroll
       for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const bf16x8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+        for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
       __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles (lane holds [16 nt + 4g + e][c]),
       // interleaved with work that does not depend on it: the K^T reads of
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       floatx4 x[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) x[nt] = zero4();
-      bf16x4 kt[2][KT][2];
+      H4 kt[2][KT][2];
       floatx4 vfl[4];
       static_assert(2 * 2 * KT == 2 * 4 * KB, "two K^T reads per product");
       constexpr int NV = (4 * KT + 16 + 4 * KB - 1) / (4 * KB);  // vector operations per product
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
           const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
           const int r0 = 32 * p + 4 * g4 + (c16 >> 2) + 16 * hf;
           const int d = state_row(mt, 4 * (c16 & 3));
-          kt[p][mt][hf] = ds_read_tr(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          kt[p][mt][hf] = ds_read_tr<T>(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
         }
 #pragma unroll
         for (int jj = 0; jj < NV; ++jj) {
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - ebv[nt][e] * x[nt][e];
-      const bf16x8 rf0 = pack<bf16>(rr[0], rr[1]), rf1 = pack<bf16>(rr[2], rr[3]);
+      const H8 rf0 = pack<T>(rr[0], rr[1]), rf1 = pack<T>(rr[2], rr[3]);
       // R goes to the output wave, which multiplies it with P Tb
       vbuf[t & 1][0][lane] = rf0;
       vbuf[t & 1][1][lane] = rf1;
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       vt[3] = mma(tbf[4], rf0, zero4());
       vt[2] = mma(tbf[3], rf1, vt[2]);
       vt[3] = mma(tbf[5], rf1, vt[3]);
-      const bf16x8 vs0 = pack<bf16>(vt[0], vt[1]), vs1 = pack<bf16>(vt[2], vt[3]);
+      const H8 vs0 = pack<T>(vt[0], vt[1]), vs1 = pack<T>(vt[2], vt[3]);
       if (INSPECT) {
         // V' itself, for the intermediate checks
         floatx4 vq[4];
@@ -356,19 +362,19 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) vq[nt][e] = vt[nt][e] / env[e];
         }
-        bf16x8* vp = (bf16x8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
-        vp[(nb * 2 + 0) * 64 + lane] = pack<bf16>(vq[0], vq[1]);
-        vp[(nb * 2 + 1) * 64 + lane] = pack<bf16>(vq[2], vq[3]);
+        H8* vp = (H8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
+        vp[(nb * 2 + 0) * 64 + lane] = pack<T>(vq[0], vq[1]);
+        vp[(nb * 2 + 1) * 64 + lane] = pack<T>(vq[2], vq[3]);
       }
       // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
-          S[mt] = mma(cat<bf16>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1, S[mt]);
+          S[mt] = mma(cat<T>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1, S[mt]);
 #pragma unroll
       for (int p = 0; p < KB; ++p) {
-        sf[p] = pack<bf16>(S[2 * p], S[2 * p + 1]);
+        sf[p] = pack<T>(S[2 * p], S[2 * p + 1]);
         sbuf[(t + 1) & 1][p][lane] = sf[p];
       }
       lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
@@ -382,20 +388,20 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     }
   } else if (w == 3) {
     for (int t = 0; t < n; ++t) {
-      const LdsSlot<DK>& sl = slot[t % NS];
+      const LdsSlot<DK, T>& sl = slot[t % NS];
       const int64_t t0 = ts + (int64_t)C * t;
       // ---------------- output wave ----------------
       // finish the previous chunk: its R was published at the last barrier
       if (t > 0) finish_output(t0prev, t - 1);
       // state part of this chunk's O^T: lane holds [column 4g + e][token 16 nt + c]
-      bf16x8 so[KB];
+      H8 so[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) so[p] = sbuf[t & 1][p][lane];
-      bf16x8 qr[4][KB];
+      H8 qr[4][KB];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int p = 0; p < KB; ++p) qr[nt][p] = *(const bf16x8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
+        for (int p = 0; p < KB; ++p) qr[nt][p] = *(const H8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
       float ebt[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) ebt[nt] = sl.eb[16 * nt + c16];
@@ -432,20 +438,27 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
   if (nblk > 0) {
     if (inspect)
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T>), dim3((unsigned)nblk), dim3(256), 0, st, P);
     else
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T>), dim3((unsigned)nblk), dim3(256), 0, st, P);
   }
   return hipGetLastError();
 }
 
-template hipError_t launch_scan_lds<64, 64>(const ScanParams&, int64_t, bool, hipStream_t);
-template hipError_t launch_scan_lds<128, 64>(const ScanParams&, int64_t, bool, hipStream_t);
-template hipError_t launch_scan_lds<64, 128>(const ScanParams&, int64_t, bool, hipStream_t);
-template hipError_t launch_scan_lds<128, 128>(const ScanParams&, int64_t, bool, hipStream_t);
+#define DRLA_SCAN_LDS_INST(DK_, DV_, T_) \
+  template hipError_t launch_scan_lds<DK_, DV_, T_>(const ScanParams&, int64_t, bool, hipStream_t);
+DRLA_SCAN_LDS_INST(64, 64, bf16)
+DRLA_SCAN_LDS_INST(128, 64, bf16)
+DRLA_SCAN_LDS_INST(64, 128, bf16)
+DRLA_SCAN_LDS_INST(128, 128, bf16)
+DRLA_SCAN_LDS_INST(64, 64, f16)
+DRLA_SCAN_LDS_INST(128, 64, f16)
+DRLA_SCAN_LDS_INST(64, 128, f16)
+DRLA_SCAN_LDS_INST(128, 128, f16)
+#undef DRLA_SCAN_LDS_INST
 
 }  // namespace drla

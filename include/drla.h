@@ -33,6 +33,10 @@
  *   h0, ht      [N, h_v, dk, dv] fp32 (key-major state per sequence, head)
  *   o           [T, h_v, dv]     io dtype
  *   cu_seqlens  [N+1] int32, cu[0] = 0, non-decreasing, cu[N] = T.
+ * io dtype: bf16, fp16 (the precision of the experiment setup, Section 7.1:
+ * FP16 q/k/v with fp32 gates and states) or fp32;
+ * arithmetic accumulates in fp32 and chunk intermediates are stored in the
+ * io dtype.
  * v-head h reads q/k head h / (h_v / h_qk) (contiguous groups).  Without
  * cu_seqlens the T tokens are N equal-length sequences (a dense batch).
  * Chunks start at every sequence start; a sequence's last chunk may be short.
@@ -74,7 +78,7 @@ typedef enum {
   DRLA_ERR_HIP = 8          /* a HIP launch or runtime call failed            */
 } drla_status;
 
-typedef enum { DRLA_BF16 = 0, DRLA_F32 = 1 } drla_dtype;
+typedef enum { DRLA_BF16 = 0, DRLA_F32 = 1, DRLA_F16 = 2 } drla_dtype;
 
 typedef struct {
   int32_t n_seqs;       /* N >= 1                                          */

@@ -1,8 +1,8 @@
 """Parity of the decode step (gdn_decode / kda_decode, through the C ABI)
 with the fp64 oracle's token recurrence.
 
-Same bar as prefill: max|x - y| / max|y| <= 2e-2 for bf16 inputs and
-<= 1e-4 for fp32 inputs, on o and on the state."""
+Same bar as prefill: max|x - y| / max|y| <= 2e-2 for bf16 inputs, 5e-3 for
+fp16 and 1e-4 for fp32, on o and on the state."""
 import numpy as np
 import pytest
 
@@ -43,7 +43,7 @@ def _inputs(kind, io, dk, dv, lens, h_qk=2, h_v=4, h0_std=0.05, seed=5):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_decode_step_matches_oracle(drla, kind, io, dk, dv):
     """Six sequences, one token each, grouped heads, a nonzero state."""

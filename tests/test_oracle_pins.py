@@ -269,6 +269,17 @@ def test_bf16_round_matches_torch():
     np.testing.assert_array_equal(ours, ref)
 
 
+def test_f16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-4, 4, 100000)).astype(np.float32)
+    # exact ties between neighbouring halves (1 + 2^-11, 1 + 3 * 2^-11) and a subnormal
+    x[:4] = np.array([1.00048828125, 1.00146484375, -1.00048828125, 3e-6], dtype=np.float32)
+    ours = W.f16_round(x)
+    ref = torch.from_numpy(x).to(torch.float16).float().numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
 def test_generator_is_deterministic_and_shaped():
     s = W.WORKLOADS["gdn_varlen"]
     assert s.lens == (6745, 1169, 1890, 2330, 1905, 6666, 7188, 4983)

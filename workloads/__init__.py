@@ -30,7 +30,7 @@ class Spec:
     lens      sequence lengths; a packed batch uses cu_seqlens.
     h_qk/h_v  query/key heads and value heads; v-head h reads q/k head
               h // (h_v // h_qk).
-    io        "bf16" or "f32": storage type of q, k, v (and o).
+    io        "bf16", "f16" or "f32": storage type of q, k, v (and o).
     g_lo/g_hi the log-gate is drawn as -U(g_lo, g_hi).
     h0_std    0 for a zero initial state, else N(0, h0_std) per element.
     varlen    True to pass cu_seqlens even for one sequence.
@@ -89,8 +89,21 @@ DECODE_WORKLOADS = {
 }
 
 
+# The prefill configs with fp16 q, k, v (the precision of the pages'
+# experiment setup).
+F16_WORKLOADS = {
+    "gdn_prefill_f16": Spec("gdn_prefill_f16", "gdn", (4096,), 16, 16, 128, 128,
+                            "f16", 0.01, 0.2, 0.0, seed=1),
+    "kda_prefill_f16": Spec("kda_prefill_f16", "kda", (4096,), 16, 16, 128, 128,
+                            "f16", 0.005, 0.15, 0.02, seed=2),
+}
+
+
 def spec_by_name(name: str) -> Spec:
-    return WORKLOADS[name] if name in WORKLOADS else DECODE_WORKLOADS[name]
+    for table in (WORKLOADS, DECODE_WORKLOADS, F16_WORKLOADS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -102,6 +115,13 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     lsb = (bits >> 16) & 1
     bits = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
     return bits.view(np.float32)
+
+
+def f16_round(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest IEEE half (ties to even), returned
+    as float32 holding exactly representable values (inputs here are far
+    inside the half range)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -120,7 +140,8 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
 def make_inputs(spec: Spec, seed: Optional[int] = None) -> dict:
     """Draw one problem.  Returns numpy arrays:
 
-    q, k   [T, h_qk, dk]   float32 (bf16-representable when io == "bf16")
+    q, k   [T, h_qk, dk]   float32 (bf16- / fp16-representable when io is
+                           "bf16" / "f16")
     v      [T, h_v, dv]    float32 (same)
     beta   [T, h_v]        float32, sigmoid(N(0,1))
     g      [T, h_v] or [T, h_v, dk]  float32 log-decay, -U(g_lo, g_hi)
@@ -144,7 +165,12 @@ def make_inputs(spec: Spec, seed: Optional[int] = None) -> dict:
     if spec.h0_std > 0:
         h0 = (spec.h0_std * rng.standard_normal(
             (len(lens), spec.h_v, spec.dk, spec.dv))).astype(np.float32)
-    cast = bf16_round if spec.io == "bf16" else (lambda a: a.astype(np.float32))
+    if spec.io == "bf16":
+        cast = bf16_round
+    elif spec.io == "f16":
+        cast = f16_round
+    else:
+        cast = lambda a: a.astype(np.float32)  # noqa: E731
     cu = np.zeros(len(lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     return dict(q=cast(q), k=cast(k), v=cast(v),
