@@ -13,6 +13,8 @@ Two independent fp64 implementations live here:
     Section 2.1 (state updated from K_t, V_t, then output read from the
     updated state with Q_t), GDN with a scalar gate and KDA with a
     per-channel gate.  This is the truth every GPU result is compared to.
+    ``recurrence_decay`` (same file) is the decay-only form of RetNet and
+    GLA that the page names in Section 8: no beta, no delta-rule erase.
 
 ``chunked``     (numpy, ``chunked.py``) -- the chunkwise Map-Reduce-Map
     evaluation the same page describes in Section 2.1 ("Chunkwise
@@ -68,6 +70,12 @@ def _load():
                           ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp,
                           ctypes.c_int]
             f.restype = ctypes.c_int
+            f = lib.oracle_decay_f64
+            f.argtypes = [ctypes.c_int, ctypes.c_int,
+                          ctypes.POINTER(ctypes.c_int64),
+                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                          ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
+            f.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -111,6 +119,30 @@ def recurrence(q, k, v, beta, g, h0=None, cu_seqlens=None, kda=False,
     return o, ht
 
 
+def recurrence_decay(q, k, v, g, h0=None, cu_seqlens=None, per_channel=False):
+    """fp64 token recurrence of decay-only linear attention (RetNet / GLA
+    style, no delta rule: S_t = Diag(e^{g_t}) S_{t-1} + k_t v_t^T,
+    o_t = S_t^T q_t).  Layouts as `recurrence`, without beta; g is
+    [T, h_v] (scalar gate) or [T, h_v, dk] (per_channel).  Returns
+    (o, ht) in float64."""
+    lib = _load()
+    q, k, v, g = map(_f64, (q, k, v, g))
+    T, h_qk, dk = q.shape
+    _, h_v, dv = v.shape
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else \
+        np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    n = len(cu) - 1
+    h0a = None if h0 is None else _f64(h0)
+    o = np.zeros((T, h_v, dv), dtype=np.float64)
+    ht = np.zeros((n, h_v, dk, dv), dtype=np.float64)
+    rc = lib.oracle_decay_f64(
+        int(bool(per_channel)), n, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        h_qk, h_v, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0a), _ptr(o), _ptr(ht))
+    if rc != 0:
+        raise ValueError("oracle: malformed arguments")
+    return o, ht
+
+
 from .chunked import chunked  # noqa: E402  (numpy form, no C needed)
 
-__all__ = ["recurrence", "chunked", "build"]
+__all__ = ["recurrence", "recurrence_decay", "chunked", "build"]

@@ -128,3 +128,65 @@ int oracle_delta_rule_f64(int kda, int n_seqs, const int64_t* cu_seqlens,
   pthread_mutex_destroy(&J.lock);
   return 0;
 }
+
+/*
+ * Decay-only linear attention (no delta rule): the temporal-decay form of
+ * RetNet and GLA that "Empowering Hybrid Attention Models on NPUs" names in
+ * Section 8 (Related Work) beside GDN and KDA.  Same layouts, no beta:
+ *
+ *   scalar gate      S_t = exp(g_t) S_{t-1} + k_t v_t^T
+ *   per-channel gate S_t = Diag(exp(g_t)) S_{t-1} + k_t v_t^T
+ *   both:            o_t = S_t^T q_t
+ *
+ * evaluated in the order: decay S; S += k v^T; o = S^T q.
+ */
+typedef struct {
+  int per_channel, n_seqs, h_qk, h_v, dk, dv;
+  const int64_t* cu;
+  const double *q, *k, *v, *g, *h0;
+  double *o, *ht;
+} decay_job_t;
+
+static void run_decay_unit(const decay_job_t* J, int unit, double* S) {
+  const int seq = unit / J->h_v, h = unit % J->h_v;
+  const int hk = h / (J->h_v / J->h_qk);
+  const int dk = J->dk, dv = J->dv;
+  const size_t sidx = ((size_t)seq * J->h_v + h) * (size_t)dk * dv;
+  if (J->h0)
+    memcpy(S, J->h0 + sidx, sizeof(double) * dk * dv);
+  else
+    memset(S, 0, sizeof(double) * dk * dv);
+  for (int64_t t = J->cu[seq]; t < J->cu[seq + 1]; ++t) {
+    const double* qt = J->q + ((size_t)t * J->h_qk + hk) * dk;
+    const double* kt = J->k + ((size_t)t * J->h_qk + hk) * dk;
+    const double* vt = J->v + ((size_t)t * J->h_v + h) * dv;
+    for (int i = 0; i < dk; ++i) {
+      const double a = J->per_channel ? exp(J->g[((size_t)t * J->h_v + h) * dk + i])
+                                      : exp(J->g[(size_t)t * J->h_v + h]);
+      for (int j = 0; j < dv; ++j) S[i * dv + j] = a * S[i * dv + j] + kt[i] * vt[j];
+    }
+    double* ot = J->o + ((size_t)t * J->h_v + h) * dv;
+    for (int j = 0; j < dv; ++j) ot[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) ot[j] += S[i * dv + j] * qt[i];
+  }
+  if (J->ht) memcpy(J->ht + sidx, S, sizeof(double) * dk * dv);
+}
+
+/* Single-threaded (test sizes).  Returns 0 on success, -1 on a malformed
+ * argument. */
+int oracle_decay_f64(int per_channel, int n_seqs, const int64_t* cu_seqlens,
+                     int h_qk, int h_v, int dk, int dv,
+                     const double* q, const double* k, const double* v,
+                     const double* g, const double* h0, double* o, double* ht) {
+  if (n_seqs < 0 || h_qk <= 0 || h_v <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (h_v % h_qk != 0) return -1;
+  if (!cu_seqlens || !q || !k || !v || !g || !o) return -1;
+  for (int s = 0; s < n_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+  decay_job_t J = {per_channel, n_seqs, h_qk, h_v, dk, dv, cu_seqlens, q, k, v, g, h0, o, ht};
+  double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+  for (int u = 0; u < n_seqs * h_v; ++u) run_decay_unit(&J, u, S);
+  free(S);
+  return 0;
+}

@@ -291,3 +291,61 @@ def test_generator_is_deterministic_and_shaped():
     np.testing.assert_allclose(np.linalg.norm(a["k"].astype(np.float64), axis=-1), 1.0, atol=1e-2)
     assert np.all(W.bf16_round(a["q"]) == a["q"])
     assert np.all((a["g"] <= -0.01) & (a["g"] >= -0.2))
+
+
+# ---- decay-only linear attention (RetNet / GLA form, no delta rule) --------
+
+def _decay_parallel_form(q, k, v, g, h0, per_channel):
+    """The quadratic ("parallel") form of decay-only linear attention, per
+    head, written independently of the token recurrence:
+      o_t = (q_t (.) e^{B_t})^T S_0 + sum_{s<=t} sum_d q_td e^{B_td - B_sd} k_sd v_s
+      S_T = Diag(e^{B_T}) S_0 + sum_s (k_s (.) e^{B_T - B_s}) v_s^T
+    with B the inclusive prefix sum of the log-gates (per key channel, or
+    one value broadcast over the channels)."""
+    q, k, v, g, h0 = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, h0))
+    T, h_v, dk = q.shape[0], v.shape[1], q.shape[2]
+    grp = h_v // q.shape[1]
+    o = np.zeros_like(v)
+    hts = []
+    for h in range(h_v):
+        qh, kh, vh = q[:, h // grp], k[:, h // grp], v[:, h]
+        gh = g[:, h] if per_channel else np.repeat(g[:, h][:, None], dk, axis=1)
+        B = np.cumsum(gh, axis=0)                                  # [T, dk]
+        S0 = h0[0, h]
+        for t in range(T):
+            w = np.exp(B[t][None, :] - B[: t + 1])                 # [t+1, dk]
+            a = (qh[t][None, :] * w * kh[: t + 1]).sum(axis=1)     # [t+1]
+            o[t, h] = (qh[t] * np.exp(B[t])) @ S0 + a @ vh[: t + 1]
+        wT = np.exp(B[-1][None, :] - B)
+        hts.append(np.exp(B[-1])[:, None] * S0 + (kh * wT).T @ vh)
+    return o, np.stack(hts)[None]
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_decay_only_matches_parallel_form(per_channel):
+    """Catches a wrong decay placement (after instead of before the write),
+    a dropped initial-state term, or an erase term left in."""
+    x = _inputs("kda" if per_channel else "gdn", lens=(23,), h_qk=1, h_v=2, dk=6, dv=4,
+                g_lo=0.05, g_hi=0.6)
+    o, ht = oracle.recurrence_decay(x["q"], x["k"], x["v"], x["g"], x["h0"],
+                                    per_channel=per_channel)
+    o_p, ht_p = _decay_parallel_form(x["q"], x["k"], x["v"], x["g"], x["h0"], per_channel)
+    assert _rel(o, o_p) < 1e-12 and _rel(ht, ht_p) < 1e-12
+
+
+def test_decay_only_without_decay_is_causal_linear_attention():
+    """g = 0, zero state: O = tril(Q K^T) V, the undecayed causal form."""
+    x = _inputs("gdn", lens=(17,), dk=5, dv=3, h0_std=0.0)
+    g = np.zeros_like(x["g"])
+    o, ht = oracle.recurrence_decay(x["q"], x["k"], x["v"], g, None)
+    Q, K, V = x["q"][:, 0].astype(np.float64), x["k"][:, 0].astype(np.float64), x["v"][:, 0]
+    assert _rel(o[:, 0], np.tril(Q @ K.T) @ V) < 1e-12
+    assert _rel(ht[0, 0], K.T @ V) < 1e-12
+
+
+def test_decay_only_uniform_channels_equal_scalar_gate():
+    x = _inputs("gdn", lens=(30,), h_qk=1, h_v=2, dk=4, dv=4)
+    gk = np.repeat(x["g"][:, :, None], 4, axis=2)
+    o1, h1 = oracle.recurrence_decay(x["q"], x["k"], x["v"], x["g"], x["h0"])
+    o2, h2 = oracle.recurrence_decay(x["q"], x["k"], x["v"], gk, x["h0"], per_channel=True)
+    assert _rel(o1, o2) < 1e-13 and _rel(h1, h2) < 1e-13
