@@ -10,7 +10,8 @@ Workloads (seeded, synthetic): gdn_prefill (default: 1 x 4096 tokens,
 16 heads, dk = dv = 128, bf16), kda_prefill, gdn_varlen, gdn_long, gdn_tiny.
 gdn_decode / kda_decode time one decode step instead (256 sequences, one
 token each, from a nonzero state), under their own metric; gdn_prefill_f16 /
-kda_prefill_f16 are the prefill configs with fp16 q, k, v.
+kda_prefill_f16 are the prefill configs with fp16 q, k, v; ret_prefill /
+gla_prefill run decay-only linear attention (no delta rule) at that shape.
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN/KDA chunked-prefill tokens/s at H16 d128 T4096; % of MFMA/HBM roofline"
 DECODE_METRIC = "GDN/KDA decode-step tokens/s (one token per sequence); % of HBM roofline"
+DECAY_METRIC = "decay-only linear attention (RetNet/GLA form) chunked-prefill tokens/s; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 (and fp16) MFMA, published
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA, published
@@ -43,7 +45,8 @@ def kernel_costs(spec, n_tokens, n_seqs):
     skipped)."""
     es = 4 if spec.io == "f32" else 2
     dk, dv, hv, hqk = spec.dk, spec.dv, spec.h_v, spec.h_qk
-    kda = spec.kind == "kda"
+    kda = spec.kind in ("kda", "gla")          # per-channel gate
+    nb = 0 if spec.kind in ("ret", "gla") else 4  # beta bytes (decay-only: none)
     th = n_tokens * hv                         # token x value head
     tq = n_tokens * hqk                        # token x query/key head
     n_chunks = sum((L + CHUNK - 1) // CHUNK for L in spec.lens)
@@ -51,7 +54,7 @@ def kernel_costs(spec, n_tokens, n_seqs):
     g_bytes = th * (dk if kda else 1) * 4
     state = n_seqs * hv * dk * dv * 4
     h0 = state if spec.h0_std > 0 else 0
-    prep_b = 2 * tq * dk * es + th * 4 + g_bytes
+    prep_b = 2 * tq * dk * es + th * nb + g_bytes
     scan_b = 2 * tq * dk * es + th * dv * es + (0 if kda else g_bytes) + h0 \
         + th * dv * es + state
     C = CHUNK
@@ -132,6 +135,21 @@ def cpu_baseline(x, spec, n_tokens, budget_s=10.0):
     repeated until about `budget_s` of wall time."""
     import oracle
     cores = len(os.sched_getaffinity(0))
+    if spec.kind in ("ret", "gla"):
+        # decay-only linear attention: the single-threaded fp64 recurrence
+        reps, t_total = 0, 0.0
+        while t_total < budget_s and reps < 1000:
+            t0 = time.perf_counter()
+            oracle.recurrence_decay(x["q"], x["k"], x["v"], x["g"], x["h0"],
+                                    x["cu_seqlens"] if x["varlen"] else None,
+                                    per_channel=spec.kind == "gla")
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return {"value": round(n_tokens * reps / t_total, 1), "unit": "tokens/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"whole {spec.name} workload ({n_tokens} tokens x {spec.h_v} heads), "
+                          f"fp64 decay-only token recurrence, {reps} run(s) in {t_total:.1f} s, "
+                          "one thread"}
     units = spec.n_seqs * spec.h_v
     used = min(cores, units)
     reps, t_total = 0, 0.0
@@ -280,7 +298,11 @@ def main():
     ht = torch.empty((n_seqs, spec.h_v, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     ws = torch.empty(max(drla.workspace_bytes(x["q"].shape, x["v"].shape, io, n_seqs, cu_host), 1),
                      dtype=torch.uint8, device=dev)
-    fn = drla.kda_prefill if spec.kind == "kda" else drla.gdn_prefill
+    if spec.kind in ("ret", "gla"):
+        def fn(q, k, v, beta, g, *a, **kw):
+            return drla.decay_prefill(q, k, v, g, *a, per_channel=spec.kind == "gla", **kw)
+    else:
+        fn = drla.kda_prefill if spec.kind == "kda" else drla.gdn_prefill
 
     def step(events=None):
         fn(q, k, v, beta, g, h0, cu, cu_seqlens_host=cu_host, workspace=ws, out=o,
@@ -340,11 +362,12 @@ def main():
     total_flops = sum(f for _, f in costs.values())
     # whole-call algorithmic I/O (q, k, v, beta, g, h0 in; o, ht out)
     es = 4 if spec.io == "f32" else 2
-    io_bytes = n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * 4
-                           + spec.h_v * (spec.dk if spec.kind == "kda" else 1) * 4) \
+    nbeta = 0 if spec.kind in ("ret", "gla") else 4
+    io_bytes = n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * nbeta
+                           + spec.h_v * (spec.dk if spec.kind in ("kda", "gla") else 1) * 4) \
         + (2 if spec.h0_std > 0 else 1) * n_seqs * spec.h_v * spec.dk * spec.dv * 4
     line = {
-        "metric": METRIC,
+        "metric": DECAY_METRIC if spec.kind in ("ret", "gla") else METRIC,
         "value": round(n_tokens / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,

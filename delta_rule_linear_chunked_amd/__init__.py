@@ -8,7 +8,10 @@ library is not built the calls raise; there is no other code path.
 """
 from ._lib import (  # noqa: F401
     KEEP_INTERMEDIATES,
+    DECAY_ONLY,
     DrlaError,
+    decay_decode,
+    decay_prefill,
     gdn_decode,
     gdn_prefill,
     kda_decode,
@@ -19,5 +22,6 @@ from ._lib import (  # noqa: F401
     workspace_layout,
 )
 
-__all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "workspace_bytes", "workspace_layout",
+__all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "decay_prefill",
+           "decay_decode", "DECAY_ONLY", "workspace_bytes", "workspace_layout",
            "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES"]

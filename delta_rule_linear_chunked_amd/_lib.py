@@ -42,6 +42,7 @@ class Layout(ctypes.Structure):
 
 
 KEEP_INTERMEDIATES = 1
+DECAY_ONLY = 2
 
 
 def lib_path() -> str:
@@ -70,6 +71,11 @@ def load_library():
             f = getattr(lib, name)
             f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             f.restype = ctypes.c_int
+        lib.decay_prefill.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+        lib.decay_prefill.restype = ctypes.c_int
+        lib.decay_decode.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.decay_decode.restype = ctypes.c_int
         lib.drla_prefill_ex.argtypes = [ctypes.c_int, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp,
                                         vp, i32p, vp, vp, vp, ctypes.c_size_t, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
@@ -157,6 +163,7 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
              cu_seqlens_host=None, output_final_state=True, workspace=None,
              out=None, final_state=None, stage_events=None, flags=0):
     lib = load_library()
+    decay = bool(flags & DECAY_ONLY)
     if q.dim() == 4:
         # dense batch [B, T, H, d]: B equal-length sequences
         if cu_seqlens is not None and q.shape[0] != 1:
@@ -176,17 +183,19 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
             raise ValueError("cu_seqlens must be int32")
     T = q.shape[0]
     for name, x in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g)):
+        if x is None and name == "beta" and decay:
+            continue
         if not x.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if k.shape != q.shape or v.shape[0] != T:
         raise ValueError("q, k must be [T, h_qk, dk] and v [T, h_v, dv]")
-    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+    if (not decay and beta.dtype != torch.float32) or g.dtype != torch.float32:
         raise ValueError("beta and g must be float32")
     h_v, dk, dv = v.shape[1], q.shape[2], v.shape[2]
     want_g = (T, h_v, dk) if kda else (T, h_v)
-    if tuple(beta.shape) != (T, h_v) or tuple(g.shape) != want_g:
+    if (not decay and tuple(beta.shape) != (T, h_v)) or tuple(g.shape) != want_g:
         raise ValueError(f"beta must be {(T, h_v)} and g {want_g}")
     prob = _problem(q, v, n_seqs, T)
     dev = q.device
@@ -212,7 +221,7 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = (ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-            beta.data_ptr(), g.data_ptr(),
+            None if beta is None else beta.data_ptr(), g.data_ptr(),
             None if initial_state is None else initial_state.data_ptr(),
             None if cu_seqlens is None else cu_seqlens.data_ptr(),
             _i32p(cu_host), o.data_ptr(), None if ht is None else ht.data_ptr(),
@@ -226,6 +235,17 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return o, ht
+
+
+def decay_prefill(q, k, v, g, initial_state=None, cu_seqlens=None, per_channel=None, **kw):
+    """Decay-only linear attention (RetNet / GLA form, no delta rule):
+    S_t = Diag(e^{g_t}) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.  g is [T, h_v]
+    (scalar gate) or [T, h_v, dk] (per-channel; per_channel=None infers it
+    from g's rank).  Other arguments and the result as gdn_prefill."""
+    if per_channel is None:
+        per_channel = g.dim() == q.dim()
+    kw["flags"] = kw.get("flags", 0) | DECAY_ONLY
+    return _prefill(bool(per_channel), q, k, v, None, g, initial_state, cu_seqlens, **kw)
 
 
 def gdn_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
@@ -242,20 +262,22 @@ def kda_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
 
 
 def _decode(kda: bool, q, k, v, beta, g, state=None, out=None, final_state=None,
-            in_place=False):
+            in_place=False, decay=False):
     lib = load_library()
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
         raise ValueError("q, k must be [N, h_qk, dk] and v [N, h_v, dv]")
     N, h_v, dk, dv = q.shape[0], v.shape[1], q.shape[2], v.shape[2]
     for name, x in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g)):
+        if x is None and name == "beta" and decay:
+            continue
         if not x.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+    if (not decay and beta.dtype != torch.float32) or g.dtype != torch.float32:
         raise ValueError("beta and g must be float32")
     want_g = (N, h_v, dk) if kda else (N, h_v)
-    if tuple(beta.shape) != (N, h_v) or tuple(g.shape) != want_g:
+    if (not decay and tuple(beta.shape) != (N, h_v)) or tuple(g.shape) != want_g:
         raise ValueError(f"beta must be {(N, h_v)} and g {want_g}")
     if state is not None and (state.dtype != torch.float32 or not state.is_contiguous()
                               or tuple(state.shape) != (N, h_v, dk, dv)):
@@ -271,10 +293,16 @@ def _decode(kda: bool, q, k, v, beta, g, state=None, out=None, final_state=None,
         ht = final_state if final_state is not None else \
             torch.empty((N, h_v, dk, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    fn = lib.kda_decode if kda else lib.gdn_decode
-    st = fn(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
-            g.data_ptr(), None if state is None else state.data_ptr(), o.data_ptr(),
-            ht.data_ptr(), stream)
+    if decay:
+        st = lib.decay_decode(int(kda), ctypes.byref(prob), q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), g.data_ptr(),
+                              None if state is None else state.data_ptr(), o.data_ptr(),
+                              ht.data_ptr(), stream)
+    else:
+        fn = lib.kda_decode if kda else lib.gdn_decode
+        st = fn(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                g.data_ptr(), None if state is None else state.data_ptr(), o.data_ptr(),
+                ht.data_ptr(), stream)
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return o, ht
@@ -291,3 +319,11 @@ def gdn_decode(q, k, v, beta, g, state=None, **kw):
 def kda_decode(q, k, v, beta, g, state=None, **kw):
     """One Kimi Delta Attention decode step; g is per key channel [N, h_v, dk]."""
     return _decode(True, q, k, v, beta, g, state, **kw)
+
+
+def decay_decode(q, k, v, g, state=None, per_channel=None, **kw):
+    """One decode step of decay-only linear attention (no beta); g [N, h_v]
+    or [N, h_v, dk].  Result as gdn_decode."""
+    if per_channel is None:
+        per_channel = g.dim() == q.dim()
+    return _decode(bool(per_channel), q, k, v, None, g, state, decay=True, **kw)

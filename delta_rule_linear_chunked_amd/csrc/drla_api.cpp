@@ -116,10 +116,12 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
     return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
   drla_status st = check_problem(p, cu_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~DRLA_KEEP_INTERMEDIATES) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY)) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  const bool decay = (flags & DRLA_DECAY_ONLY) != 0;
+  if (decay) beta = nullptr;  // unused without the delta rule
   const int64_t T = p->total_tokens;
-  if (T > 0 && (!q || !k || !v || !beta || !g || !o))
-    return fail(DRLA_ERR_NULL, "q, k, v, beta, g and o must be non-NULL");
+  if (T > 0 && (!q || !k || !v || (!beta && !decay) || !g || !o))
+    return fail(DRLA_ERR_NULL, decay ? "q, k, v, g and o must be non-NULL" : "q, k, v, beta, g and o must be non-NULL");
   const void* ptrs[] = {q, k, v, beta, g, h0, cu_dev, o, ht, ws};
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
@@ -181,6 +183,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
   a.f16 = p->io_dtype == DRLA_F16 ? 1 : 0;
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
+  a.decay_only = decay ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
@@ -189,15 +192,17 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   return DRLA_OK;
 }
 
-drla_status run_decode(bool kda, const drla_problem* p, const void* q, const void* k, const void* v,
+drla_status run_decode(bool kda, bool decay, const drla_problem* p, const void* q, const void* k, const void* v,
                        const float* beta, const float* g, const float* h0, void* o, float* ht, void* stream) {
+  if (decay) beta = nullptr;  // unused without the delta rule
   int64_t nc = 0;
   drla_status st = check_problem(p, nullptr, &nc);
   if (st != DRLA_OK) return st;
   if (p->total_tokens != p->n_seqs)
     return fail(DRLA_ERR_SHAPE, "decode: total_tokens (%lld) must equal n_seqs (%d), one token each",
                 (long long)p->total_tokens, p->n_seqs);
-  if (!q || !k || !v || !beta || !g || !o) return fail(DRLA_ERR_NULL, "q, k, v, beta, g and o must be non-NULL");
+  if (!q || !k || !v || (!beta && !decay) || !g || !o)
+    return fail(DRLA_ERR_NULL, decay ? "q, k, v, g and o must be non-NULL" : "q, k, v, beta, g and o must be non-NULL");
   const void* ptrs[] = {q, k, v, beta, g, h0, o, ht};
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
@@ -237,6 +242,7 @@ drla_status run_decode(bool kda, const drla_problem* p, const void* q, const voi
   a.kda = kda ? 1 : 0;
   a.f32 = p->io_dtype == DRLA_F32 ? 1 : 0;
   a.f16 = p->io_dtype == DRLA_F16 ? 1 : 0;
+  a.decay_only = decay ? 1 : 0;
   a.stream = stream;
   const hipError_t e = drla_launch_decode(&a);
   if (e != hipSuccess) return fail(DRLA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -250,12 +256,25 @@ extern "C" {
 
 drla_status gdn_decode(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
                        const float* g, const float* h0, void* o, float* ht, void* stream) {
-  return run_decode(false, p, q, k, v, beta, g, h0, o, ht, stream);
+  return run_decode(false, false, p, q, k, v, beta, g, h0, o, ht, stream);
 }
 
 drla_status kda_decode(const drla_problem* p, const void* q, const void* k, const void* v, const float* beta,
                        const float* g, const float* h0, void* o, float* ht, void* stream) {
-  return run_decode(true, p, q, k, v, beta, g, h0, o, ht, stream);
+  return run_decode(true, false, p, q, k, v, beta, g, h0, o, ht, stream);
+}
+
+drla_status decay_prefill(int per_channel, const drla_problem* p, const void* q, const void* k, const void* v,
+                          const float* g, const float* h0, const int32_t* cu_seqlens_dev,
+                          const int32_t* cu_seqlens_host, void* o, float* ht, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run(per_channel != 0, DRLA_DECAY_ONLY, p, q, k, v, nullptr, g, h0, cu_seqlens_dev, cu_seqlens_host, o,
+             ht, workspace, workspace_bytes, stream, nullptr);
+}
+
+drla_status decay_decode(int per_channel, const drla_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* h0, void* o, float* ht, void* stream) {
+  return run_decode(per_channel != 0, true, p, q, k, v, nullptr, g, h0, o, ht, stream);
 }
 
 size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_host) {
@@ -273,7 +292,7 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
   drla_status st = check_problem(p, cu_seqlens_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~DRLA_KEEP_INTERMEDIATES) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY)) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   layout_of(p, nc, cu_seqlens_host != nullptr, kda != 0, flags, out);
   return DRLA_OK;
 }

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     if (KDA) al[tid] = __expf(P.g[((int64_t)n * P.h_v + h) * DK + tid]);
   }
   if (tid < DV) vs[tid] = to_f(vg[tid]);
-  const float beta = P.beta[(int64_t)n * P.h_v + h];
+  const float beta = P.decay_only ? 1.f : P.beta[(int64_t)n * P.h_v + h];
   const float ag = KDA ? 1.f : __expf(P.g[(int64_t)n * P.h_v + h]);
   __syncthreads();
 
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
   float x = 0.f;
 #pragma unroll
   for (int q = 0; q < RG; ++q) x += part[0][q][j];
+  if (P.decay_only) x = 0.f;  // no delta rule: S += k v^T
   const float u = beta * (vs[j] - x);
 
   // rank-one update, its store, and this row group's share of o = S^T q
@@ -114,6 +115,7 @@ hipError_t drla_launch_decode(const drla_decode_args* a) {
   P.ht = a->ht;
   P.h_qk = a->h_qk;
   P.h_v = a->h_v;
+  P.decay_only = a->decay_only;
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
   if (units == 0) return hipSuccess;
   hipStream_t st = (hipStream_t)a->stream;

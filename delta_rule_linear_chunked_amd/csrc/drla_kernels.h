@@ -20,6 +20,7 @@ struct PrepParams {
   Sched s;
   int32_t h_qk, h_v, grp;
   int64_t nc;
+  int32_t decay_only;  // no delta rule: beta = 1, A = 0 (T = I); beta may be null
 };
 
 struct ScanParams {
@@ -41,6 +42,7 @@ struct ScanParams {
   Sched s;
   int32_t h_qk, h_v, grp;
   int64_t nc;
+  int32_t decay_only;  // no delta rule: R = V (no X term)
 };
 
 // One decode step: every input row is one sequence's token.
@@ -54,6 +56,7 @@ struct DecodeParams {
   void* o;            // [N, h_v, dv]
   float* ht;          // [N, h_v, dk, dv] or null; may be h0
   int32_t h_qk, h_v;
+  int32_t decay_only;  // no delta rule: S = a S + k v^T; beta unused
 };
 
 hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st);

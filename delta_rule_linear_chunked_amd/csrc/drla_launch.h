@@ -25,6 +25,7 @@ typedef struct {
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;
   int32_t kda, f32, f16, inspect;  // f32 / f16: io dtype (neither: bf16)
+  int32_t decay_only;              // decay-only linear attention (no delta rule)
   void* stream;
   void* const* stage_events;  // NULL, or 3 hipEvent_t recorded at kernel boundaries
 } drla_launch_args;
@@ -42,6 +43,7 @@ typedef struct {
   float* ht;
   int32_t n_seqs, h_qk, h_v, dk, dv;
   int32_t kda, f32, f16;
+  int32_t decay_only;
   void* stream;
 } drla_decode_args;
 

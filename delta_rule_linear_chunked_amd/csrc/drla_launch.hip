@@ -35,6 +35,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   pp.h_v = a->h_v;
   pp.grp = grp;
   pp.nc = nc;
+  pp.decay_only = a->decay_only;
 
   ScanParams sp = {};
   sp.q = a->q;
@@ -57,6 +58,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   sp.h_v = a->h_v;
   sp.grp = grp;
   sp.nc = nc;
+  sp.decay_only = a->decay_only;
 
   mark(0);
   if (e == hipSuccess && s.chunk_seq && a->n_seqs > 0)

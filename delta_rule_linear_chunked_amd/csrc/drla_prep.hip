@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       }
     }
     if (tid < C) {
-      bpre = tid < U.len ? P.beta[(U.t0 + tid) * P.h_v + U.h] : 0.f;
+      bpre = tid < U.len ? (P.decay_only ? 1.f : P.beta[(U.t0 + tid) * P.h_v + U.h]) : 0.f;
       if (!KDA) gpre = tid < U.len ? P.g[(U.t0 + tid) * P.h_v + U.h] : 0.f;
     }
     if (KDA) {
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * g4 + e, i = 16 * t + c16;
           float x = 0.f;
-          if (i < r) {
+          if (i < r && !P.decay_only) {
             x = betas[r] * acc[t][e];
             if (!KDA) x *= __expf(bs[r] - bs[i]);
           }

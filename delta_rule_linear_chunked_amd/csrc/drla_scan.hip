@@ -350,8 +350,9 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
       pb[1] = sl.pm[w < 2 ? 0 : 2 * w - 1][lane];
       __builtin_amdgcn_sched_barrier(0);
     }
+    const float ex = P.decay_only ? 0.f : eb;  // decay-only: R = V
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(vv[e]) - eb * xt[e]);
+    for (int e = 0; e < 4; ++e) rdst[8 * e] = (ET)(to_f(vv[e]) - ex * xt[e]);
     lds_barrier();  // R of all token tiles is in Rf
     const V8 rf0 = Rf[0][lane], rf1 = Rf[1][lane];
     floatx4 vt[4];

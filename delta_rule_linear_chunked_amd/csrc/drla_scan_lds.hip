@@ -334,12 +334,13 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // R = V - diag(e^b) X, as B fragments (inner = token)
+      // R = V - diag(e^b) X, as B fragments (inner = token); decay-only: R = V
+      const float xsc = P.decay_only ? 0.f : 1.f;
       floatx4 rr[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - ebv[nt][e] * x[nt][e];
+        for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - xsc * ebv[nt][e] * x[nt][e];
       const H8 rf0 = pack<T>(rr[0], rr[1]), rf1 = pack<T>(rr[2], rr[3]);
       // R goes to the output wave, which multiplies it with P Tb
       vbuf[t & 1][0][lane] = rf0;

@@ -147,11 +147,35 @@ drla_status kda_decode(const drla_problem* p, const void* q, const void* k,
                        const void* v, const float* beta, const float* g,
                        const float* h0, void* o, float* ht, void* stream);
 
+/* Decay-only linear attention, the temporal-decay form of RetNet and GLA
+ * ("Empowering Hybrid Attention Models on NPUs", Section 8, Related Work):
+ * no delta rule and no beta,
+ *   S_t = Diag(exp(g_t)) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,
+ * with a scalar gate g [T, h_v] (per_channel == 0) or a per-key-channel gate
+ * g [T, h_v, dk] (per_channel != 0).  Same kernels, layouts, workspace,
+ * ownership and errors as gdn_prefill / kda_prefill (beta is not passed);
+ * chunkwise this is the delta-rule form with T = I and no state read in V'. */
+drla_status decay_prefill(int per_channel, const drla_problem* p, const void* q,
+                          const void* k, const void* v, const float* g,
+                          const float* h0, const int32_t* cu_seqlens_dev,
+                          const int32_t* cu_seqlens_host, void* o, float* ht,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode step of decay-only linear attention: as gdn_decode / kda_decode
+ * without beta (S = Diag(exp(g)) S + k v^T, o = S^T q). */
+drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
+                         const void* k, const void* v, const float* g,
+                         const float* h0, void* o, float* ht, void* stream);
+
 /* Flags of drla_prefill_ex. */
 #define DRLA_KEEP_INTERMEDIATES 1 /* also write V' and the per-chunk state (tests) */
+#define DRLA_DECAY_ONLY 2         /* decay-only linear attention (decay_prefill); beta unused */
 
 /* gdn_prefill (kda == 0) or kda_prefill (kda != 0) with options.
- *   flags         0 or DRLA_KEEP_INTERMEDIATES.  With the flag the kernels
+ *   flags         DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY, both, or 0.
+ *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
+ *                 per-channel gate; beta is ignored and may be NULL).
+ *                 With DRLA_KEEP_INTERMEDIATES the kernels
  *                 also store, per (value head, chunk), V' = U - W S (the
  *                 "v_c" intermediate of Section 5) and the state entering the
  *                 chunk, at the offsets drla_workspace_layout reports for the

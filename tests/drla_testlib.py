@@ -58,6 +58,8 @@ def run_oracle(x, heads=None, threads=None):
         v, beta, g = v[:, heads], beta[:, heads], g[:, heads]
         h0 = None if h0 is None else h0[:, heads]
     cu = x["cu_seqlens"] if x["varlen"] else None
+    if x["kind"] in ("ret", "gla"):  # decay-only linear attention
+        return oracle.recurrence_decay(q, k, v, g, h0, cu, per_channel=x["kind"] == "gla")
     return oracle.recurrence(q, k, v, beta, g, h0, cu, kda=x["kind"] == "kda",
                              threads=threads)
 

@@ -103,6 +103,23 @@ def test_decode_validation_errors(lib):
     assert "overlap" in lib.drla_last_error().decode()
 
 
+def test_decay_entry_points_validate(lib):
+    """decay_prefill / decay_decode take no beta and check the rest as the
+    delta-rule calls do (fake aligned addresses, never dereferenced)."""
+    b = 1 << 40
+    p = _prob(n_seqs=1, T=256)
+    args = [b + 0x1000000, b + 0x2000000, b + 0x3000000, b + 0x4000000, None, None, None,
+            b + 0x6000000, None, b + 0x70000000, 1 << 40, None]
+    assert lib.decay_prefill(0, ctypes.byref(p), None, *args[1:]) == 1      # null q
+    assert lib.decay_prefill(0, ctypes.byref(_prob(dk=96)), *args) == 3   # unsupported dk
+    assert lib.decay_prefill(1, ctypes.byref(p), *args[:9], 0, 0, None) == 6  # no workspace
+    pd = _prob(n_seqs=4, T=4)
+    assert lib.decay_decode(0, ctypes.byref(pd), b, b + 0x100000, b + 0x200000, None,
+                            None, b + 0x300000, None, None) == 1       # null g
+    assert lib.decay_decode(1, ctypes.byref(_prob(n_seqs=4, T=8)), b, b + 0x100000, b + 0x200000,
+                            b + 0x400000, None, b + 0x300000, None, None) == 2
+
+
 def test_cu_seqlens_validation(lib):
     p = _prob(n_seqs=3, T=100)
     dev = ctypes.cast(ctypes.c_void_p(1 << 47), ctypes.POINTER(ctypes.c_int32))

@@ -26,7 +26,9 @@ class Spec:
     """One synthetic prefill problem.
 
     kind      "gdn" (scalar log-gate per token and v-head) or "kda"
-              (per-channel log-gate per token, v-head and key channel).
+              (per-channel log-gate per token, v-head and key channel);
+              "ret" / "gla": decay-only linear attention (no delta rule;
+              beta is drawn but unused) with a scalar / per-channel gate.
     lens      sequence lengths; a packed batch uses cu_seqlens.
     h_qk/h_v  query/key heads and value heads; v-head h reads q/k head
               h // (h_v // h_qk).
@@ -99,8 +101,18 @@ F16_WORKLOADS = {
 }
 
 
+# Decay-only linear attention at the prefill configs' shape (the RetNet /
+# GLA form: scalar and per-channel gates).
+DECAY_WORKLOADS = {
+    "ret_prefill": Spec("ret_prefill", "ret", (4096,), 16, 16, 128, 128, "bf16",
+                        0.01, 0.2, 0.02, seed=7),
+    "gla_prefill": Spec("gla_prefill", "gla", (4096,), 16, 16, 128, 128, "bf16",
+                        0.005, 0.15, 0.02, seed=8),
+}
+
+
 def spec_by_name(name: str) -> Spec:
-    for table in (WORKLOADS, DECODE_WORKLOADS, F16_WORKLOADS):
+    for table in (WORKLOADS, DECODE_WORKLOADS, F16_WORKLOADS, DECAY_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -159,7 +171,7 @@ def make_inputs(spec: Spec, seed: Optional[int] = None) -> dict:
     k = _unit_rows(rng.standard_normal((T, spec.h_qk, spec.dk)))
     v = rng.standard_normal((T, spec.h_v, spec.dv))
     beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, spec.h_v))))
-    gshape = (T, spec.h_v) if spec.kind == "gdn" else (T, spec.h_v, spec.dk)
+    gshape = (T, spec.h_v) if spec.kind in ("gdn", "ret") else (T, spec.h_v, spec.dk)
     g = -rng.uniform(spec.g_lo, spec.g_hi, size=gshape)
     h0 = None
     if spec.h0_std > 0:
