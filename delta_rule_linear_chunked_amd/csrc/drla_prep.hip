@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   constexpr int U_BYTES = NT * KS_BYTES > TS_BYTES ? NT * KS_BYTES : TS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
   __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
-  __shared__ float bs[C];
-  __shared__ float betas[C];
+  __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float betas[C];
   __shared__ float Btot[KDA ? NPART : 1][KDA ? DK : 1];
   __shared__ float cnl[KDA ? DK : 1];            // KDA: e^{B_n - B_m} per key channel
   __shared__ float ebm[KDA ? DK : 1];            // KDA: e^{B_m} per key channel
@@ -323,32 +323,40 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
           pt[t] = mma(kc[t][p], qf[p], pt[t]);    // P^T tile (t, pr) = K_t Q_pr^T
         }
       // A: strictly lower part, scaled by beta_r (and e^{b_r - b_i} for GDN);
-      // tiles past the diagonal are never read
+      // tiles past the diagonal are never read.  The gate values come from
+      // LDS once per lane: this lane's four rows as one vector, one column
+      // per tile.
+      const floatx4 betr = *(const floatx4*)&betas[16 * rt + 4 * g4];
+      const floatx4 bsr = *(const floatx4*)&bs[16 * rt + 4 * g4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t > rt) continue;
+        const float bsi = bs[16 * t + c16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * g4 + e, i = 16 * t + c16;
           float x = 0.f;
           if (i < r && !P.decay_only) {
-            x = betas[r] * acc[t][e];
-            if (!KDA) x *= __expf(bs[r] - bs[i]);
+            x = betr[e] * acc[t][e];
+            if (!KDA) x *= __expf(bsr[e] - bsi);
           }
           As[r][i] = x;
         }
       }
       // P: tiles jt = 2p, 2p+1 of P^T form fragment (pr, p) of P (outer =
       // query token, inner = key token); inclusive lower part only
+      const float bsq = bs[rq];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        const floatx4 bsj = *(const floatx4*)&bs[16 * t + 4 * g4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * t + 4 * g4 + e;
           float x = 0.f;
-          if (j <= rq) x = KDA ? pt[t][e] : pt[t][e] * __expf(bs[rq] - bs[j]);
+          if (j <= rq) x = KDA ? pt[t][e] : pt[t][e] * __expf(bsq - bsj[e]);
           pt[t][e] = x;
         }
+      }
       pfr[0] = pack<ET>(pt[0], pt[1]);
       pfr[1] = pack<ET>(pt[2], pt[3]);
       if (!LF) {

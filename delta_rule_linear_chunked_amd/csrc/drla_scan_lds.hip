@@ -69,7 +69,9 @@ __device__ __forceinline__ int swz(int r, int j) {
   return r * (DK * 2) + ((j ^ (r & (NCH - 1))) << 4);
 }
 
-template <int DK, int DV, bool INSPECT, typename T>
+// DECAY: decay-only linear attention (no delta rule): R = V, so the state
+// wave reads no K rows and runs no X products.
+template <int DK, int DV, bool INSPECT, typename T, bool DECAY>
 __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
@@ -293,10 +295,12 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       }
       const float gam = sl.eb[C - 1];
       H8 kr[KB][4];
+      if constexpr (!DECAY) {
 #pragma unroll
-      for (int p = 0; p < KB; ++p)
+        for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+          for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+      }
       __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles (lane holds [16 nt + 4g + e][c]),
       // interleaved with work that does not depend on it: the K^T reads of
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       constexpr int NV = (4 * KT + 16 + 4 * KB - 1) / (4 * KB);  // vector operations per product
 #pragma unroll
       for (int i = 0; i < 4 * KB; ++i) {
-        x[i % 4] = mma(kr[i / 4][i % 4], sf[i / 4], x[i % 4]);
+        if constexpr (!DECAY) x[i % 4] = mma(kr[i / 4][i % 4], sf[i / 4], x[i % 4]);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
@@ -335,12 +339,11 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // R = V - diag(e^b) X, as B fragments (inner = token); decay-only: R = V
-      const float xsc = P.decay_only ? 0.f : 1.f;
       floatx4 rr[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[nt][e] = vfl[nt][e] - xsc * ebv[nt][e] * x[nt][e];
+        for (int e = 0; e < 4; ++e) rr[nt][e] = DECAY ? vfl[nt][e] : vfl[nt][e] - ebv[nt][e] * x[nt][e];
       const H8 rf0 = pack<T>(rr[0], rr[1]), rf1 = pack<T>(rr[2], rr[3]);
       // R goes to the output wave, which multiplies it with P Tb
       vbuf[t & 1][0][lane] = rf0;
@@ -442,10 +445,14 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
   if (nblk > 0) {
-    if (inspect)
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    if (P.decay_only && inspect)
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else if (P.decay_only)
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+    else if (inspect)
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
     else
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
   }
   return hipGetLastError();
 }
