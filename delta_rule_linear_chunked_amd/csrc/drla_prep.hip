@@ -80,12 +80,13 @@ __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e
 // unit are in flight (K, Q, beta, g into registers).  KT: write K~^T (the
 // register-fed scans need it; the LDS-fed one transposes K itself).
 //
-// KDA: every thread owns one key channel d and C / NPART rows of the chunk;
-// it forms the cumulative gate B of its rows in registers and scales its
-// elements of K and Q once -- K e^{B - B_m}, K e^{B_m - B}, Q e^{B - B_m},
-// with the reference B_m = B of row C/2 - 1 keeping the exponents small --
-// so the products and the chunk operands only multiply by per-channel
-// constants (e^{B_m}, e^{B_n - B_m}).
+// KDA: every thread owns eight adjacent key channels and a run of GR rows of
+// the chunk; it forms the cumulative gate B of its rows in registers (the
+// runs' offsets come from one exclusive scan over the runs per channel) and
+// scales its elements of K and Q once, 16 bytes at a time -- K e^{B - B_m},
+// K e^{B_m - B}, Q e^{B - B_m}, with the reference B_m = B of row C/2 - 1
+// keeping the exponents small -- so the products and the chunk operands
+// only multiply by per-channel constants (e^{B_m}, e^{B_n - B_m}).
 //
 // LDS is reused across phases: K (and KDA's scaled tiles) live until the
 // chunk operands are written, T from the solve on, in the same bytes.
@@ -97,8 +98,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   constexpr int KB = DK / 32;
   constexpr int KP = DK + 16 / (int)sizeof(ET);  // padded row: 16-byte aligned, 4-bank skew
   constexpr int TP = C + 4;
-  constexpr int NPART = 256 / DK;                // KDA gate: row parts per channel
-  constexpr int RPP = C / NPART;
+  constexpr int CG = DK / 8;                     // KDA gate: groups of 8 channels
+  constexpr int GP = 256 / CG;                   // KDA gate: runs of rows per channel
+  constexpr int GR = C / GP;                     // KDA gate: rows per run
   constexpr bool LF = !KDA && !KT;               // operands for the LDS-fed scan
   constexpr int KV = DK / PE;                    // 16-byte pieces per K row
   constexpr int NKV = C * KV / 256;              // K pieces per thread
@@ -110,9 +112,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
   __shared__ __attribute__((aligned(16))) float bs[C];
   __shared__ __attribute__((aligned(16))) float betas[C];
-  __shared__ float Btot[KDA ? NPART : 1][KDA ? DK : 1];
-  __shared__ float cnl[KDA ? DK : 1];            // KDA: e^{B_n - B_m} per key channel
-  __shared__ float ebm[KDA ? DK : 1];            // KDA: e^{B_m} per key channel
+  __shared__ __attribute__((aligned(16))) float bms[KDA ? DK : 1];  // KDA: B_m per key channel
+  __shared__ __attribute__((aligned(16))) float cnl[KDA ? DK : 1];  // KDA: e^{B_n - B_m} per key channel
+  __shared__ __attribute__((aligned(16))) float ebm[KDA ? DK : 1];  // KDA: e^{B_m} per key channel
   ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows; KDA: K e^{B - B_m} (phases 0-1)
   ET(*Kn)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: K e^{B_m - B}
   ET(*Qs)[KP] = (ET(*)[KP])(un + 2 * KS_BYTES);  // KDA: Q rows, then Q e^{B - B_m}
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   V16 qvpre[KDA ? NKV : 1];  // KDA: Q rows, staged like K
   V8 qpre[KDA ? 1 : KB];     // GDN: Q fragments of this wave's P tile
   float bpre = 0.f, gpre = 0.f;
-  float gvpre[KDA ? RPP : 1];
+  floatx4 gvpre[KDA ? GR : 1][2];  // KDA: gates of this thread's rows and 8 channels
   auto load = [&](const Unit& U) {
 #pragma unroll
     for (int i = 0; i < NKV; ++i) {
@@ -175,11 +177,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       if (!KDA) gpre = tid < U.len ? P.g[(U.t0 + tid) * P.h_v + U.h] : 0.f;
     }
     if (KDA) {
-      const int d = tid % DK, part = tid / DK;
+      const int d0 = 8 * (tid % CG), part = tid / CG;
 #pragma unroll
-      for (int i = 0; i < RPP; ++i) {
-        const int r = part * RPP + i;
-        gvpre[i] = r < U.len ? P.g[((U.t0 + r) * P.h_v + U.h) * DK + d] : 0.f;
+      for (int i = 0; i < GR; ++i) {
+        const int r = part * GR + i;
+        gvpre[i][0] = gvpre[i][1] = zero4();
+        if (r < U.len) {
+          const floatx4* gp = (const floatx4*)(P.g + ((U.t0 + r) * P.h_v + U.h) * DK + d0);
+          gvpre[i][0] = gp[0];
+          gvpre[i][1] = gp[1];
+        }
       }
     }
   };
@@ -229,18 +236,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         bs[tid] = x;
       }
     }
-    // KDA: per key channel d, NPART runs of RPP rows; prefix sums in
-    // registers, the run offsets added after the barrier
-    float bv[KDA ? RPP : 1];
+    // KDA: per key channel, GP runs of GR rows; prefix sums in registers,
+    // the runs' totals to LDS (in the bytes A takes later)
+    floatx4 bv[KDA ? GR : 1][2];
+    float* const Bt = &As[0][0];  // [GP][DK] run totals, then their exclusive prefix
     if (KDA) {
-      const int d = tid % DK, part = tid / DK;
-      float run = 0.f;
+      const int d0 = 8 * (tid % CG), part = tid / CG;
+      floatx4 run0 = zero4(), run1 = zero4();
 #pragma unroll
-      for (int i = 0; i < RPP; ++i) {
-        run += gvpre[i];
-        bv[i] = run;
+      for (int i = 0; i < GR; ++i) {
+        run0 += gvpre[i][0];
+        run1 += gvpre[i][1];
+        bv[i][0] = run0;
+        bv[i][1] = run1;
       }
-      Btot[part][d] = run;
+      *(floatx4*)&Bt[part * DK + d0] = run0;
+      *(floatx4*)&Bt[part * DK + d0 + 4] = run1;
     }
     const int64_t unext = u + gridDim.x;
     Unit Un = U;
@@ -250,31 +261,55 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
     }
     __syncthreads();
     if (KDA) {
-      // B of this thread's rows, the reference B_m (row C/2 - 1: the end of
-      // the first NPART/2 runs) and B_n; then the scaled elements
-      const int d = tid % DK, part = tid / DK;
-      float off = 0.f, bm = 0.f, bn = 0.f;
+      // one thread per key channel: the runs' exclusive prefix (in place),
+      // the reference B_m (row C/2 - 1: the end of the first GP/2 runs) and
+      // B_n with the per-channel factors
+      if (tid < DK) {
+        float acc = 0.f, bm = 0.f;
 #pragma unroll
-      for (int q2 = 0; q2 < NPART; ++q2) {
-        const float tq = Btot[q2][d];
-        if (q2 < part) off += tq;
-        if (q2 < NPART / 2) bm += tq;
-        bn += tq;
+        for (int q2 = 0; q2 < GP; ++q2) {
+          const float tq = Bt[q2 * DK + tid];
+          Bt[q2 * DK + tid] = acc;
+          acc += tq;
+          if (q2 == GP / 2 - 1) bm = acc;
+        }
+        bms[tid] = bm;
+        cnl[tid] = __expf(acc - bm);
+        ebm[tid] = __expf(bm);
+        P.gam[ch * DK + tid] = __expf(acc);
       }
+      __syncthreads();
+      // B - B_m of this thread's elements, then the scaled tiles, 16 bytes
+      // of a row at a time
+      const int d0 = 8 * (tid % CG), part = tid / CG;
+      const floatx4 o0 = *(const floatx4*)&Bt[part * DK + d0] - *(const floatx4*)&bms[d0];
+      const floatx4 o1 = *(const floatx4*)&Bt[part * DK + d0 + 4] - *(const floatx4*)&bms[d0 + 4];
 #pragma unroll
-      for (int i = 0; i < RPP; ++i) {
-        const int r = part * RPP + i;
-        const float x = bv[i] + off - bm;
-        const float e = __expf(x), ei = __expf(-x);
-        const float kv = to_f(Ks[r][d]);
-        Ks[r][d] = (ET)(kv * e);
-        Kn[r][d] = (ET)(kv * ei);
-        Qs[r][d] = (ET)(to_f(Qs[r][d]) * e);
-      }
-      if (part == 0) {
-        cnl[d] = __expf(bn - bm);
-        ebm[d] = __expf(bm);
-        P.gam[ch * DK + d] = __expf(bn);
+      for (int i = 0; i < GR; ++i) {
+        const int r = part * GR + i;
+        float xb[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xb[c] = bv[i][0][c] + o0[c];
+          xb[c + 4] = bv[i][1][c] + o1[c];
+        }
+#pragma unroll
+        for (int pc = 0; pc < 8 / PE; ++pc) {
+          const V16 kv = *(const V16*)&Ks[r][d0 + pc * PE];
+          const V16 qv = *(const V16*)&Qs[r][d0 + pc * PE];
+          V16 ks, kn, qs;
+#pragma unroll
+          for (int c = 0; c < PE; ++c) {
+            const float x = xb[pc * PE + c];
+            const float e = __expf(x), ei = __expf(-x);
+            ks[c] = (ET)(to_f(kv[c]) * e);
+            kn[c] = (ET)(to_f(kv[c]) * ei);
+            qs[c] = (ET)(to_f(qv[c]) * e);
+          }
+          *(V16*)&Ks[r][d0 + pc * PE] = ks;
+          *(V16*)&Kn[r][d0 + pc * PE] = kn;
+          *(V16*)&Qs[r][d0 + pc * PE] = qs;
+        }
       }
       __syncthreads();
     }
