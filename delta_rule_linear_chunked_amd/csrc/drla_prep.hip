@@ -447,19 +447,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
     // ---- phase 2: #3 Solve --------------------------------------------------------
     if (wv == 0) {
       // level 0: the four 16x16 diagonal blocks of T by forward substitution,
-      // one column per lane (block lane/16, column lane%16)
-      // (rows of A read four at a time, four partial sums per row)
+      // one column per lane (block lane/16, column lane%16).  Rows of A are
+      // read four entries at a time, LA rows ahead of the row being solved,
+      // so that the 16-step chain does not wait on each row's reads; four
+      // partial sums per row.
+      constexpr int LA = 3;
       const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
+      floatx4 ar[16][4];
+      auto read_row = [&](int r) {
+#pragma unroll
+        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) ar[r][i4] = *(const floatx4*)&As[o + r][o + 4 * i4];
+      };
+#pragma unroll
+      for (int r = 1; r <= LA; ++r) read_row(r);
       float t[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        if (r >= 1 && r + LA < 16) read_row(r + LA);
         float acc[4] = {(r == cc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-          const floatx4 a = *(const floatx4*)&As[o + r][o + 4 * i4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (4 * i4 + e < r) acc[e] -= a[e] * t[4 * i4 + e];
+            if (4 * i4 + e < r) acc[e] -= ar[r][i4][e] * t[4 * i4 + e];
         }
         t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
