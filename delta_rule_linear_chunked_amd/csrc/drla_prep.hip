@@ -592,7 +592,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 // per variant and device: the variants differ in registers and LDS).
 template <int DK, bool KDA, typename ET, bool KT>
 static int64_t resident_groups() {
-  auto kern = prep_kernel<DK, KDA, ET, KT, !KDA>;
+  auto kern = prep_kernel<DK, KDA, ET, KT, true>;
   static int64_t cached[16] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -609,8 +609,8 @@ static int64_t resident_groups() {
 
 template <int DK, bool KDA, typename ET, bool KT>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  auto kern = prep_kernel<DK, KDA, ET, KT, !KDA>;
-  const int64_t fit = KDA ? nblk : resident_groups<DK, KDA, ET, KT>();
+  auto kern = prep_kernel<DK, KDA, ET, KT, true>;
+  const int64_t fit = resident_groups<DK, KDA, ET, KT>();
   const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, nblk);
   return hipGetLastError();
