@@ -194,6 +194,24 @@ def test_kda_with_uniform_gate_equals_gdn(drla, io):
     assert rel_err(_np(o_k), _np(o_g)) <= tol and rel_err(_np(h_k), _np(h_g)) <= tol
 
 
+# Strong decay.  GDN takes e^{b_r - b_i} and e^{b_n - b_r} directly, so any
+# gate is in range.  KDA (and decay-only with per-channel gates) scales the
+# chunk's K and Q rows by e^{+-(B_r - B_m)} about the per-channel reference
+# B_m = B of row 31, so 32 max|g| must stay below the log of the largest
+# value of the tiles' type: 88 for bf16 and fp32, 11 for fp16.
+@pytest.mark.parametrize("kind,io,g_lo,g_hi", [
+    ("gdn", "bf16", 2.0, 8.0), ("gdn", "f16", 2.0, 8.0),
+    ("kda", "bf16", 1.0, 2.5), ("kda", "f32", 1.0, 2.5), ("kda", "f16", 0.1, 0.3)])
+def test_strong_decay_in_supported_range(drla, kind, io, g_lo, g_hi):
+    print(f"case strong-decay kind={kind} io={io} g=-U({g_lo},{g_hi})", flush=True)
+    x = _case(kind, io, 128, 128, lens=(300, 64), h_qk=1, h_v=2, h0_std=0.05,
+              g_lo=g_lo, g_hi=g_hi)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"strong-decay {kind}/{io}", x, _np(o), _np(ht), o_ref, ht_ref)
+
+
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
 def test_grouped_heads_equal_repeated_dense(drla, kind):
     """Value head h reads q/k head h // (h_v / h_qk): the grouped call equals
