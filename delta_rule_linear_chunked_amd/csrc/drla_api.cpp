@@ -70,7 +70,7 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
     nc = (int64_t)p->n_seqs * ((L + DRLA_CHUNK - 1) / DRLA_CHUNK);
   }
   if (nc * p->h_v > INT32_MAX) return fail(DRLA_ERR_SHAPE, "too many (chunk, head) pairs");
-  if ((int64_t)p->n_seqs * p->h_v * (p->dv / 16) > INT32_MAX) return fail(DRLA_ERR_SHAPE, "too many sequences");
+  if (((int64_t)p->n_seqs * p->h_v + 7) * (p->dv / 16) > INT32_MAX) return fail(DRLA_ERR_SHAPE, "too many sequences");
   *n_chunks = nc;
   return DRLA_OK;
 }
@@ -83,7 +83,9 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   size_t off = 0;
   L->n_chunks = nc;
   L->sched = off;
-  off = align_up(off + (varlen ? (2 * (size_t)nc + p->n_seqs + 1) * 4 : 0));
+  // packed input: chunk -> sequence, chunk -> first token, sequence -> first
+  // chunk, and the sequences longest first
+  off = align_up(off + (varlen ? (2 * (size_t)nc + 2 * (size_t)p->n_seqs + 1) * 4 : 0));
   L->tb = off;
   off = align_up(off + ncH * 8 * frag);
   L->pm = off;

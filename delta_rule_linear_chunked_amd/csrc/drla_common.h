@@ -201,6 +201,7 @@ struct Sched {
   const int32_t* chunk_seq;    // [nc] sequence of each chunk (packed input), else null
   const int32_t* chunk_start;  // [nc] first token of each chunk
   const int32_t* seq_chunk0;   // [N+1] first chunk of each sequence
+  const int32_t* seq_order;    // [N] sequences, longest first (packed input), else null
   const int32_t* cu;           // [N+1] device cu_seqlens (packed input)
   int64_t seq_len;             // dense batch: tokens per sequence
   int32_t cps;                 // dense batch: chunks per sequence
@@ -228,6 +229,33 @@ __device__ __forceinline__ void chunk_of(const Sched& s, int64_t c, int& seq, in
     const int64_t n = s.seq_len - local * C;
     len = (int)(n > C ? C : n);
   }
+}
+
+// Scan workgroup -> (sequence, value head, column block).  The hardware
+// deals workgroups to the eight XCDs round-robin by index, so the column
+// blocks of one (sequence, head) unit, which read the same K, Q and prep
+// operands, are given indices that land on one XCD and share its L2.  Dense
+// batch: units in order.  Packed input: units are dealt longest sequence
+// first, unit rank r to XCD r % 8, so that the longest chains start first
+// on every XCD; the grid then covers a multiple of eight units and the
+// workgroups past the last unit have nothing to do (returns false).
+__device__ __forceinline__ bool scan_item(const Sched& s, int h_v, int nbk, int& seq, int& h, int& nb) {
+  const int bid = blockIdx.x, G = gridDim.x;
+  if (s.seq_order) {
+    const int y = bid / 8;
+    const int r = (y / nbk) * 8 + bid % 8;
+    nb = y % nbk;
+    if (r >= s.n_seqs * h_v) return false;
+    seq = s.seq_order[r / h_v];
+    h = r % h_v;
+    return seq >= 0 && seq < s.n_seqs;
+  }
+  const int b = G % 8 == 0 ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int unit = b / nbk;
+  nb = b - unit * nbk;
+  seq = unit / h_v;
+  h = unit - seq * h_v;
+  return true;
 }
 
 // Chunks [c0, c1) of sequence `seq`, clamped to [0, nc).

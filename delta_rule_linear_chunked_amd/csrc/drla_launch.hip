@@ -65,7 +65,10 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     e = launch_schedule(a->cu_dev, a->n_seqs, nc, (int32_t*)(ws + a->off_sched), st);
   if (e == hipSuccess) e = launch_prep<DK, KDA, ET>(pp, nc * a->h_v, st);
   mark(1);
-  const int64_t nscan = (int64_t)a->n_seqs * a->h_v * (DV / 16);
+  // packed input: the scan deals (sequence, head) units in groups of eight
+  // (scan_item); the grid covers whole groups
+  const int64_t units = (int64_t)a->n_seqs * a->h_v;
+  const int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
   if (e == hipSuccess) {
     if constexpr (kLdsScan)
       e = launch_scan_lds<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
@@ -86,6 +89,7 @@ hipError_t drla_launch(const drla_launch_args* a) {
     s.chunk_seq = sched;
     s.chunk_start = sched + a->n_chunks;
     s.seq_chunk0 = sched + 2 * a->n_chunks;
+    s.seq_order = sched + 2 * a->n_chunks + a->n_seqs + 1;
     s.cu = a->cu_dev;
   } else {
     s.seq_len = a->n_seqs > 0 ? a->total_tokens / a->n_seqs : 0;

@@ -71,6 +71,28 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
   if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
 }
 
+// Sequences ranked longest first (ties by index) for the scan's dealing
+// order: one thread per sequence counts the longer ones, the lengths staged
+// through LDS 256 at a time.  seq_order[rank] = sequence.
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* cu, int n_seqs, int32_t* seq_order) {
+  __shared__ int32_t lens[256];
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  const int32_t mine = s < n_seqs ? cu[s + 1] - cu[s] : 0;
+  int rank = 0;
+  for (int base = 0; base < n_seqs; base += 256) {
+    const int o = base + threadIdx.x;
+    lens[threadIdx.x] = o < n_seqs ? cu[o + 1] - cu[o] : -1;
+    __syncthreads();
+    const int m = n_seqs - base < 256 ? n_seqs - base : 256;
+    for (int i = 0; i < m; ++i) {
+      const int32_t l = lens[i];
+      rank += (l > mine || (l == mine && base + i < s)) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  if (s < n_seqs) seq_order[rank] = s;
+}
+
 // Position of element e (0..31) of a 32-element block in fragment order:
 // element kmap(g, j) at 8g + j.
 __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
@@ -630,6 +652,8 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
 hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu, n_seqs, nc, sched, sched + nc,
                      sched + 2 * nc);
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0, st, cu, n_seqs,
+                     sched + 2 * nc + n_seqs + 1);
   return hipGetLastError();
 }
 

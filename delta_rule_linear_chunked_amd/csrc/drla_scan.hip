@@ -163,14 +163,8 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g4 = lane >> 4, c16 = lane & 15;
-  // Consecutive workgroups go to different XCDs; renumber so that the NB
-  // column blocks of one (sequence, head), which read the same K, Q and prep
-  // operands, run on one XCD and share its L2.
-  int b = blockIdx.x;
-  const int G = gridDim.x;
-  if (G % 8 == 0) b = (b % 8) * (G / 8) + b / 8;
-  const int unit = b / NB, nb = b - unit * NB;
-  const int seq = unit / P.h_v, h = unit - seq * P.h_v;
+  int seq, h, nb;
+  if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) return;  // the whole workgroup: past the last unit
 
   ScanCtx x;
   x.h = h;

@@ -90,11 +90,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
-  int b = blockIdx.x;
-  const int G = gridDim.x;
-  if (G % 8 == 0) b = (b % 8) * (G / 8) + b / 8;  // column blocks of a head on one XCD
-  const int unit = b / NB, nb = b - unit * NB;
-  const int seq = unit / P.h_v, h = unit - seq * P.h_v;
+  int seq, h, nb;
+  if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) return;  // the whole workgroup: past the last unit
   const int hk = h / P.grp;
 
   int64_t ts, te, c0, nch;

@@ -96,6 +96,20 @@ def test_varlen_grouped_ragged(drla, kind, io):
     np.testing.assert_array_equal(_np(ht)[5], x["h0"][5])
 
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_varlen_unsorted_lengths(drla, kind, io):
+    """Packed input is scanned longest sequence first, units dealt to the
+    XCDs in groups of eight: lengths out of order (one empty) and a unit
+    count (6 x 3 = 18) that is not a multiple of eight."""
+    print(f"case varlen-unsorted kind={kind} io={io}", flush=True)
+    x = _case(kind, io, 128, 128, lens=(64, 700, 5, 300, 0, 129), h_qk=1, h_v=3, h0_std=0.05)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"varlen-unsorted {kind}/{io}", x, _np(o), _np(ht), o_ref, ht_ref)
+
+
 def test_dense_batch_equals_packed(drla):
     """A [B, T, H, d] dense batch is B sequences of T tokens."""
     x = _case("gdn", "bf16", 128, 128, lens=(96, 96, 96), h_qk=2, h_v=2, h0_std=0.02)
