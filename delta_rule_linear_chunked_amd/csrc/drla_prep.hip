@@ -24,6 +24,8 @@
 //   the decay factors: GDN e^{b_r} and e^{b_n - b_r} per token row;
 //   KDA e^{b_n} per key channel, and K e^{B}, Q e^{B}.
 // All are written in MFMA fragment order (drla_common.h).
+#include <atomic>
+
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -611,22 +613,25 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 }
 
 // Workgroups of one prep kernel variant that fit on the chip at once (cached
-// per variant and device: the variants differ in registers and LDS).
+// per variant and device: the variants differ in registers and LDS).  Host
+// threads may race to fill an entry; they all compute the same value.
 template <int DK, bool KDA, typename ET, bool KT>
 static int64_t resident_groups() {
   auto kern = prep_kernel<DK, KDA, ET, KT, true>;
-  static int64_t cached[16] = {};
+  static std::atomic<int64_t> cached[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (cached[dev] == 0) {
+  int64_t fit = cached[dev].load(std::memory_order_relaxed);
+  if (fit == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    cached[dev] = (int64_t)per_cu * cus;
+    fit = (int64_t)per_cu * cus;
+    cached[dev].store(fit, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return fit;
 }
 
 template <int DK, bool KDA, typename ET, bool KT>
