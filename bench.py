@@ -64,6 +64,16 @@ def kernel_costs(spec, n_tokens, n_seqs):
     return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f)}
 
 
+def call_io_bytes(spec, n_tokens, n_seqs):
+    """Algorithmic I/O of one whole call: q, k, v, beta, g and h0 (if any)
+    in; o and ht out."""
+    es = 4 if spec.io == "f32" else 2
+    nbeta = 0 if spec.kind in ("ret", "gla") else 4
+    return n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * nbeta
+                       + spec.h_v * (spec.dk if spec.kind in ("kda", "gla") else 1) * 4) \
+        + (2 if spec.h0_std > 0 else 1) * n_seqs * spec.h_v * spec.dk * spec.dv * 4
+
+
 class Hip:
     """Raw HIP events through libamdhip64 (the library records them on the
     stream its kernels run on)."""
@@ -360,12 +370,7 @@ def main():
     roof["algorithmic_flops_per_launch"] = int(flops)
 
     total_flops = sum(f for _, f in costs.values())
-    # whole-call algorithmic I/O (q, k, v, beta, g, h0 in; o, ht out)
-    es = 4 if spec.io == "f32" else 2
-    nbeta = 0 if spec.kind in ("ret", "gla") else 4
-    io_bytes = n_tokens * (2 * spec.h_qk * spec.dk * es + spec.h_v * spec.dv * es * 2 + spec.h_v * nbeta
-                           + spec.h_v * (spec.dk if spec.kind in ("kda", "gla") else 1) * 4) \
-        + (2 if spec.h0_std > 0 else 1) * n_seqs * spec.h_v * spec.dk * spec.dv * 4
+    io_bytes = call_io_bytes(spec, n_tokens, n_seqs)
     line = {
         "metric": DECAY_METRIC if spec.kind in ("ret", "gla") else METRIC,
         "value": round(n_tokens / (ms_step * 1e-3), 1),
