@@ -9,6 +9,7 @@ library is not built the calls raise; there is no other code path.
 from ._lib import (  # noqa: F401
     KEEP_INTERMEDIATES,
     DECAY_ONLY,
+    SERIAL,
     DrlaError,
     decay_decode,
     decay_prefill,
@@ -24,4 +25,4 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "decay_prefill",
            "decay_decode", "DECAY_ONLY", "workspace_bytes", "workspace_layout",
-           "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES"]
+           "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES", "SERIAL"]

@@ -38,11 +38,12 @@ class Problem(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("sched", "tb", "pm", "kt", "kw", "qw", "gam", "vp", "h",
-                                       "total")]
+                                       "seg", "total")]
 
 
 KEEP_INTERMEDIATES = 1
 DECAY_ONLY = 2
+SERIAL = 4
 
 
 def lib_path() -> str:
@@ -170,7 +171,8 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
             raise ValueError("with cu_seqlens, pass packed [T, H, d] inputs (or batch 1)")
         n_seqs = 1 if cu_seqlens is not None else q.shape[0]
         q, k, v = (x.reshape(-1, x.shape[-2], x.shape[-1]) for x in (q, k, v))
-        beta = beta.reshape(-1, beta.shape[-1])
+        if beta is not None:
+            beta = beta.reshape(-1, beta.shape[-1])
         g = g.reshape(-1, *g.shape[2:])
     elif q.dim() == 3:
         n_seqs = 1

@@ -105,6 +105,18 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
+  // Segment-mode scan (dense GDN or scalar decay-only calls with 16-bit
+  // inputs and dk = dv whose scan, three workgroups per (sequence, head,
+  // column block), fits the 256 compute units at once): the state after
+  // segment 0, segment 1's two final states (fp32), the first again as
+  // 16-bit fragments, and segment 1's transition outputs G, laid out as o
+  const bool seg_ok = !varlen && !kda && p->io_dtype != DRLA_F32 && p->dk == p->dv &&
+                      3 * (int64_t)p->n_seqs * p->h_v * (p->dv / 16) <= 256;
+  L->seg = seg_ok ? off : 0;
+  if (seg_ok)
+    off = align_up(off + 3 * (size_t)p->n_seqs * p->h_v * p->dk * p->dv * 4 +
+                   (size_t)p->n_seqs * p->h_v * p->dk * p->dv * es +
+                   (size_t)p->total_tokens * p->h_v * p->dk * es);
   L->total = off;
 }
 
@@ -118,7 +130,8 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
     return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
   drla_status st = check_problem(p, cu_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY)) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
+    return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   const bool decay = (flags & DRLA_DECAY_ONLY) != 0;
   if (decay) beta = nullptr;  // unused without the delta rule
   const int64_t T = p->total_tokens;
@@ -174,6 +187,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.off_gam = L.gam;
   a.off_vp = L.vp;
   a.off_h = L.h;
+  a.off_seg = L.seg;
   a.total_tokens = T;
   a.n_chunks = nc;
   a.n_seqs = p->n_seqs;
@@ -186,6 +200,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.f16 = p->io_dtype == DRLA_F16 ? 1 : 0;
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.decay_only = decay ? 1 : 0;
+  a.serial = (flags & DRLA_SERIAL) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
@@ -280,12 +295,13 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q, 
 }
 
 size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_host) {
-  // The KDA layout is the larger one; GDN calls use a prefix of it.
+  // Enough for either gate kind: the larger of the two layouts.
   int64_t nc = 0;
   if (check_problem(p, cu_seqlens_host, &nc) != DRLA_OK) return 0;
-  drla_layout L;
+  drla_layout L, G;
   layout_of(p, nc, cu_seqlens_host != nullptr, true, 0, &L);
-  return L.total;
+  layout_of(p, nc, cu_seqlens_host != nullptr, false, 0, &G);
+  return L.total > G.total ? L.total : G.total;
 }
 
 drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t* cu_seqlens_host, int flags,
@@ -294,7 +310,8 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
   drla_status st = check_problem(p, cu_seqlens_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY)) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
+    return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   layout_of(p, nc, cu_seqlens_host != nullptr, kda != 0, flags, out);
   return DRLA_OK;
 }

@@ -258,6 +258,21 @@ __device__ __forceinline__ bool scan_item(const Sched& s, int h_v, int nbk, int&
   return true;
 }
 
+// Segment-mode scan workgroup -> (unit, column block, kind): kind 1 =
+// segment 0, 2 = segment 1 from zero, 3 = segment 1 transition.  3K
+// workgroups for K = units x nbk (K a multiple of 8), all resident at once.
+// A unit's 3 nbk workgroups take consecutive places in one XCD's share of
+// the indices, so that its value and transition blocks, which read the same
+// chunks, mostly share an L2.
+__device__ __forceinline__ void seg_item(int units, int nbk, int& unit, int& nb, int& kind) {
+  const int bid = blockIdx.x, K3 = 3 * units * nbk;
+  const int l = (bid % 8) * (K3 / 8) + bid / 8;
+  unit = l / (3 * nbk);
+  const int r = l - unit * 3 * nbk;
+  kind = 1 + r / nbk;
+  nb = r - (kind - 1) * nbk;
+}
+
 // Chunks [c0, c1) of sequence `seq`, clamped to [0, nc).
 __device__ __forceinline__ void seq_chunks(const Sched& s, int seq, int64_t nc, int64_t& c0, int64_t& c1) {
   if (s.chunk_seq) {

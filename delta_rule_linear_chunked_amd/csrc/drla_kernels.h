@@ -23,6 +23,22 @@ struct PrepParams {
   int32_t decay_only;  // no delta rule: beta = 1, A = 0 (T = I); beta may be null
 };
 
+// Segment-parallel scan (dense batch, dk = dv): every sequence's chunks are
+// split at s1.  Segment 0 is scanned from h0; segment 1 both from a zero
+// state (its local outputs into o, final state into n) and, by as many
+// "transition" workgroups, from the identity with V = 0 (outputs G into g,
+// final state M into m).  Then the true results of segment 1 are
+// o += G mid and ht = n + M mid, mid being the state segment 0 leaves.
+struct SegParams {
+  int32_t s1;   // > 0: segment mode, first chunk of segment 1
+  void* g;      // [T, h_v, dk] in the io type, like o
+  float* mid;   // [N, h_v, dk, dv]
+  float* n;     // [N, h_v, dk, dv]
+  float* m;     // [N, h_v, dk, dk]
+  void* midf;   // mid in the io type as A fragments: per (sequence, head),
+                // dv/16 column tiles x dk/32 key blocks x 64 lanes x 8
+};
+
 struct ScanParams {
   const void* q;
   const void* k;
@@ -43,6 +59,7 @@ struct ScanParams {
   int32_t h_qk, h_v, grp;
   int64_t nc;
   int32_t decay_only;  // no delta rule: R = V (no X term)
+  SegParams seg;       // LDS-fed scan only
 };
 
 // One decode step: every input row is one sequence's token.
@@ -70,6 +87,10 @@ hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStrea
 // GDN with 16-bit inputs (T = bf16 or f16): the LDS-fed scan (drla_scan_lds.hip)
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
+
+// After a segment-mode scan: o += G mid over segment 1, ht = n + M mid.
+template <int DK, typename T>
+hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st);
 
 }  // namespace drla
 

@@ -21,11 +21,13 @@ typedef struct {
   void* workspace;
   // byte offsets into the workspace; vp/h only used when inspect != 0
   size_t off_sched, off_tb, off_pm, off_kt, off_kw, off_qw, off_gam, off_vp, off_h;
+  size_t off_seg;  // 0, or the segment-mode scan's G and states (dense calls)
   int64_t total_tokens;
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;
   int32_t kda, f32, f16, inspect;  // f32 / f16: io dtype (neither: bf16)
   int32_t decay_only;              // decay-only linear attention (no delta rule)
+  int32_t serial;                  // scan every sequence in one pass (no segment split)
   void* stream;
   void* const* stage_events;  // NULL, or 3 hipEvent_t recorded at kernel boundaries
 } drla_launch_args;

@@ -3,7 +3,22 @@
 #include "drla_common.h"
 #include "drla_kernels.h"
 
+#include <atomic>
+
 namespace drla {
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cached[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 template <int DK, int DV, bool KDA, typename ET>
 static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
@@ -68,12 +83,39 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   // packed input: the scan deals (sequence, head) units in groups of eight
   // (scan_item); the grid covers whole groups
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
-  const int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
+  int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
+  // Segment mode (SegParams): a dense call whose scan uses at most a third
+  // of the compute units, so that the three kinds of workgroups (one per
+  // compute unit: the scan's LDS) all run at once; the split is in the
+  // middle.  (With two kinds per unit resident at once and a later split
+  // the scan's period per chunk grows with the occupancy more than the
+  // shorter segments save.)
+  bool seg = false;
+  if constexpr (kLdsScan && DK == DV) {
+    const int64_t K = units * (DV / 16);
+    const int cus = device_cus();
+    if (a->off_seg && !a->inspect && !a->serial && !s.chunk_seq && K % 8 == 0 && cus > 0 && 3 * K <= cus &&
+        s.cps >= 8) {
+      seg = true;
+      sp.seg.s1 = s.cps / 2;
+      char* sg = ws + a->off_seg;
+      const size_t state_bytes = (size_t)units * DK * DV * 4;
+      sp.seg.mid = (float*)sg;
+      sp.seg.n = (float*)(sg + state_bytes);
+      sp.seg.m = (float*)(sg + 2 * state_bytes);
+      sp.seg.midf = sg + 3 * state_bytes;
+      sp.seg.g = sg + 3 * state_bytes + state_bytes / 2;
+      nscan = 3 * K;
+    }
+  }
   if (e == hipSuccess) {
     if constexpr (kLdsScan)
       e = launch_scan_lds<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
     else
       e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
+  }
+  if constexpr (kLdsScan && DK == DV) {
+    if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, s.cps, st);
   }
   mark(2);
   return e;

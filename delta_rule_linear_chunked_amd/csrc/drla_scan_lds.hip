@@ -91,7 +91,15 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
   int seq, h, nb;
-  if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) return;  // the whole workgroup: past the last unit
+  int kind = 0;  // 0: whole sequence; segment mode: 1, 2, 3 (seg_item)
+  if (P.seg.s1 > 0) {
+    int unit;
+    seg_item(P.s.n_seqs * P.h_v, NB, unit, nb, kind);
+    seq = unit / P.h_v;
+    h = unit - seq * P.h_v;
+  } else if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) {
+    return;  // the whole workgroup: past the last unit
+  }
   const int hk = h / P.grp;
 
   int64_t ts, te, c0, nch;
@@ -107,8 +115,19 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     te = ts + P.s.seq_len;
     c0 = (int64_t)seq * P.s.cps;
     nch = P.s.cps;
+    if (kind == 1) {
+      nch = P.seg.s1;
+    } else if (kind > 1) {  // segment 1: chunks [s1, cps)
+      ts += (int64_t)C * P.seg.s1;
+      c0 += P.seg.s1;
+      nch = P.s.cps - P.seg.s1;
+    }
   }
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
+  // segment 1 transition blocks scan V = 0 from the identity
+  const float vsc = kind == 3 ? 0.f : 1.f;
+  T* const obase = (T*)(kind == 3 ? P.seg.g : P.o);
+  float* const sout = kind == 0 ? P.ht : kind == 1 ? P.seg.mid : kind == 2 ? P.seg.n : P.seg.m;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
   const int col = 16 * nb + c16;
   const T* kg = (const T*)P.k;
@@ -214,7 +233,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S[mt][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] : 0.f;
+        S[mt][e] = kind == 3   ? (state_row(mt, 4 * g4 + e) == col ? 1.f : 0.f)
+                   : kind != 2 && P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col]
+                                       : 0.f;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
       sf[p] = pack<T>(S[2 * p], S[2 * p + 1]);
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     o[3] = mma(vf1, pmf[5], o[3]);
     const int64_t left = te - t0i;
     const uint32_t len = (uint32_t)(left < C ? left : C);
-    const rsrc_t orr = make_rsrc((T*)P.o + t0i * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+    const rsrc_t orr = make_rsrc(obase + t0i * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<T>(o[nt]));
   };
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
             S[j / 4][j % 4] *= gam;
           } else if (j < 4 * KT + 16) {
             const int q2 = j - 4 * KT;
-            vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]);
+            vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]) * vsc;
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -380,12 +401,19 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       }
       lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
-    if (P.ht) {
+    if (sout) {
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          P.ht[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = S[mt][e];
+          sout[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = S[mt][e];
+    }
+    if (kind == 1) {
+      // the same state, packed as it entered the last product: the A
+      // fragments (outer = column, inner = key channel) of the fix-up
+      H8* mf = (H8*)P.seg.midf + (((int64_t)seq * P.h_v + h) * NB + nb) * (KB * 64);
+#pragma unroll
+      for (int p = 0; p < KB; ++p) mf[p * 64 + lane] = sf[p];
     }
   } else if (w == 3) {
     for (int t = 0; t < n; ++t) {
@@ -438,6 +466,115 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 }
+
+// Segment mode, second step (see SegParams).  Workgroups [0, units * ng):
+// one (unit, cpb consecutive chunks of segment 1) each, O^T += mid^T G^T
+// for the chunks' tokens: mid's A fragments (outer = state column, inner =
+// key channels 32p + 8g + j), written by the segment-0 scan, are staged in
+// LDS once; G is read as row fragments (outer = token, the same channels);
+// wave w takes tokens 16w .. 16w + 15 of each chunk and updates o 8 bytes
+// per lane.  The rest: one (unit, 16 state columns) each, ht = n + M mid
+// in fp32.
+template <int DK, typename T>
+__global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t units, int32_t n1, int32_t cpb) {
+  typedef typename VT<T>::v8 H8;
+  typedef typename VT<T>::v4 H4;
+  constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
+  __shared__ H8 af[CT * KB * 64];                            // mid as A fragments
+  __shared__ __attribute__((aligned(16))) float mb[DK][16];  // part B: mid, 16 columns
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int b = blockIdx.x;
+  const int ng = (n1 + cpb - 1) / cpb;
+  if (b < units * ng) {
+    const int u = b / ng, cg = b - u * ng;
+    const int seq = u / P.h_v, h = u - seq * P.h_v;
+    const H8* mf = (const H8*)P.seg.midf + (int64_t)u * (CT * KB * 64);
+#pragma unroll
+    for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
+    __syncthreads();
+    const uint32_t kstride = (uint32_t)P.h_v * DK * 2;  // G has o's layout
+    const int cend = (cg + 1) * cpb < n1 ? (cg + 1) * cpb : n1;
+    for (int c = cg * cpb; c < cend; ++c) {
+      const int64_t t0 = (int64_t)seq * P.s.seq_len + (int64_t)(P.seg.s1 + c) * C;
+      const int64_t left = (int64_t)seq * P.s.seq_len + P.s.seq_len - t0;
+      const uint32_t len = (uint32_t)(left < C ? left : C);
+      const rsrc_t gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * 2);
+      const rsrc_t orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+      // lane: columns 16 ct + 4g + e of token 16 w + c
+      const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * 2;
+      H8 gf[KB];
+      H4 ov[CT];
+#pragma unroll
+      for (int p = 0; p < KB; ++p)
+        gf[p] = bload<H8>(gr, (uint32_t)(16 * w + c16) * kstride + (uint32_t)(32 * p + 8 * g4) * 2);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 32 * ct);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < KB; ++p) acc = mma(af[(ct * KB + p) * 64 + lane], gf[p], acc);
+        floatx4 sum;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] = to_f(ov[ct][e]) + acc[e];
+        bstore(orr, off0 + 32 * ct, pack4<T>(sum));
+      }
+    }
+  } else {
+    const int bb = b - units * ng, u = bb / CT, cb = bb - u * CT;
+    const int64_t base = (int64_t)u * DK * DV;
+#pragma unroll
+    for (int i = tid; i < DK * 16; i += 256) mb[i / 16][i % 16] = P.seg.mid[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16];
+    __syncthreads();
+    // thread: row r, columns 8 hh .. 8 hh + 7 of this block
+    const int r = tid >> 1, hh = tid & 1;
+    if (r < DK) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = P.seg.n[base + (int64_t)r * DV + 16 * cb + 8 * hh + q];
+      const float* mrow = P.seg.m + (int64_t)u * DK * DK + (int64_t)r * DK;
+#pragma unroll 8
+      for (int j = 0; j < DK; j += 4) {
+        const floatx4 mv = *(const floatx4*)(mrow + j);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const floatx4 lo = *(const floatx4*)&mb[j + jj][8 * hh];
+          const floatx4 hi = *(const floatx4*)&mb[j + jj][8 * hh + 4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[q] += mv[jj] * lo[q];
+            acc[q + 4] += mv[jj] * hi[q];
+          }
+        }
+      }
+      if (P.ht) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) P.ht[base + (int64_t)r * DV + 16 * cb + 8 * hh + q] = acc[q];
+      }
+    }
+  }
+}
+
+template <int DK, typename T>
+hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st) {
+  const int32_t n1 = cps - P.seg.s1;
+  // chunks per workgroup: one while that leaves at most a workgroup per
+  // compute unit (256), at most four (each workgroup loads mid once)
+  const int64_t per = n_units * n1 / 256;
+  const int32_t cpb = per < 1 ? 1 : per > 4 ? 4 : (int32_t)per;
+  const int64_t nblk = n_units * ((n1 + cpb - 1) / cpb) + n_units * (DK / 16);
+  hipLaunchKernelGGL((seg_fix_kernel<DK, T>), dim3((unsigned)nblk), dim3(256), 0, st, P, (int32_t)n_units, n1, cpb);
+  return hipGetLastError();
+}
+
+#define DRLA_SEG_FIX_INST(DK_, T_) \
+  template hipError_t launch_seg_fix<DK_, T_>(const ScanParams&, int64_t, int32_t, hipStream_t);
+DRLA_SEG_FIX_INST(64, bf16)
+DRLA_SEG_FIX_INST(128, bf16)
+DRLA_SEG_FIX_INST(64, f16)
+DRLA_SEG_FIX_INST(128, f16)
+#undef DRLA_SEG_FIX_INST
 
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {

@@ -177,9 +177,17 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
 /* Flags of drla_prefill_ex. */
 #define DRLA_KEEP_INTERMEDIATES 1 /* also write V' and the per-chunk state (tests) */
 #define DRLA_DECAY_ONLY 2         /* decay-only linear attention (decay_prefill); beta unused */
+#define DRLA_SERIAL 4             /* scan every sequence in one pass (no segment split) */
 
 /* gdn_prefill (kda == 0) or kda_prefill (kda != 0) with options.
- *   flags         DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY, both, or 0.
+ *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY
+ *                 and DRLA_SERIAL, or 0.  DRLA_SERIAL turns off the
+ *                 segment-parallel scan (same results up to rounding),
+ *                 which dense scalar-gate calls with 16-bit inputs, dk ==
+ *                 dv and at least 8 chunks per sequence take when
+ *                 U = n_seqs * h_v * dv/16 is a multiple of 8 and 3U is at
+ *                 most the device's compute units: each sequence's chunks
+ *                 are split in half and the halves scanned at once.
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels
@@ -224,11 +232,17 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
- * Elements are io dtype except gam (fp32).  n_chunks is the total chunk
+ *   seg (dense scalar-gate calls with 16-bit inputs and dk == dv whose
+ *        n_seqs * h_v * dv/16 is at most 85, else 0): the segment-split
+ *        scan's three fp32 states per (sequence, head) -- after the first
+ *        segment, the second segment's from zero, its map of the entering
+ *        state -- then the first again as io-type fragments, then the map's
+ *        contribution to o per token, laid out as o
+ * Elements are io dtype except gam and the seg states (fp32).  n_chunks is the total chunk
  * count over all sequences.  Returns DRLA_OK or a validation error. */
 typedef struct {
   int64_t n_chunks;
-  size_t sched, tb, pm, kt, kw, qw, gam, vp, h, total;
+  size_t sched, tb, pm, kt, kw, qw, gam, vp, h, seg, total;
 } drla_layout;
 drla_status drla_workspace_layout(int kda, const drla_problem* p,
                                   const int32_t* cu_seqlens_host, int flags,

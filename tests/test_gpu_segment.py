@@ -1,0 +1,109 @@
+"""The segment-split scan of dense calls that use at most a third of the chip.
+
+Such a call scans chunks [0, s1) of every (sequence, head) from the initial
+state, and chunks [s1, n) twice at the same time: from a zero state with the
+real values, and from the identity with V = 0 (which gives the linear map of
+the entering state on the outputs and on the final state).  A second kernel
+adds the map applied to the state after chunk s1 - 1.  The cases take ragged
+last chunks, grouped heads, dk = 64 and 128, a dense batch, no initial
+state, no final state, the fewest chunks the split takes, and the
+decay-only form; each is checked against the oracle, and against the
+one-pass scan of the same call (DRLA_SERIAL), which must differ in rounding
+somewhere (else the split did not run).  A call too wide for the split must
+equal the one-pass scan bit for bit."""
+import numpy as np
+import pytest
+
+import workloads as W
+from drla_testlib import TOL, rel_err, run_oracle, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def drla():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import delta_rule_linear_chunked_amd as m
+    m.load_library()
+    return m
+
+
+def _call(drla, kind, d, dense_batch, flags, want_ht):
+    q, k, v, beta, g, h0 = d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"]
+    if dense_batch > 1:
+        q, k, v = (x.view(dense_batch, -1, *x.shape[1:]) for x in (q, k, v))
+        beta, g = (x.view(dense_batch, -1, *x.shape[1:]) for x in (beta, g))
+    if kind == "ret":
+        return drla.decay_prefill(q, k, v, g, h0, per_channel=False, flags=flags,
+                                  output_final_state=want_ht)
+    return drla.gdn_prefill(q, k, v, beta, g, h0, flags=flags, output_final_state=want_ht)
+
+
+# (kind, io, h_qk, h_v, d, lens, h0_std, want_ht)
+CASES = [
+    ("gdn", "bf16", 2, 4, 128, (1000,), 0.05, True),      # ragged tail
+    ("gdn", "f16", 4, 4, 64, (777,), 0.05, True),         # d = 64
+    ("gdn", "bf16", 4, 8, 128, (1000,), 0.0, True),       # 192 scan workgroups
+    ("gdn", "bf16", 2, 16, 64, (2000,), 0.05, True),      # 16 heads of d = 64
+    ("ret", "bf16", 2, 4, 128, (600, 600), 0.05, True),   # dense batch
+    ("gdn", "bf16", 2, 4, 128, (3000,), 0.05, False),     # no final state
+    ("ret", "f16", 1, 4, 64, (520,), 0.0, True),          # eight chunks, the least
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-h{c[3]}-d{c[4]}-{c[5]}" for c in CASES])
+def test_segment_split_matches_oracle_and_one_pass(drla, case):
+    kind, io, h_qk, h_v, dk, lens, h0_std, want_ht = case
+    print(f"case segment kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} lens={lens} "
+          f"h0_std={h0_std} ht={want_ht}", flush=True)
+    spec = W.small_spec(kind, lens=lens, h_qk=h_qk, h_v=h_v, dk=dk, dv=dk, io=io,
+                        g_lo=0.01, g_hi=0.2, h0_std=h0_std, seed=41)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    nb = len(lens)
+    o, ht = _call(drla, kind, d, nb, 0, want_ht)
+    o1, ht1 = _call(drla, kind, d, nb, drla.SERIAL, want_ht)
+    torch.cuda.synchronize()
+    o, o1 = (t.reshape(-1, h_v, dk).float().cpu().numpy() for t in (o, o1))
+    o_ref, ht_ref = run_oracle(x)
+    tol = TOL[io]
+    eo, eo1 = rel_err(o, o_ref), rel_err(o1, o_ref)
+    print(f"  rel_err o split={eo:.3e} one-pass={eo1:.3e} (tol {tol:g})", flush=True)
+    assert np.isfinite(o).all() and eo <= tol
+    assert rel_err(o, o1) <= tol
+    assert not np.array_equal(o, o1), "the split scan did not run"
+    if want_ht:
+        ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
+        eh = rel_err(ht, ht_ref)
+        print(f"  rel_err ht split={eh:.3e} one-pass={rel_err(ht1, ht_ref):.3e}", flush=True)
+        assert np.isfinite(ht).all() and eh <= tol
+    else:
+        assert ht is None and ht1 is None
+
+
+def test_segment_split_repeatable(drla):
+    """Two calls of the split scan on the same inputs agree bit for bit (no
+    workgroup reads what another of the same call is still writing)."""
+    print("case segment repeatable", flush=True)
+    spec = W.small_spec("gdn", lens=(2000,), h_qk=4, h_v=8, dk=128, dv=128, io="bf16",
+                        g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=42)
+    d = to_device(W.make_inputs(spec))
+    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_wide_call_runs_one_pass(drla):
+    """16 heads of d = 128 need 384 split workgroups, more than a 256-CU chip
+    holds at once: the call takes the one-pass scan."""
+    print("case segment wide call", flush=True)
+    spec = W.small_spec("gdn", lens=(1000,), h_qk=4, h_v=16, dk=128, dv=128, io="bf16",
+                        g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=43)
+    d = to_device(W.make_inputs(spec))
+    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -141,7 +141,7 @@ def test_workspace_bytes_and_layout(lib):
     n = lib.drla_workspace_bytes(ctypes.byref(p), None)
     lay = Layout()
     assert lib.drla_workspace_layout(1, ctypes.byref(p), None, 0, ctypes.byref(lay)) == 0
-    assert lay.total == n and lay.n_chunks == 64
+    assert lay.n_chunks == 64
     per = 64 * 16                       # (chunk, head) pairs
     frag = 64 * 8 * 2                   # one bf16 fragment
     assert lay.pm - lay.tb == per * 8 * frag
@@ -150,13 +150,23 @@ def test_workspace_bytes_and_layout(lib):
     assert lay.qw - lay.kw == per * 64 * 128 * 2
     assert lay.gam - lay.qw == per * 64 * 128 * 2
     assert lay.total - lay.gam == per * 128 * 4
-    assert lay.vp == 0 and lay.h == 0
+    assert lay.vp == 0 and lay.h == 0 and lay.seg == 0   # KDA: no segment-split scan
     # GDN with bf16 inputs needs neither K~^T nor the KDA operands; its decay
     # factors are 2 x 64 floats per chunk
     gl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
     assert gl.kt == 0 and gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kt
-    assert gl.total - gl.gam == per * 128 * 4 and gl.total < n
+    assert gl.seg == 0                  # 16 heads x 8 column blocks x 3 > 256
+    assert gl.total - gl.gam == per * 128 * 4
+    assert n == max(lay.total, gl.total)
+    # the segment-split scan (8 heads x 8 column blocks x 3 <= 256 CUs):
+    # three fp32 states per head, the first as bf16 fragments, and G laid
+    # out like o
+    p8 = _prob(n_seqs=1, h_qk=8, h_v=8, dk=128, dv=128, io=0, T=4096)
+    sl = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(sl)) == 0
+    assert sl.seg - sl.gam == 64 * 8 * 128 * 4
+    assert sl.total - sl.seg == 3 * 8 * 128 * 128 * 4 + 8 * 128 * 128 * 2 + 4096 * 8 * 128 * 2
     # fp32 inputs keep K~^T for the register-fed scan
     pf = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=1, T=4096)
     fl = Layout()
@@ -167,13 +177,19 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
     assert kl.vp == gl.total and kl.h - kl.vp == per * 64 * 128 * 2
     assert kl.total - kl.h == per * 128 * 128 * 2
-    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 3
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 0
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 8, ctypes.byref(kl)) == 3
+    # 11 heads of 8 column blocks: 264 scan workgroups, no segment region
+    p11 = _prob(n_seqs=1, h_qk=11, h_v=11, dk=128, dv=128, io=0, T=4096)
+    assert lib.drla_workspace_layout(0, ctypes.byref(p11), None, 0, ctypes.byref(kl)) == 0
+    assert kl.seg == 0
     cu, _c = _i32([0, 1, 65, 65, 200])
     p2 = _prob(n_seqs=4, T=200)
     lay2 = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p2), cu, 0, ctypes.byref(lay2)) == 0
     assert lay2.n_chunks == 1 + 1 + 0 + 3
     assert lay2.tb >= (2 * 5 + 4 + 1) * 4      # chunk table first
+    assert lay2.seg == 0                        # packed input: no segment split
     assert lib.drla_workspace_bytes(ctypes.byref(_prob(dk=80)), None) == 0
 
 
