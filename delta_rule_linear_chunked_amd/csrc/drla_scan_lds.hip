@@ -124,8 +124,6 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     }
   }
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
-  // segment 1 transition blocks scan V = 0 from the identity
-  const float vsc = kind == 3 ? 0.f : 1.f;
   T* const obase = (T*)(kind == 3 ? P.seg.g : P.o);
   float* const sout = kind == 0 ? P.ht : kind == 1 ? P.seg.mid : kind == 2 ? P.seg.n : P.seg.m;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
@@ -160,7 +158,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   };
   auto v_rsrc = [&](int i) -> rsrc_t {
     const T* src = vg + ((ts + (int64_t)C * i) * P.h_v + h) * DV + 16 * nb;
-    return make_rsrc(src, (chunk_len(i) - 1) * vstride + 32);
+    // segment 1 transition blocks scan V = 0 from the identity: an empty
+    // range makes every V copy write zeros
+    return make_rsrc(src, kind == 3 ? 0u : (chunk_len(i) - 1) * vstride + 32);
   };
   auto frag_rsrc = [&](int i) -> rsrc_t {
     const int64_t ch = (int64_t)h * P.nc + c0 + i;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
             S[j / 4][j % 4] *= gam;
           } else if (j < 4 * KT + 16) {
             const int q2 = j - 4 * KT;
-            vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]) * vsc;
+            vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
