@@ -75,6 +75,14 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
   return DRLA_OK;
 }
 
+// Segments the workspace provides for (drla_seg_count at 256 compute
+// units); 1 for calls the split does not take.
+static int32_t seg_count(const drla_problem* p, bool varlen, bool kda) {
+  if (varlen || kda || p->io_dtype == DRLA_F32 || p->dk != p->dv || p->n_seqs < 1) return 1;
+  const int64_t cps = (p->total_tokens / p->n_seqs + DRLA_CHUNK - 1) / DRLA_CHUNK;
+  return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), cps, 256);
+}
+
 void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int flags, drla_layout* L) {
   const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
   const size_t ncH = (size_t)nc * p->h_v;
@@ -105,18 +113,12 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
-  // Segment-mode scan (dense GDN or scalar decay-only calls with 16-bit
-  // inputs and dk = dv whose scan, three workgroups per (sequence, head,
-  // column block), fits the 256 compute units at once): the state after
-  // segment 0, segment 1's two final states (fp32), the first again as
-  // 16-bit fragments, and segment 1's transition outputs G, laid out as o
-  const bool seg_ok = !varlen && !kda && p->io_dtype != DRLA_F32 && p->dk == p->dv &&
-                      3 * (int64_t)p->n_seqs * p->h_v * (p->dv / 16) <= 256;
-  L->seg = seg_ok ? off : 0;
-  if (seg_ok)
-    off = align_up(off + 3 * (size_t)p->n_seqs * p->h_v * p->dk * p->dv * 4 +
-                   (size_t)p->n_seqs * p->h_v * p->dk * p->dv * es +
-                   (size_t)p->total_tokens * p->h_v * p->dk * es);
+  // Segment-split scan (dense scalar-gate calls with 16-bit inputs and
+  // dk = dv that leave most of a 256-CU chip idle): its states and G
+  const int32_t np = seg_count(p, varlen, kda);
+  L->seg = np > 1 ? off : 0;
+  if (np > 1)
+    off = align_up(off + drla_seg_offsets((int64_t)p->n_seqs * p->h_v, p->dk, p->total_tokens, p->h_v, np, es).total);
   L->total = off;
 }
 
@@ -188,6 +190,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.off_vp = L.vp;
   a.off_h = L.h;
   a.off_seg = L.seg;
+  a.seg_np = L.seg ? seg_count(p, cu_dev != nullptr, kda) : 1;
   a.total_tokens = T;
   a.n_chunks = nc;
   a.n_seqs = p->n_seqs;

@@ -258,19 +258,29 @@ __device__ __forceinline__ bool scan_item(const Sched& s, int h_v, int nbk, int&
   return true;
 }
 
-// Segment-mode scan workgroup -> (unit, column block, kind): kind 1 =
-// segment 0, 2 = segment 1 from zero, 3 = segment 1 transition.  3K
-// workgroups for K = units x nbk (K a multiple of 8), all resident at once.
-// A unit's 3 nbk workgroups take consecutive places in one XCD's share of
-// the indices, so that its value and transition blocks, which read the same
-// chunks, mostly share an L2.
-__device__ __forceinline__ void seg_item(int units, int nbk, int& unit, int& nb, int& kind) {
-  const int bid = blockIdx.x, K3 = 3 * units * nbk;
-  const int l = (bid % 8) * (K3 / 8) + bid / 8;
-  unit = l / (3 * nbk);
-  const int r = l - unit * 3 * nbk;
-  kind = 1 + r / nbk;
-  nb = r - (kind - 1) * nbk;
+// Segment-mode scan workgroup -> (unit, column block, kind, segment):
+// kind 1 = segment 0; for segments 1 .. np - 1, kind 2 = from zero, 3 =
+// transition.  (2 np - 1) K workgroups for K = units x nbk, all resident at
+// once.  A unit's (2 np - 1) nbk workgroups take consecutive places in one
+// XCD's share of the indices (when the count is a multiple of 8), so that
+// a segment's value and transition blocks, which read the same chunks,
+// mostly share an L2.
+__device__ __forceinline__ void seg_item(int units, int nbk, int np, int& unit, int& nb, int& kind, int& sg) {
+  const int bid = blockIdx.x, per = (2 * np - 1) * nbk, W = units * per;
+  const int l = W % 8 == 0 ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  unit = l / per;
+  int r = l - unit * per;
+  if (r < nbk) {
+    kind = 1;
+    sg = 0;
+    nb = r;
+  } else {
+    r -= nbk;
+    sg = 1 + r / (2 * nbk);
+    r -= (sg - 1) * 2 * nbk;
+    kind = 2 + r / nbk;
+    nb = r % nbk;
+  }
 }
 
 // Chunks [c0, c1) of sequence `seq`, clamped to [0, nc).

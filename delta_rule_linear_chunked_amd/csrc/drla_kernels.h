@@ -24,19 +24,23 @@ struct PrepParams {
 };
 
 // Segment-parallel scan (dense batch, dk = dv): every sequence's chunks are
-// split at s1.  Segment 0 is scanned from h0; segment 1 both from a zero
-// state (its local outputs into o, final state into n) and, by as many
-// "transition" workgroups, from the identity with V = 0 (outputs G into g,
-// final state M into m).  Then the true results of segment 1 are
-// o += G mid and ht = n + M mid, mid being the state segment 0 leaves.
+// split into np segments of s1 chunks (the last takes the rest).  Segment
+// 0 is scanned from h0 (final state into mid).  Every later segment s is
+// scanned both from a zero state (its local outputs into o, final state
+// into n[s-1]) and, by as many "transition" workgroups, from the identity
+// with V = 0 (outputs G into g, final state M into m[s-1]).  With E_1 = mid
+// and E_{s+1} = N_s + M_s E_s (seg_compose), segment s's true outputs are
+// o += G E_s (seg_fix) and ht = E_np.
 struct SegParams {
-  int32_t s1;   // > 0: segment mode, first chunk of segment 1
+  int32_t s1;   // > 0: segment mode; chunks of every segment but the last
+  int32_t np;   // segments
+  int64_t us;   // elements of one state set: sequences x heads x dk x dv
   void* g;      // [T, h_v, dk] in the io type, like o
   float* mid;   // [N, h_v, dk, dv]
-  float* n;     // [N, h_v, dk, dv]
-  float* m;     // [N, h_v, dk, dk]
-  void* midf;   // mid in the io type as A fragments: per (sequence, head),
-                // dv/16 column tiles x dk/32 key blocks x 64 lanes x 8
+  float* n;     // [np - 1][N, h_v, dk, dv]
+  float* m;     // [np - 1][N, h_v, dk, dk]
+  void* midf;   // [np - 1] E_s in the io type as A fragments: per (sequence,
+                // head), dv/16 column tiles x dk/32 key blocks x 64 lanes x 8
 };
 
 struct ScanParams {
@@ -89,6 +93,8 @@ template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
 
 // After a segment-mode scan: o += G mid over segment 1, ht = n + M mid.
+template <int DK, typename T>
+hipError_t launch_seg_compose(const ScanParams& P, int64_t n_units, hipStream_t st);
 template <int DK, typename T>
 hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st);
 

@@ -8,6 +8,38 @@
 
 #define DRLA_CHUNK_TOKENS 64
 
+// Segment count of the segment-split scan of a dense call (1: no split):
+// the most P <= 16 for which the scan's (2P - 1) K workgroups all fit on
+// `cus` compute units at once (one per CU; K = sequences x heads x dv/16)
+// and every segment has at least 4 chunks (cps: chunks per sequence).
+static inline int32_t drla_seg_count(int64_t K, int64_t cps, int64_t cus) {
+  int32_t np = 1;
+  for (int32_t p = 2; p <= 16; ++p)
+    if (K > 0 && (2 * p - 1) * K <= cus && cps >= 4 * p) np = p;
+  return np;
+}
+
+// Layout of the seg region (byte offsets from its start) for `units`
+// (sequence, head) pairs of a d x d state, T tokens in all, h_v heads, np
+// segments and io elements of `es` bytes: the state after segment 0, then
+// np - 1 zero-start final states N, np - 1 transition maps M (all fp32),
+// np - 1 entering states as io-type MFMA fragments, then G [T, h_v, d].
+typedef struct {
+  size_t mid, n, m, f, g, total;
+} drla_seg_layout;
+static inline drla_seg_layout drla_seg_offsets(int64_t units, int64_t d, int64_t T, int64_t h_v, int32_t np,
+                                               size_t es) {
+  const size_t us = (size_t)units * d * d;
+  drla_seg_layout L;
+  L.mid = 0;
+  L.n = L.mid + us * 4;
+  L.m = L.n + (size_t)(np - 1) * us * 4;
+  L.f = L.m + (size_t)(np - 1) * us * 4;
+  L.g = L.f + (size_t)(np - 1) * us * es;
+  L.total = L.g + (size_t)T * h_v * d * es;
+  return L;
+}
+
 typedef struct {
   const void* q;
   const void* k;
@@ -21,7 +53,8 @@ typedef struct {
   void* workspace;
   // byte offsets into the workspace; vp/h only used when inspect != 0
   size_t off_sched, off_tb, off_pm, off_kt, off_kw, off_qw, off_gam, off_vp, off_h;
-  size_t off_seg;  // 0, or the segment-mode scan's G and states (dense calls)
+  size_t off_seg;  // 0, or the segment-mode scan's states and G (dense calls)
+  int32_t seg_np;  // segments the seg region holds (drla_seg_count at 256 CUs)
   int64_t total_tokens;
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;

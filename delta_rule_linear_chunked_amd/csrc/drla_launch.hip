@@ -84,28 +84,30 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   // (scan_item); the grid covers whole groups
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
   int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
-  // Segment mode (SegParams): a dense call whose scan uses at most a third
-  // of the compute units, so that the three kinds of workgroups (one per
-  // compute unit: the scan's LDS) all run at once; the split is in the
-  // middle.  (With two kinds per unit resident at once and a later split
-  // the scan's period per chunk grows with the occupancy more than the
-  // shorter segments save.)
+  // Segment mode (SegParams): a dense call whose scan leaves most of the
+  // chip idle takes np segments, as many as let all (2 np - 1) K scan
+  // workgroups (one per compute unit: the scan's LDS) run at once.  (With
+  // more workgroups than compute units the scan's period per chunk grows
+  // with the occupancy more than the shorter segments save.)
   bool seg = false;
   if constexpr (kLdsScan && DK == DV) {
     const int64_t K = units * (DV / 16);
     const int cus = device_cus();
-    if (a->off_seg && !a->inspect && !a->serial && !s.chunk_seq && K % 8 == 0 && cus > 0 && 3 * K <= cus &&
-        s.cps >= 8) {
+    int32_t np = cus > 0 ? drla_seg_count(K, s.cps, cus) : 1;
+    if (np > a->seg_np) np = a->seg_np;  // what the workspace holds
+    if (a->off_seg && !a->inspect && !a->serial && !s.chunk_seq && np > 1) {
       seg = true;
-      sp.seg.s1 = s.cps / 2;
+      const drla_seg_layout L = drla_seg_offsets(units, DK, a->total_tokens, a->h_v, a->seg_np, sizeof(ET));
       char* sg = ws + a->off_seg;
-      const size_t state_bytes = (size_t)units * DK * DV * 4;
-      sp.seg.mid = (float*)sg;
-      sp.seg.n = (float*)(sg + state_bytes);
-      sp.seg.m = (float*)(sg + 2 * state_bytes);
-      sp.seg.midf = sg + 3 * state_bytes;
-      sp.seg.g = sg + 3 * state_bytes + state_bytes / 2;
-      nscan = 3 * K;
+      sp.seg.s1 = (int32_t)(s.cps / np);
+      sp.seg.np = np;
+      sp.seg.us = units * DK * DV;
+      sp.seg.mid = (float*)(sg + L.mid);
+      sp.seg.n = (float*)(sg + L.n);
+      sp.seg.m = (float*)(sg + L.m);
+      sp.seg.midf = sg + L.f;
+      sp.seg.g = sg + L.g;
+      nscan = (2 * np - 1) * K;
     }
   }
   if (e == hipSuccess) {
@@ -115,6 +117,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
       e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
   }
   if constexpr (kLdsScan && DK == DV) {
+    if (seg && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);
     if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, s.cps, st);
   }
   mark(2);

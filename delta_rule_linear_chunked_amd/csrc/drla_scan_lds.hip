@@ -91,10 +91,10 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
   int seq, h, nb;
-  int kind = 0;  // 0: whole sequence; segment mode: 1, 2, 3 (seg_item)
+  int kind = 0, sg = 0;  // 0: whole sequence; segment mode: 1, 2, 3 and the segment (seg_item)
   if (P.seg.s1 > 0) {
     int unit;
-    seg_item(P.s.n_seqs * P.h_v, NB, unit, nb, kind);
+    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, unit, nb, kind, sg);
     seq = unit / P.h_v;
     h = unit - seq * P.h_v;
   } else if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) {
@@ -117,15 +117,17 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     nch = P.s.cps;
     if (kind == 1) {
       nch = P.seg.s1;
-    } else if (kind > 1) {  // segment 1: chunks [s1, cps)
-      ts += (int64_t)C * P.seg.s1;
-      c0 += P.seg.s1;
-      nch = P.s.cps - P.seg.s1;
+    } else if (kind > 1) {  // segment sg: chunks [sg s1, (sg + 1) s1), the last to the end
+      ts += (int64_t)C * P.seg.s1 * sg;
+      c0 += (int64_t)P.seg.s1 * sg;
+      nch = sg == P.seg.np - 1 ? P.s.cps - (int64_t)P.seg.s1 * sg : P.seg.s1;
     }
   }
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
   T* const obase = (T*)(kind == 3 ? P.seg.g : P.o);
-  float* const sout = kind == 0 ? P.ht : kind == 1 ? P.seg.mid : kind == 2 ? P.seg.n : P.seg.m;
+  float* const sout = kind == 0   ? P.ht
+                      : kind == 1 ? P.seg.mid
+                                  : (kind == 2 ? P.seg.n : P.seg.m) + (int64_t)(sg - 1) * P.seg.us;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
   const int col = 16 * nb + c16;
   const T* kg = (const T*)P.k;
@@ -467,114 +469,208 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   }
 }
 
-// Segment mode, second step (see SegParams).  Workgroups [0, units * ng):
-// one (unit, cpb consecutive chunks of segment 1) each, O^T += mid^T G^T
-// for the chunks' tokens: mid's A fragments (outer = state column, inner =
-// key channels 32p + 8g + j), written by the segment-0 scan, are staged in
-// LDS once; G is read as row fragments (outer = token, the same channels);
-// wave w takes tokens 16w .. 16w + 15 of each chunk and updates o 8 bytes
-// per lane.  The rest: one (unit, 16 state columns) each, ht = n + M mid
-// in fp32.
+// Segment mode, second step (see SegParams): one workgroup per (unit, 16
+// state columns) chains the entering states in fp32, E_1 = mid, E_{s+1} =
+// N_s + M_s E_s, writes E_2 .. E_{np-1} as the fix-up's A fragments (E_1's
+// come from the segment-0 scan) and ht = E_np.  The product runs on fp32
+// MFMA (16x16x4): wave w takes row tiles RW w .. RW w + RW - 1 of M_s, the
+// B operand (E_s, k = 16 (kk / 4) + 4g + kk % 4 in step kk) sits in
+// registers, the A operand comes from M_s staged in LDS (rows padded by 4
+// floats, so a 16-lane phase of the 16-byte reads hits distinct banks).
+// M_{s+1} and N_{s+1} are loaded while step s computes.
 template <int DK, typename T>
-__global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t units, int32_t n1, int32_t cpb) {
+__global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t units) {
+  typedef typename VT<T>::v8 H8;
+  constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
+  constexpr int LD = DK + 4;             // padded row of M in LDS
+  constexpr int LE = 20;                 // padded row of E in LDS
+  constexpr int NM = DK * DK / 4 / 256;  // floatx4 loads of M per thread
+  constexpr int RW = DK / 64;            // row tiles per wave
+  constexpr int KS = DK / 4;             // MFMA steps over k
+  __shared__ __attribute__((aligned(16))) float mb[2][DK * LD];  // M_s, double-buffered
+  __shared__ __attribute__((aligned(16))) float eb[DK * LE];     // E_s, this block's 16 columns
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int u = blockIdx.x / CT, cb = blockIdx.x - u * CT;
+  const int64_t base = (int64_t)u * DK * DV;
+  floatx4 mr[NM], nr[RW], nc[RW];
+  auto load = [&](int s) {  // M_s (coalesced) and this lane's N_s entries into registers
+    const int64_t so = (int64_t)(s - 1) * P.seg.us + base;
+    const floatx4* m4 = (const floatx4*)(P.seg.m + so);
+#pragma unroll
+    for (int f = 0; f < NM; ++f) mr[f] = m4[f * 256 + tid];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        nr[i][e] = P.seg.n[so + (int64_t)(16 * (RW * w + i) + 4 * g4 + e) * DV + 16 * cb + c16];
+  };
+  auto stage = [&](int buf) {  // registers -> LDS rows
+#pragma unroll
+    for (int f = 0; f < NM; ++f) {
+      const int e = 4 * (f * 256 + tid);
+      *(floatx4*)&mb[buf][(e / DK) * LD + e % DK] = mr[f];
+    }
+  };
+  for (int i = tid; i < DK * 16; i += 256) eb[(i / 16) * LE + i % 16] = P.seg.mid[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16];
+  load(1);
+  stage(0);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) nc[i] = nr[i];
+  __syncthreads();
+  for (int s = 1; s < P.seg.np; ++s) {
+    const bool more = s + 1 < P.seg.np;
+    if (more) load(s + 1);  // in flight during this step
+    if (s >= 2) {
+      // E_s as fragments: lane 16g + c of key block p holds column 16 cb + c
+      // at key channels 32p + 8g + j
+      H8* mf = (H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + ((int64_t)u * CT + cb) * (KB * 64);
+      for (int f = tid; f < KB * 64; f += 256) {
+        const int p = f / 64, l = f % 64, g = l >> 4, c = l & 15;
+        H8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (T)eb[(32 * p + 8 * g + j) * LE + c];
+        mf[f] = x;
+      }
+    }
+    float bf[KS];  // B: E_s[k][c16], k = 16 (kk / 4) + 4 g + kk % 4
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) bf[kk] = eb[(16 * (kk >> 2) + 4 * g4 + (kk & 3)) * LE + c16];
+    floatx4 acc[RW];
+    const float* mbuf = mb[(s - 1) & 1];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      acc[i] = nc[i];
+      const float* arow = mbuf + (16 * (RW * w + i) + c16) * LD + 4 * g4;
+#pragma unroll
+      for (int kq = 0; kq < KS / 4; ++kq) {
+        const floatx4 a4 = *(const floatx4*)(arow + 16 * kq);  // M[row c][16 kq + 4g + j]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[j], bf[4 * kq + j], acc[i], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every read of E_s and of M_s's buffer is done
+    // lane: rows 16 rt + 4g + e, column c16
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eb[(16 * (RW * w + i) + 4 * g4 + e) * LE + c16] = acc[i][e];
+    if (more) {
+      stage(s & 1);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) nc[i] = nr[i];
+    }
+    __syncthreads();
+  }
+  if (P.ht) {
+    for (int i = tid; i < DK * 16; i += 256)
+      P.ht[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16] = eb[(i / 16) * LE + i % 16];
+  }
+}
+
+// Segment mode, last step: one workgroup per (unit, segment s >= 1, cpb
+// consecutive chunks of it), O^T += E_s^T G^T for the chunks' tokens.  E_s's
+// A fragments (outer = state column, inner = key channels 32p + 8g + j) are
+// staged in LDS once; G is read as row fragments (outer = token, the same
+// channels); wave w takes tokens 16w .. 16w + 15 of each chunk and updates o
+// 8 bytes per lane.  ng workgroups per segment cover the longest (last).
+template <int DK, typename T>
+__global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, int32_t cpb) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
   constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
-  __shared__ H8 af[CT * KB * 64];                            // mid as A fragments
-  __shared__ __attribute__((aligned(16))) float mb[DK][16];  // part B: mid, 16 columns
+  __shared__ H8 af[CT * KB * 64];  // E_s as A fragments
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int b = blockIdx.x;
-  const int ng = (n1 + cpb - 1) / cpb;
-  if (b < units * ng) {
-    const int u = b / ng, cg = b - u * ng;
-    const int seq = u / P.h_v, h = u - seq * P.h_v;
-    const H8* mf = (const H8*)P.seg.midf + (int64_t)u * (CT * KB * 64);
+  const int nsg = P.seg.np - 1;
+  const int u = blockIdx.x / (nsg * ng), rem = blockIdx.x - u * (nsg * ng);
+  const int s = 1 + rem / ng, cg = rem - (s - 1) * ng;
+  const int seq = u / P.h_v, h = u - seq * P.h_v;
+  const int cs = s * P.seg.s1, ce = s == P.seg.np - 1 ? (int)P.s.cps : cs + P.seg.s1;
+  const int cb = cs + cg * cpb, cend = cb + cpb < ce ? cb + cpb : ce;
+  if (cb >= cend) return;  // the whole workgroup: past its segment's end
+  const H8* mf = (const H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + (int64_t)u * (CT * KB * 64);
 #pragma unroll
-    for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
-    __syncthreads();
-    const uint32_t kstride = (uint32_t)P.h_v * DK * 2;  // G has o's layout
-    const int cend = (cg + 1) * cpb < n1 ? (cg + 1) * cpb : n1;
-    for (int c = cg * cpb; c < cend; ++c) {
-      const int64_t t0 = (int64_t)seq * P.s.seq_len + (int64_t)(P.seg.s1 + c) * C;
-      const int64_t left = (int64_t)seq * P.s.seq_len + P.s.seq_len - t0;
-      const uint32_t len = (uint32_t)(left < C ? left : C);
-      const rsrc_t gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * 2);
-      const rsrc_t orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
-      // lane: columns 16 ct + 4g + e of token 16 w + c
-      const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * 2;
-      H8 gf[KB];
-      H4 ov[CT];
+  for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
+  __syncthreads();
+  const uint32_t kstride = (uint32_t)P.h_v * DK * 2;  // G has o's layout
+  // lane: columns 16 ct + 4g + e of token 16 w + c
+  const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * 2;
+  const uint32_t goff = (uint32_t)(16 * w + c16) * kstride + (uint32_t)(8 * g4) * 2;
+  auto rsrcs = [&](int c, rsrc_t& gr, rsrc_t& orr) {
+    const int64_t t0 = (int64_t)seq * P.s.seq_len + (int64_t)c * C;
+    const int64_t left = (int64_t)seq * P.s.seq_len + P.s.seq_len - t0;
+    const uint32_t len = (uint32_t)(left < C ? left : C);
+    gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * 2);
+    orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+  };
+  // the next chunk's G and o are loaded while this one is multiplied and stored
+  rsrc_t gr, orr;
+  rsrcs(cb, gr, orr);
+  H8 gf[KB];
+  H4 ov[CT];
 #pragma unroll
-      for (int p = 0; p < KB; ++p)
-        gf[p] = bload<H8>(gr, (uint32_t)(16 * w + c16) * kstride + (uint32_t)(32 * p + 8 * g4) * 2);
+  for (int p = 0; p < KB; ++p) gf[p] = bload<H8>(gr, goff + 64 * p);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 32 * ct);
+  for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 32 * ct);
+  for (int c = cb; c < cend; ++c) {
+    rsrc_t grn = gr, orn = orr;
+    H8 gn[KB];
+    H4 on[CT];
+    if (c + 1 < cend) {
+      rsrcs(c + 1, grn, orn);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        floatx4 acc = zero4();
+      for (int p = 0; p < KB; ++p) gn[p] = bload<H8>(grn, goff + 64 * p);
 #pragma unroll
-        for (int p = 0; p < KB; ++p) acc = mma(af[(ct * KB + p) * 64 + lane], gf[p], acc);
-        floatx4 sum;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum[e] = to_f(ov[ct][e]) + acc[e];
-        bstore(orr, off0 + 32 * ct, pack4<T>(sum));
-      }
+      for (int ct = 0; ct < CT; ++ct) on[ct] = bload<H4>(orn, off0 + 32 * ct);
     }
-  } else {
-    const int bb = b - units * ng, u = bb / CT, cb = bb - u * CT;
-    const int64_t base = (int64_t)u * DK * DV;
 #pragma unroll
-    for (int i = tid; i < DK * 16; i += 256) mb[i / 16][i % 16] = P.seg.mid[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16];
-    __syncthreads();
-    // thread: row r, columns 8 hh .. 8 hh + 7 of this block
-    const int r = tid >> 1, hh = tid & 1;
-    if (r < DK) {
-      float acc[8];
+    for (int ct = 0; ct < CT; ++ct) {
+      floatx4 acc = zero4();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = P.seg.n[base + (int64_t)r * DV + 16 * cb + 8 * hh + q];
-      const float* mrow = P.seg.m + (int64_t)u * DK * DK + (int64_t)r * DK;
-#pragma unroll 8
-      for (int j = 0; j < DK; j += 4) {
-        const floatx4 mv = *(const floatx4*)(mrow + j);
+      for (int p = 0; p < KB; ++p) acc = mma(af[(ct * KB + p) * 64 + lane], gf[p], acc);
+      floatx4 sum;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const floatx4 lo = *(const floatx4*)&mb[j + jj][8 * hh];
-          const floatx4 hi = *(const floatx4*)&mb[j + jj][8 * hh + 4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[q] += mv[jj] * lo[q];
-            acc[q + 4] += mv[jj] * hi[q];
-          }
-        }
-      }
-      if (P.ht) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) P.ht[base + (int64_t)r * DV + 16 * cb + 8 * hh + q] = acc[q];
-      }
+      for (int e = 0; e < 4; ++e) sum[e] = to_f(ov[ct][e]) + acc[e];
+      bstore(orr, off0 + 32 * ct, pack4<T>(sum));
     }
+    gr = grn;
+    orr = orn;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) gf[p] = gn[p];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ov[ct] = on[ct];
   }
 }
 
 template <int DK, typename T>
-hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st) {
-  const int32_t n1 = cps - P.seg.s1;
-  // chunks per workgroup: one while that leaves at most a workgroup per
-  // compute unit (256), at most four (each workgroup loads mid once)
-  const int64_t per = n_units * n1 / 256;
-  const int32_t cpb = per < 1 ? 1 : per > 4 ? 4 : (int32_t)per;
-  const int64_t nblk = n_units * ((n1 + cpb - 1) / cpb) + n_units * (DK / 16);
-  hipLaunchKernelGGL((seg_fix_kernel<DK, T>), dim3((unsigned)nblk), dim3(256), 0, st, P, (int32_t)n_units, n1, cpb);
+hipError_t launch_seg_compose(const ScanParams& P, int64_t n_units, hipStream_t st) {
+  hipLaunchKernelGGL((seg_compose_kernel<DK, T>), dim3((unsigned)(n_units * (DK / 16))), dim3(256), 0, st, P,
+                     (int32_t)n_units);
   return hipGetLastError();
 }
 
-#define DRLA_SEG_FIX_INST(DK_, T_) \
+template <int DK, typename T>
+hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st) {
+  const int32_t last = cps - (P.seg.np - 1) * P.seg.s1;  // the longest segment
+  // chunks per workgroup: one while that leaves at most a workgroup per
+  // compute unit (256), at most four (each workgroup loads E_s once)
+  const int64_t per = n_units * (cps - P.seg.s1) / 256;
+  const int32_t cpb = per < 1 ? 1 : per > 4 ? 4 : (int32_t)per;
+  const int32_t ng = (last + cpb - 1) / cpb;
+  const int64_t nblk = n_units * (P.seg.np - 1) * ng;
+  hipLaunchKernelGGL((seg_fix_kernel<DK, T>), dim3((unsigned)nblk), dim3(256), 0, st, P, ng, cpb);
+  return hipGetLastError();
+}
+
+#define DRLA_SEG_INST(DK_, T_)                                                                      \
+  template hipError_t launch_seg_compose<DK_, T_>(const ScanParams&, int64_t, hipStream_t);         \
   template hipError_t launch_seg_fix<DK_, T_>(const ScanParams&, int64_t, int32_t, hipStream_t);
-DRLA_SEG_FIX_INST(64, bf16)
-DRLA_SEG_FIX_INST(128, bf16)
-DRLA_SEG_FIX_INST(64, f16)
-DRLA_SEG_FIX_INST(128, f16)
-#undef DRLA_SEG_FIX_INST
+DRLA_SEG_INST(64, bf16)
+DRLA_SEG_INST(128, bf16)
+DRLA_SEG_INST(64, f16)
+DRLA_SEG_INST(128, f16)
+#undef DRLA_SEG_INST
 
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {

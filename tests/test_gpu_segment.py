@@ -1,16 +1,20 @@
-"""The segment-split scan of dense calls that use at most a third of the chip.
+"""The segment-split scan of dense calls that leave most of the chip idle.
 
-Such a call scans chunks [0, s1) of every (sequence, head) from the initial
-state, and chunks [s1, n) twice at the same time: from a zero state with the
-real values, and from the identity with V = 0 (which gives the linear map of
-the entering state on the outputs and on the final state).  A second kernel
-adds the map applied to the state after chunk s1 - 1.  The cases take ragged
-last chunks, grouped heads, dk = 64 and 128, a dense batch, no initial
-state, no final state, the fewest chunks the split takes, and the
-decay-only form; each is checked against the oracle, and against the
-one-pass scan of the same call (DRLA_SERIAL), which must differ in rounding
-somewhere (else the split did not run).  A call too wide for the split must
-equal the one-pass scan bit for bit."""
+Such a call splits every sequence's chunks into np segments (np = 2 when
+three scan workgroups per column block fill a third of the chip, up to 16
+for a single head).  Segment 0 is scanned from the initial state; every
+later one twice at the same time: from a zero state with the real values,
+and from the identity with V = 0 (the linear map of the entering state on
+the outputs and on the final state).  A compose kernel chains the entering
+states and a fix-up adds each segment's map applied to its entering state.
+The cases take 2, 3, 4, 6, 8 and 11 segments, an uneven last segment,
+workgroup counts that are not a multiple of 8, ragged last chunks, grouped
+heads, dk = 64 and 128, a dense batch, no initial state, no final state, the
+fewest chunks a split takes, and the decay-only form; each is checked
+against the oracle, and against the one-pass scan of the same call
+(DRLA_SERIAL), which must differ in rounding somewhere (else the split did
+not run).  A call too wide for the split equals the one-pass scan bit for
+bit."""
 import numpy as np
 import pytest
 
@@ -43,13 +47,16 @@ def _call(drla, kind, d, dense_batch, flags, want_ht):
 
 # (kind, io, h_qk, h_v, d, lens, h0_std, want_ht)
 CASES = [
-    ("gdn", "bf16", 2, 4, 128, (1000,), 0.05, True),      # ragged tail
-    ("gdn", "f16", 4, 4, 64, (777,), 0.05, True),         # d = 64
-    ("gdn", "bf16", 4, 8, 128, (1000,), 0.0, True),       # 192 scan workgroups
-    ("gdn", "bf16", 2, 16, 64, (2000,), 0.05, True),      # 16 heads of d = 64
+    ("gdn", "bf16", 2, 4, 128, (1000,), 0.05, True),      # 4 segments, ragged tail
+    ("gdn", "f16", 4, 4, 64, (777,), 0.05, True),         # 3 segments, last of 5 chunks
+    ("gdn", "bf16", 4, 8, 128, (1000,), 0.0, True),       # 2 segments, 192 workgroups
+    ("gdn", "bf16", 2, 16, 64, (2000,), 0.05, True),      # 2 segments, 16 heads of d = 64
     ("ret", "bf16", 2, 4, 128, (600, 600), 0.05, True),   # dense batch
     ("gdn", "bf16", 2, 4, 128, (3000,), 0.05, False),     # no final state
     ("ret", "f16", 1, 4, 64, (520,), 0.0, True),          # eight chunks, the least
+    ("gdn", "bf16", 1, 1, 128, (3000,), 0.05, True),      # 11 segments, last of 7 chunks
+    ("gdn", "f16", 2, 2, 64, (2000,), 0.05, True),        # 8 segments
+    ("ret", "bf16", 1, 1, 64, (1500,), 0.05, True),       # 6 segments, 44 workgroups
 ]
 
 
@@ -87,7 +94,7 @@ def test_segment_split_repeatable(drla):
     """Two calls of the split scan on the same inputs agree bit for bit (no
     workgroup reads what another of the same call is still writing)."""
     print("case segment repeatable", flush=True)
-    spec = W.small_spec("gdn", lens=(2000,), h_qk=4, h_v=8, dk=128, dv=128, io="bf16",
+    spec = W.small_spec("gdn", lens=(4000,), h_qk=2, h_v=2, dk=128, dv=128, io="bf16",
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=42)
     d = to_device(W.make_inputs(spec))
     a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])

@@ -167,6 +167,11 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(sl)) == 0
     assert sl.seg - sl.gam == 64 * 8 * 128 * 4
     assert sl.total - sl.seg == 3 * 8 * 128 * 128 * 4 + 8 * 128 * 128 * 2 + 4096 * 8 * 128 * 2
+    # 2 heads: 8 segments of 15 x 16 workgroups; seven N, M and fragment sets
+    p2h = _prob(n_seqs=1, h_qk=2, h_v=2, dk=128, dv=128, io=0, T=65536)
+    assert lib.drla_workspace_layout(0, ctypes.byref(p2h), None, 0, ctypes.byref(sl)) == 0
+    us = 2 * 128 * 128
+    assert sl.total - sl.seg == us * 4 + 7 * 2 * us * 4 + 7 * us * 2 + 65536 * 2 * 128 * 2
     # fp32 inputs keep K~^T for the register-fed scan
     pf = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=1, T=4096)
     fl = Layout()
