@@ -183,11 +183,12 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY
  *                 and DRLA_SERIAL, or 0.  DRLA_SERIAL turns off the
  *                 segment-parallel scan (same results up to rounding),
- *                 which dense scalar-gate calls with 16-bit inputs, dk ==
- *                 dv and at least 8 chunks per sequence take when
- *                 U = n_seqs * h_v * dv/16 is a multiple of 8 and 3U is at
- *                 most the device's compute units: each sequence's chunks
- *                 are split in half and the halves scanned at once.
+ *                 which dense scalar-gate calls with 16-bit inputs and dk ==
+ *                 dv take when U = n_seqs * h_v * dv/16 is small: each
+ *                 sequence's chunks are split into the most np <= 16
+ *                 segments of at least 4 chunks for which (2 np - 1) U is
+ *                 at most the device's compute units (and at most 256),
+ *                 and the segments are scanned at once.
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels
@@ -232,12 +233,12 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
- *   seg (dense scalar-gate calls with 16-bit inputs and dk == dv whose
- *        n_seqs * h_v * dv/16 is at most 85, else 0): the segment-split
- *        scan's three fp32 states per (sequence, head) -- after the first
- *        segment, the second segment's from zero, its map of the entering
- *        state -- then the first again as io-type fragments, then the map's
- *        contribution to o per token, laid out as o
+ *   seg (dense scalar-gate calls with 16-bit inputs and dk == dv that the
+ *        segment split takes on a 256-CU device, else 0): for np segments,
+ *        the fp32 state after the first segment, np - 1 zero-start final
+ *        states and np - 1 maps of the entering state (fp32, per (sequence,
+ *        head)), np - 1 entering states as io-type fragments, then the
+ *        maps' contribution to o per token, laid out as o
  * Elements are io dtype except gam and the seg states (fp32).  n_chunks is the total chunk
  * count over all sequences.  Returns DRLA_OK or a validation error. */
 typedef struct {
