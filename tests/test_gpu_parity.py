@@ -354,7 +354,7 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
 # ---- the five named workloads ----------------------------------------------
 
 def _workload(drla, name, heads=None):
-    spec = W.WORKLOADS[name]
+    spec = W.spec_by_name(name)
     print(f"workload {name}: lens={spec.lens[:8]} h_qk={spec.h_qk} h_v={spec.h_v} "
           f"d={spec.dk} io={spec.io} heads={heads}", flush=True)
     x = W.make_inputs(spec)
@@ -370,6 +370,12 @@ def _workload(drla, name, heads=None):
 
 def test_workload_gdn_tiny(drla):
     _workload(drla, "gdn_tiny")
+
+
+def test_workload_gdn_long_h2(drla):
+    """One 65,536-token sequence with 2 heads: the segment-split scan at 8
+    segments, against the oracle over the whole sequence."""
+    _workload(drla, "gdn_long_h2")
 
 
 def test_workload_gdn_prefill(drla):

@@ -111,8 +111,16 @@ DECAY_WORKLOADS = {
 }
 
 
+# Long-context prefill with few heads per GPU: one 65,536-token sequence
+# with 2 value heads (16 heads sharded over 8 GPUs by head), d = 128.
+FEW_HEAD_WORKLOADS = {
+    "gdn_long_h2": Spec("gdn_long_h2", "gdn", (65536,), 2, 2, 128, 128, "bf16",
+                        0.001, 0.05, 0.02, seed=9),
+}
+
+
 def spec_by_name(name: str) -> Spec:
-    for table in (WORKLOADS, DECODE_WORKLOADS, F16_WORKLOADS, DECAY_WORKLOADS):
+    for table in (WORKLOADS, DECODE_WORKLOADS, F16_WORKLOADS, DECAY_WORKLOADS, FEW_HEAD_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)
