@@ -122,6 +122,9 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   L->total = off;
 }
 
+// Packed input that the kernels take as such: more than one sequence.
+static bool packed(const drla_problem* p, const int32_t* cu_host) { return cu_host != nullptr && p->n_seqs > 1; }
+
 drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const void* k, const void* v,
                 const float* beta, const float* g, const float* h0, const int32_t* cu_dev,
                 const int32_t* cu_host, void* o, float* ht, void* ws, size_t ws_bytes, void* stream,
@@ -134,6 +137,8 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   if (st != DRLA_OK) return st;
   if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
     return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  // one packed sequence (cu_seqlens = {0, T}, checked above) is a dense call
+  if (cu_host && !packed(p, cu_host)) cu_dev = cu_host = nullptr;
   const bool decay = (flags & DRLA_DECAY_ONLY) != 0;
   if (decay) beta = nullptr;  // unused without the delta rule
   const int64_t T = p->total_tokens;
@@ -302,8 +307,8 @@ size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_hos
   int64_t nc = 0;
   if (check_problem(p, cu_seqlens_host, &nc) != DRLA_OK) return 0;
   drla_layout L, G;
-  layout_of(p, nc, cu_seqlens_host != nullptr, true, 0, &L);
-  layout_of(p, nc, cu_seqlens_host != nullptr, false, 0, &G);
+  layout_of(p, nc, packed(p, cu_seqlens_host), true, 0, &L);
+  layout_of(p, nc, packed(p, cu_seqlens_host), false, 0, &G);
   return L.total > G.total ? L.total : G.total;
 }
 
@@ -315,7 +320,7 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (st != DRLA_OK) return st;
   if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
     return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
-  layout_of(p, nc, cu_seqlens_host != nullptr, kda != 0, flags, out);
+  layout_of(p, nc, packed(p, cu_seqlens_host), kda != 0, flags, out);
   return DRLA_OK;
 }
 

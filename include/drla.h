@@ -101,6 +101,8 @@ size_t drla_workspace_bytes(const drla_problem* p,
  *   q, k, v, beta, g      device inputs, layouts above
  *   h0                    device [N,h_v,dk,dv] fp32 initial state, or NULL (zeros)
  *   cu_seqlens_dev/_host  the same [N+1] array on device and host, or both NULL
+ *                         (with N = 1 the call is run, and its workspace laid
+ *                         out, as the dense call; the arrays are not read)
  *   o                     device output [T,h_v,dv] in io dtype
  *   ht                    device output [N,h_v,dk,dv] fp32 final state, or NULL;
  *                         may be exactly h0 (in-place state update)

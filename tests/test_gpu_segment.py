@@ -114,3 +114,19 @@ def test_wide_call_runs_one_pass(drla):
     b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_one_packed_sequence_is_dense(drla):
+    """One sequence passed with cu_seqlens = {0, T} takes the dense path, the
+    segment split included: the same bits as the call without cu_seqlens."""
+    print("case segment one packed sequence", flush=True)
+    spec = W.small_spec("gdn", lens=(3000,), h_qk=2, h_v=2, dk=128, dv=128, io="bf16",
+                        g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=44)
+    d = to_device(W.make_inputs(spec))
+    cu = torch.tensor([0, 3000], dtype=torch.int32, device="cuda")
+    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], cu, cu_seqlens_host=[0, 3000])
+    c = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert not torch.equal(a[0], c[0]), "the split scan did not run"

@@ -172,6 +172,13 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p2h), None, 0, ctypes.byref(sl)) == 0
     us = 2 * 128 * 128
     assert sl.total - sl.seg == us * 4 + 7 * 2 * us * 4 + 7 * us * 2 + 65536 * 2 * 128 * 2
+    # one sequence passed with cu_seqlens {0, T} is laid out as the dense call
+    cu1, _c1 = _i32([0, 4096])
+    dl, pl = Layout(), Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(dl)) == 0
+    assert lib.drla_workspace_layout(0, ctypes.byref(p8), cu1, 0, ctypes.byref(pl)) == 0
+    assert (pl.tb, pl.seg, pl.total) == (dl.tb, dl.seg, dl.total) and pl.seg > 0
+    assert lib.drla_workspace_bytes(ctypes.byref(p8), cu1) == lib.drla_workspace_bytes(ctypes.byref(p8), None)
     # fp32 inputs keep K~^T for the register-fed scan
     pf = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=1, T=4096)
     fl = Layout()
