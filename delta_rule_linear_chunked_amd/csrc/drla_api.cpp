@@ -75,15 +75,28 @@ drla_status check_problem(const drla_problem* p, const int32_t* cu_host, int64_t
   return DRLA_OK;
 }
 
-// Segments the workspace provides for (drla_seg_count at 256 compute
-// units); 1 for calls the split does not take.
-static int32_t seg_count(const drla_problem* p, bool varlen, bool kda) {
-  if (varlen || kda || p->io_dtype == DRLA_F32 || p->dk != p->dv || p->n_seqs < 1) return 1;
-  const int64_t cps = (p->total_tokens / p->n_seqs + DRLA_CHUNK - 1) / DRLA_CHUNK;
-  return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), cps, 256);
+// Chunks of the longest sequence (cu_host: a checked packed layout, or NULL
+// for a dense batch).
+static int64_t max_chunks(const drla_problem* p, const int32_t* cu_host) {
+  if (p->n_seqs < 1) return 0;
+  if (!cu_host) return (p->total_tokens / p->n_seqs + DRLA_CHUNK - 1) / DRLA_CHUNK;
+  int64_t m = 0;
+  for (int s = 0; s < p->n_seqs; ++s) {
+    const int64_t c = ((int64_t)cu_host[s + 1] - cu_host[s] + DRLA_CHUNK - 1) / DRLA_CHUNK;
+    m = c > m ? c : m;
+  }
+  return m;
 }
 
-void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int flags, drla_layout* L) {
+// Segments the workspace provides for (drla_seg_count at 256 compute
+// units, over the longest sequence); 1 for calls the split does not take.
+static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda) {
+  if (kda || p->io_dtype == DRLA_F32 || p->dk != p->dv || p->n_seqs < 1) return 1;
+  return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
+}
+
+void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, bool kda, int flags,
+               drla_layout* L) {
   const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
   const size_t ncH = (size_t)nc * p->h_v;
   const size_t frag = 64 * 8 * es;  // one operand fragment
@@ -115,7 +128,7 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, bool kda, int fla
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
   // Segment-split scan (dense scalar-gate calls with 16-bit inputs and
   // dk = dv that leave most of a 256-CU chip idle): its states and G
-  const int32_t np = seg_count(p, varlen, kda);
+  const int32_t np = seg_count(p, max_cps, kda);
   L->seg = np > 1 ? off : 0;
   if (np > 1)
     off = align_up(off + drla_seg_offsets((int64_t)p->n_seqs * p->h_v, p->dk, p->total_tokens, p->h_v, np, es).total);
@@ -148,7 +161,8 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
   drla_layout L;
-  layout_of(p, nc, cu_dev != nullptr, kda, flags, &L);
+  const int64_t max_cps = max_chunks(p, cu_host);
+  layout_of(p, nc, cu_dev != nullptr, max_cps, kda, flags, &L);
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(DRLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : 0);
   const size_t es = p->io_dtype == DRLA_F32 ? 4 : 2;
@@ -195,7 +209,8 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.off_vp = L.vp;
   a.off_h = L.h;
   a.off_seg = L.seg;
-  a.seg_np = L.seg ? seg_count(p, cu_dev != nullptr, kda) : 1;
+  a.seg_np = L.seg ? seg_count(p, max_cps, kda) : 1;
+  a.max_cps = max_cps;
   a.total_tokens = T;
   a.n_chunks = nc;
   a.n_seqs = p->n_seqs;
@@ -307,8 +322,10 @@ size_t drla_workspace_bytes(const drla_problem* p, const int32_t* cu_seqlens_hos
   int64_t nc = 0;
   if (check_problem(p, cu_seqlens_host, &nc) != DRLA_OK) return 0;
   drla_layout L, G;
-  layout_of(p, nc, packed(p, cu_seqlens_host), true, 0, &L);
-  layout_of(p, nc, packed(p, cu_seqlens_host), false, 0, &G);
+  const bool pk = packed(p, cu_seqlens_host);
+  const int64_t mc = max_chunks(p, pk ? cu_seqlens_host : nullptr);
+  layout_of(p, nc, pk, mc, true, 0, &L);
+  layout_of(p, nc, pk, mc, false, 0, &G);
   return L.total > G.total ? L.total : G.total;
 }
 
@@ -320,7 +337,8 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (st != DRLA_OK) return st;
   if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
     return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
-  layout_of(p, nc, packed(p, cu_seqlens_host), kda != 0, flags, out);
+  const bool pk = packed(p, cu_seqlens_host);
+  layout_of(p, nc, pk, max_chunks(p, pk ? cu_seqlens_host : nullptr), kda != 0, flags, out);
   return DRLA_OK;
 }
 

@@ -23,8 +23,8 @@ struct PrepParams {
   int32_t decay_only;  // no delta rule: beta = 1, A = 0 (T = I); beta may be null
 };
 
-// Segment-parallel scan (dense batch, dk = dv): every sequence's chunks are
-// split into np segments of s1 chunks (the last takes the rest).  Segment
+// Segment-parallel scan (dk = dv): every sequence's n chunks are split into
+// np segments of n / np chunks (the last takes the rest).  Segment
 // 0 is scanned from h0 (final state into mid).  Every later segment s is
 // scanned both from a zero state (its local outputs into o, final state
 // into n[s-1]) and, by as many "transition" workgroups, from the identity
@@ -32,7 +32,7 @@ struct PrepParams {
 // and E_{s+1} = N_s + M_s E_s (seg_compose), segment s's true outputs are
 // o += G E_s (seg_fix) and ht = E_np.
 struct SegParams {
-  int32_t s1;   // > 0: segment mode; chunks of every segment but the last
+  int32_t s1;   // > 0: segment mode (the longest sequence's segment length)
   int32_t np;   // segments
   int64_t us;   // elements of one state set: sequences x heads x dk x dv
   void* g;      // [T, h_v, dk] in the io type, like o

@@ -55,6 +55,7 @@ typedef struct {
   size_t off_sched, off_tb, off_pm, off_kt, off_kw, off_qw, off_gam, off_vp, off_h;
   size_t off_seg;  // 0, or the segment-mode scan's states and G (dense calls)
   int32_t seg_np;  // segments the seg region holds (drla_seg_count at 256 CUs)
+  int64_t max_cps; // chunks of the longest sequence
   int64_t total_tokens;
   int64_t n_chunks;
   int32_t n_seqs, h_qk, h_v, dk, dv;

@@ -93,13 +93,13 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   if constexpr (kLdsScan && DK == DV) {
     const int64_t K = units * (DV / 16);
     const int cus = device_cus();
-    int32_t np = cus > 0 ? drla_seg_count(K, s.cps, cus) : 1;
+    int32_t np = cus > 0 ? drla_seg_count(K, a->max_cps, cus) : 1;
     if (np > a->seg_np) np = a->seg_np;  // what the workspace holds
-    if (a->off_seg && !a->inspect && !a->serial && !s.chunk_seq && np > 1) {
+    if (a->off_seg && !a->inspect && !a->serial && np > 1) {
       seg = true;
       const drla_seg_layout L = drla_seg_offsets(units, DK, a->total_tokens, a->h_v, a->seg_np, sizeof(ET));
       char* sg = ws + a->off_seg;
-      sp.seg.s1 = (int32_t)(s.cps / np);
+      sp.seg.s1 = (int32_t)(a->max_cps / np);  // of the longest sequence (>= 4: segment mode)
       sp.seg.np = np;
       sp.seg.us = units * DK * DV;
       sp.seg.mid = (float*)(sg + L.mid);
@@ -118,7 +118,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   }
   if constexpr (kLdsScan && DK == DV) {
     if (seg && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);
-    if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, s.cps, st);
+    if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, (int32_t)a->max_cps, st);
   }
   mark(2);
   return e;

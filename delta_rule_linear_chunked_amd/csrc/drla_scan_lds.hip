@@ -115,12 +115,18 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     te = ts + P.s.seq_len;
     c0 = (int64_t)seq * P.s.cps;
     nch = P.s.cps;
+  }
+  if (kind > 0) {
+    // segment sg of this sequence: chunks [sg s1, (sg + 1) s1), the last to
+    // the end, s1 = nch / np (0 for a sequence of fewer chunks than
+    // segments: its last segment takes them all)
+    const int64_t s1 = nch / P.seg.np;
     if (kind == 1) {
-      nch = P.seg.s1;
-    } else if (kind > 1) {  // segment sg: chunks [sg s1, (sg + 1) s1), the last to the end
-      ts += (int64_t)C * P.seg.s1 * sg;
-      c0 += (int64_t)P.seg.s1 * sg;
-      nch = sg == P.seg.np - 1 ? P.s.cps - (int64_t)P.seg.s1 * sg : P.seg.s1;
+      nch = s1;
+    } else {
+      ts += (int64_t)C * s1 * sg;
+      c0 += s1 * sg;
+      nch = sg == P.seg.np - 1 ? nch - s1 * sg : s1;
     }
   }
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
@@ -586,7 +592,22 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
   const int u = blockIdx.x / (nsg * ng), rem = blockIdx.x - u * (nsg * ng);
   const int s = 1 + rem / ng, cg = rem - (s - 1) * ng;
   const int seq = u / P.h_v, h = u - seq * P.h_v;
-  const int cs = s * P.seg.s1, ce = s == P.seg.np - 1 ? (int)P.s.cps : cs + P.seg.s1;
+  // the sequence's tokens and chunks, as the scan takes them
+  int64_t ts, te, n_i;
+  if (P.s.chunk_seq) {
+    ts = P.s.cu[seq];
+    te = P.s.cu[seq + 1];
+    int64_t c0, c1;
+    seq_chunks(P.s, seq, P.nc, c0, c1);
+    n_i = te > ts ? (te - ts + C - 1) / C : 0;
+    if (n_i > c1 - c0) n_i = c1 - c0;
+  } else {
+    ts = (int64_t)seq * P.s.seq_len;
+    te = ts + P.s.seq_len;
+    n_i = P.s.cps;
+  }
+  const int s1 = (int)(n_i / P.seg.np);
+  const int cs = s * s1, ce = s == P.seg.np - 1 ? (int)n_i : cs + s1;
   const int cb = cs + cg * cpb, cend = cb + cpb < ce ? cb + cpb : ce;
   if (cb >= cend) return;  // the whole workgroup: past its segment's end
   const H8* mf = (const H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + (int64_t)u * (CT * KB * 64);
@@ -598,8 +619,8 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
   const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * 2;
   const uint32_t goff = (uint32_t)(16 * w + c16) * kstride + (uint32_t)(8 * g4) * 2;
   auto rsrcs = [&](int c, rsrc_t& gr, rsrc_t& orr) {
-    const int64_t t0 = (int64_t)seq * P.s.seq_len + (int64_t)c * C;
-    const int64_t left = (int64_t)seq * P.s.seq_len + P.s.seq_len - t0;
+    const int64_t t0 = ts + (int64_t)c * C;
+    const int64_t left = te - t0;
     const uint32_t len = (uint32_t)(left < C ? left : C);
     gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * 2);
     orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
@@ -652,10 +673,11 @@ hipError_t launch_seg_compose(const ScanParams& P, int64_t n_units, hipStream_t 
 
 template <int DK, typename T>
 hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st) {
-  const int32_t last = cps - (P.seg.np - 1) * P.seg.s1;  // the longest segment
+  // cps: chunks of the longest sequence; no segment is longer than cps/np + np
+  const int32_t last = cps / P.seg.np + P.seg.np;
   // chunks per workgroup: one while that leaves at most a workgroup per
   // compute unit (256), at most four (each workgroup loads E_s once)
-  const int64_t per = n_units * (cps - P.seg.s1) / 256;
+  const int64_t per = n_units * (cps - cps / P.seg.np) / 256;
   const int32_t cpb = per < 1 ? 1 : per > 4 ? 4 : (int32_t)per;
   const int32_t ng = (last + cpb - 1) / cpb;
   const int64_t nblk = n_units * (P.seg.np - 1) * ng;

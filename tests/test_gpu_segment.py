@@ -130,3 +130,43 @@ def test_one_packed_sequence_is_dense(drla):
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert not torch.equal(a[0], c[0]), "the split scan did not run"
+
+
+# packed batches: (kind, io, h_qk, h_v, d, lens)
+PACKED = [
+    ("gdn", "bf16", 2, 2, 128, (1500, 700, 0, 2100)),   # 2 segments, an empty sequence
+    ("gdn", "bf16", 1, 1, 128, (3000, 100, 0)),         # 5 segments; 2 chunks: the last takes both
+    ("ret", "f16", 1, 2, 64, (900, 2500)),              # 8 segments, one of 1 chunk each but the last
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[f"{c[0]}-{c[1]}-h{c[3]}-d{c[4]}-{c[5]}" for c in PACKED])
+def test_segment_split_packed(drla, case):
+    """Packed input: each sequence splits its own chunks into the call's np
+    segments; against the oracle and the one-pass scan."""
+    kind, io, h_qk, h_v, dk, lens = case
+    print(f"case segment packed kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} lens={lens}", flush=True)
+    spec = W.small_spec(kind, lens=lens, h_qk=h_qk, h_v=h_v, dk=dk, dv=dk, io=io,
+                        g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=45)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+
+    def call(flags):
+        if kind == "ret":
+            return drla.decay_prefill(d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu"],
+                                      cu_seqlens_host=d["cu_host"], per_channel=False, flags=flags)
+        return drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
+                                cu_seqlens_host=d["cu_host"], flags=flags)
+    o, ht = call(0)
+    o1, ht1 = call(drla.SERIAL)
+    torch.cuda.synchronize()
+    o, o1 = o.float().cpu().numpy(), o1.float().cpu().numpy()
+    ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
+    o_ref, ht_ref = run_oracle(x)
+    tol = TOL[io]
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e} one-pass o={rel_err(o1, o_ref):.3e} (tol {tol:g})", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    assert eo <= tol and eh <= tol
+    assert rel_err(o, o1) <= tol and rel_err(ht, ht1) <= tol
+    assert not np.array_equal(o, o1), "the split scan did not run"
