@@ -185,12 +185,13 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY
  *                 and DRLA_SERIAL, or 0.  DRLA_SERIAL turns off the
  *                 segment-parallel scan (same results up to rounding),
- *                 which dense scalar-gate calls with 16-bit inputs and dk ==
- *                 dv take when U = n_seqs * h_v * dv/16 is small: each
- *                 sequence's chunks are split into the most np <= 16
- *                 segments of at least 4 chunks for which (2 np - 1) U is
- *                 at most the device's compute units (and at most 256),
- *                 and the segments are scanned at once.
+ *                 which scalar-gate calls with 16-bit inputs and dk == dv
+ *                 take when U = n_seqs * h_v * dv/16 is small: each
+ *                 sequence's chunks are split into np segments (n / np
+ *                 chunks each, the last takes the rest), np the most up to
+ *                 16 for which (2 np - 1) U is at most the device's compute
+ *                 units (and at most 256) and the longest sequence has at
+ *                 least 4 np chunks, and the segments are scanned at once.
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels
@@ -235,7 +236,7 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
- *   seg (dense scalar-gate calls with 16-bit inputs and dk == dv that the
+ *   seg (scalar-gate calls with 16-bit inputs and dk == dv that the
  *        segment split takes on a 256-CU device, else 0): for np segments,
  *        the fp32 state after the first segment, np - 1 zero-start final
  *        states and np - 1 maps of the entering state (fp32, per (sequence,
