@@ -208,3 +208,36 @@ def test_workspace_bytes_and_layout(lib):
 def test_status_strings(lib):
     for s in range(9):
         assert lib.drla_status_str(s)
+
+
+def _seg_np(units_cb, max_cps, cus=256):
+    """The segment count rule as the header states it: the most np <= 16 with
+    (2 np - 1) U <= cus and at least 4 np chunks in the longest sequence."""
+    np_ = 1
+    for p in range(2, 17):
+        if (2 * p - 1) * units_cb <= cus and max_cps >= 4 * p:
+            np_ = p
+    return np_
+
+
+@pytest.mark.parametrize("h_v,d,lens", [
+    (1, 128, (3000,)), (2, 128, (65536,)), (4, 64, (8192,)), (8, 128, (4096,)),
+    (11, 128, (4096,)), (1, 64, (1500,)), (2, 128, (1500, 700, 0, 2100)), (1, 128, (3000, 100, 0)),
+    (4, 128, (200,)), (16, 64, (2000,)),
+])
+def test_segment_region_follows_the_count_rule(lib, h_v, d, lens):
+    """The seg region holds mid, np - 1 sets of N and M (fp32), np - 1
+    entering states in bf16, and G [T, h_v, d] in bf16."""
+    from delta_rule_linear_chunked_amd._lib import Layout
+    n, T = len(lens), sum(lens)
+    p = _prob(n_seqs=n, h_qk=1, h_v=h_v, dk=d, dv=d, io=0, T=T)
+    cu, _c = _i32([0] + [sum(lens[:i + 1]) for i in range(n)])
+    lay = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), cu if n > 1 else None, 0, ctypes.byref(lay)) == 0
+    np_ = _seg_np(n * h_v * d // 16, max((L + 63) // 64 for L in lens))
+    if np_ == 1:
+        assert lay.seg == 0
+        return
+    us = n * h_v * d * d
+    assert lay.seg > 0
+    assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * 2 + T * h_v * d * 2
