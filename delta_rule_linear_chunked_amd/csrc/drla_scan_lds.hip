@@ -479,19 +479,20 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
 // state columns) chains the entering states in fp32, E_1 = mid, E_{s+1} =
 // N_s + M_s E_s, writes E_2 .. E_{np-1} as the fix-up's A fragments (E_1's
 // come from the segment-0 scan) and ht = E_np.  The product runs on fp32
-// MFMA (16x16x4): wave w takes row tiles RW w .. RW w + RW - 1 of M_s, the
+// MFMA (16x16x4): dk/16 waves, wave w takes row tile w of M_s, the
 // B operand (E_s, k = 16 (kk / 4) + 4g + kk % 4 in step kk) sits in
 // registers, the A operand comes from M_s staged in LDS (rows padded by 4
 // floats, so a 16-lane phase of the 16-byte reads hits distinct banks).
 // M_{s+1} and N_{s+1} are loaded while step s computes.
 template <int DK, typename T>
-__global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t units) {
+__global__ __launch_bounds__(DK * 4) void seg_compose_kernel(ScanParams P, int32_t units) {
   typedef typename VT<T>::v8 H8;
   constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
   constexpr int LD = DK + 4;             // padded row of M in LDS
   constexpr int LE = 20;                 // padded row of E in LDS
-  constexpr int NM = DK * DK / 4 / 256;  // floatx4 loads of M per thread
-  constexpr int RW = DK / 64;            // row tiles per wave
+  constexpr int NT = DK * 4;             // threads: one wave per row tile
+  constexpr int NM = DK * DK / 4 / NT;   // floatx4 loads of M per thread
+  constexpr int RW = 1;                  // row tiles per wave
   constexpr int KS = DK / 4;             // MFMA steps over k
   __shared__ __attribute__((aligned(16))) float mb[2][DK * LD];  // M_s, double-buffered
   __shared__ __attribute__((aligned(16))) float eb[DK * LE];     // E_s, this block's 16 columns
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t 
     const int64_t so = (int64_t)(s - 1) * P.seg.us + base;
     const floatx4* m4 = (const floatx4*)(P.seg.m + so);
 #pragma unroll
-    for (int f = 0; f < NM; ++f) mr[f] = m4[f * 256 + tid];
+    for (int f = 0; f < NM; ++f) mr[f] = m4[f * NT + tid];
 #pragma unroll
     for (int i = 0; i < RW; ++i)
 #pragma unroll
@@ -514,11 +515,11 @@ __global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t 
   auto stage = [&](int buf) {  // registers -> LDS rows
 #pragma unroll
     for (int f = 0; f < NM; ++f) {
-      const int e = 4 * (f * 256 + tid);
+      const int e = 4 * (f * NT + tid);
       *(floatx4*)&mb[buf][(e / DK) * LD + e % DK] = mr[f];
     }
   };
-  for (int i = tid; i < DK * 16; i += 256) eb[(i / 16) * LE + i % 16] = P.seg.mid[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16];
+  for (int i = tid; i < DK * 16; i += NT) eb[(i / 16) * LE + i % 16] = P.seg.mid[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16];
   load(1);
   stage(0);
 #pragma unroll
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t 
       // E_s as fragments: lane 16g + c of key block p holds column 16 cb + c
       // at key channels 32p + 8g + j
       H8* mf = (H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + ((int64_t)u * CT + cb) * (KB * 64);
-      for (int f = tid; f < KB * 64; f += 256) {
+      for (int f = tid; f < KB * 64; f += NT) {
         const int p = f / 64, l = f % 64, g = l >> 4, c = l & 15;
         H8 x;
 #pragma unroll
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(256) void seg_compose_kernel(ScanParams P, int32_t 
     __syncthreads();
   }
   if (P.ht) {
-    for (int i = tid; i < DK * 16; i += 256)
+    for (int i = tid; i < DK * 16; i += NT)
       P.ht[base + (int64_t)(i / 16) * DV + 16 * cb + i % 16] = eb[(i / 16) * LE + i % 16];
   }
 }
@@ -666,7 +667,7 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
 
 template <int DK, typename T>
 hipError_t launch_seg_compose(const ScanParams& P, int64_t n_units, hipStream_t st) {
-  hipLaunchKernelGGL((seg_compose_kernel<DK, T>), dim3((unsigned)(n_units * (DK / 16))), dim3(256), 0, st, P,
+  hipLaunchKernelGGL((seg_compose_kernel<DK, T>), dim3((unsigned)(n_units * (DK / 16))), dim3(DK * 4), 0, st, P,
                      (int32_t)n_units);
   return hipGetLastError();
 }
