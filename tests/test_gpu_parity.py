@@ -390,7 +390,38 @@ def test_workload_gdn_varlen(drla):
     _workload(drla, "gdn_varlen")
 
 
-def test_workload_gdn_long_sampled_heads(drla):
-    """65,536 tokens x 32 heads on the GPU; the oracle recomputes three heads
-    (first, middle, last) over the whole sequence."""
-    _workload(drla, "gdn_long", heads=[0, 17, 31])
+def test_workload_gdn_long(drla):
+    """65,536 tokens x 32 heads on the GPU, every head against the oracle
+    over the whole sequence.  The oracle runs sixteen heads per call to bound
+    host memory; the error metrics are taken over all 32 heads at once
+    (max|x - y| and max|y| accumulated across the batches)."""
+    name = "gdn_long"
+    spec = W.spec_by_name(name)
+    print(f"workload {name}: lens={spec.lens} h_qk={spec.h_qk} h_v={spec.h_v} "
+          f"d={spec.dk} io={spec.io} all heads, oracle 16 heads per call", flush=True)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o, ht = _np(o), _np(ht)
+    del d
+    acc = {"o": [0.0, 0.0, 0.0, 0.0], "ht": [0.0, 0.0, 0.0, 0.0]}  # max|x-y|, max|y|, sum d^2, sum y^2
+    for h0 in range(0, spec.h_v, 16):
+        heads = list(range(h0, min(h0 + 16, spec.h_v)))
+        o_ref, ht_ref = run_oracle(x, heads=heads)
+        for key, got, ref in (("o", o[:, heads], o_ref), ("ht", ht[:, heads], ht_ref)):
+            got = np.asarray(got, dtype=np.float64)
+            ref = np.asarray(ref, dtype=np.float64)
+            assert np.isfinite(got).all(), f"{name}: non-finite {key} in heads {heads}"
+            diff = got - ref
+            a = acc[key]
+            a[0] = max(a[0], float(np.abs(diff).max()))
+            a[1] = max(a[1], float(np.abs(ref).max()))
+            a[2] += float((diff * diff).sum())
+            a[3] += float((ref * ref).sum())
+        print(f"{name}: heads {heads[0]}..{heads[-1]} compared", flush=True)
+    tol = TOL[x["io"]]
+    for key, a in acc.items():
+        err = a[0] / a[1]
+        print(f"{name}: rel_err {key}={err:.3e} nmse {key}={a[2] / a[3]:.2e} (tol {tol:g}, 32 heads)",
+              flush=True)
+        assert err <= tol, f"{name}: {key} error {err}"
