@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     KEEP_INTERMEDIATES,
     DECAY_ONLY,
     SERIAL,
+    NOALLOC_SCRATCH_BYTES,
     DrlaError,
     decay_decode,
     decay_prefill,
@@ -19,10 +20,12 @@ from ._lib import (  # noqa: F401
     kda_prefill,
     lib_path,
     load_library,
+    prefill_noalloc,
     workspace_bytes,
     workspace_layout,
 )
 
 __all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "decay_prefill",
            "decay_decode", "DECAY_ONLY", "workspace_bytes", "workspace_layout",
-           "load_library", "lib_path", "DrlaError", "KEEP_INTERMEDIATES", "SERIAL"]
+           "load_library", "lib_path", "prefill_noalloc", "DrlaError", "KEEP_INTERMEDIATES", "SERIAL",
+           "NOALLOC_SCRATCH_BYTES"]

@@ -81,6 +81,9 @@ def load_library():
                                         vp, i32p, vp, vp, vp, ctypes.c_size_t, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
         lib.drla_prefill_ex.restype = ctypes.c_int
+        lib.drla_prefill_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp,
+                                             vp, i32p, vp, vp, vp]
+        lib.drla_prefill_noalloc.restype = ctypes.c_int
         lib.drla_workspace_bytes.argtypes = [pp, i32p]
         lib.drla_workspace_bytes.restype = ctypes.c_size_t
         lib.drla_workspace_layout.argtypes = [ctypes.c_int, pp, i32p, ctypes.c_int,
@@ -234,6 +237,42 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
     else:
         fn = lib.kda_prefill if kda else lib.gdn_prefill
         st = fn(*args)
+    if st != 0:
+        raise DrlaError(st, lib.drla_last_error().decode())
+    return o, ht
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DRLA_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_noalloc(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
+                    cu_seqlens_host=None, out=None, final_state=None, flags=0):
+    """drla_prefill_noalloc: the prefill without a workspace argument (the
+    library's own per-GPU scratch array serves instead).  Packed [T, H, d]
+    inputs; o and the final state are allocated here unless `out` and
+    `final_state` are given (the C call itself allocates nothing).  Returns
+    (o, final_state)."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, dk]")
+    cu_host = _host_cu(cu_seqlens, cu_seqlens_host)
+    n_seqs = 1 if cu_host is None else cu_host.numel() - 1
+    T, h_v, dk, dv = q.shape[0], v.shape[1], q.shape[2], v.shape[2]
+    for name, x in (("q", q), ("k", k), ("v", v), ("g", g)):
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    prob = _problem(q, v, n_seqs, T)
+    dev = q.device
+    o = out if out is not None else torch.empty((T, h_v, dv), dtype=q.dtype, device=dev)
+    ht = final_state if final_state is not None else \
+        torch.empty((n_seqs, h_v, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.drla_prefill_noalloc(
+        int(kda), int(flags), ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        None if beta is None else beta.data_ptr(), g.data_ptr(),
+        None if initial_state is None else initial_state.data_ptr(),
+        None if cu_seqlens is None else cu_seqlens.data_ptr(), _i32p(cu_host),
+        o.data_ptr(), ht.data_ptr(), stream)
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return o, ht

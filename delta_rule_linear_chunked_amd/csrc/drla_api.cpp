@@ -7,12 +7,20 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/drla.h"
 #include "drla_launch.h"
 
 static_assert(DRLA_CHUNK == DRLA_CHUNK_TOKENS, "chunk size mismatch");
+
+// Scratch memory of drla_prefill_noalloc: a fixed array in this library's
+// device code object, one copy per GPU, held until the process ends.  In
+// host code `scratch` is only a stand-in symbol; its device address comes
+// from hipGetSymbolAddress (scratch_address below) and only that address
+// is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DRLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -27,6 +35,29 @@ drla_status fail(drla_status s, const char* fmt, ...) {
   va_end(ap);
   g_last_error = buf;
   return s;
+}
+
+// Device address of `scratch` on the current device, resolved once per
+// device (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+drla_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DRLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DRLA_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DRLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DRLA_OK;
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -365,6 +396,29 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
                             void* const* stage_events) {
   return run(kda != 0, flags, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, workspace,
              workspace_bytes, stream, stage_events);
+}
+
+drla_status drla_prefill_noalloc(int kda, int flags, const drla_problem* p, const void* q, const void* k,
+                                 const void* v, const float* beta, const float* g, const float* h0,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, void* o,
+                                 float* ht, void* stream) {
+  // the workspace this call needs, checked against the scratch array before
+  // anything touches the device
+  drla_layout L;
+  const drla_status st = drla_workspace_layout(kda, p, cu_seqlens_host, flags, &L);
+  if (st != DRLA_OK) return st;
+  if (L.total > DRLA_NOALLOC_SCRATCH_BYTES)
+    return fail(DRLA_ERR_WORKSPACE,
+                "drla_prefill_noalloc: this call needs %zu bytes of scratch, more than the %llu bytes the "
+                "library holds; call gdn_prefill / kda_prefill with a workspace instead",
+                L.total, (unsigned long long)DRLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (L.total > 0) {
+    const drla_status sa = scratch_address(&ws);
+    if (sa != DRLA_OK) return sa;
+  }
+  return run(kda != 0, flags, p, q, k, v, beta, g, h0, cu_seqlens_dev, cu_seqlens_host, o, ht, ws,
+             ws ? (size_t)DRLA_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
 }
 
 const char* drla_status_str(drla_status s) {

@@ -252,6 +252,31 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p,
                                   const int32_t* cu_seqlens_host, int flags,
                                   drla_layout* out);
 
+/* Bytes of the library's own scratch array (per GPU) that
+ * drla_prefill_noalloc uses in place of a workspace: 64 MiB. */
+#define DRLA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* drla_prefill_ex without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The call allocates nothing: its
+ * kernels use a fixed scratch array of DRLA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its device
+ * address is looked up once per device, at the first call there).
+ *   kda, flags, p, q ... ht, stream   as drla_prefill_ex (no stage events)
+ * Errors as drla_prefill_ex; a call whose workspace (drla_workspace_layout
+ * for the same kda, problem, lengths and flags) exceeds the scratch array
+ * returns DRLA_ERR_WORKSPACE before touching the device.  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different host threads without ordering)
+ * race and give wrong results.  Calls ordered on one stream are safe; no
+ * call relies on what an earlier one left in the array. */
+drla_status drla_prefill_noalloc(int kda, int flags, const drla_problem* p,
+                                 const void* q, const void* k, const void* v,
+                                 const float* beta, const float* g,
+                                 const float* h0, const int32_t* cu_seqlens_dev,
+                                 const int32_t* cu_seqlens_host, void* o,
+                                 float* ht, void* stream);
+
 const char* drla_status_str(drla_status s);
 const char* drla_last_error(void);
 int drla_version(void);

@@ -241,3 +241,17 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens):
     us = n * h_v * d * d
     assert lay.seg > 0
     assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * 2 + T * h_v * d * 2
+
+
+def test_noalloc_rejects_oversize_before_the_device(lib):
+    """drla_prefill_noalloc refuses a call whose workspace exceeds its
+    scratch array (64 MiB) with DRLA_ERR_WORKSPACE, before any HIP call
+    (fake aligned addresses, never dereferenced)."""
+    b = 1 << 40
+    p = _prob(n_seqs=1, h_qk=16, h_v=16, T=32768)
+    args = [b + 0x1000000, b + 0x20000000, b + 0x40000000, b + 0x60000000, b + 0x70000000,
+            None, None, None, b + 0x80000000, None, None]
+    assert lib.drla_prefill_noalloc(0, 0, ctypes.byref(p), *args) == 6
+    assert "scratch" in lib.drla_last_error().decode()
+    # validation errors come first, as for the workspace call
+    assert lib.drla_prefill_noalloc(0, 0, ctypes.byref(_prob(dk=96)), *args) == 3
