@@ -38,12 +38,13 @@ class Problem(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("sched", "tb", "pm", "kt", "kw", "qw", "gam", "vp", "h",
-                                       "seg", "total")]
+                                       "seg", "hs", "total")]
 
 
 KEEP_INTERMEDIATES = 1
 DECAY_ONLY = 2
 SERIAL = 4
+HEAD_SCAN = 8
 
 
 def lib_path() -> str:

@@ -34,7 +34,8 @@ def hipcc() -> str:
 
 def sources():
     return [os.path.join(CSRC, f) for f in
-            ("drla_prep.hip", "drla_scan.hip", "drla_scan_lds.hip", "drla_decode.hip", "drla_launch.hip",
+            ("drla_prep.hip", "drla_scan.hip", "drla_scan_lds.hip", "drla_hscan.hip", "drla_decode.hip",
+             "drla_launch.hip",
              "drla_api.cpp")]
 
 

@@ -119,9 +119,26 @@ static int64_t max_chunks(const drla_problem* p, const int32_t* cu_host) {
   return m;
 }
 
-// Segments the workspace provides for (drla_seg_count at 256 compute
-// units, over the longest sequence); 1 for calls the split does not take.
-static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda) {
+constexpr int kKnownFlags = DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL | DRLA_HEAD_SCAN;
+
+// The head-resident scan (DRLA_HEAD_SCAN) serves scalar-gate calls with
+// 16-bit inputs (GDN, decay-only) that keep no intermediates.
+static bool uses_hs(const drla_problem* p, bool kda, int flags) {
+  return (flags & DRLA_HEAD_SCAN) && !kda && p->io_dtype != DRLA_F32 && !(flags & DRLA_KEEP_INTERMEDIATES);
+}
+
+// Segments per sequence the hs region provides for (drla_hs_count at 256
+// compute units; one pass when dk != dv or with DRLA_SERIAL).
+static int32_t hs_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
+  if (!uses_hs(p, kda, flags) || p->dk != p->dv || (flags & DRLA_SERIAL) || p->n_seqs < 1) return 1;
+  return drla_hs_count((int64_t)p->n_seqs * p->h_v, max_cps, 256);
+}
+
+// Segments the per-16-column scan's seg region provides for (drla_seg_count
+// at 256 compute units, over the longest sequence); 1 for calls the split
+// does not take.
+static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
+  if (uses_hs(p, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
   if (kda || p->io_dtype == DRLA_F32 || p->dk != p->dv || p->n_seqs < 1) return 1;
   return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
 }
@@ -157,12 +174,17 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, 
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
-  // Segment-split scan (dense scalar-gate calls with 16-bit inputs and
-  // dk = dv that leave most of a 256-CU chip idle): its states and G
-  const int32_t np = seg_count(p, max_cps, kda);
+  // Segment-split per-16-column scan (scalar-gate calls with 16-bit inputs
+  // and dk = dv that leave most of a 256-CU chip idle): its states and G
+  const int32_t np = seg_count(p, max_cps, kda, flags);
   L->seg = np > 1 ? off : 0;
   if (np > 1)
     off = align_up(off + drla_seg_offsets((int64_t)p->n_seqs * p->h_v, p->dk, p->total_tokens, p->h_v, np, es).total);
+  // Head-resident scan (DRLA_HEAD_SCAN) with segments: the segments' states
+  // and maps
+  const int32_t hnp = hs_count(p, max_cps, kda, flags);
+  L->hs = hnp > 1 ? off : 0;
+  if (hnp > 1) off = align_up(off + drla_hs_bytes((int64_t)p->n_seqs * p->h_v, p->dk, p->dv, hnp, es));
   L->total = off;
 }
 
@@ -179,8 +201,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
     return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
   drla_status st = check_problem(p, cu_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
-    return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~kKnownFlags) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   // one packed sequence (cu_seqlens = {0, T}, checked above) is a dense call
   if (cu_host && !packed(p, cu_host)) cu_dev = cu_host = nullptr;
   const bool decay = (flags & DRLA_DECAY_ONLY) != 0;
@@ -240,7 +261,9 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.off_vp = L.vp;
   a.off_h = L.h;
   a.off_seg = L.seg;
-  a.seg_np = L.seg ? seg_count(p, max_cps, kda) : 1;
+  a.seg_np = L.seg ? seg_count(p, max_cps, kda, flags) : 1;
+  a.off_hs = L.hs;
+  a.hs_np = L.hs ? hs_count(p, max_cps, kda, flags) : 1;
   a.max_cps = max_cps;
   a.total_tokens = T;
   a.n_chunks = nc;
@@ -255,6 +278,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.decay_only = decay ? 1 : 0;
   a.serial = (flags & DRLA_SERIAL) ? 1 : 0;
+  a.head_scan = uses_hs(p, kda, flags) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
@@ -366,8 +390,7 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
   drla_status st = check_problem(p, cu_seqlens_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~(DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL))
-    return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~kKnownFlags) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   const bool pk = packed(p, cu_seqlens_host);
   layout_of(p, nc, pk, max_chunks(p, pk ? cu_seqlens_host : nullptr), kda != 0, flags, out);
   return DRLA_OK;
@@ -438,6 +461,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 3; }
+int drla_version(void) { return 4; }
 
 }  // extern "C"

@@ -66,6 +66,33 @@ struct ScanParams {
   SegParams seg;       // LDS-fed scan only
 };
 
+// Head-resident scan (drla_hscan.hip): GDN and decay-only linear attention
+// with a scalar gate and 16-bit inputs.  One workgroup per (unit, segment),
+// all dv state columns; np segments per sequence (n / np chunks each, the
+// last takes the rest), stitched by the segments' affine state maps.
+struct HScanParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* h0;
+  void* o;
+  float* ht;
+  const void* tb;    // prep: diag(e^{b_n - b}) Tb, 8 fragments per (head, chunk)
+  const void* pm;    // prep: P Tb, 8 fragments per (head, chunk)
+  const float* gam;  // prep: e^{b_r} then e^{b_n - b_r}, 128 floats per (head, chunk)
+  float* en;         // np - 1 state sets (N_s, then E_{s+1}), tile order, fp32
+  void* phi;         // np - 2 segment maps Phi_1 .. Phi_{np-2}, A fragments, io type
+  Sched s;
+  int32_t h_qk, h_v, grp;
+  int64_t nc;
+  int32_t np;     // segments per sequence (1: one pass)
+  int32_t units;  // (sequence, head) units; indexed by rank (longest first when packed)
+  int32_t decay_only;
+};
+
+template <int DK, int DV, typename T>
+hipError_t launch_hscan(const HScanParams& P, hipStream_t st);
+
 // One decode step: every input row is one sequence's token.
 struct DecodeParams {
   const void* q;   // [N, h_qk, dk]

@@ -19,6 +19,31 @@ static inline int32_t drla_seg_count(int64_t K, int64_t cps, int64_t cus) {
   return np;
 }
 
+// Segments per sequence of the head-resident scan: as many as give every
+// (sequence, head) unit's segments one compute unit each (units x np <=
+// cus), at most about sqrt(9 n) for n chunks of the longest sequence (the
+// serial compose step grows with np while the segment scans shrink with
+// n / np), at least two chunks per segment, at most 128.  Fewer than three
+// segments gain nothing over one pass: 1.
+static inline int32_t drla_hs_count(int64_t units, int64_t max_cps, int64_t cus) {
+  if (units <= 0 || max_cps <= 0) return 1;
+  int64_t np = cus / units;
+  int64_t cap = 1;
+  while ((cap + 1) * (cap + 1) <= 9 * max_cps) ++cap;
+  if (np > cap) np = cap;
+  if (np > max_cps / 2) np = max_cps / 2;
+  if (np > 128) np = 128;
+  return np < 3 ? 1 : (int32_t)np;
+}
+
+// Bytes of the head-resident scan's region for `units` units, np segments,
+// dk x dv states and io elements of `es` bytes: np - 1 fp32 state sets, then
+// np - 2 segment maps (dk x dk, io type).
+static inline size_t drla_hs_bytes(int64_t units, int64_t dk, int64_t dv, int32_t np, size_t es) {
+  if (np <= 1) return 0;
+  return (size_t)(np - 1) * units * dk * dv * 4 + (size_t)(np > 2 ? np - 2 : 0) * units * dk * dk * es;
+}
+
 // Layout of the seg region (byte offsets from its start) for `units`
 // (sequence, head) pairs of a d x d state, T tokens in all, h_v heads, np
 // segments and io elements of `es` bytes: the state after segment 0, then
@@ -54,6 +79,8 @@ typedef struct {
   // byte offsets into the workspace; vp/h only used when inspect != 0
   size_t off_sched, off_tb, off_pm, off_kt, off_kw, off_qw, off_gam, off_vp, off_h;
   size_t off_seg;  // 0, or the segment-mode scan's states and G (dense calls)
+  size_t off_hs;   // 0, or the head-resident scan's segment states and maps
+  int32_t hs_np;   // segments the hs region holds (drla_hs_count at 256 CUs)
   int32_t seg_np;  // segments the seg region holds (drla_seg_count at 256 CUs)
   int64_t max_cps; // chunks of the longest sequence
   int64_t total_tokens;
@@ -62,6 +89,7 @@ typedef struct {
   int32_t kda, f32, f16, inspect;  // f32 / f16: io dtype (neither: bf16)
   int32_t decay_only;              // decay-only linear attention (no delta rule)
   int32_t serial;                  // scan every sequence in one pass (no segment split)
+  int32_t head_scan;               // GDN 16-bit: the head-resident scan (DRLA_HEAD_SCAN)
   void* stream;
   void* const* stage_events;  // NULL, or 3 hipEvent_t recorded at kernel boundaries
 } drla_launch_args;

@@ -80,6 +80,44 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     e = launch_schedule(a->cu_dev, a->n_seqs, nc, (int32_t*)(ws + a->off_sched), st);
   if (e == hipSuccess) e = launch_prep<DK, KDA, ET>(pp, nc * a->h_v, st);
   mark(1);
+  // Head-resident scan (DRLA_HEAD_SCAN; scalar gate, 16-bit inputs): one
+  // workgroup per (sequence, head) unit and segment
+  if constexpr (kLdsScan) {
+    if (a->head_scan && !a->inspect) {
+      HScanParams hp = {};
+      hp.q = a->q;
+      hp.k = a->k;
+      hp.v = a->v;
+      hp.h0 = a->h0;
+      hp.o = a->o;
+      hp.ht = a->ht;
+      hp.tb = pp.tb;
+      hp.pm = pp.pm;
+      hp.gam = pp.gam;
+      hp.s = s;
+      hp.h_qk = a->h_qk;
+      hp.h_v = a->h_v;
+      hp.grp = grp;
+      hp.nc = nc;
+      hp.units = (int32_t)((int64_t)a->n_seqs * a->h_v);
+      hp.decay_only = a->decay_only;
+      int32_t np = 1;
+      if (a->off_hs && DK == DV && !a->serial) {
+        const int cus = device_cus();
+        np = cus > 0 ? drla_hs_count(hp.units, a->max_cps, cus) : 1;
+        if (np > a->hs_np) np = a->hs_np;  // what the workspace holds
+      }
+      hp.np = np;
+      if (np > 1) {
+        char* hs = ws + a->off_hs;
+        hp.en = (float*)hs;
+        hp.phi = hs + (size_t)(a->hs_np - 1) * hp.units * DK * DV * 4;
+      }
+      if (e == hipSuccess) e = launch_hscan<DK, DV, ET>(hp, st);
+      mark(2);
+      return e;
+    }
+  }
   // packed input: the scan deals (sequence, head) units in groups of eight
   // (scan_item); the grid covers whole groups
   const int64_t units = (int64_t)a->n_seqs * a->h_v;

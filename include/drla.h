@@ -20,10 +20,12 @@
  * evaluated chunkwise (64 tokens) in the Map-Reduce-Map form of Section 2.1:
  * a chunk-parallel prep kernel (operators #1-#3 Gate, KKT, Solve, and the
  * factor T diag(beta) that operator #4 W/U is built from, kept unexpanded
- * as in Section 5's operator rewriting) and one kernel that runs the
- * sequential state scan (#5 H) and the output (#6 O) chunk by chunk, state
- * first-read, then output, then in-place update (Section 5, "cross-chunk
- * reordering").  Results equal the recurrence up to rounding.
+ * as in Section 5's operator rewriting), then the state scan (#5 H) fused
+ * with the output (#6 O) chunk by chunk, state first-read, then output,
+ * then in-place update (Section 5, "cross-chunk reordering").  Sequences
+ * can be scanned as segments at once, stitched by the segments' affine
+ * state maps (Section 4, Chunk-Seg-Seg mapping).  Results equal the
+ * recurrence up to rounding.
  *
  * Layouts (row-major, token-major, sequences packed back to back):
  *   q, k        [T, h_qk, dk]    io dtype
@@ -180,18 +182,33 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
 #define DRLA_KEEP_INTERMEDIATES 1 /* also write V' and the per-chunk state (tests) */
 #define DRLA_DECAY_ONLY 2         /* decay-only linear attention (decay_prefill); beta unused */
 #define DRLA_SERIAL 4             /* scan every sequence in one pass (no segment split) */
+#define DRLA_HEAD_SCAN 8          /* scalar gate, 16-bit io: the head-resident scan */
 
 /* gdn_prefill (kda == 0) or kda_prefill (kda != 0) with options.
- *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY
- *                 and DRLA_SERIAL, or 0.  DRLA_SERIAL turns off the
- *                 segment-parallel scan (same results up to rounding),
- *                 which scalar-gate calls with 16-bit inputs and dk == dv
- *                 take when U = n_seqs * h_v * dv/16 is small: each
- *                 sequence's chunks are split into np segments (n / np
- *                 chunks each, the last takes the rest), np the most up to
- *                 16 for which (2 np - 1) U is at most the device's compute
- *                 units (and at most 256) and the longest sequence has at
- *                 least 4 np chunks, and the segments are scanned at once.
+ *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY,
+ *                 DRLA_SERIAL and DRLA_HEAD_SCAN, or 0.
+ *                 The state scan runs one workgroup per (sequence, head,
+ *                 16 state columns).  Scalar-gate calls with 16-bit inputs
+ *                 and dk == dv whose U = n_seqs * h_v * dv/16 column blocks
+ *                 leave most of the device idle split every sequence's
+ *                 chunks into np segments (n / np chunks each, the last
+ *                 takes the rest) that are scanned at once: np the most up
+ *                 to 16 for which (2 np - 1) U is at most the device's
+ *                 compute units (and at most 256) and the longest sequence
+ *                 has at least 4 np chunks.
+ *                 DRLA_HEAD_SCAN (scalar gate, 16-bit inputs, not with
+ *                 DRLA_KEEP_INTERMEDIATES) runs the head-resident scan
+ *                 instead: one workgroup per (sequence, head) unit holds all
+ *                 dv state columns; when the units leave compute units idle
+ *                 and dk == dv, each sequence's n chunks are split into np
+ *                 segments scanned at once and stitched by their affine
+ *                 state maps (Section 4, Chunk-Seg-Seg mapping): np the most
+ *                 with n_seqs h_v np at most the compute units (at most
+ *                 256), np^2 <= 9 n_max, at least two chunks per segment of
+ *                 the longest sequence (n_max chunks) and np <= 128; fewer
+ *                 than three segments run one pass.
+ *                 DRLA_SERIAL runs either scan in one pass (same results up
+ *                 to rounding).
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels
@@ -236,17 +253,23 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
- *   seg (scalar-gate calls with 16-bit inputs and dk == dv that the
- *        segment split takes on a 256-CU device, else 0): for np segments,
- *        the fp32 state after the first segment, np - 1 zero-start final
- *        states and np - 1 maps of the entering state (fp32, per (sequence,
- *        head)), np - 1 entering states as io-type fragments, then the
- *        maps' contribution to o per token, laid out as o
- * Elements are io dtype except gam and the seg states (fp32).  n_chunks is the total chunk
- * count over all sequences.  Returns DRLA_OK or a validation error. */
+ *   seg (calls with a scalar gate, 16-bit inputs and dk == dv that the
+ *        segment split takes on a 256-CU device, else 0):
+ *        for np segments, the fp32 state after the first segment, np - 1
+ *        zero-start final states and np - 1 maps of the entering state
+ *        (fp32, per (sequence, head)), np - 1 entering states as io-type
+ *        fragments, then the maps' contribution to o per token, laid out as o
+ *   hs (DRLA_HEAD_SCAN calls that split into np > 1 segments on a 256-CU
+ *        device, else 0): np - 1 fp32 state sets of dk x dv per (sequence, head) unit
+ *        (the segments' zero-start final states, replaced in place by the
+ *        states entering segments 1 .. np - 1), then np - 2 segment maps of
+ *        dk x dk per unit in io type
+ * Elements are io dtype except gam and the seg and hs states (fp32).
+ * n_chunks is the total chunk count over all sequences.  Returns DRLA_OK or
+ * a validation error. */
 typedef struct {
   int64_t n_chunks;
-  size_t sched, tb, pm, kt, kw, qw, gam, vp, h, seg, total;
+  size_t sched, tb, pm, kt, kw, qw, gam, vp, h, seg, hs, total;
 } drla_layout;
 drla_status drla_workspace_layout(int kda, const drla_problem* p,
                                   const int32_t* cu_seqlens_host, int flags,

@@ -1,20 +1,23 @@
-"""The segment-split scan of dense calls that leave most of the chip idle.
+"""The segment split of calls that leave most of the chip idle, in both
+scans that have one.
 
-Such a call splits every sequence's chunks into np segments (np = 2 when
-three scan workgroups per column block fill a third of the chip, up to 16
-for a single head).  Segment 0 is scanned from the initial state; every
-later one twice at the same time: from a zero state with the real values,
-and from the identity with V = 0 (the linear map of the entering state on
-the outputs and on the final state).  A compose kernel chains the entering
-states and a fix-up adds each segment's map applied to its entering state.
-The cases take 2, 3, 4, 6, 8 and 11 segments, an uneven last segment,
-workgroup counts that are not a multiple of 8, ragged last chunks, grouped
-heads, dk = 64 and 128, a dense batch, no initial state, no final state, the
-fewest chunks a split takes, and the decay-only form; each is checked
-against the oracle, and against the one-pass scan of the same call
-(DRLA_SERIAL), which must differ in rounding somewhere (else the split did
-not run).  A call too wide for the split equals the one-pass scan bit for
-bit."""
+Per-16-column scan (the default): segment 0 from the initial state, every
+later one from zero and from the identity, then a compose and an output
+fix-up.  Head-resident scan (DRLA_HEAD_SCAN): every sequence's chunks are
+split into np segments; a transition kernel computes each segment's affine
+state map (Phi, N) at once, a compose kernel chains the states entering the
+segments, and the value kernel rescans every segment from its entering
+state with the outputs.
+
+Whether a call splits follows each scan's rule (the workspace layout
+reports the split's region).  The cases take 2 to 16 segments, uneven last
+segments, ragged last chunks, grouped heads, dk = 64 and 128, a dense batch,
+no initial state, no final state, short and empty packed sequences and the
+decay-only form; each is checked against the oracle and against the
+one-pass scan of the same call (DRLA_SERIAL).  The split call runs on a
+workspace filled with NaN bytes: when the rule splits it, the split's first
+state set must have been written (and nothing the call reads may be a
+leftover NaN); when it does not, the result equals one pass bit for bit."""
 import numpy as np
 import pytest
 
@@ -34,15 +37,45 @@ def drla():
     return m
 
 
-def _call(drla, kind, d, dense_batch, flags, want_ht):
+PATHS = ["head", "column"]
+
+
+def _base(drla, path):
+    return drla.HEAD_SCAN if path == "head" else 0
+
+
+def _splits(drla, x, path, kind, n_seqs=1, cu_host=None):
+    """(does the call split, workspace bytes, byte range of the split's first
+    state set): the layout holds the split's region when it splits."""
+    io = {"bf16": torch.bfloat16, "f16": torch.float16}[x["io"]]
+    lay = drla.workspace_layout(x["q"].shape, x["v"].shape, io, n_seqs=n_seqs,
+                                cu_seqlens_host=cu_host, kda=False,
+                                flags=_base(drla, path) | (drla.DECAY_ONLY if kind == "ret" else 0))
+    off = lay["hs" if path == "head" else "seg"]
+    units = n_seqs * x["h_v"]
+    return off != 0, lay["total"], (off, off + units * x["dk"] * x["dv"] * 4)
+
+
+def _nan_workspace(nbytes):
+    """A workspace whose every float reads NaN (bytes 0xFF)."""
+    return torch.full((max(nbytes, 1),), 255, dtype=torch.uint8, device="cuda")
+
+
+def _written(ws, rng):
+    """The split wrote the first state set of its region: every float finite."""
+    a, b = rng
+    return bool(torch.isfinite(ws[a:b].view(torch.float32)).all())
+
+
+def _call(drla, kind, d, dense_batch, flags, want_ht, ws=None):
     q, k, v, beta, g, h0 = d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"]
     if dense_batch > 1:
         q, k, v = (x.view(dense_batch, -1, *x.shape[1:]) for x in (q, k, v))
         beta, g = (x.view(dense_batch, -1, *x.shape[1:]) for x in (beta, g))
     if kind == "ret":
         return drla.decay_prefill(q, k, v, g, h0, per_channel=False, flags=flags,
-                                  output_final_state=want_ht)
-    return drla.gdn_prefill(q, k, v, beta, g, h0, flags=flags, output_final_state=want_ht)
+                                  output_final_state=want_ht, workspace=ws)
+    return drla.gdn_prefill(q, k, v, beta, g, h0, flags=flags, output_final_state=want_ht, workspace=ws)
 
 
 # (kind, io, h_qk, h_v, d, lens, h0_std, want_ht)
@@ -60,27 +93,34 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-h{c[3]}-d{c[4]}-{c[5]}" for c in CASES])
-def test_segment_split_matches_oracle_and_one_pass(drla, case):
+def test_segment_split_matches_oracle_and_one_pass(drla, case, path):
     kind, io, h_qk, h_v, dk, lens, h0_std, want_ht = case
-    print(f"case segment kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} lens={lens} "
-          f"h0_std={h0_std} ht={want_ht}", flush=True)
     spec = W.small_spec(kind, lens=lens, h_qk=h_qk, h_v=h_v, dk=dk, dv=dk, io=io,
                         g_lo=0.01, g_hi=0.2, h0_std=h0_std, seed=41)
     x = W.make_inputs(spec)
+    nb = len(lens)  # a dense batch of nb equal sequences (no cu_seqlens)
+    splits, wsb, rng = _splits(drla, x, path, kind, n_seqs=nb)
+    print(f"case segment path={path} kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} lens={lens} "
+          f"h0_std={h0_std} ht={want_ht} splits={splits}", flush=True)
     d = to_device(x)
-    nb = len(lens)
-    o, ht = _call(drla, kind, d, nb, 0, want_ht)
-    o1, ht1 = _call(drla, kind, d, nb, drla.SERIAL, want_ht)
+    base = _base(drla, path)
+    ws = _nan_workspace(wsb)
+    o, ht = _call(drla, kind, d, nb, base, want_ht, ws)
+    o1, ht1 = _call(drla, kind, d, nb, base | drla.SERIAL, want_ht)
     torch.cuda.synchronize()
     o, o1 = (t.reshape(-1, h_v, dk).float().cpu().numpy() for t in (o, o1))
     o_ref, ht_ref = run_oracle(x)
     tol = TOL[io]
     eo, eo1 = rel_err(o, o_ref), rel_err(o1, o_ref)
     print(f"  rel_err o split={eo:.3e} one-pass={eo1:.3e} (tol {tol:g})", flush=True)
-    assert np.isfinite(o).all() and eo <= tol
+    assert np.isfinite(o).all() and eo <= tol and eo1 <= tol
     assert rel_err(o, o1) <= tol
-    assert not np.array_equal(o, o1), "the split scan did not run"
+    if splits:
+        assert _written(ws, rng), "the split scan did not run"
+    else:
+        assert np.array_equal(o, o1), "a call the rule does not split differs from one pass"
     if want_ht:
         ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
         eh = rel_err(ht, ht_ref)
@@ -90,22 +130,25 @@ def test_segment_split_matches_oracle_and_one_pass(drla, case):
         assert ht is None and ht1 is None
 
 
-def test_segment_split_repeatable(drla):
+@pytest.mark.parametrize("path", PATHS)
+def test_segment_split_repeatable(drla, path):
     """Two calls of the split scan on the same inputs agree bit for bit (no
     workgroup reads what another of the same call is still writing)."""
-    print("case segment repeatable", flush=True)
+    print(f"case segment repeatable path={path}", flush=True)
     spec = W.small_spec("gdn", lens=(4000,), h_qk=2, h_v=2, dk=128, dv=128, io="bf16",
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=42)
     d = to_device(W.make_inputs(spec))
-    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
-    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
+    f = _base(drla, path)
+    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=f)
+    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=f)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 def test_wide_call_runs_one_pass(drla):
-    """16 heads of d = 128 need 384 split workgroups, more than a 256-CU chip
-    holds at once: the call takes the one-pass scan."""
+    """Per-16-column scan: 16 heads of d = 128 need 384 split workgroups, more
+    than a 256-CU chip holds at once: the call takes the one-pass scan.  (The
+    head-resident scan splits this call: 16 units x 8 segments.)"""
     print("case segment wide call", flush=True)
     spec = W.small_spec("gdn", lens=(1000,), h_qk=4, h_v=16, dk=128, dv=128, io="bf16",
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=43)
@@ -116,17 +159,20 @@ def test_wide_call_runs_one_pass(drla):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_one_packed_sequence_is_dense(drla):
+@pytest.mark.parametrize("path", PATHS)
+def test_one_packed_sequence_is_dense(drla, path):
     """One sequence passed with cu_seqlens = {0, T} takes the dense path, the
     segment split included: the same bits as the call without cu_seqlens."""
-    print("case segment one packed sequence", flush=True)
+    print(f"case segment one packed sequence path={path}", flush=True)
     spec = W.small_spec("gdn", lens=(3000,), h_qk=2, h_v=2, dk=128, dv=128, io="bf16",
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=44)
     d = to_device(W.make_inputs(spec))
     cu = torch.tensor([0, 3000], dtype=torch.int32, device="cuda")
-    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
-    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], cu, cu_seqlens_host=[0, 3000])
-    c = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    f = _base(drla, path)
+    a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=f)
+    b = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], cu, cu_seqlens_host=[0, 3000],
+                         flags=f)
+    c = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=f | drla.SERIAL)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert not torch.equal(a[0], c[0]), "the split scan did not run"
@@ -140,25 +186,32 @@ PACKED = [
 ]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", PACKED, ids=[f"{c[0]}-{c[1]}-h{c[3]}-d{c[4]}-{c[5]}" for c in PACKED])
-def test_segment_split_packed(drla, case):
+def test_segment_split_packed(drla, case, path):
     """Packed input: each sequence splits its own chunks into the call's np
     segments; against the oracle and the one-pass scan."""
     kind, io, h_qk, h_v, dk, lens = case
-    print(f"case segment packed kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} lens={lens}", flush=True)
     spec = W.small_spec(kind, lens=lens, h_qk=h_qk, h_v=h_v, dk=dk, dv=dk, io=io,
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=45)
     x = W.make_inputs(spec)
+    cu_host = [int(c) for c in x["cu_seqlens"]]
+    splits, wsb, rng = _splits(drla, x, path, kind, n_seqs=len(lens), cu_host=cu_host)
+    print(f"case segment packed path={path} kind={kind} io={io} h_qk={h_qk} h_v={h_v} d={dk} "
+          f"lens={lens} splits={splits}", flush=True)
     d = to_device(x)
+    base = _base(drla, path)
+    ws = _nan_workspace(wsb)
 
-    def call(flags):
+    def call(flags, ws=None):
         if kind == "ret":
             return drla.decay_prefill(d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu"],
-                                      cu_seqlens_host=d["cu_host"], per_channel=False, flags=flags)
+                                      cu_seqlens_host=d["cu_host"], per_channel=False, flags=flags,
+                                      workspace=ws)
         return drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
-                                cu_seqlens_host=d["cu_host"], flags=flags)
-    o, ht = call(0)
-    o1, ht1 = call(drla.SERIAL)
+                                cu_seqlens_host=d["cu_host"], flags=flags, workspace=ws)
+    o, ht = call(base, ws)
+    o1, ht1 = call(base | drla.SERIAL)
     torch.cuda.synchronize()
     o, o1 = o.float().cpu().numpy(), o1.float().cpu().numpy()
     ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
@@ -169,4 +222,7 @@ def test_segment_split_packed(drla, case):
     assert np.isfinite(o).all() and np.isfinite(ht).all()
     assert eo <= tol and eh <= tol
     assert rel_err(o, o1) <= tol and rel_err(ht, ht1) <= tol
-    assert not np.array_equal(o, o1), "the split scan did not run"
+    if splits:
+        assert _written(ws, rng), "the split scan did not run"
+    else:
+        assert np.array_equal(o, o1)

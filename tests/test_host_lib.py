@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
             "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 3
+    assert lib.drla_version() == 4
 
 
 def _prob(n_seqs=1, h_qk=2, h_v=4, dk=128, dv=128, io=0, T=256):
@@ -156,16 +156,21 @@ def test_workspace_bytes_and_layout(lib):
     gl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
     assert gl.kt == 0 and gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kt
-    assert gl.seg == 0                  # 16 heads x 8 column blocks x 3 > 256
+    assert gl.seg == 0 and gl.hs == 0   # 16 heads x 8 column blocks x 3 > 256
     assert gl.total - gl.gam == per * 128 * 4
     assert n == max(lay.total, gl.total)
-    # the segment-split scan (8 heads x 8 column blocks x 3 <= 256 CUs):
-    # three fp32 states per head, the first as bf16 fragments, and G laid
-    # out like o
+    # with DRLA_HEAD_SCAN (8): the head-resident scan splits 16 units into 16
+    # segments of 4 chunks: 15 fp32 state sets and 14 bf16 segment maps per unit
+    hl = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 8, ctypes.byref(hl)) == 0
+    assert hl.seg == 0 and hl.hs == hl.gam + per * 128 * 4
+    assert hl.total - hl.hs == 15 * 16 * 128 * 128 * 4 + 14 * 16 * 128 * 128 * 2
+    # its segment split (8 heads x 8 column blocks x 3 <= 256 CUs): three
+    # fp32 states per head, the first as bf16 fragments, and G laid out like o
     p8 = _prob(n_seqs=1, h_qk=8, h_v=8, dk=128, dv=128, io=0, T=4096)
     sl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(sl)) == 0
-    assert sl.seg - sl.gam == 64 * 8 * 128 * 4
+    assert sl.seg - sl.gam == 64 * 8 * 128 * 4 and sl.hs == 0
     assert sl.total - sl.seg == 3 * 8 * 128 * 128 * 4 + 8 * 128 * 128 * 2 + 4096 * 8 * 128 * 2
     # 2 heads: 8 segments of 15 x 16 workgroups; seven N, M and fragment sets
     p2h = _prob(n_seqs=1, h_qk=2, h_v=2, dk=128, dv=128, io=0, T=65536)
@@ -174,10 +179,12 @@ def test_workspace_bytes_and_layout(lib):
     assert sl.total - sl.seg == us * 4 + 7 * 2 * us * 4 + 7 * us * 2 + 65536 * 2 * 128 * 2
     # one sequence passed with cu_seqlens {0, T} is laid out as the dense call
     cu1, _c1 = _i32([0, 4096])
-    dl, pl = Layout(), Layout()
-    assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(dl)) == 0
-    assert lib.drla_workspace_layout(0, ctypes.byref(p8), cu1, 0, ctypes.byref(pl)) == 0
-    assert (pl.tb, pl.seg, pl.total) == (dl.tb, dl.seg, dl.total) and pl.seg > 0
+    for flags in (0, 8):
+        dl, pl = Layout(), Layout()
+        assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, flags, ctypes.byref(dl)) == 0
+        assert lib.drla_workspace_layout(0, ctypes.byref(p8), cu1, flags, ctypes.byref(pl)) == 0
+        assert (pl.tb, pl.seg, pl.hs, pl.total) == (dl.tb, dl.seg, dl.hs, dl.total)
+        assert (pl.hs if flags else pl.seg) > 0
     assert lib.drla_workspace_bytes(ctypes.byref(p8), cu1) == lib.drla_workspace_bytes(ctypes.byref(p8), None)
     # fp32 inputs keep K~^T for the register-fed scan
     pf = _prob(n_seqs=1, h_qk=16, h_v=16, dk=128, dv=128, io=1, T=4096)
@@ -189,8 +196,10 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
     assert kl.vp == gl.total and kl.h - kl.vp == per * 64 * 128 * 2
     assert kl.total - kl.h == per * 128 * 128 * 2
+    assert kl.hs == 0 and kl.seg == 0   # intermediates: the per-16-column scan, one pass
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 0
-    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 8, ctypes.byref(kl)) == 3
+    assert kl.hs == 0 and kl.seg == 0   # DRLA_SERIAL: one pass
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 16, ctypes.byref(kl)) == 3
     # 11 heads of 8 column blocks: 264 scan workgroups, no segment region
     p11 = _prob(n_seqs=1, h_qk=11, h_v=11, dk=128, dv=128, io=0, T=4096)
     assert lib.drla_workspace_layout(0, ctypes.byref(p11), None, 0, ctypes.byref(kl)) == 0
@@ -201,7 +210,7 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p2), cu, 0, ctypes.byref(lay2)) == 0
     assert lay2.n_chunks == 1 + 1 + 0 + 3
     assert lay2.tb >= (2 * 5 + 4 + 1) * 4      # chunk table first
-    assert lay2.seg == 0                        # packed input: no segment split
+    assert lay2.seg == 0 and lay2.hs == 0     # 3 chunks at most: one pass
     assert lib.drla_workspace_bytes(ctypes.byref(_prob(dk=80)), None) == 0
 
 
@@ -220,11 +229,15 @@ def _seg_np(units_cb, max_cps, cus=256):
     return np_
 
 
-@pytest.mark.parametrize("h_v,d,lens", [
+SEG_SHAPES = [
     (1, 128, (3000,)), (2, 128, (65536,)), (4, 64, (8192,)), (8, 128, (4096,)),
     (11, 128, (4096,)), (1, 64, (1500,)), (2, 128, (1500, 700, 0, 2100)), (1, 128, (3000, 100, 0)),
-    (4, 128, (200,)), (16, 64, (2000,)),
-])
+    (4, 128, (200,)), (16, 64, (2000,)), (16, 128, (4096,)), (32, 128, (65536,)),
+    (32, 128, (6745, 1169, 1890, 2330, 1905, 6666, 7188, 4983)),
+]
+
+
+@pytest.mark.parametrize("h_v,d,lens", SEG_SHAPES)
 def test_segment_region_follows_the_count_rule(lib, h_v, d, lens):
     """The seg region holds mid, np - 1 sets of N and M (fp32), np - 1
     entering states in bf16, and G [T, h_v, d] in bf16."""
@@ -241,6 +254,43 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens):
     us = n * h_v * d * d
     assert lay.seg > 0
     assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * 2 + T * h_v * d * 2
+
+
+def _hs_np(units, max_cps, cus=256):
+    """The head-resident scan's segment count as the header states it: the
+    most np with units x np <= cus, np^2 <= 9 n_max, at least two chunks per
+    segment of the longest sequence and np <= 128; fewer than three: one
+    pass."""
+    np_ = min(cus // units, int((9 * max_cps) ** 0.5), max_cps // 2, 128)
+    while (np_ + 1) ** 2 <= 9 * max_cps and np_ + 1 <= min(cus // units, max_cps // 2, 128):
+        np_ += 1
+    while np_ * np_ > 9 * max_cps:
+        np_ -= 1
+    return np_ if np_ >= 3 else 1
+
+
+@pytest.mark.parametrize("h_v,d,lens", SEG_SHAPES)
+def test_head_scan_region_follows_the_count_rule(lib, h_v, d, lens):
+    """DRLA_HEAD_SCAN: the hs region holds np - 1 fp32 state sets and np - 2
+    segment maps (dk x dk, bf16) per (sequence, head) unit."""
+    from delta_rule_linear_chunked_amd._lib import Layout
+    n, T = len(lens), sum(lens)
+    p = _prob(n_seqs=n, h_qk=1, h_v=h_v, dk=d, dv=d, io=0, T=T)
+    cu, _c = _i32([0] + [sum(lens[:i + 1]) for i in range(n)])
+    lay = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), cu if n > 1 else None, 8, ctypes.byref(lay)) == 0
+    units = n * h_v
+    np_ = _hs_np(units, max((L + 63) // 64 for L in lens))
+    assert lay.seg == 0
+    if np_ == 1:
+        assert lay.hs == 0
+        return
+    assert lay.hs > 0
+    assert lay.total - lay.hs == (np_ - 1) * units * d * d * 4 + (np_ - 2) * units * d * d * 2
+    # dk != dv: one pass
+    pq = _prob(n_seqs=n, h_qk=1, h_v=h_v, dk=d, dv=192 - d, io=0, T=T)
+    assert lib.drla_workspace_layout(0, ctypes.byref(pq), cu if n > 1 else None, 8, ctypes.byref(lay)) == 0
+    assert lay.hs == 0
 
 
 def test_noalloc_rejects_oversize_before_the_device(lib):
