@@ -107,15 +107,25 @@ __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e
 // KDA: every thread owns eight adjacent key channels and a run of GR rows of
 // the chunk; it forms the cumulative gate B of its rows in registers (the
 // runs' offsets come from one exclusive scan over the runs per channel) and
-// scales its elements of K and Q once, 16 bytes at a time -- K e^{B - B_m},
-// K e^{B_m - B}, Q e^{B - B_m}, with the reference B_m = B of row C/2 - 1
-// keeping the exponents small -- so the products and the chunk operands
-// only multiply by per-channel constants (e^{B_m}, e^{B_n - B_m}).
+// writes B log2(e) to a table in LDS beside the raw K and Q rows.  The
+// products A and P weigh every key channel by e^{B_r - B_i} (r >= i, so the
+// exponent is never positive); each operand fragment is scaled as it is
+// loaded, about a reference row chosen per 16-row tile so that no factor
+// can overflow:
+//   off-diagonal tiles (row tile I > column tile J): the first row of row
+//     tile I, m = 16 I; X_r e^{B_r - B_m} and K_i e^{B_m - B_i} are both
+//     at most |X_r|, |K_i| (any gate), and go to the 16-bit products;
+//   diagonal tiles: the tile's row 16 I + 8; the factors lie within
+//     e^{+-8 max|g|} and go to fp32 products (16x16x4 fp32 MFMA), so the
+//     gate need only satisfy 8 |g| < 88 per token and channel.
+// The scan's operands K e^{B}, Q e^{B}, (K e^{B_n - B})^T and e^{B_n}
+// take non-positive exponents only.
 //
-// LDS is reused across phases: K (and KDA's scaled tiles) live until the
-// chunk operands are written, T from the solve on, in the same bytes.
+// LDS is reused across phases: K (and KDA's Q rows and B table) live until
+// the chunk operands are written, T from the solve on, in the same bytes;
+// KDA's A and the runs' totals take the bytes of the B table.
 template <int DK, bool KDA, typename ET, bool KT, bool PF>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits) {
+__global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(PrepParams P, int64_t nunits) {
   typedef typename VT<ET>::v8 V8;
   typedef typename VT<ET>::v16b V16;
   constexpr int PE = VT<ET>::per16;
@@ -130,18 +140,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
   constexpr int TS_BYTES = C * TP * 4;
-  constexpr int NT = KDA ? 3 : 1;                // K-sized tiles: KDA K e^{B-B_m}, K e^{B_m-B}, Q e^{B-B_m}
-  constexpr int U_BYTES = NT * KS_BYTES > TS_BYTES ? NT * KS_BYTES : TS_BYTES;
+  constexpr int NT = KDA ? 2 : 1;                // K-sized tiles: K rows, and KDA's Q rows
+  constexpr int BP = DK + 4;                     // KDA: padded row of the B table (floats)
+  constexpr int BL_BYTES = KDA ? C * BP * 4 : 0;
+  static_assert(!KDA || (BL_BYTES >= C * TP * 4 && BL_BYTES >= 256 / (DK / 8) * DK * 4),
+                "KDA: A and the runs' totals fit in the bytes of the B table");
+  constexpr int U_BYTES = NT * KS_BYTES + BL_BYTES > TS_BYTES ? NT * KS_BYTES + BL_BYTES : TS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
-  __shared__ __attribute__((aligned(16))) float As[C][TP];  // A
+  __shared__ __attribute__((aligned(16))) float As_st[KDA ? 1 : C][TP];  // A (GDN)
   __shared__ __attribute__((aligned(16))) float bs[C];
   __shared__ __attribute__((aligned(16))) float betas[C];
-  __shared__ __attribute__((aligned(16))) float bms[KDA ? DK : 1];  // KDA: B_m per key channel
-  __shared__ __attribute__((aligned(16))) float cnl[KDA ? DK : 1];  // KDA: e^{B_n - B_m} per key channel
-  __shared__ __attribute__((aligned(16))) float ebm[KDA ? DK : 1];  // KDA: e^{B_m} per key channel
-  ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows; KDA: K e^{B - B_m} (phases 0-1)
-  ET(*Kn)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: K e^{B_m - B}
-  ET(*Qs)[KP] = (ET(*)[KP])(un + 2 * KS_BYTES);  // KDA: Q rows, then Q e^{B - B_m}
+  ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
+  ET(*Qs)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: Q rows (phases 0-1)
+  float(*Bl)[BP] = (float(*)[BP])(un + NT * KS_BYTES);  // KDA: B log2(e) (phases 0-1)
+  float(*As)[TP] = KDA ? (float(*)[TP])(un + NT * KS_BYTES) : As_st;  // A (KDA: after the B table)
   float(*Ts)[TP] = (float(*)[TP])un;             // T (phase 2 on)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -285,95 +297,137 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
     }
     __syncthreads();
     if (KDA) {
-      // one thread per key channel: the runs' exclusive prefix (in place),
-      // the reference B_m (row C/2 - 1: the end of the first GP/2 runs) and
-      // B_n with the per-channel factors
+      // one thread per key channel: the runs' exclusive prefix (in place)
+      // and e^{B_n} (rows past the end of the chunk carry the last B)
       if (tid < DK) {
-        float acc = 0.f, bm = 0.f;
+        float acc = 0.f;
 #pragma unroll
         for (int q2 = 0; q2 < GP; ++q2) {
           const float tq = Bt[q2 * DK + tid];
           Bt[q2 * DK + tid] = acc;
           acc += tq;
-          if (q2 == GP / 2 - 1) bm = acc;
         }
-        bms[tid] = bm;
-        cnl[tid] = __expf(acc - bm);
-        ebm[tid] = __expf(bm);
         P.gam[ch * DK + tid] = __expf(acc);
       }
       __syncthreads();
-      // B - B_m of this thread's elements, then the scaled tiles, 16 bytes
-      // of a row at a time
       const int d0 = 8 * (tid % CG), part = tid / CG;
-      const floatx4 o0 = *(const floatx4*)&Bt[part * DK + d0] - *(const floatx4*)&bms[d0];
-      const floatx4 o1 = *(const floatx4*)&Bt[part * DK + d0 + 4] - *(const floatx4*)&bms[d0 + 4];
+      const floatx4 o0 = *(const floatx4*)&Bt[part * DK + d0];
+      const floatx4 o1 = *(const floatx4*)&Bt[part * DK + d0 + 4];
+      __syncthreads();  // the runs' totals are read; the B table takes their bytes
+      constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
       for (int i = 0; i < GR; ++i) {
         const int r = part * GR + i;
-        float xb[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          xb[c] = bv[i][0][c] + o0[c];
-          xb[c + 4] = bv[i][1][c] + o1[c];
-        }
-#pragma unroll
-        for (int pc = 0; pc < 8 / PE; ++pc) {
-          const V16 kv = *(const V16*)&Ks[r][d0 + pc * PE];
-          const V16 qv = *(const V16*)&Qs[r][d0 + pc * PE];
-          V16 ks, kn, qs;
-#pragma unroll
-          for (int c = 0; c < PE; ++c) {
-            const float x = xb[pc * PE + c];
-            const float e = __expf(x), ei = __expf(-x);
-            ks[c] = (ET)(to_f(kv[c]) * e);
-            kn[c] = (ET)(to_f(kv[c]) * ei);
-            qs[c] = (ET)(to_f(qv[c]) * e);
-          }
-          *(V16*)&Ks[r][d0 + pc * PE] = ks;
-          *(V16*)&Kn[r][d0 + pc * PE] = kn;
-          *(V16*)&Qs[r][d0 + pc * PE] = qs;
-        }
+        *(floatx4*)&Bl[r][d0] = (bv[i][0] + o0) * kLog2e;
+        *(floatx4*)&Bl[r][d0 + 4] = (bv[i][1] + o1) * kLog2e;
       }
       __syncthreads();
     }
 
     // ---- phase 1: products and the chunk operands --------------------------------
-    // K row fragment of token tile t, inner block p.  KDA: K e^{B - B_m}
-    // for the row side of a product (sg > 0), K e^{B_m - B} for the column
-    // side.
-    auto kfrag = [&](int t, int p, float sg) -> V8 {
+    // GDN: K row fragment of token tile t, inner block p
+    auto kfrag = [&](int t, int p) -> V8 {
       const int r = 16 * t + c16;
       if (LF) return *(const V8*)&Ks[r][32 * p + 8 * g4];
-      return row_slots<ET>(KDA && sg < 0.f ? &Kn[r][32 * p] : &Ks[r][32 * p], g4);
+      return row_slots<ET>(&Ks[r][32 * p], g4);
+    };
+    // KDA: fragment of row `xrow` (K or Q) at the eight contiguous key
+    // channels d .. d + 7, each weighted by 2^{x}, x = brow - bref (right:
+    // bref - brow) in the B table's units; the caller picks bref so that
+    // x <= 0
+    typedef typename VT<ET>::v4 V4;
+    auto kda_frag = [&](const ET* xrow, const float* brow, const float* bref, int d, bool right) -> V8 {
+      const V4 x0 = *(const V4*)(xrow + d), x1 = *(const V4*)(xrow + d + 4);
+      const floatx4 b0 = *(const floatx4*)(brow + d), b1 = *(const floatx4*)(brow + d + 4);
+      const floatx4 r0 = *(const floatx4*)(bref + d), r1 = *(const floatx4*)(bref + d + 4);
+      V8 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[j] = (ET)(to_f(x0[j]) * __builtin_amdgcn_exp2f(right ? r0[j] - b0[j] : b0[j] - r0[j]));
+        y[j + 4] = (ET)(to_f(x1[j]) * __builtin_amdgcn_exp2f(right ? r1[j] - b1[j] : b1[j] - r1[j]));
+      }
+      return y;
     };
 
     // P of this wave's row tile as B fragments of P^T (kept for the LDS-fed
     // scan's form, which stores P Tb instead of P)
     V8 pfr[2];
-    // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w).  Every
-    // wave multiplies its row tile with all four column tiles (the products
-    // past the diagonal are dropped), so all K fragments are read from LDS
-    // at once and no branch splits the reads from the products.
-    {
-      const int rt = wv;
+    // #2 KKT (row tile w of A) and the output Map's P (row tile 3 - w)
+    const int rt = wv;
+    floatx4 acc[4], pt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = zero4();
+      pt[t] = zero4();
+    }
+    if constexpr (KDA) {
+      // Off-diagonal tiles about the first row of the row tile (factors at
+      // most 1), 16-bit products; diagonal tiles about the tile's row 8
+      // (factors within e^{+-8 max|g|}), fp32 products.  Tiles past the
+      // diagonal are not formed.
+      const float* refA = &Bl[16 * rt][0];
+      const float* refP = &Bl[16 * pr][0];
+      const int rA = 16 * rt + c16, rP = 16 * pr + c16;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        const int d = 32 * p + 8 * g4;
+        const V8 ar = kda_frag(&Ks[rA][0], &Bl[rA][0], refA, d, false);
+        const V8 qr = kda_frag(&Qs[rP][0], &Bl[rP][0], refP, d, false);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          if (t < rt) acc[t] = mma(ar, kda_frag(&Ks[16 * t + c16][0], &Bl[16 * t + c16][0], refA, d, true), acc[t]);
+          if (t < pr) pt[t] = mma(kda_frag(&Ks[16 * t + c16][0], &Bl[16 * t + c16][0], refP, d, true), qr, pt[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // diagonal: A tile (rt, rt) = (K e^{B - B_c}) (K e^{B_c - B})^T and
+      // P^T tile (pr, pr) = (K e^{B_c' - B}) (Q e^{B - B_c'})^T, row tile
+      // rows r, their middle rows c, c'
+      auto diag = [&](int r, int c, bool withq, floatx4 accd) -> floatx4 {
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+          const int d = 32 * p + 8 * g4;
+          const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
+          const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
+          const floatx4 c0 = *(const floatx4*)&Bl[c][d], c1 = *(const floatx4*)&Bl[c][d + 4];
+          floatx8 lf, rf;
+          if (withq) {
+            const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              rf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(c0[j] - b0[j]);
+              lf[j] = to_f(q0[j]) * __builtin_amdgcn_exp2f(b0[j] - c0[j]);
+              rf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(c1[j] - b1[j]);
+              lf[j + 4] = to_f(q1[j]) * __builtin_amdgcn_exp2f(b1[j] - c1[j]);
+            }
+            accd = mma(rf, lf, accd);  // P^T: key token outer on the A side
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              lf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(b0[j] - c0[j]);
+              rf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(c0[j] - b0[j]);
+              lf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(b1[j] - c1[j]);
+              rf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(c1[j] - b1[j]);
+            }
+            accd = mma(lf, rf, accd);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return accd;
+      };
+      acc[rt] = diag(rA, 16 * rt + 8, false, acc[rt]);
+      pt[pr] = diag(rP, 16 * pr + 8, true, pt[pr]);
+    } else {
+      // Every wave multiplies its row tile with all four column tiles (the
+      // products past the diagonal are dropped), so all K fragments are read
+      // from LDS at once and no branch splits the reads from the products.
       V8 ar[KB], kc[4][KB];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) ar[p] = kfrag(rt, p, 1.f);
+      for (int p = 0; p < KB; ++p) ar[p] = kfrag(rt, p);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int p = 0; p < KB; ++p) kc[t][p] = kfrag(t, p, -1.f);
-      if (KDA) {
-#pragma unroll
-        for (int p = 0; p < KB; ++p) qf[p] = row_slots<ET>(&Qs[rq][32 * p], g4);
-      }
-      floatx4 acc[4], pt[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[t] = zero4();
-        pt[t] = zero4();
-      }
+        for (int p = 0; p < KB; ++p) kc[t][p] = kfrag(t, p);
 #pragma unroll
       for (int p = 0; p < KB; ++p)
 #pragma unroll
@@ -381,6 +435,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
           acc[t] = mma(ar[p], kc[t][p], acc[t]);  // A tile (rt, t)
           pt[t] = mma(kc[t][p], qf[p], pt[t]);    // P^T tile (t, pr) = K_t Q_pr^T
         }
+    }
+    // A and P from the products: A to LDS for the solve, P to the workspace
+    // (KDA: after the chunk operands below, whose reads of the B table must
+    // end before A takes its bytes)
+    auto store_ap = [&]() {
       // A: strictly lower part, scaled by beta_r (and e^{b_r - b_i} for GDN);
       // tiles past the diagonal are never read.  The gate values come from
       // LDS once per lane: this lane's four rows as one vector, one column
@@ -423,9 +482,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
         pg[(pr * 2 + 0) * 64 + lane] = pfr[0];
         pg[(pr * 2 + 1) * 64 + lane] = pfr[1];
       }
-    }
+    };
+    if (!KDA) store_ap();
     // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
-    // of state tile mt in the scan's row order, inner = token block p).
+    // of state tile mt in the scan's row order, inner = token block p);
+    // KDA: K (.) e^{B_n - B}
     if (KT) {
       constexpr int NF = (DK / 16) * 2;
       V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
@@ -436,7 +497,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 32 * p + kmap(g4, j);
-          x[j] = KDA ? (ET)(to_f(Kn[i][d]) * cnl[d]) : (ET)(to_f(Ks[i][d]) * __expf(bs[C - 1] - bs[i]));
+          x[j] = KDA ? (ET)(to_f(Ks[i][d]) * __builtin_amdgcn_exp2f(Bl[C - 1][d] - Bl[i][d]))
+                     : (ET)(to_f(Ks[i][d]) * __expf(bs[C - 1] - bs[i]));
         }
         ktg[f * 64 + lane] = x;
       }
@@ -448,18 +510,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P, int64_t nunits)
       V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
       for (int f = wv; f < 4 * KB; f += 4) {
         const int nt = f / KB, p = f - nt * KB;
-        const int r = 16 * nt + c16;
-        V8 xk = *(const V8*)&Ks[r][32 * p + 8 * g4];
-        V8 xq = *(const V8*)&Qs[r][32 * p + 8 * g4];
+        const int r = 16 * nt + c16, d = 32 * p + 8 * g4;
+        const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
+        const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
+        const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
+        V8 xk, xq;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = ebm[32 * p + 8 * g4 + j];
-          xk[j] = (ET)(to_f(xk[j]) * e);
-          xq[j] = (ET)(to_f(xq[j]) * e);
+        for (int j = 0; j < 4; ++j) {
+          const float e0 = __builtin_amdgcn_exp2f(b0[j]), e1 = __builtin_amdgcn_exp2f(b1[j]);
+          xk[j] = (ET)(to_f(k0[j]) * e0);
+          xq[j] = (ET)(to_f(q0[j]) * e0);
+          xk[j + 4] = (ET)(to_f(k1[j]) * e1);
+          xq[j + 4] = (ET)(to_f(q1[j]) * e1);
         }
         kwg[f * 64 + lane] = xk;
         qwg[f * 64 + lane] = xq;
       }
+      __syncthreads();  // the B table is read; A takes its bytes
+      store_ap();
     } else if (tid < C) {
       // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
       // holds e^{b_n} (rows past the end carry the last b)

@@ -119,13 +119,16 @@ drla_status gdn_prefill(const drla_problem* p, const void* q, const void* k,
 
 /* Kimi Delta Attention chunked prefill: identical to gdn_prefill except that
  * g is per key channel, [T, h_v, dk] fp32.
- * Gate range: the chunk's K and Q rows are scaled per key channel by
- * exp(+-(B_r - B_m)), B the in-chunk cumulative gate and B_m its value at
- * row 31, so within every 64-token chunk 32 max|g| must stay below 88 for
- * bf16 and fp32 inputs and below 11 for fp16 inputs (the largest finite
- * value of the scaled tiles' type); outside it the results are not finite.
- * gdn_prefill takes exponentials of gate differences directly and accepts
- * any g <= 0.  The same bound holds for decay_prefill with per_channel. */
+ * Gate range: any g <= 0 whose magnitude, summed over the tokens between
+ * any row of a 16-token tile of a chunk and the tile's ninth row, stays
+ * below 88 per key channel (|g| < 11 per token suffices, a per-token decay
+ * above e^{-11}).  The in-chunk products weigh each key channel by
+ * e^{B_r - B_i} (B the in-chunk cumulative gate, r >= i): tiles below the
+ * diagonal factor it about their row tile's first row (both factors at most
+ * 1, any gate), the diagonal tiles about their ninth row in fp32 (factors
+ * within e^{+-8 max|g|}).  gdn_prefill takes exponentials of gate
+ * differences directly and accepts any g <= 0.  The same range holds for
+ * decay_prefill with per_channel. */
 drla_status kda_prefill(const drla_problem* p, const void* q, const void* k,
                         const void* v, const float* beta, const float* g,
                         const float* h0, const int32_t* cu_seqlens_dev,

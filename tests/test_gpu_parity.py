@@ -209,19 +209,28 @@ def test_kda_with_uniform_gate_equals_gdn(drla, io):
 
 
 # Strong decay.  GDN takes e^{b_r - b_i} and e^{b_n - b_r} directly, so any
-# gate is in range.  KDA (and decay-only with per-channel gates) scales the
-# chunk's K and Q rows by e^{+-(B_r - B_m)} about the per-channel reference
-# B_m = B of row 31, so 32 max|g| must stay below the log of the largest
-# value of the tiles' type: 88 for bf16 and fp32, 11 for fp16.
+# gate is in range.  KDA (and decay-only with per-channel gates) weighs each
+# key channel of the in-chunk products by e^{B_r - B_i}, factored about the
+# first row of the row tile below the diagonal (factors at most 1: any gate)
+# and about the ninth row of the tile on the diagonal in fp32 (factors
+# within e^{+-8 max|g|}): |g| < 11 per token.  The cases reach the edge of
+# that range (8 x 10.8 = 86.4) and a per-token decay down to e^{-10.8}.
 @pytest.mark.parametrize("kind,io,g_lo,g_hi", [
     ("gdn", "bf16", 2.0, 8.0), ("gdn", "f16", 2.0, 8.0),
-    ("kda", "bf16", 1.0, 2.5), ("kda", "f32", 1.0, 2.5), ("kda", "f16", 0.1, 0.3)])
+    ("kda", "bf16", 2.0, 8.0), ("kda", "f32", 2.0, 8.0), ("kda", "f16", 2.0, 8.0),
+    ("kda", "bf16", 9.0, 10.8), ("kda", "f32", 9.0, 10.8), ("kda", "f16", 0.0, 10.8),
+    ("gla", "bf16", 2.0, 8.0), ("gla", "f16", 0.0, 10.8)])
 def test_strong_decay_in_supported_range(drla, kind, io, g_lo, g_hi):
     print(f"case strong-decay kind={kind} io={io} g=-U({g_lo},{g_hi})", flush=True)
     x = _case(kind, io, 128, 128, lens=(300, 64), h_qk=1, h_v=2, h0_std=0.05,
               g_lo=g_lo, g_hi=g_hi)
     d = to_device(x)
-    o, ht = _call(drla, x, d)
+    if kind == "gla":
+        o, ht = drla.decay_prefill(d["q"], d["k"], d["v"], d["g"], d["h0"], d["cu"],
+                                   cu_seqlens_host=d["cu_host"], per_channel=True)
+        torch.cuda.synchronize()
+    else:
+        o, ht = _call(drla, x, d)
     o_ref, ht_ref = run_oracle(x)
     _check(f"strong-decay {kind}/{io}", x, _np(o), _np(ht), o_ref, ht_ref)
 
