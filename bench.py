@@ -1,7 +1,11 @@
 """Throughput of chunked delta-rule prefill on one MI355X.
 
 One step = one full prefill call (prep, scan and output kernels) over the
-workload's inputs, already resident in HBM.  Prints one JSON line.
+workload's inputs, already resident in HBM.  Every step is timed on its own
+with HIP events on the launch stream; ms_per_step is the median.  The
+roofline is priced against the published peaks and against the peaks this
+GPU sustains in two microbenchmarks (libdrla_peaks.so: a streaming copy and
+chains of dependent MFMAs).  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
@@ -19,6 +23,7 @@ import argparse
 import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -140,43 +145,161 @@ def load_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(x, spec, n_tokens, budget_s=10.0):
-    """The fp64 oracle on this host's cores over the whole workload,
-    repeated until about `budget_s` of wall time."""
+def _nmse(x, y):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    d = float((y * y).sum())
+    return float(((x - y) ** 2).sum() / d) if d > 0 else float((x * x).sum())
+
+
+def _rel_err(x, y):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = float(np.abs(y).max()) if y.size else 0.0
+    num = float(np.abs(x - y).max()) if y.size else 0.0
+    return num / den if den > 0 else num
+
+
+def _oracle_heads(oracle, x, spec, heads, threads):
+    """The fp64 oracle over the listed value heads only (their q/k heads and
+    gates with them)."""
+    grp = spec.h_v // spec.h_qk
+    hk = [h // grp for h in heads]
+    q, k = x["q"][:, hk], x["k"][:, hk]
+    v, g = x["v"][:, heads], x["g"][:, heads]
+    h0 = None if x["h0"] is None else x["h0"][:, heads]
+    cu = x["cu_seqlens"] if x["varlen"] else None
+    if spec.kind in ("ret", "gla"):
+        return oracle.recurrence_decay(q, k, v, g, h0, cu, per_channel=spec.kind == "gla")
+    return oracle.recurrence(q, k, v, x["beta"][:, heads], g, h0, cu, kda=spec.kind == "kda",
+                             threads=threads)
+
+
+def cpu_baseline(x, spec, n_tokens, budget_s=10.0, o_gpu=None, ht_gpu=None):
+    """The fp64 oracle on this host's cores over the whole workload, repeated
+    until about `budget_s` of wall time, and on one core over a sample of
+    heads.  Its first whole-workload result also gives the GPU result's
+    error (NMSE and max-relative) on the bench workload.  Returns
+    (cpu_baseline object, parity object or None)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    if spec.kind in ("ret", "gla"):
-        # decay-only linear attention: the single-threaded fp64 recurrence
-        reps, t_total = 0, 0.0
-        while t_total < budget_s and reps < 1000:
-            t0 = time.perf_counter()
-            oracle.recurrence_decay(x["q"], x["k"], x["v"], x["g"], x["h0"],
-                                    x["cu_seqlens"] if x["varlen"] else None,
-                                    per_channel=spec.kind == "gla")
-            t_total += time.perf_counter() - t0
-            reps += 1
-        return {"value": round(n_tokens * reps / t_total, 1), "unit": "tokens/s", "cores": 1,
-                "kind": "oracle",
-                "sample": f"whole {spec.name} workload ({n_tokens} tokens x {spec.h_v} heads), "
-                          f"fp64 decay-only token recurrence, {reps} run(s) in {t_total:.1f} s, "
-                          "one thread"}
+    decay = spec.kind in ("ret", "gla")
     units = spec.n_seqs * spec.h_v
-    used = min(cores, units)
-    reps, t_total = 0, 0.0
+    used = 1 if decay else min(cores, units)
+    all_heads = list(range(spec.h_v))
+    reps, t_total, first = 0, 0.0, None
     while t_total < budget_s and reps < 1000:
         t0 = time.perf_counter()
-        oracle.recurrence(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"],
-                          x["cu_seqlens"] if x["varlen"] else None,
-                          kda=spec.kind == "kda", threads=cores)
+        res = _oracle_heads(oracle, x, spec, all_heads, cores)
         t_total += time.perf_counter() - t0
         reps += 1
+        if first is None:
+            first = res
         if reps == 1 and t_total > budget_s:
             break
-    return {"value": round(n_tokens * reps / t_total, 1), "unit": "tokens/s", "cores": used,
+    # one core: whole heads, one after another, for about a third of the budget
+    h1, t1 = 0, 0.0
+    while h1 < spec.h_v and (h1 == 0 or t1 < budget_s / 3):
+        t0 = time.perf_counter()
+        _oracle_heads(oracle, x, spec, [h1], 1)
+        t1 += time.perf_counter() - t0
+        h1 += 1
+    one = n_tokens * h1 / spec.h_v / t1
+    what = "decay-only token recurrence" if decay else "token recurrence"
+    base = {"value": round(n_tokens * reps / t_total, 1), "unit": "tokens/s", "cores": used,
             "kind": "oracle",
             "sample": f"whole {spec.name} workload ({n_tokens} tokens x {spec.h_v} heads), "
-                      f"fp64 token recurrence, {reps} run(s) in {t_total:.1f} s, "
-                      f"threads over {units} (sequence, head) units on {cores} host cores"}
+                      f"fp64 {what}, {reps} run(s) in {t_total:.1f} s, "
+                      + ("one thread" if decay else
+                         f"threads over {units} (sequence, head) units on {cores} host cores"),
+            "one_core": {"value": round(one, 1), "unit": "tokens/s", "cores": 1,
+                         "sample": f"{h1} of {spec.h_v} heads of the workload, all tokens, one "
+                                   f"thread, {t1:.1f} s, scaled to the whole workload"}}
+    parity = None
+    if o_gpu is not None:
+        o_ref, ht_ref = first
+        parity = {"vs": "fp64 oracle (token recurrence), whole bench workload",
+                  "nmse_o": float(f"{_nmse(o_gpu, o_ref):.3e}"),
+                  "nmse_ht": float(f"{_nmse(ht_gpu, ht_ref):.3e}"),
+                  "rel_err_o": float(f"{_rel_err(o_gpu, o_ref):.3e}"),
+                  "rel_err_ht": float(f"{_rel_err(ht_gpu, ht_ref):.3e}")}
+    return base, parity
+
+
+PEAKS_LIB = os.path.join(ROOT, "delta_rule_linear_chunked_amd", "_build", "libdrla_peaks.so")
+
+
+def measure_peaks(torch, hip, stream, io):
+    """Attainable peaks of this GPU: HBM bandwidth of a streaming copy (2 GiB
+    read + 2 GiB written, the best of three grid sizes) and MFMA throughput
+    of chains of dependent MFMAs in the workload's dtype (bf16 and fp16
+    16x16x32, fp32 16x16x4).  Each figure is the best of five launches'
+    mean, timed with HIP events on `stream`."""
+    if not os.path.exists(PEAKS_LIB):
+        raise RuntimeError(f"{PEAKS_LIB} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.drla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.drla_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int)]
+    lib.drla_peak_mfma_grid.argtypes = [ctypes.c_int]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    e0, e1 = hip.event(), hip.event()
+    sp = ctypes.c_void_p(stream)
+
+    def timed(launch, n=5):
+        launch()
+        launch()
+        hip.lib.hipEventRecord(ctypes.c_void_p(e0), sp)
+        for _ in range(n):
+            launch()
+        hip.lib.hipEventRecord(ctypes.c_void_p(e1), sp)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(e0, e1) / n
+
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best_bw, best_blocks = 0.0, 0
+    for per_cu in (8, 16, 32):
+        def launch(b=per_cu * cus):
+            rc = lib.drla_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                    nbytes, b, sp)
+            if rc != 0:
+                raise RuntimeError(f"drla_peak_copy failed ({rc})")
+        bw = 2 * nbytes / (timed(launch) * 1e-3) / 1e9
+        if bw > best_bw:
+            best_bw, best_blocks = bw, per_cu * cus
+    torch.cuda.synchronize()
+    if not torch.equal(dst[:: (1 << 20)], src[:: (1 << 20)]):
+        raise RuntimeError("peak copy produced wrong data")
+    del src, dst
+
+    kind = {"bf16": 0, "f16": 1}.get(io, 2)
+    iters = 2048 if kind == 2 else 4096
+    grid = lib.drla_peak_mfma_grid(0)
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    flops = ctypes.c_double()
+
+    def mlaunch():
+        rc = lib.drla_peak_mfma(ctypes.c_void_p(out.data_ptr()), kind, iters, grid, sp,
+                                ctypes.byref(flops), None)
+        if rc != 0:
+            raise RuntimeError(f"drla_peak_mfma failed ({rc})")
+    ms = timed(mlaunch)
+    tflops = flops.value / (ms * 1e-3) / 1e12
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return {"hbm_copy_gbs": round(best_bw, 1),
+            "hbm_copy": f"2 GiB read + 2 GiB written, 16-byte non-temporal loads/stores, "
+                        f"{best_blocks} workgroups of 256",
+            "mfma_tflops": round(tflops, 1),
+            "mfma": f"{['bf16 16x16x32', 'fp16 16x16x32', 'fp32 16x16x4'][kind]}, 8 dependent "
+                    f"chains per wave, {grid} workgroups of 4 waves, {iters} rounds"}
 
 
 def copy_calibration(torch, dev, mib):
@@ -193,6 +316,63 @@ def copy_calibration(torch, dev, mib):
     torch.cuda.synchronize()
     print(f"copy calibration: {n * 2} bytes read and {n * 2} bytes written per dispatch",
           file=sys.stderr)
+
+
+def _pk(peaks, key):
+    return None if peaks is None else peaks[key]
+
+
+def _frac(achieved, peak, digits=4):
+    return None if peak is None else round(achieved / peak, digits)
+
+
+def timed_steps(torch, hip, stream, step, steps, stage_events):
+    """Runs `steps` steps back to back on `stream`, each timed on its own:
+    a HIP event at every step's start (with stage_events, the three events
+    the library records at the start, between prep and scan, and at the end
+    of the call), one after the last.  Returns (per-step ms, per-stage ms
+    lists, host wall seconds).  A step's time runs from its start event to
+    the next step's, so it includes whatever separates two calls."""
+    sp = ctypes.c_void_p(stream)
+    evs = [[hip.event() for _ in range(3 if stage_events else 1)] for _ in range(steps)]
+    end = hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if stage_events:
+            step(evs[i])
+        else:
+            hip.lib.hipEventRecord(ctypes.c_void_p(evs[i][0]), sp)
+            step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(end), sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    starts = [e[0] for e in evs] + [end]
+    per_step = [hip.elapsed_ms(starts[i], starts[i + 1]) for i in range(steps)]
+    stages = {}
+    if stage_events:
+        stages = {"prep": [hip.elapsed_ms(e[0], e[1]) for e in evs],
+                  "scan": [hip.elapsed_ms(e[1], e[2]) for e in evs]}
+    for e in [x for es in evs for x in es] + [end]:
+        hip.destroy(e)
+    return per_step, stages, wall
+
+
+def mean_step_ms(torch, hip, stream, step, steps):
+    """Mean ms per step over `steps` back-to-back steps with no events
+    between them (two events around the whole run)."""
+    sp = ctypes.c_void_p(stream)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), sp)
+    for _ in range(steps):
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), sp)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return ms
 
 
 def decode_bench(args, spec, x, torch, drla):
@@ -217,24 +397,18 @@ def decode_bench(args, spec, x, torch, drla):
         step()
     torch.cuda.synchronize()
     hip = Hip()
-    e0, e1 = hip.event(), hip.event()
     stream = torch.cuda.current_stream().cuda_stream
-    t0 = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
-    for _ in range(args.steps):
-        step()
-    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = hip.elapsed_ms(e0, e1) / args.steps
-    hip.destroy(e0)
-    hip.destroy(e1)
+    ms_mean = mean_step_ms(torch, hip, stream, step, args.steps)
+    per_step, _, wall = timed_steps(torch, hip, stream, step, args.steps, False)
+    ms_step = statistics.median(per_step)
+    peaks = None if args.no_peaks else measure_peaks(torch, hip, stream, spec.io)
     es = 4 if spec.io == "f32" else 2
     kda = spec.kind == "kda"
     # algorithmic bytes: q, k, v, beta, g, h0 in; o, new state out
     bytes_ = N * (2 * spec.h_qk * spec.dk * es + 2 * spec.h_v * spec.dv * es + spec.h_v * 4
                   + spec.h_v * (spec.dk if kda else 1) * 4) + 2 * N * spec.h_v * spec.dk * spec.dv * 4
     ach = bytes_ / (ms_step * 1e-3) / 1e9
+    traffic = load_traffic("decode", spec.name)
     line = {
         "metric": DECODE_METRIC,
         "value": round(N / (ms_step * 1e-3), 1),
@@ -253,14 +427,23 @@ def decode_bench(args, spec, x, torch, drla):
                    "h_qk": spec.h_qk, "h_v": spec.h_v, "dk": spec.dk, "dv": spec.dv,
                    "io": spec.io},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "decode",
-                     "traffic": load_traffic("decode", spec.name),
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "peak_measured": _pk(peaks, "hbm_copy_gbs"),
+                     "frac_measured": _frac(ach, _pk(peaks, "hbm_copy_gbs")), "kernel": "decode",
+                     "traffic": traffic,
+                     "traffic_gbs": None if traffic is None else
+                     round(traffic / (ms_step * 1e-3) / 1e9, 1),
                      "kernel_ms": {"decode": round(ms_step, 5)},
                      "algorithmic_bytes_per_launch": int(bytes_)},
-        "path": {"host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "path": {"ms_per_step_mean_no_events": round(ms_mean, 5),
+                 "ms_per_step_min": round(min(per_step), 5),
+                 "ms_per_step_max": round(max(per_step), 5),
+                 "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "peaks": peaks,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, spec, N, args.cpu_budget)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(
+            x, spec, N, args.cpu_budget, o.float().cpu().numpy(), ht.float().cpu().numpy())
     copy_calibration(torch, dev, args.copy_calibration)
     print(json.dumps(line), flush=True)
 
@@ -273,6 +456,8 @@ def main():
     ap.add_argument("--workload", default="gdn_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak microbenchmarks (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the bench, run a plain elementwise copy of MIB MiB (bf16 negate: "
                          "reads and writes MIB MiB) five times, the reference dispatch that scales "
@@ -309,68 +494,63 @@ def main():
     ws = torch.empty(max(drla.workspace_bytes(x["q"].shape, x["v"].shape, io, n_seqs, cu_host), 1),
                      dtype=torch.uint8, device=dev)
     if spec.kind in ("ret", "gla"):
-        def fn(q, k, v, beta, g, *a, **kw):
-            return drla.decay_prefill(q, k, v, g, *a, per_channel=spec.kind == "gla", **kw)
+        call = drla.prepare_prefill(spec.kind == "gla", q, k, v, None, g, h0, cu,
+                                    cu_seqlens_host=cu_host, workspace=ws, out=o,
+                                    final_state=ht, flags=drla.DECAY_ONLY)
     else:
-        fn = drla.kda_prefill if spec.kind == "kda" else drla.gdn_prefill
-
-    def step(events=None):
-        fn(q, k, v, beta, g, h0, cu, cu_seqlens_host=cu_host, workspace=ws, out=o,
-           final_state=ht, stage_events=events)
+        call = drla.prepare_prefill(spec.kind == "kda", q, k, v, beta, g, h0, cu,
+                                    cu_seqlens_host=cu_host, workspace=ws, out=o,
+                                    final_state=ht)
 
     for _ in range(args.warmup):
-        step()
+        call()
     torch.cuda.synchronize()
     hip = Hip()
-    e0, e1 = hip.event(), hip.event()
     stream = torch.cuda.current_stream().cuda_stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
-    for _ in range(args.steps):
-        step()
-    hip.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = hip.elapsed_ms(e0, e1)
-    ms_step = ms_total / args.steps
-
-    # per-kernel durations, live, with events at the stage boundaries
-    stage = {"prep": 0.0, "scan": 0.0}
-    evs = [hip.event() for _ in range(3)]
-    for _ in range(args.steps):
-        step(evs)
-        torch.cuda.synchronize()
-        stage["prep"] += hip.elapsed_ms(evs[0], evs[1])
-        stage["scan"] += hip.elapsed_ms(evs[1], evs[2])
-    for key in stage:
-        stage[key] /= args.steps
-    for e in evs + [e0, e1]:
-        hip.destroy(e)
+    ms_mean = mean_step_ms(torch, hip, stream, call, args.steps)
+    # the timed region: one event at every step's start, the median step;
+    # then the same steps with the library's three stage events, the median
+    # time of each stage (more events per step, so a separate run)
+    per_step, _, wall = timed_steps(torch, hip, stream, call, args.steps, False)
+    ms_step = statistics.median(per_step)
+    _, stages, _ = timed_steps(torch, hip, stream, call, args.steps, True)
+    stage = {kk: statistics.median(vv) for kk, vv in stages.items()}
+    peaks = None if args.no_peaks else measure_peaks(torch, hip, stream, spec.io)
 
     costs = kernel_costs(spec, n_tokens, n_seqs)
     dom = max(stage, key=stage.get)
     bytes_, flops = costs[dom]
     t_s = stage[dom] * 1e-3
     intensity = flops / bytes_
-    ridge = (F32_PEAK_TFLOPS if spec.io == "f32" else BF16_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = F32_PEAK_TFLOPS if spec.io == "f32" else BF16_PEAK_TFLOPS
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
         ach = bytes_ / t_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "peak_measured": _pk(peaks, "hbm_copy_gbs"),
+                "frac_measured": _frac(ach, _pk(peaks, "hbm_copy_gbs"))}
     else:
         ach = flops / t_s / 1e12
-        peak = F32_PEAK_TFLOPS if spec.io == "f32" else BF16_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4)}
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(ach / mfma_peak, 4), "peak_measured": _pk(peaks, "mfma_tflops"),
+                "frac_measured": _frac(ach, _pk(peaks, "mfma_tflops"))}
     roof["kernel"] = dom
     roof["traffic"] = load_traffic(dom, spec.name)
+    # HBM bytes per dispatch from the committed counter profiles (null when
+    # they were taken on other kernel sources) over the live kernel times
+    traffic_gbs = {}
+    for kk in stage:
+        tb = load_traffic(kk, spec.name)
+        traffic_gbs[kk] = None if tb is None else round(tb / (stage[kk] * 1e-3) / 1e9, 1)
+    roof["traffic_gbs"] = traffic_gbs
     roof["kernel_ms"] = {kk: round(vv, 5) for kk, vv in stage.items()}
     roof["algorithmic_bytes_per_launch"] = int(bytes_)
     roof["algorithmic_flops_per_launch"] = int(flops)
 
     total_flops = sum(f for _, f in costs.values())
     io_bytes = call_io_bytes(spec, n_tokens, n_seqs)
+    io_gbs = io_bytes / (ms_step * 1e-3) / 1e9
+    path_tflops = total_flops / (ms_step * 1e-3) / 1e12
     line = {
         "metric": DECAY_METRIC if spec.kind in ("ret", "gla") else METRIC,
         "value": round(n_tokens / (ms_step * 1e-3), 1),
@@ -390,13 +570,20 @@ def main():
                    "dk": spec.dk, "dv": spec.dv, "chunk": CHUNK, "io": spec.io},
         "roofline": roof,
         "path": {"algorithmic_io_bytes": int(io_bytes),
-                 "io_roofline_frac": round(io_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "io_roofline_frac": round(io_gbs / HBM_PEAK_GBS, 4),
+                 "io_roofline_frac_measured": _frac(io_gbs, _pk(peaks, "hbm_copy_gbs")),
                  "kernel_flops": int(total_flops),
-                 "mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                 "mfma_frac": round(path_tflops / mfma_peak, 5),
+                 "mfma_frac_measured": _frac(path_tflops, _pk(peaks, "mfma_tflops"), 5),
+                 "ms_per_step_mean_no_events": round(ms_mean, 5),
+                 "ms_per_step_min": round(min(per_step), 5),
+                 "ms_per_step_max": round(max(per_step), 5),
                  "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+        "peaks": peaks,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, spec, n_tokens, args.cpu_budget)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(
+            x, spec, n_tokens, args.cpu_budget, o.float().cpu().numpy(), ht.float().cpu().numpy())
     copy_calibration(torch, dev, args.copy_calibration)
     print(json.dumps(line), flush=True)
 

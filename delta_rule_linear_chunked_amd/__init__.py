@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     HEAD_SCAN,
     NOALLOC_SCRATCH_BYTES,
     DrlaError,
+    PreparedPrefill,
     decay_decode,
     decay_prefill,
     gdn_decode,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     lib_path,
     load_library,
     prefill_noalloc,
+    prepare_prefill,
     workspace_bytes,
     workspace_layout,
 )
@@ -29,4 +31,4 @@ from ._lib import (  # noqa: F401
 __all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "decay_prefill",
            "decay_decode", "DECAY_ONLY", "workspace_bytes", "workspace_layout",
            "load_library", "lib_path", "prefill_noalloc", "DrlaError", "KEEP_INTERMEDIATES", "SERIAL", "HEAD_SCAN",
-           "NOALLOC_SCRATCH_BYTES"]
+           "NOALLOC_SCRATCH_BYTES", "prepare_prefill", "PreparedPrefill"]

@@ -85,6 +85,8 @@ def load_library():
         lib.drla_prefill_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp,
                                              vp, i32p, vp, vp, vp]
         lib.drla_prefill_noalloc.restype = ctypes.c_int
+        lib.drla_prefill_status.argtypes = [pp, i32p, vp, vp]
+        lib.drla_prefill_status.restype = ctypes.c_int
         lib.drla_workspace_bytes.argtypes = [pp, i32p]
         lib.drla_workspace_bytes.restype = ctypes.c_size_t
         lib.drla_workspace_layout.argtypes = [ctypes.c_int, pp, i32p, ctypes.c_int,
@@ -164,9 +166,61 @@ def workspace_layout(q_shape, v_shape, io_dtype=torch.bfloat16, n_seqs=1,
     return {n: getattr(out, n) for n, _ in Layout._fields_}
 
 
+class PreparedPrefill:
+    """One prefill call with its arguments validated and marshalled once;
+    calling the object launches that call again (one C call) on the same
+    buffers and stream, optionally with three stage events.  The tensors it
+    was prepared from must stay alive and keep their storage."""
+
+    def __init__(self, lib, kda, flags, args, o, ht, keep):
+        self._lib, self._kda, self._flags, self._args = lib, int(kda), int(flags), args
+        self._fn = lib.kda_prefill if kda else lib.gdn_prefill
+        self.out, self.final_state = o, ht
+        self._keep = keep  # the Problem struct, host lengths, workspace
+
+    def __call__(self, stage_events=None, verify_lengths=False):
+        if stage_events is not None or self._flags:
+            evs = None if stage_events is None else (ctypes.c_void_p * 3)(*stage_events)
+            st = self._lib.drla_prefill_ex(self._kda, self._flags, *self._args, evs)
+        else:
+            st = self._fn(*self._args)
+        if st != 0:
+            raise DrlaError(st, self._lib.drla_last_error().decode())
+        if verify_lengths:
+            self.check_lengths()
+        return self.out, self.final_state
+
+    def check_lengths(self):
+        """drla_prefill_status of the last launch (waits for its stream):
+        raises DrlaError if the device cu_seqlens differed from the host
+        copy (the call then ran as empty sequences)."""
+        a = self._args
+        st = self._lib.drla_prefill_status(a[0], a[8], a[11], a[13])
+        if st != 0:
+            raise DrlaError(st, self._lib.drla_last_error().decode())
+
+
 def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
              cu_seqlens_host=None, output_final_state=True, workspace=None,
-             out=None, final_state=None, stage_events=None, flags=0):
+             out=None, final_state=None, stage_events=None, flags=0, verify_lengths=False):
+    return _prepare(kda, q, k, v, beta, g, initial_state, cu_seqlens, cu_seqlens_host,
+                    output_final_state, workspace, out, final_state, flags)(stage_events,
+                                                                            verify_lengths)
+
+
+def prepare_prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
+                    cu_seqlens_host=None, output_final_state=True, workspace=None,
+                    out=None, final_state=None, flags=0) -> PreparedPrefill:
+    """Validate and marshal one gdn_prefill (kda=False) or kda_prefill call
+    (arguments as there; decay-only with flags=DECAY_ONLY and beta=None) on
+    the current stream, without launching it.  Returns a PreparedPrefill;
+    each call of it launches the prefill."""
+    return _prepare(kda, q, k, v, beta, g, initial_state, cu_seqlens, cu_seqlens_host,
+                    output_final_state, workspace, out, final_state, flags)
+
+
+def _prepare(kda, q, k, v, beta, g, initial_state, cu_seqlens, cu_seqlens_host,
+             output_final_state, workspace, out, final_state, flags):
     lib = load_library()
     decay = bool(flags & DECAY_ONLY)
     if q.dim() == 4:
@@ -232,22 +286,16 @@ def _prefill(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
             None if cu_seqlens is None else cu_seqlens.data_ptr(),
             _i32p(cu_host), o.data_ptr(), None if ht is None else ht.data_ptr(),
             workspace.data_ptr(), workspace.numel(), stream)
-    if stage_events is not None or flags:
-        evs = None if stage_events is None else (ctypes.c_void_p * 3)(*stage_events)
-        st = lib.drla_prefill_ex(int(kda), int(flags), *args, evs)
-    else:
-        fn = lib.kda_prefill if kda else lib.gdn_prefill
-        st = fn(*args)
-    if st != 0:
-        raise DrlaError(st, lib.drla_last_error().decode())
-    return o, ht
+    return PreparedPrefill(lib, kda, flags, args, o, ht,
+                           (prob, cu_host, workspace, q, k, v, beta, g, initial_state, cu_seqlens))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # DRLA_NOALLOC_SCRATCH_BYTES
 
 
 def prefill_noalloc(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=None,
-                    cu_seqlens_host=None, out=None, final_state=None, flags=0):
+                    cu_seqlens_host=None, out=None, final_state=None, flags=0,
+                    verify_lengths=False):
     """drla_prefill_noalloc: the prefill without a workspace argument (the
     library's own per-GPU scratch array serves instead).  Packed [T, H, d]
     inputs; o and the final state are allocated here unless `out` and
@@ -274,6 +322,8 @@ def prefill_noalloc(kda: bool, q, k, v, beta, g, initial_state=None, cu_seqlens=
         None if initial_state is None else initial_state.data_ptr(),
         None if cu_seqlens is None else cu_seqlens.data_ptr(), _i32p(cu_host),
         o.data_ptr(), ht.data_ptr(), stream)
+    if st == 0 and verify_lengths:
+        st = lib.drla_prefill_status(ctypes.byref(prob), _i32p(cu_host), None, stream)
     if st != 0:
         raise DrlaError(st, lib.drla_last_error().decode())
     return o, ht
@@ -294,7 +344,13 @@ def gdn_prefill(q, k, v, beta, g, initial_state=None, cu_seqlens=None, **kw):
     """Gated DeltaNet chunked prefill.  q,k [T,h_qk,dk] (or [B,T,h_qk,dk]),
     v [T,h_v,dv], beta [T,h_v] fp32, g [T,h_v] fp32 log-decay,
     initial_state [N,h_v,dk,dv] fp32 or None, cu_seqlens int32 [N+1] device
-    tensor or None.  Returns (o [T,h_v,dv], final_state [N,h_v,dk,dv])."""
+    tensor or None.  Returns (o [T,h_v,dv], final_state [N,h_v,dk,dv]).
+
+    Keywords: cu_seqlens_host (the same lengths on the host; without it they
+    are copied from the device, a synchronisation), output_final_state,
+    workspace, out, final_state, flags, stage_events, verify_lengths (wait
+    for the call and raise DrlaError if the device and host lengths
+    differed, in which case it ran as empty sequences)."""
     return _prefill(False, q, k, v, beta, g, initial_state, cu_seqlens, **kw)
 
 

@@ -1,5 +1,6 @@
-"""Builds libdrla.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree
-under delta_rule_linear_chunked_amd/_build/."""
+"""Builds libdrla.so (HIP kernels + C ABI) and libdrla_peaks.so (the
+attainable-peak microbenchmarks the benchmark prices its roofline with) for
+gfx950 with hipcc, in-tree under delta_rule_linear_chunked_amd/_build/."""
 from __future__ import annotations
 
 import os
@@ -13,6 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD, "libdrla.so")
+PEAKS_LIB = os.path.join(BUILD, "libdrla_peaks.so")
+PEAKS_SRC = os.path.join(CSRC, "drla_peaks.hip")
 
 ARCH = "gfx950"
 # Packed fp32 vector ops are kept off: hipcc would otherwise form
@@ -40,11 +43,12 @@ def sources():
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source and link libdrla.so.  Always recompiles."""
+    """Compile every source and link libdrla.so and libdrla_peaks.so.
+    Always recompiles."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     cmds, objs = [], []
-    for src in sources():
+    for src in sources() + [PEAKS_SRC]:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         cmd = [cc, *HIPFLAGS, *extra, "-c", src, "-o", obj]
         if src.endswith(".cpp"):
@@ -57,12 +61,13 @@ def build(verbose: bool = False, extra=()) -> str:
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         for f in [ex.submit(subprocess.check_call, c) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    for lib, parts in ((LIB, objs[:-1]), (PEAKS_LIB, objs[-1:])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *parts]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -153,8 +153,8 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, 
   L->n_chunks = nc;
   L->sched = off;
   // packed input: chunk -> sequence, chunk -> first token, sequence -> first
-  // chunk, and the sequences longest first
-  off = align_up(off + (varlen ? (2 * (size_t)nc + 2 * (size_t)p->n_seqs + 1) * 4 : 0));
+  // chunk, the sequences longest first, the checked lengths, a status word
+  off = align_up(off + (varlen ? (size_t)drla_sched_words(nc, p->n_seqs) * 4 : 0));
   L->tb = off;
   off = align_up(off + ncH * 8 * frag);
   L->pm = off;
@@ -248,6 +248,8 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.g = g;
   a.h0 = h0;
   a.cu_dev = cu_dev;
+  if (cu_host)
+    for (int i = 0; i <= p->n_seqs; ++i) a.cu_hash += drla_cu_mix((uint64_t)i, (uint32_t)cu_host[i]);
   a.o = o;
   a.ht = ht;
   a.workspace = ws;
@@ -444,6 +446,39 @@ drla_status drla_prefill_noalloc(int kda, int flags, const drla_problem* p, cons
              ws ? (size_t)DRLA_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
 }
 
+drla_status drla_prefill_status(const drla_problem* p, const int32_t* cu_seqlens_host, const void* workspace,
+                                void* stream) {
+  int64_t nc = 0;
+  const drla_status st = check_problem(p, cu_seqlens_host, &nc);
+  if (st != DRLA_OK) return st;
+  if (!packed(p, cu_seqlens_host) || p->n_seqs < 1) return DRLA_OK;  // no device lengths read
+  drla_layout L;
+  layout_of(p, nc, true, max_chunks(p, cu_seqlens_host), false, 0, &L);
+  const void* ws = workspace;
+  if (!ws) {
+    void* sp = nullptr;
+    const drla_status sa = scratch_address(&sp);
+    if (sa != DRLA_OK) return sa;
+    ws = sp;
+  }
+  if (!aligned16(ws)) return fail(DRLA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const char* word = (const char*)ws + L.sched + (size_t)drla_sched_status(nc, p->n_seqs) * 4;
+  int32_t v = -1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(DRLA_ERR_HIP, "reading the status word failed: %s", hipGetErrorString(e));
+  if (v == 0) {
+    g_last_error.clear();
+    return DRLA_OK;
+  }
+  if (v == 1)
+    return fail(DRLA_ERR_SEQLENS,
+                "cu_seqlens_dev differed from cu_seqlens_host: the call ran as empty sequences "
+                "(o not written, final states = initial states)");
+  return fail(DRLA_ERR_SEQLENS, "no status word (%d): no packed call has run on this workspace", (int)v);
+}
+
 const char* drla_status_str(drla_status s) {
   switch (s) {
     case DRLA_OK: return "ok";
@@ -461,6 +496,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 4; }
+int drla_version(void) { return 5; }
 
 }  // extern "C"

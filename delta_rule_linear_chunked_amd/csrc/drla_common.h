@@ -202,7 +202,7 @@ struct Sched {
   const int32_t* chunk_start;  // [nc] first token of each chunk
   const int32_t* seq_chunk0;   // [N+1] first chunk of each sequence
   const int32_t* seq_order;    // [N] sequences, longest first (packed input), else null
-  const int32_t* cu;           // [N+1] device cu_seqlens (packed input)
+  const int32_t* cu;           // [N+1] cu_seqlens as checked by schedule_kernel (packed input)
   int64_t seq_len;             // dense batch: tokens per sequence
   int32_t cps;                 // dense batch: chunks per sequence
   int32_t n_seqs;

@@ -461,7 +461,6 @@ __device__ __forceinline__ int64_t hs_tile_off(int ctg, int mt, int kt, int lane
 template <int DK, int DV, typename T, bool DECAY>
 __global__ __launch_bounds__(448) void hscan_value_kernel(HScanParams P) {
   constexpr int NCW = 4, CT = DV / 64, NS = 2, PF = 4, KT = DK / 16;
-  typedef HCopy<DK, DV, T, true, 2> CP;   // two copy waves
   typedef HCopy<DK, DV, T, true, 1> TP;   // one touch wave
   __shared__ HSlot<DK, DV, T, true> slot[NS];
   __shared__ __attribute__((aligned(16))) float sink[64];

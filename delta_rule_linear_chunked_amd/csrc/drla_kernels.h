@@ -107,7 +107,8 @@ struct DecodeParams {
   int32_t decay_only;  // no delta rule: S = a S + k v^T; beta unused
 };
 
-hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st);
+hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int64_t T, int64_t max_cps,
+                           uint64_t hash, int32_t* sched, hipStream_t st);
 
 template <int DK, bool KDA, typename ET>
 hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st);

@@ -65,6 +65,25 @@ static inline drla_seg_layout drla_seg_offsets(int64_t units, int64_t d, int64_t
   return L;
 }
 
+// Fingerprint of a cu_seqlens array: the sum over its entries i of a
+// 64-bit mix (the splitmix64 finaliser, Steele, Lea and Flood 2014) of
+// (i, cu[i]).  The host takes it over cu_seqlens_host, the schedule kernel
+// over the device copy; a sum is order-free, so the kernel's threads add
+// their entries in any order.
+__host__ __device__ static inline uint64_t drla_cu_mix(uint64_t i, uint32_t v) {
+  uint64_t z = ((i << 32) | v) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// The schedule region of a packed call, in int32 words from its start:
+// chunk_seq [nc], chunk_start [nc], seq_chunk0 [n + 1], seq_order [n],
+// the checked lengths cu [n + 1], the status word [1].
+static inline int64_t drla_sched_words(int64_t nc, int64_t n) { return 2 * nc + 3 * n + 3; }
+static inline int64_t drla_sched_cu(int64_t nc, int64_t n) { return 2 * nc + 2 * n + 1; }
+static inline int64_t drla_sched_status(int64_t nc, int64_t n) { return 2 * nc + 3 * n + 2; }
+
 typedef struct {
   const void* q;
   const void* k;
@@ -73,6 +92,7 @@ typedef struct {
   const float* g;
   const float* h0;
   const int32_t* cu_dev;  // NULL for a dense batch
+  uint64_t cu_hash;       // drla_cu_mix summed over cu_seqlens_host
   void* o;
   float* ht;
   void* workspace;

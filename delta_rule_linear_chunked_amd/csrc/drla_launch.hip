@@ -77,7 +77,8 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
 
   mark(0);
   if (e == hipSuccess && s.chunk_seq && a->n_seqs > 0)
-    e = launch_schedule(a->cu_dev, a->n_seqs, nc, (int32_t*)(ws + a->off_sched), st);
+    e = launch_schedule(a->cu_dev, a->n_seqs, nc, a->total_tokens, a->max_cps, a->cu_hash,
+                        (int32_t*)(ws + a->off_sched), st);
   if (e == hipSuccess) e = launch_prep<DK, KDA, ET>(pp, nc * a->h_v, st);
   mark(1);
   // Head-resident scan (DRLA_HEAD_SCAN; scalar gate, 16-bit inputs): one
@@ -173,7 +174,7 @@ hipError_t drla_launch(const drla_launch_args* a) {
     s.chunk_start = sched + a->n_chunks;
     s.seq_chunk0 = sched + 2 * a->n_chunks;
     s.seq_order = sched + 2 * a->n_chunks + a->n_seqs + 1;
-    s.cu = a->cu_dev;
+    s.cu = sched + drla_sched_cu(a->n_chunks, a->n_seqs);  // the checked copy
   } else {
     s.seq_len = a->n_seqs > 0 ? a->total_tokens / a->n_seqs : 0;
     s.cps = (int32_t)((s.seq_len + C - 1) / C);

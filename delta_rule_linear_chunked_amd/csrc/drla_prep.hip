@@ -26,18 +26,69 @@
 // All are written in MFMA fragment order (drla_common.h).
 #include <atomic>
 
+#include <type_traits>
+
 #include "drla_common.h"
 #include "drla_kernels.h"
 
 namespace drla {
 
-// Chunk table for packed input: one workgroup, prefix sum of the
-// per-sequence chunk counts.  Entries past `nc` are never written.
+// Chunk table of packed input, built from a checked copy of the device
+// cu_seqlens (the kernels after this one read only the copy).  The device
+// array must equal the host copy the call was sized and validated with:
+// cu[0] = 0, non-decreasing, cu[n] = T, at most max_cps chunks in a
+// sequence, nc chunks in all, and the fingerprint of its n + 1 entries equal
+// to the host's.  A call that passes runs on the device lengths (now bounded
+// by T and by the workspace).  One that fails runs as n empty sequences:
+// every chunk entry empty, the copy all zero, so no kernel reads a token,
+// o is not written and each final state is the initial one; the status
+// word is then 1 (else 0).
 __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_seqs, int64_t nc,
+                                                        int64_t T, int64_t max_cps, uint64_t hash,
                                                         int32_t* chunk_seq, int32_t* chunk_start,
-                                                        int32_t* seq_chunk0) {
+                                                        int32_t* seq_chunk0, int32_t* cu_ok,
+                                                        int32_t* status) {
   __shared__ int32_t sc[256];
+  __shared__ unsigned long long h_sum, c_sum;
+  __shared__ int bad;
   const int t = threadIdx.x;
+  if (t == 0) {
+    h_sum = 0;
+    c_sum = 0;
+    bad = 0;
+  }
+  __syncthreads();
+  uint64_t h = 0, cs = 0;
+  int b = 0;
+  for (int s = t; s <= n_seqs; s += 256) {
+    const int32_t a = cu[s];
+    h += drla_cu_mix((uint64_t)s, (uint32_t)a);
+    if ((s == 0 && a != 0) || (s == n_seqs && (int64_t)a != T)) b = 1;
+    if (s < n_seqs) {
+      const int64_t L = (int64_t)cu[s + 1] - a;
+      const int64_t c = L > 0 ? (L + C - 1) / C : 0;
+      if (L < 0 || c > max_cps) b = 1;
+      cs += (uint64_t)c;
+    }
+  }
+  atomicAdd(&h_sum, (unsigned long long)h);
+  atomicAdd(&c_sum, (unsigned long long)cs);
+  if (b) atomicOr(&bad, 1);
+  __syncthreads();
+  const bool ok = bad == 0 && h_sum == hash && c_sum == (unsigned long long)nc;
+  if (!ok) {
+    for (int64_t c = t; c < nc; c += 256) {
+      chunk_seq[c] = -1;
+      chunk_start[c] = 0;
+    }
+    for (int s = t; s <= n_seqs; s += 256) {
+      seq_chunk0[s] = 0;
+      cu_ok[s] = 0;
+    }
+    if (t == 0) status[0] = 1;
+    return;
+  }
+  for (int s = t; s <= n_seqs; s += 256) cu_ok[s] = cu[s];
   int64_t carry = 0;
   for (int base = 0; base < n_seqs; base += 256) {
     const int s = base + t;
@@ -70,7 +121,10 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
     carry += sc[255];
     __syncthreads();
   }
-  if (t == 0) seq_chunk0[n_seqs] = (int32_t)carry;
+  if (t == 0) {
+    seq_chunk0[n_seqs] = (int32_t)carry;
+    status[0] = 0;
+  }
 }
 
 // Sequences ranked longest first (ties by index) for the scan's dealing
@@ -116,8 +170,9 @@ __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e
 //     tile I, m = 16 I; X_r e^{B_r - B_m} and K_i e^{B_m - B_i} are both
 //     at most |X_r|, |K_i| (any gate), and go to the 16-bit products;
 //   diagonal tiles: the tile's row 16 I + 8; the factors lie within
-//     e^{+-8 max|g|} and go to fp32 products (16x16x4 fp32 MFMA), so the
-//     gate need only satisfy 8 |g| < 88 per token and channel.
+//     e^{+-8 max|g|}, which bf16 and fp32 operands hold (fp16 ones go to
+//     fp32 products, 16x16x4 fp32 MFMA), so the gate need only satisfy
+//     8 |g| < 88 per token and channel.
 // The scan's operands K e^{B}, Q e^{B}, (K e^{B_n - B})^T and e^{B_n}
 // take non-positive exponents only.
 //
@@ -150,6 +205,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   __shared__ __attribute__((aligned(16))) float As_st[KDA ? 1 : C][TP];  // A (GDN)
   __shared__ __attribute__((aligned(16))) float bs[C];
   __shared__ __attribute__((aligned(16))) float betas[C];
+  __shared__ floatx4 pxch[KDA ? 64 : 1];  // KDA: one P^T tile passed between waves
   ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
   ET(*Qs)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: Q rows (phases 0-1)
   float(*Bl)[BP] = (float(*)[BP])(un + NT * KS_BYTES);  // KDA: B log2(e) (phases 0-1)
@@ -361,62 +417,102 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       pt[t] = zero4();
     }
     if constexpr (KDA) {
-      // Off-diagonal tiles about the first row of the row tile (factors at
-      // most 1), 16-bit products; diagonal tiles about the tile's row 8
-      // (factors within e^{+-8 max|g|}), fp32 products.  Tiles past the
-      // diagonal are not formed.
-      const float* refA = &Bl[16 * rt][0];
-      const float* refP = &Bl[16 * pr][0];
-      const int rA = 16 * rt + c16, rP = 16 * pr + c16;
+      // Tiles of A (row tile I, column tile J <= I) and of P^T (J, I), each
+      // factored about a reference row of its own so that no factor
+      // overflows:
+      //   J < I: the row tile's first row m = 16 I; rows (K and Q of tile I)
+      //     X_r e^{B_r - B_m}, columns K_i e^{B_m - B_i}, every factor at
+      //     most 1 for any gate; 16-bit products;
+      //   J = I: the tile's row c = 16 I + 8; factors within e^{+-8 max|g|},
+      //     products in the operand type (bf16 and fp32 hold them; fp32
+      //     products for fp16 operands).
+      // A tile and its P^T tile share their column operand and the K and Q
+      // rows of a tile share their factors, so a wave takes whole row tiles
+      // and diagonals, balanced by their exponentials (per lane and inner
+      // block: 8 per row tile, 8 per column tile, 16 per diagonal):
+      //   wave 0: row tile 3 against column tiles 0, 1, 2;
+      //   wave 1: row tile 2 against 0, 1, and diagonal 0;
+      //   wave 2: row tile 1 against 0, and diagonal 1;
+      //   wave 3: diagonals 2 and 3.
+      // acc[] and pt[] hold the wave's A and P^T tiles in that order.
+      constexpr bool kF32Diag = std::is_same<ET, f16>::value;
+      typedef typename std::conditional<kF32Diag, floatx8, V8>::type DV8;
+      // 2^{+-(Bl[r] - Bl[m])} at channels d .. d + 7
+      auto factors = [&](int r, int m, int d, bool right) -> floatx8 {
+        const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
+        const floatx4 m0 = *(const floatx4*)&Bl[m][d], m1 = *(const floatx4*)&Bl[m][d + 4];
+        floatx8 f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[j] = __builtin_amdgcn_exp2f(right ? m0[j] - b0[j] : b0[j] - m0[j]);
+          f[j + 4] = __builtin_amdgcn_exp2f(right ? m1[j] - b1[j] : b1[j] - m1[j]);
+        }
+        return f;
+      };
+      auto scaled = [&](const ET* xrow, int d, const floatx8& f) -> V8 {
+        const V4 x0 = *(const V4*)(xrow + d), x1 = *(const V4*)(xrow + d + 4);
+        V8 y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = (ET)(to_f(x0[j]) * f[j]);
+          y[j + 4] = (ET)(to_f(x1[j]) * f[j + 4]);
+        }
+        return y;
+      };
+      auto scaled_d = [&](const ET* xrow, int d, const floatx8& f) -> DV8 {
+        if constexpr (kF32Diag) {
+          const V4 x0 = *(const V4*)(xrow + d), x1 = *(const V4*)(xrow + d + 4);
+          floatx8 y;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            y[j] = to_f(x0[j]) * f[j];
+            y[j + 4] = to_f(x1[j]) * f[j + 4];
+          }
+          return y;
+        } else {
+          return scaled(xrow, d, f);
+        }
+      };
+      // row tile I against column tiles 0 .. nj-1, into acc[0 .. nj), pt[0 .. nj)
+      auto offdiag = [&](int I, int nj, int d) {
+        const int r = 16 * I + c16, m = 16 * I;
+        const floatx8 f = factors(r, m, d, false);
+        const V8 kr = scaled(&Ks[r][0], d, f), qr = scaled(&Qs[r][0], d, f);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          if (t < nj) {
+            const V8 kc = kda_frag(&Ks[16 * t + c16][0], &Bl[16 * t + c16][0], &Bl[m][0], d, true);
+            acc[t] = mma(kr, kc, acc[t]);
+            pt[t] = mma(kc, qr, pt[t]);
+          }
+        }
+      };
+      // diagonal tile I, into acc[sl], pt[sl]
+      auto diag = [&](int I, int sl, int d) {
+        const int r = 16 * I + c16, c = 16 * I + 8;
+        const floatx8 f = factors(r, c, d, false), gi = factors(r, c, d, true);
+        const DV8 kg = scaled_d(&Ks[r][0], d, gi);
+        acc[sl] = mma(scaled_d(&Ks[r][0], d, f), kg, acc[sl]);
+        pt[sl] = mma(kg, scaled_d(&Qs[r][0], d, f), pt[sl]);
+      };
 #pragma unroll
       for (int p = 0; p < KB; ++p) {
         const int d = 32 * p + 8 * g4;
-        const V8 ar = kda_frag(&Ks[rA][0], &Bl[rA][0], refA, d, false);
-        const V8 qr = kda_frag(&Qs[rP][0], &Bl[rP][0], refP, d, false);
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          if (t < rt) acc[t] = mma(ar, kda_frag(&Ks[16 * t + c16][0], &Bl[16 * t + c16][0], refA, d, true), acc[t]);
-          if (t < pr) pt[t] = mma(kda_frag(&Ks[16 * t + c16][0], &Bl[16 * t + c16][0], refP, d, true), qr, pt[t]);
+        if (wv == 0) {
+          offdiag(3, 3, d);
+        } else if (wv == 1) {
+          offdiag(2, 2, d);
+          diag(0, 2, d);
+        } else if (wv == 2) {
+          offdiag(1, 1, d);
+          diag(1, 1, d);
+        } else {
+          diag(2, 0, d);
+          diag(3, 1, d);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // diagonal: A tile (rt, rt) = (K e^{B - B_c}) (K e^{B_c - B})^T and
-      // P^T tile (pr, pr) = (K e^{B_c' - B}) (Q e^{B - B_c'})^T, row tile
-      // rows r, their middle rows c, c'
-      auto diag = [&](int r, int c, bool withq, floatx4 accd) -> floatx4 {
-#pragma unroll
-        for (int p = 0; p < KB; ++p) {
-          const int d = 32 * p + 8 * g4;
-          const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
-          const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
-          const floatx4 c0 = *(const floatx4*)&Bl[c][d], c1 = *(const floatx4*)&Bl[c][d + 4];
-          floatx8 lf, rf;
-          if (withq) {
-            const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              rf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(c0[j] - b0[j]);
-              lf[j] = to_f(q0[j]) * __builtin_amdgcn_exp2f(b0[j] - c0[j]);
-              rf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(c1[j] - b1[j]);
-              lf[j + 4] = to_f(q1[j]) * __builtin_amdgcn_exp2f(b1[j] - c1[j]);
-            }
-            accd = mma(rf, lf, accd);  // P^T: key token outer on the A side
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              lf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(b0[j] - c0[j]);
-              rf[j] = to_f(k0[j]) * __builtin_amdgcn_exp2f(c0[j] - b0[j]);
-              lf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(b1[j] - c1[j]);
-              rf[j + 4] = to_f(k1[j]) * __builtin_amdgcn_exp2f(c1[j] - b1[j]);
-            }
-            accd = mma(lf, rf, accd);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        return accd;
-      };
-      acc[rt] = diag(rA, 16 * rt + 8, false, acc[rt]);
-      pt[pr] = diag(rP, 16 * pr + 8, true, pt[pr]);
+      if (wv == 0) pxch[lane] = pt[2];  // P^T tile (2, 3), packed by wave 3
     } else {
       // Every wave multiplies its row tile with all four column tiles (the
       // products past the diagonal are dropped), so all K fragments are read
@@ -483,6 +579,50 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         pg[(pr * 2 + 1) * 64 + lane] = pfr[1];
       }
     };
+    // KDA: the tiles of the wave's assignment above
+    auto store_ap_kda = [&]() {
+      auto put_a = [&](int I, int J, const floatx4& v) {
+        const floatx4 betr = *(const floatx4*)&betas[16 * I + 4 * g4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * I + 4 * g4 + e, i = 16 * J + c16;
+          As[r][i] = (i < r && !P.decay_only) ? betr[e] * v[e] : 0.f;
+        }
+      };
+      // diagonal P^T tile (I, I): keys j <= query r
+      auto mask_p = [&](floatx4 v) -> floatx4 {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * g4 + e > c16) v[e] = 0.f;
+        return v;
+      };
+      V8* pg = (V8*)P.pm + ch * (8 * 64);
+      const floatx4 z = zero4();
+      // fragment (I, p) of P: P^T tiles J = 2p, 2p + 1 of row tile I
+      if (wv == 0) {
+        put_a(3, 0, acc[0]);
+        put_a(3, 1, acc[1]);
+        put_a(3, 2, acc[2]);
+        pg[6 * 64 + lane] = pack<ET>(pt[0], pt[1]);
+      } else if (wv == 1) {
+        put_a(2, 0, acc[0]);
+        put_a(2, 1, acc[1]);
+        put_a(0, 0, acc[2]);
+        pg[4 * 64 + lane] = pack<ET>(pt[0], pt[1]);
+        pg[0 * 64 + lane] = pack<ET>(mask_p(pt[2]), z);
+        pg[1 * 64 + lane] = pack<ET>(z, z);
+      } else if (wv == 2) {
+        put_a(1, 0, acc[0]);
+        put_a(1, 1, acc[1]);
+        pg[2 * 64 + lane] = pack<ET>(pt[0], mask_p(pt[1]));
+        pg[3 * 64 + lane] = pack<ET>(z, z);
+      } else {
+        put_a(2, 2, acc[0]);
+        put_a(3, 3, acc[1]);
+        pg[5 * 64 + lane] = pack<ET>(mask_p(pt[0]), z);
+        pg[7 * 64 + lane] = pack<ET>(pxch[lane], mask_p(pt[1]));
+      }
+    };
     if (!KDA) store_ap();
     // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
     // of state tile mt in the scan's row order, inner = token block p);
@@ -527,7 +667,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         qwg[f * 64 + lane] = xq;
       }
       __syncthreads();  // the B table is read; A takes its bytes
-      store_ap();
+      store_ap_kda();
     } else if (tid < C) {
       // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
       // holds e^{b_n} (rows past the end carry the last b)
@@ -722,10 +862,12 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
     return launch_prep_v<DK, false, ET, false>(P, nblk, st);
 }
 
-hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int32_t* sched, hipStream_t st) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu, n_seqs, nc, sched, sched + nc,
-                     sched + 2 * nc);
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0, st, cu, n_seqs,
+hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int64_t T, int64_t max_cps,
+                           uint64_t hash, int32_t* sched, hipStream_t st) {
+  int32_t* cu_ok = sched + drla_sched_cu(nc, n_seqs);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu, n_seqs, nc, T, max_cps, hash, sched,
+                     sched + nc, sched + 2 * nc, cu_ok, sched + drla_sched_status(nc, n_seqs));
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0, st, cu_ok, n_seqs,
                      sched + 2 * nc + n_seqs + 1);
   return hipGetLastError();
 }

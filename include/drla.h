@@ -104,7 +104,18 @@ size_t drla_workspace_bytes(const drla_problem* p,
  *   h0                    device [N,h_v,dk,dv] fp32 initial state, or NULL (zeros)
  *   cu_seqlens_dev/_host  the same [N+1] array on device and host, or both NULL
  *                         (with N = 1 the call is run, and its workspace laid
- *                         out, as the dense call; the arrays are not read)
+ *                         out, as the dense call; the arrays are not read).
+ *                         The host copy is validated here and sizes the
+ *                         launch and the workspace; the kernels take the
+ *                         lengths from the device copy, which the first
+ *                         kernel checks against the host copy (cu[0] = 0,
+ *                         non-decreasing, cu[N] = T, chunk counts, and a
+ *                         64-bit fingerprint of all N+1 entries).  If the
+ *                         two differ the call runs as N empty sequences: no
+ *                         token is read, o is left unwritten, ht = h0 (zeros
+ *                         without h0), and drla_prefill_status reports
+ *                         DRLA_ERR_SEQLENS; the call itself, asynchronous,
+ *                         has already returned DRLA_OK.
  *   o                     device output [T,h_v,dv] in io dtype
  *   ht                    device output [N,h_v,dk,dv] fp32 final state, or NULL;
  *                         may be exactly h0 (in-place state update)
@@ -302,6 +313,21 @@ drla_status drla_prefill_noalloc(int kda, int flags, const drla_problem* p,
                                  const float* h0, const int32_t* cu_seqlens_dev,
                                  const int32_t* cu_seqlens_host, void* o,
                                  float* ht, void* stream);
+
+/* Whether the device and host cu_seqlens of the last packed prefill call
+ * that used `workspace` agreed (see cu_seqlens_dev/_host at gdn_prefill).
+ * p and cu_seqlens_host: that call's; workspace: its workspace, or NULL for
+ * this GPU's drla_prefill_noalloc scratch (the current device's).  Waits
+ * for `stream` (the call's stream), then reads the status word the call's
+ * first kernel wrote into the workspace's schedule region.  Returns DRLA_OK
+ * if they agreed or the call was not packed (N = 1 or no cu_seqlens: no
+ * device lengths are read), DRLA_ERR_SEQLENS if they differed (or the word
+ * holds no status), DRLA_ERR_HIP if the read failed, and the validation
+ * errors of drla_workspace_bytes for a malformed p or cu_seqlens_host.
+ * Costs a device-to-host copy and a stream synchronisation: a debugging or
+ * checking aid, not part of the prefill. */
+drla_status drla_prefill_status(const drla_problem* p, const int32_t* cu_seqlens_host,
+                                const void* workspace, void* stream);
 
 const char* drla_status_str(drla_status s);
 const char* drla_last_error(void);

@@ -20,8 +20,8 @@ def lib():
     return _lib.load_library()
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(names))
@@ -34,7 +34,46 @@ def test_exports_every_declared_function(lib):
             "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 4
+    assert lib.drla_version() == 5
+
+
+def test_prefill_status_needs_no_device_for_unpacked_calls(lib):
+    """drla_prefill_status: a dense call (no cu_seqlens) or one packed
+    sequence reads no device lengths, so it is DRLA_OK without a device; a
+    malformed problem is refused."""
+    p = _prob(n_seqs=1, T=256)
+    assert lib.drla_prefill_status(ctypes.byref(p), None, None, None) == 0
+    cu, keep = _i32([0, 256])
+    assert lib.drla_prefill_status(ctypes.byref(p), cu, None, None) == 0
+    bad = _prob(n_seqs=2, T=256)
+    cu2, keep2 = _i32([0, 300, 256])
+    assert lib.drla_prefill_status(ctypes.byref(bad), cu2, None, None) == 5
+
+
+def test_peaks_library_exports_its_header():
+    """libdrla_peaks.so (the benchmark's attainable-peak kernels) exports
+    what include/drla_peaks.h declares and refuses bad arguments before any
+    launch."""
+    from delta_rule_linear_chunked_amd import build
+    if not os.path.exists(build.PEAKS_LIB):
+        build.build()
+    peaks = ctypes.CDLL(build.PEAKS_LIB)
+    names = _declared_functions(os.path.join(ROOT, "include", "drla_peaks.h"))
+    assert set(names) == {"drla_peak_copy", "drla_peak_mfma", "drla_peak_mfma_grid"}
+    for n in names:
+        assert hasattr(peaks, n), n
+    peaks.drla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_int, ctypes.c_void_p]
+    base = 1 << 40
+    assert peaks.drla_peak_copy(base, base + (1 << 30), 100, 0, None) == 1   # not a multiple of 64
+    assert peaks.drla_peak_copy(base, base + 64, 128, 0, None) == 1          # overlapping
+    assert peaks.drla_peak_copy(base + 8, base + (1 << 30), 128, 0, None) == 1  # misaligned
+    assert peaks.drla_peak_copy(None, base, 128, 0, None) == 1
+    peaks.drla_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert peaks.drla_peak_mfma(base, 3, 10, 1, None, None, None) == 1       # unknown kind
+    assert peaks.drla_peak_mfma(base, 0, 0, 1, None, None, None) == 1        # no iterations
+    assert peaks.drla_peak_mfma_grid(7) == 7
 
 
 def _prob(n_seqs=1, h_qk=2, h_v=4, dk=128, dv=128, io=0, T=256):
