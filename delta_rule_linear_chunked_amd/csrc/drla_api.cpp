@@ -139,7 +139,7 @@ static int32_t hs_count(const drla_problem* p, int64_t max_cps, bool kda, int fl
 // does not take.
 static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
   if (uses_hs(p, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
-  if (kda || p->io_dtype == DRLA_F32 || p->dk != p->dv || p->n_seqs < 1) return 1;
+  if (p->dk != p->dv || p->n_seqs < 1) return 1;
   return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
 }
 
@@ -174,8 +174,8 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, 
   if (keep) off = align_up(off + ncH * DRLA_CHUNK * p->dv * es);
   L->h = keep ? off : 0;
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
-  // Segment-split per-16-column scan (scalar-gate calls with 16-bit inputs
-  // and dk = dv that leave most of a 256-CU chip idle): its states and G
+  // Segment-split per-16-column scan (calls with dk = dv that leave most of
+  // a 256-CU chip idle): its states and G
   const int32_t np = seg_count(p, max_cps, kda, flags);
   L->seg = np > 1 ? off : 0;
   if (np > 1)

@@ -63,7 +63,7 @@ struct ScanParams {
   int32_t h_qk, h_v, grp;
   int64_t nc;
   int32_t decay_only;  // no delta rule: R = V (no X term)
-  SegParams seg;       // LDS-fed scan only
+  SegParams seg;       // segment mode (both per-16-column scans)
 };
 
 // Head-resident scan (drla_hscan.hip): GDN and decay-only linear attention

@@ -123,13 +123,14 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   // (scan_item); the grid covers whole groups
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
   int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
-  // Segment mode (SegParams): a dense call whose scan leaves most of the
-  // chip idle takes np segments, as many as let all (2 np - 1) K scan
-  // workgroups (one per compute unit: the scan's LDS) run at once.  (With
-  // more workgroups than compute units the scan's period per chunk grows
-  // with the occupancy more than the shorter segments save.)
+  // Segment mode (SegParams): a call whose scan leaves most of the chip
+  // idle takes np segments, as many as let all (2 np - 1) K scan workgroups
+  // (one per compute unit) run at once.  (With more workgroups than compute
+  // units the scan's period per chunk grows with the occupancy more than
+  // the shorter segments save.)  Both scans take it: the LDS-fed one (GDN,
+  // 16-bit) and the register-fed one (KDA, fp32).
   bool seg = false;
-  if constexpr (kLdsScan && DK == DV) {
+  if constexpr (DK == DV) {
     const int64_t K = units * (DV / 16);
     const int cus = device_cus();
     int32_t np = cus > 0 ? drla_seg_count(K, a->max_cps, cus) : 1;
@@ -155,7 +156,7 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     else
       e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
   }
-  if constexpr (kLdsScan && DK == DV) {
+  if constexpr (DK == DV) {
     if (seg && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);
     if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, (int32_t)a->max_cps, st);
   }

@@ -58,10 +58,12 @@ struct ScanOps {
 };
 
 struct ScanCtx {
-  int64_t ts;    // first token of the sequence
-  int64_t te;    // one past its last token
+  int64_t ts;    // first token of the sequence (of the segment, in segment mode)
+  int64_t te;    // one past the sequence's last token
   int64_t c0;    // workspace index of its first chunk
   int h, hk, nb, w, lane;
+  bool vzero;    // V read as zero (segment transition blocks)
+  void* obase;   // o, or G for segment transition blocks
 };
 
 // The six nonzero Tb fragments (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) sit at
@@ -130,7 +132,7 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
     o.gam = bload<float>(gr, last);
   }
   const size_t vrow = (size_t)P.h_v * DV;
-  o.orsrc = make_rsrc((ET*)P.o + t0 * vrow, len * vrow * es);
+  o.orsrc = make_rsrc((ET*)x.obase + t0 * vrow, len * vrow * es);
   if constexpr (RING) return;
   const rsrc_t ktr = make_rsrc((const V8*)P.kt + ch * (C * DK / 8), C * DK * es);
 #pragma unroll
@@ -143,7 +145,7 @@ __device__ __forceinline__ void scan_load(ScanOps<DK, KDA, ET>& o, const ScanPar
   const rsrc_t pmr = make_rsrc((const V8*)P.pm + ch * (8 * 64), 8 * 64 * sizeof(V8));
   o.pb[0] = fload<V8>(pmr, loff, 2 * w);
   o.pb[1] = fload<V8>(pmr, loff, 2 * w + 1);  // zero for w < 2
-  const rsrc_t vr = make_rsrc((const ET*)P.v + t0 * vrow, len * vrow * es);
+  const rsrc_t vr = make_rsrc((const ET*)P.v + t0 * vrow, x.vzero ? 0u : (uint32_t)(len * vrow * es));
   o.vv = bload<V4>(vr, (uint32_t)(((size_t)rw * P.h_v + x.h) * DV + 16 * x.nb + 4 * g4) * es);
 }
 
@@ -164,7 +166,15 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g4 = lane >> 4, c16 = lane & 15;
   int seq, h, nb;
-  if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) return;  // the whole workgroup: past the last unit
+  int kind = 0, sg = 0;  // 0: whole sequence; segment mode: 1, 2, 3 and the segment (seg_item)
+  if (P.seg.s1 > 0) {
+    int unit;
+    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, unit, nb, kind, sg);
+    seq = unit / P.h_v;
+    h = unit - seq * P.h_v;
+  } else if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) {
+    return;  // the whole workgroup: past the last unit
+  }
 
   ScanCtx x;
   x.h = h;
@@ -186,6 +196,27 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
     x.c0 = (int64_t)seq * P.s.cps;
     n = P.s.cps;
   }
+  if (kind > 0) {
+    // segment sg of this sequence: chunks [sg s1, (sg + 1) s1), the last to
+    // the end, s1 = n / np (0 for a sequence of fewer chunks than segments:
+    // its last segment takes them all)
+    const int64_t s1 = n / P.seg.np;
+    if (kind == 1) {
+      n = s1;
+    } else {
+      x.ts += (int64_t)C * s1 * sg;
+      x.c0 += s1 * sg;
+      n = sg == P.seg.np - 1 ? n - s1 * sg : s1;
+    }
+  }
+  // segment transition blocks (kind 3) scan V = 0 from the identity and
+  // write G in place of o; the final state goes to ht, or to the segment
+  // mode's state sets
+  x.vzero = kind == 3;
+  x.obase = kind == 3 ? P.seg.g : P.o;
+  float* const sout = kind == 0   ? P.ht
+                      : kind == 1 ? P.seg.mid
+                                  : (kind == 2 ? P.seg.n : P.seg.m) + (int64_t)(sg - 1) * P.seg.us;
   const int col = 16 * nb + c16;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
 
@@ -219,7 +250,8 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
           const int64_t t0 = x.ts + (int64_t)C * i;
           const int64_t left = x.te - t0;
           const uint32_t len = (uint32_t)(left < C ? left : C);
-          const rsrc_t vr = make_rsrc((const ET*)P.v + (t0 * P.h_v + h) * DV + 16 * nb, (len - 1) * vstride + 32);
+          const rsrc_t vr = make_rsrc((const ET*)P.v + (t0 * P.h_v + h) * DV + 16 * nb,
+                                      x.vzero ? 0u : (len - 1) * vstride + 16 * es);
           lds_dma16(vr, voff, 0, &sl.v[0][0]);
           lds_dma16(vr, voff + 32 * vstride, 0, &sl.v[32][0]);
         }
@@ -258,8 +290,12 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[m][e] = P.h0 ? P.h0[sbase + (int64_t)state_row(w * MT + m, 4 * g4 + e) * DV + col] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int row = state_row(w * MT + m, 4 * g4 + e);
+      S[m][e] = kind == 3                 ? (row == col ? 1.f : 0.f)
+                : kind != 2 && P.h0 ? P.h0[sbase + (int64_t)row * DV + col]
+                                    : 0.f;
+    }
   auto put_state = [&]() {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -446,12 +482,23 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
       }
     }
   }
-  if (P.ht) {
+  if (sout) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        P.ht[sbase + (int64_t)state_row(w * MT + m, 4 * g4 + e) * DV + col] = S[m][e];
+        sout[sbase + (int64_t)state_row(w * MT + m, 4 * g4 + e) * DV + col] = S[m][e];
+  }
+  if (kind == 1) {
+    // the same state as the fix-up's A fragments (outer = column, inner =
+    // key channels 32p + 8g + j) in the io type, each wave its own tiles
+    // (half a fragment each, as put_state packs them)
+    V8* mf = (V8*)P.seg.midf + (((int64_t)seq * P.h_v + h) * NB + nb) * (KB * 64);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mt = w * MT + m;
+      ((V4*)&mf[(mt >> 1) * 64 + lane])[mt & 1] = pack4<ET>(S[m]);
+    }
   }
 }
 

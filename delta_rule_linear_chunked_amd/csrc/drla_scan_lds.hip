@@ -615,16 +615,17 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
 #pragma unroll
   for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
   __syncthreads();
-  const uint32_t kstride = (uint32_t)P.h_v * DK * 2;  // G has o's layout
+  constexpr uint32_t es = sizeof(T);
+  const uint32_t kstride = (uint32_t)P.h_v * DK * es;  // G has o's layout
   // lane: columns 16 ct + 4g + e of token 16 w + c
-  const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * 2;
-  const uint32_t goff = (uint32_t)(16 * w + c16) * kstride + (uint32_t)(8 * g4) * 2;
+  const uint32_t off0 = (uint32_t)(((16 * w + c16) * P.h_v + h) * DV + 4 * g4) * es;
+  const uint32_t goff = (uint32_t)(16 * w + c16) * kstride + (uint32_t)(8 * g4) * es;
   auto rsrcs = [&](int c, rsrc_t& gr, rsrc_t& orr) {
     const int64_t t0 = ts + (int64_t)c * C;
     const int64_t left = te - t0;
     const uint32_t len = (uint32_t)(left < C ? left : C);
-    gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * 2);
-    orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+    gr = make_rsrc((const T*)P.seg.g + (t0 * P.h_v + h) * DK, (len - 1) * kstride + DK * es);
+    orr = make_rsrc((T*)P.o + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * es));
   };
   // the next chunk's G and o are loaded while this one is multiplied and stored
   rsrc_t gr, orr;
@@ -632,9 +633,9 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
   H8 gf[KB];
   H4 ov[CT];
 #pragma unroll
-  for (int p = 0; p < KB; ++p) gf[p] = bload<H8>(gr, goff + 64 * p);
+  for (int p = 0; p < KB; ++p) gf[p] = bload<H8>(gr, goff + 32 * es * p);
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 32 * ct);
+  for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 16 * es * ct);
   for (int c = cb; c < cend; ++c) {
     rsrc_t grn = gr, orn = orr;
     H8 gn[KB];
@@ -642,9 +643,9 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
     if (c + 1 < cend) {
       rsrcs(c + 1, grn, orn);
 #pragma unroll
-      for (int p = 0; p < KB; ++p) gn[p] = bload<H8>(grn, goff + 64 * p);
+      for (int p = 0; p < KB; ++p) gn[p] = bload<H8>(grn, goff + 32 * es * p);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) on[ct] = bload<H4>(orn, off0 + 32 * ct);
+      for (int ct = 0; ct < CT; ++ct) on[ct] = bload<H4>(orn, off0 + 16 * es * ct);
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -654,7 +655,7 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
       floatx4 sum;
 #pragma unroll
       for (int e = 0; e < 4; ++e) sum[e] = to_f(ov[ct][e]) + acc[e];
-      bstore(orr, off0 + 32 * ct, pack4<T>(sum));
+      bstore(orr, off0 + 16 * es * ct, pack4<T>(sum));
     }
     gr = grn;
     orr = orn;
@@ -693,6 +694,8 @@ DRLA_SEG_INST(64, bf16)
 DRLA_SEG_INST(128, bf16)
 DRLA_SEG_INST(64, f16)
 DRLA_SEG_INST(128, f16)
+DRLA_SEG_INST(64, float)
+DRLA_SEG_INST(128, float)
 #undef DRLA_SEG_INST
 
 template <int DK, int DV, typename T>

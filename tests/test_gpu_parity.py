@@ -387,6 +387,13 @@ def test_workload_gdn_long_h2(drla):
     _workload(drla, "gdn_long_h2")
 
 
+def test_workload_kda_long_h2(drla):
+    """One 65,536-token KDA sequence with 2 heads: the register-fed scan's
+    segment split at 8 segments, against the oracle over the whole
+    sequence."""
+    _workload(drla, "kda_long_h2")
+
+
 def test_workload_gdn_prefill(drla):
     _workload(drla, "gdn_prefill")
 

@@ -189,7 +189,7 @@ def test_workspace_bytes_and_layout(lib):
     assert lay.qw - lay.kw == per * 64 * 128 * 2
     assert lay.gam - lay.qw == per * 64 * 128 * 2
     assert lay.total - lay.gam == per * 128 * 4
-    assert lay.vp == 0 and lay.h == 0 and lay.seg == 0   # KDA: no segment-split scan
+    assert lay.vp == 0 and lay.h == 0 and lay.seg == 0   # 16 x 8 blocks: no segment split
     # GDN with bf16 inputs needs neither K~^T nor the KDA operands; its decay
     # factors are 2 x 64 floats per chunk
     gl = Layout()
@@ -276,23 +276,26 @@ SEG_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("kda,io", [(0, 0), (1, 0), (1, 2), (0, 1), (1, 1)])
 @pytest.mark.parametrize("h_v,d,lens", SEG_SHAPES)
-def test_segment_region_follows_the_count_rule(lib, h_v, d, lens):
-    """The seg region holds mid, np - 1 sets of N and M (fp32), np - 1
-    entering states in bf16, and G [T, h_v, d] in bf16."""
+def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
+    """The seg region (GDN and KDA, every io type) holds mid, np - 1 sets of
+    N and M (fp32), np - 1 entering states in the io type, and G
+    [T, h_v, d] in the io type."""
     from delta_rule_linear_chunked_amd._lib import Layout
     n, T = len(lens), sum(lens)
-    p = _prob(n_seqs=n, h_qk=1, h_v=h_v, dk=d, dv=d, io=0, T=T)
+    es = 4 if io == 1 else 2
+    p = _prob(n_seqs=n, h_qk=1, h_v=h_v, dk=d, dv=d, io=io, T=T)
     cu, _c = _i32([0] + [sum(lens[:i + 1]) for i in range(n)])
     lay = Layout()
-    assert lib.drla_workspace_layout(0, ctypes.byref(p), cu if n > 1 else None, 0, ctypes.byref(lay)) == 0
+    assert lib.drla_workspace_layout(kda, ctypes.byref(p), cu if n > 1 else None, 0, ctypes.byref(lay)) == 0
     np_ = _seg_np(n * h_v * d // 16, max((L + 63) // 64 for L in lens))
     if np_ == 1:
         assert lay.seg == 0
         return
     us = n * h_v * d * d
     assert lay.seg > 0
-    assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * 2 + T * h_v * d * 2
+    assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * es + T * h_v * d * es
 
 
 def _hs_np(units, max_cps, cus=256):

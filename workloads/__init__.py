@@ -116,6 +116,8 @@ DECAY_WORKLOADS = {
 FEW_HEAD_WORKLOADS = {
     "gdn_long_h2": Spec("gdn_long_h2", "gdn", (65536,), 2, 2, 128, 128, "bf16",
                         0.001, 0.05, 0.02, seed=9),
+    "kda_long_h2": Spec("kda_long_h2", "kda", (65536,), 2, 2, 128, 128, "bf16",
+                        0.001, 0.05, 0.02, seed=10),
 }
 
 
