@@ -111,13 +111,14 @@ class Hip:
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources and headers of the library; a traffic
-    figure measured on other sources no longer describes these kernels."""
+    """sha256 over the HIP sources and headers of the library (not the
+    peak microbenchmarks); a traffic figure measured on other sources no
+    longer describes these kernels."""
     import hashlib
     csrc = os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h")) and name != "drla_peaks.hip":
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -233,21 +234,19 @@ PEAKS_LIB = os.path.join(ROOT, "delta_rule_linear_chunked_amd", "_build", "libdr
 
 def measure_peaks(torch, hip, stream, io):
     """Attainable peaks of this GPU: HBM bandwidth of a streaming copy (2 GiB
-    read + 2 GiB written, the best of three grid sizes) and MFMA throughput
+    read + 2 GiB written) and MFMA throughput
     of chains of dependent MFMAs in the workload's dtype (bf16 and fp16
-    16x16x32, fp32 16x16x4).  Each figure is the best of five launches'
-    mean, timed with HIP events on `stream`."""
+    16x16x32, fp32 16x16x4).  Each figure is the mean of five launches
+    after two untimed ones, timed with HIP events on `stream`."""
     if not os.path.exists(PEAKS_LIB):
         raise RuntimeError(f"{PEAKS_LIB} is not built (run __graft_entry__.build())")
     lib = ctypes.CDLL(PEAKS_LIB)
-    lib.drla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                   ctypes.c_void_p]
+    lib.drla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.drla_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int)]
     lib.drla_peak_mfma_grid.argtypes = [ctypes.c_int]
     dev = torch.device("cuda:0")
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     e0, e1 = hip.event(), hip.event()
     sp = ctypes.c_void_p(stream)
 
@@ -264,16 +263,13 @@ def measure_peaks(torch, hip, stream, io):
     nbytes = 2 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    best_bw, best_blocks = 0.0, 0
-    for per_cu in (8, 16, 32):
-        def launch(b=per_cu * cus):
-            rc = lib.drla_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                    nbytes, b, sp)
-            if rc != 0:
-                raise RuntimeError(f"drla_peak_copy failed ({rc})")
-        bw = 2 * nbytes / (timed(launch) * 1e-3) / 1e9
-        if bw > best_bw:
-            best_bw, best_blocks = bw, per_cu * cus
+
+    def launch():
+        rc = lib.drla_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                nbytes, sp)
+        if rc != 0:
+            raise RuntimeError(f"drla_peak_copy failed ({rc})")
+    best_bw = 2 * nbytes / (timed(launch) * 1e-3) / 1e9
     torch.cuda.synchronize()
     if not torch.equal(dst[:: (1 << 20)], src[:: (1 << 20)]):
         raise RuntimeError("peak copy produced wrong data")
@@ -295,8 +291,8 @@ def measure_peaks(torch, hip, stream, io):
     hip.destroy(e0)
     hip.destroy(e1)
     return {"hbm_copy_gbs": round(best_bw, 1),
-            "hbm_copy": f"2 GiB read + 2 GiB written, 16-byte non-temporal loads/stores, "
-                        f"{best_blocks} workgroups of 256",
+            "hbm_copy": "2 GiB read + 2 GiB written, one 16-byte non-temporal load and store "
+                        "per thread",
             "mfma_tflops": round(tflops, 1),
             "mfma": f"{['bf16 16x16x32', 'fp16 16x16x32', 'fp32 16x16x4'][kind]}, 8 dependent "
                     f"chains per wave, {grid} workgroups of 4 waves, {iters} rounds"}

@@ -21,19 +21,14 @@ int cu_count() {
   return cus;
 }
 
-// Each thread moves four 16-byte vectors per trip, all four loads issued
-// before the first store.  n4 counts groups of four vectors (64 bytes).
+// One 16-byte vector per thread, non-temporal both ways, one workgroup per
+// 4 KiB: of the forms measured on the MI355X (grid-stride loops with 2 to 8
+// vectors per thread, block tiles of 2 to 8 vectors, plain or non-temporal
+// accesses, hipMemcpy) the fastest.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
-                                                   u32x4* __restrict__ dst, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
-    const int64_t base = (i / 256) * 1024 + (i % 256);  // 256-thread groups of 4 x 256 vectors
-    u32x4 x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = __builtin_nontemporal_load(&src[base + 256 * j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(x[j], &dst[base + 256 * j]);
-  }
+                                                   u32x4* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
 // Eight accumulator chains per wave; every MFMA of a chain waits for the
@@ -76,38 +71,17 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int 
 
 }  // namespace
 
-extern "C" int drla_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
-  if (!src || !dst || bytes == 0 || bytes % 64 != 0) return 1;
+extern "C" int drla_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16 != 0) return 1;
   if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return 1;
   const char* s = (const char*)src;
   const char* d = (const char*)dst;
   if (s < d + bytes && d < s + bytes) return 1;
-  const int64_t n4 = (int64_t)(bytes / 64);
-  // the index map moves whole groups of 1024 vectors; a tail that is not a
-  // whole group goes through a second launch with its own base
-  const int64_t whole = (n4 / 256) * 256;
-  if (blocks <= 0) {
-    const int cus = cu_count();
-    if (cus <= 0) return 2;
-    blocks = 16 * cus;
-  }
-  hipStream_t st = (hipStream_t)stream;
-  if (whole > 0) {
-    const int64_t need = whole / 256;
-    const int grid = (int)(need < blocks ? need : blocks);
-    copy_kernel<<<grid, 256, 0, st>>>((const u32x4*)src, (u32x4*)dst, whole);
-    if (hipGetLastError() != hipSuccess) return 2;
-  }
-  const int64_t rest = n4 - whole;  // < 256 groups of 64 bytes
-  if (rest > 0) {
-    const size_t off = (size_t)whole * 64;
-    // rest groups of four vectors laid out with stride 256 vectors would
-    // overrun; copy the tail as plain bytes
-    if (hipMemcpyAsync((char*)dst + off, (const char*)src + off, (size_t)rest * 64,
-                       hipMemcpyDeviceToDevice, st) != hipSuccess)
-      return 2;
-  }
-  return 0;
+  const int64_t n = (int64_t)(bytes / 16);
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffff) return 1;
+  copy_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((const u32x4*)src, (u32x4*)dst, n);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 extern "C" int drla_peak_mfma_grid(int blocks) {

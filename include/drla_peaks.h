@@ -20,12 +20,11 @@
 extern "C" {
 #endif
 
-/* dst[0 .. bytes) = src[0 .. bytes): 16-byte non-temporal loads and stores,
- * four per thread in flight, a grid of `blocks` 256-thread workgroups
- * striding over the buffer (blocks <= 0: 16 per compute unit).  `bytes` must
- * be a positive multiple of 64 and src, dst 16-byte aligned and disjoint.
- * The caller owns both buffers. */
-int drla_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
+/* dst[0 .. bytes) = src[0 .. bytes): one 16-byte non-temporal load and
+ * store per thread, one 256-thread workgroup per 4 KiB.  `bytes` must be a
+ * positive multiple of 16, at most 2^31 workgroups' worth, and src, dst
+ * 16-byte aligned and disjoint.  The caller owns both buffers. */
+int drla_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Matrix-core throughput: `blocks` workgroups of 256 threads (blocks <= 0:
  * 8 per compute unit), every wave runs `iters` rounds of 8 independent

@@ -63,12 +63,12 @@ def test_peaks_library_exports_its_header():
     for n in names:
         assert hasattr(peaks, n), n
     peaks.drla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                     ctypes.c_int, ctypes.c_void_p]
+                                     ctypes.c_void_p]
     base = 1 << 40
-    assert peaks.drla_peak_copy(base, base + (1 << 30), 100, 0, None) == 1   # not a multiple of 64
-    assert peaks.drla_peak_copy(base, base + 64, 128, 0, None) == 1          # overlapping
-    assert peaks.drla_peak_copy(base + 8, base + (1 << 30), 128, 0, None) == 1  # misaligned
-    assert peaks.drla_peak_copy(None, base, 128, 0, None) == 1
+    assert peaks.drla_peak_copy(base, base + (1 << 30), 100, None) == 1   # not a multiple of 16
+    assert peaks.drla_peak_copy(base, base + 64, 128, None) == 1          # overlapping
+    assert peaks.drla_peak_copy(base + 8, base + (1 << 30), 128, None) == 1  # misaligned
+    assert peaks.drla_peak_copy(None, base, 128, None) == 1
     peaks.drla_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert peaks.drla_peak_mfma(base, 3, 10, 1, None, None, None) == 1       # unknown kind
