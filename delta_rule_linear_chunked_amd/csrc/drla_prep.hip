@@ -49,15 +49,8 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
                                                         int32_t* seq_chunk0, int32_t* cu_ok,
                                                         int32_t* status) {
   __shared__ int32_t sc[256];
-  __shared__ unsigned long long h_sum, c_sum;
-  __shared__ int bad;
+  __shared__ unsigned long long red[3][4];  // per wave: fingerprint, chunks, failed checks
   const int t = threadIdx.x;
-  if (t == 0) {
-    h_sum = 0;
-    c_sum = 0;
-    bad = 0;
-  }
-  __syncthreads();
   uint64_t h = 0, cs = 0;
   int b = 0;
   for (int s = t; s <= n_seqs; s += 256) {
@@ -71,11 +64,25 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
       cs += (uint64_t)c;
     }
   }
-  atomicAdd(&h_sum, (unsigned long long)h);
-  atomicAdd(&c_sum, (unsigned long long)cs);
-  if (b) atomicOr(&bad, 1);
+  // sums over the workgroup: within each wave by shuffles, then the four
+  // waves' partial sums through LDS (no atomics)
+  uint64_t bb = (uint64_t)b;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    h += __shfl_xor(h, off);
+    cs += __shfl_xor(cs, off);
+    bb |= __shfl_xor(bb, off);
+  }
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = h;
+    red[1][t >> 6] = cs;
+    red[2][t >> 6] = bb;
+  }
   __syncthreads();
-  const bool ok = bad == 0 && h_sum == hash && c_sum == (unsigned long long)nc;
+  const uint64_t h_sum = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const uint64_t c_sum = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const bool ok = (red[2][0] | red[2][1] | red[2][2] | red[2][3]) == 0 && h_sum == hash &&
+                  c_sum == (uint64_t)nc;
   if (!ok) {
     for (int64_t c = t; c < nc; c += 256) {
       chunk_seq[c] = -1;
