@@ -121,16 +121,22 @@ static int64_t max_chunks(const drla_problem* p, const int32_t* cu_host) {
 
 constexpr int kKnownFlags = DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL | DRLA_HEAD_SCAN;
 
-// The head-resident scan (DRLA_HEAD_SCAN) serves scalar-gate calls with
-// 16-bit inputs (GDN, decay-only) that keep no intermediates.
-static bool uses_hs(const drla_problem* p, bool kda, int flags) {
-  return (flags & DRLA_HEAD_SCAN) && !kda && p->io_dtype != DRLA_F32 && !(flags & DRLA_KEEP_INTERMEDIATES);
+// The head-resident scan serves scalar-gate calls with 16-bit inputs (GDN,
+// decay-only) that keep no intermediates: always with DRLA_HEAD_SCAN, and
+// without flags where its timing model predicts it faster
+// (drla_auto_head_scan, at 256 compute units like the workspace); with
+// DRLA_SERIAL alone the per-16-column scan runs in one pass.
+static bool uses_hs(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
+  if (kda || p->io_dtype == DRLA_F32 || (flags & DRLA_KEEP_INTERMEDIATES)) return false;
+  if (flags & DRLA_HEAD_SCAN) return true;
+  if (flags & DRLA_SERIAL) return false;
+  return p->n_seqs >= 1 && drla_auto_head_scan((int64_t)p->n_seqs * p->h_v, max_cps, p->dk, p->dv, 256);
 }
 
 // Segments per sequence the hs region provides for (drla_hs_count at 256
 // compute units; one pass when dk != dv or with DRLA_SERIAL).
 static int32_t hs_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
-  if (!uses_hs(p, kda, flags) || p->dk != p->dv || (flags & DRLA_SERIAL) || p->n_seqs < 1) return 1;
+  if (!uses_hs(p, max_cps, kda, flags) || p->dk != p->dv || (flags & DRLA_SERIAL) || p->n_seqs < 1) return 1;
   return drla_hs_count((int64_t)p->n_seqs * p->h_v, max_cps, 256);
 }
 
@@ -138,7 +144,7 @@ static int32_t hs_count(const drla_problem* p, int64_t max_cps, bool kda, int fl
 // at 256 compute units, over the longest sequence); 1 for calls the split
 // does not take.
 static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
-  if (uses_hs(p, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
+  if (uses_hs(p, max_cps, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
   if (p->dk != p->dv || p->n_seqs < 1) return 1;
   return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
 }
@@ -280,7 +286,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.decay_only = decay ? 1 : 0;
   a.serial = (flags & DRLA_SERIAL) ? 1 : 0;
-  a.head_scan = uses_hs(p, kda, flags) ? 1 : 0;
+  a.head_scan = uses_hs(p, max_cps, kda, flags) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);

@@ -36,6 +36,24 @@ static inline int32_t drla_hs_count(int64_t units, int64_t max_cps, int64_t cus)
   return np < 3 ? 1 : (int32_t)np;
 }
 
+// Whether a call without DRLA_HEAD_SCAN or DRLA_SERIAL takes the
+// head-resident scan: GDN or decay-only, 16-bit inputs, dk = dv = 128 (the
+// shapes its timing model was measured on), when the model predicts it at
+// least 10 % faster than the per-16-column scan.  Scan-stage models from
+// MI355X measurements (microseconds, n chunks of the longest sequence):
+// head-resident 36 + 8.5 ceil(n / np_hs); per-16-column 0.9 ceil(n / np_seg)
+// plus 12 for the compose and fix-up when it splits.
+static inline bool drla_auto_head_scan(int64_t units, int64_t max_cps, int32_t dk, int32_t dv,
+                                       int64_t cus) {
+  if (dk != 128 || dv != 128 || units <= 0 || max_cps <= 0) return false;
+  const int32_t nh = drla_hs_count(units, max_cps, cus);
+  if (nh < 3) return false;
+  const int32_t ns = drla_seg_count(units * (dv / 16), max_cps, cus);
+  const double t_head = 36.0 + 8.5 * (double)((max_cps + nh - 1) / nh);
+  const double t_col = 0.9 * (double)((max_cps + ns - 1) / ns) + (ns > 1 ? 12.0 : 0.0);
+  return t_head < 0.9 * t_col;
+}
+
 // Bytes of the head-resident scan's region for `units` units, np segments,
 // dk x dv states and io elements of `es` bytes: np - 1 fp32 state sets, then
 // np - 2 segment maps (dk x dk, io type).

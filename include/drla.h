@@ -202,8 +202,8 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY,
  *                 DRLA_SERIAL and DRLA_HEAD_SCAN, or 0.
  *                 The state scan runs one workgroup per (sequence, head,
- *                 16 state columns).  Scalar-gate calls with 16-bit inputs
- *                 and dk == dv whose U = n_seqs * h_v * dv/16 column blocks
+ *                 16 state columns).  Calls with dk == dv whose
+ *                 U = n_seqs * h_v * dv/16 column blocks
  *                 leave most of the device idle split every sequence's
  *                 chunks into np segments (n / np chunks each, the last
  *                 takes the rest) that are scanned at once: np the most up
@@ -220,9 +220,14 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *                 with n_seqs h_v np at most the compute units (at most
  *                 256), np^2 <= 9 n_max, at least two chunks per segment of
  *                 the longest sequence (n_max chunks) and np <= 128; fewer
- *                 than three segments run one pass.
+ *                 than three segments run one pass.  Without flags,
+ *                 scalar-gate calls with 16-bit inputs and dk = dv = 128
+ *                 take the head-resident scan where its measured timing
+ *                 model predicts it at least 10% faster (8 to 16 heads and
+ *                 long sequences; the rule is the one in the library's
+ *                 launch header, drla_auto_head_scan, at 256 compute units).
  *                 DRLA_SERIAL runs either scan in one pass (same results up
- *                 to rounding).
+ *                 to rounding); alone it selects the per-16-column scan.
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels
@@ -267,14 +272,14 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *   vp, h (only with DRLA_KEEP_INTERMEDIATES, else 0): V' (outer value tile,
  *        inner token block, index tile*2 + block) and the state entering the
  *        chunk (outer value tile, inner key block, index tile*(dk/32) + block)
- *   seg (calls with a scalar gate, 16-bit inputs and dk == dv that the
- *        segment split takes on a 256-CU device, else 0):
+ *   seg (calls with dk == dv that the segment split takes on a 256-CU
+ *        device, else 0):
  *        for np segments, the fp32 state after the first segment, np - 1
  *        zero-start final states and np - 1 maps of the entering state
  *        (fp32, per (sequence, head)), np - 1 entering states as io-type
  *        fragments, then the maps' contribution to o per token, laid out as o
- *   hs (DRLA_HEAD_SCAN calls that split into np > 1 segments on a 256-CU
- *        device, else 0): np - 1 fp32 state sets of dk x dv per (sequence, head) unit
+ *   hs (head-resident scan calls that split into np > 1 segments on a
+ *        256-CU device, else 0): np - 1 fp32 state sets of dk x dv per (sequence, head) unit
  *        (the segments' zero-start final states, replaced in place by the
  *        states entering segments 1 .. np - 1), then np - 2 segment maps of
  *        dk x dk per unit in io type

@@ -92,3 +92,33 @@ def test_head_scan_repeatable(drla):
     a = _run(drla, x, drla.HEAD_SCAN)
     b = _run(drla, x, drla.HEAD_SCAN)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("h_v,T,io", [(16, 16384, "bf16"), (8, 16384, "f16")])
+def test_automatic_head_scan(drla, h_v, T, io):
+    """Without flags the call takes the head-resident scan at these shapes
+    (its timing model predicts it faster; the layout shows the hs region):
+    against the oracle and against the per-16-column scan (DRLA_SERIAL)."""
+    print(f"case automatic head scan h_v={h_v} T={T} io={io}", flush=True)
+    # weak gates, so that the state entering each segment still matters
+    spec = W.small_spec("gdn", lens=(T,), h_qk=h_v // 2, h_v=h_v, dk=128, dv=128, io=io,
+                        g_lo=0.001, g_hi=0.05, h0_std=0.05, seed=61)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    lay = drla.workspace_layout(d["q"].shape, d["v"].shape, d["q"].dtype)
+    assert lay["hs"] > 0 and lay["seg"] == 0, "the layout should show the head-resident scan"
+    ws = torch.full((lay["total"],), 255, dtype=torch.uint8, device="cuda")
+    o, ht = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], workspace=ws)
+    torch.cuda.synchronize()
+    first_set = ws[lay["hs"]:lay["hs"] + h_v * 128 * 128 * 4].view(torch.float32)
+    assert bool(torch.isfinite(first_set).all()), "the head-resident split did not run"
+    o1, ht1 = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    o, o1 = o.float().cpu().numpy(), o1.float().cpu().numpy()
+    ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
+    o_ref, ht_ref = run_oracle(x)
+    tol = TOL[io]
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e} (column scan {rel_err(o1, o_ref):.3e})", flush=True)
+    assert np.isfinite(o).all() and eo <= tol and eh <= tol
+    assert rel_err(o1, o_ref) <= tol and rel_err(o, o1) <= tol

@@ -298,6 +298,30 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
     assert lay.total - lay.seg == us * 4 + 2 * (np_ - 1) * us * 4 + (np_ - 1) * us * es + T * h_v * d * es
 
 
+@pytest.mark.parametrize("kda,io,h_v,d,T,flags,want", [
+    (0, 0, 16, 128, 16384, 0, True),      # 16 heads, long: the head-resident scan
+    (0, 2, 8, 128, 16384, 0, True),       # fp16, 8 heads
+    (0, 0, 16, 128, 16384, 4, False),     # DRLA_SERIAL keeps the per-16-column scan
+    (0, 0, 16, 128, 4096, 0, False),      # short: per-16-column
+    (0, 0, 32, 128, 65536, 0, False),     # 32 heads: per-16-column
+    (0, 0, 2, 128, 65536, 0, False),      # 2 heads: the per-16-column split
+    (1, 0, 16, 128, 16384, 0, False),     # KDA: per-16-column
+    (0, 1, 16, 128, 16384, 0, False),     # fp32: per-16-column
+    (0, 0, 16, 64, 16384, 0, False),      # d = 64: per-16-column
+])
+def test_automatic_head_scan_choice(lib, kda, io, h_v, d, T, flags, want):
+    """Without flags, scalar-gate 16-bit calls at d = 128 take the
+    head-resident scan where its timing model predicts it faster; the
+    workspace layout shows the choice (hs region, no seg region)."""
+    from delta_rule_linear_chunked_amd._lib import Layout
+    p = _prob(n_seqs=1, h_qk=1, h_v=h_v, dk=d, dv=d, io=io, T=T)
+    lay = Layout()
+    assert lib.drla_workspace_layout(kda, ctypes.byref(p), None, flags, ctypes.byref(lay)) == 0
+    assert (lay.hs > 0) == want
+    if want:
+        assert lay.seg == 0
+
+
 def _hs_np(units, max_cps, cus=256):
     """The head-resident scan's segment count as the header states it: the
     most np with units x np <= cus, np^2 <= 9 n_max, at least two chunks per
