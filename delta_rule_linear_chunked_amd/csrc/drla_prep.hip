@@ -33,6 +33,11 @@
 
 namespace drla {
 
+// Batches of at most this many sequences: the schedule kernel keeps their
+// lengths and first chunks in LDS, writes the chunk table with every thread
+// and ranks the sequences itself.
+constexpr int kScheduleLdsSeqs = 1024;
+
 // Chunk table of packed input, built from a checked copy of the device
 // cu_seqlens (the kernels after this one read only the copy).  The device
 // array must equal the host copy the call was sized and validated with:
@@ -47,14 +52,19 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
                                                         int64_t T, int64_t max_cps, uint64_t hash,
                                                         int32_t* chunk_seq, int32_t* chunk_start,
                                                         int32_t* seq_chunk0, int32_t* cu_ok,
-                                                        int32_t* status) {
+                                                        int32_t* seq_order, int32_t* status) {
+  constexpr int kLds = kScheduleLdsSeqs;
   __shared__ int32_t sc[256];
+  __shared__ int32_t cul[kLds + 1];  // the lengths (n <= kLds)
+  __shared__ int32_t sc0[kLds + 1];  // first chunk of each sequence (n <= kLds)
   __shared__ unsigned long long red[3][4];  // per wave: fingerprint, chunks, failed checks
   const int t = threadIdx.x;
+  const bool small = n_seqs <= kLds;
   uint64_t h = 0, cs = 0;
   int b = 0;
   for (int s = t; s <= n_seqs; s += 256) {
     const int32_t a = cu[s];
+    if (small) cul[s] = a;
     h += drla_cu_mix((uint64_t)s, (uint32_t)a);
     if ((s == 0 && a != 0) || (s == n_seqs && (int64_t)a != T)) b = 1;
     if (s < n_seqs) {
@@ -91,19 +101,20 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
     for (int s = t; s <= n_seqs; s += 256) {
       seq_chunk0[s] = 0;
       cu_ok[s] = 0;
+      if (small && s < n_seqs) seq_order[s] = s;  // all empty: ranked by index
     }
     if (t == 0) status[0] = 1;
     return;
   }
-  for (int s = t; s <= n_seqs; s += 256) cu_ok[s] = cu[s];
+  for (int s = t; s <= n_seqs; s += 256) cu_ok[s] = small ? cul[s] : cu[s];
   int64_t carry = 0;
   for (int base = 0; base < n_seqs; base += 256) {
     const int s = base + t;
     int cnt = 0;
     int64_t st = 0;
     if (s < n_seqs) {
-      st = cu[s];
-      const int64_t L = (int64_t)cu[s + 1] - st;
+      st = small ? cul[s] : cu[s];
+      const int64_t L = (int64_t)(small ? cul[s + 1] : cu[s + 1]) - st;
       cnt = L > 0 ? (int)((L + C - 1) / C) : 0;
     }
     sc[t] = cnt;
@@ -117,11 +128,15 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
     const int64_t excl = carry + sc[t] - cnt;
     if (s < n_seqs) {
       seq_chunk0[s] = (int32_t)excl;
-      for (int j = 0; j < cnt; ++j) {
-        const int64_t idx = excl + j;
-        if (idx < nc) {
-          chunk_seq[idx] = s;
-          chunk_start[idx] = (int32_t)(st + (int64_t)C * j);
+      if (small) {
+        sc0[s] = (int32_t)excl;
+      } else {
+        for (int j = 0; j < cnt; ++j) {
+          const int64_t idx = excl + j;
+          if (idx < nc) {
+            chunk_seq[idx] = s;
+            chunk_start[idx] = (int32_t)(st + (int64_t)C * j);
+          }
         }
       }
     }
@@ -131,6 +146,33 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* cu, int n_
   if (t == 0) {
     seq_chunk0[n_seqs] = (int32_t)carry;
     status[0] = 0;
+  }
+  if (small) {
+    // the sequences ranked longest first (ties by index) for the scan's
+    // dealing order, from the lengths in LDS (larger batches: rank_kernel)
+    for (int s = t; s < n_seqs; s += 256) {
+      const int32_t mine = cul[s + 1] - cul[s];
+      int rank = 0;
+      for (int j = 0; j < n_seqs; ++j) {
+        const int32_t l = cul[j + 1] - cul[j];
+        rank += (l > mine || (l == mine && j < s)) ? 1 : 0;
+      }
+      seq_order[rank] = s;
+    }
+    // every thread a run of chunks: the sequence holding chunk c is the last
+    // s with sc0[s] <= c (sc0[0] = 0 <= c < nc = sc0[n]), found by bisection
+    if (t == 0) sc0[n_seqs] = (int32_t)carry;
+    __syncthreads();
+    for (int64_t c = t; c < nc; c += 256) {
+      int lo = 0, hi = n_seqs;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sc0[mid] <= c) lo = mid;
+        else hi = mid;
+      }
+      chunk_seq[c] = lo;
+      chunk_start[c] = cul[lo] + (int32_t)(C * (c - sc0[lo]));
+    }
   }
 }
 
@@ -872,10 +914,13 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
 hipError_t launch_schedule(const int32_t* cu, int n_seqs, int64_t nc, int64_t T, int64_t max_cps,
                            uint64_t hash, int32_t* sched, hipStream_t st) {
   int32_t* cu_ok = sched + drla_sched_cu(nc, n_seqs);
+  int32_t* order = sched + 2 * nc + n_seqs + 1;
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, st, cu, n_seqs, nc, T, max_cps, hash, sched,
-                     sched + nc, sched + 2 * nc, cu_ok, sched + drla_sched_status(nc, n_seqs));
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0, st, cu_ok, n_seqs,
-                     sched + 2 * nc + n_seqs + 1);
+                     sched + nc, sched + 2 * nc, cu_ok, order, sched + drla_sched_status(nc, n_seqs));
+  // batches the schedule kernel keeps in LDS are ranked there
+  if (n_seqs > kScheduleLdsSeqs)
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0, st, cu_ok, n_seqs,
+                       order);
   return hipGetLastError();
 }
 

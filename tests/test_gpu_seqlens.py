@@ -136,3 +136,21 @@ def test_many_sequences_fingerprint(drla):
     moved[i] -= 1  # same chunk total unless a boundary is crossed; the fingerprint differs
     with pytest.raises(drla.DrlaError):
         _run(drla, "gdn", d, torch.tensor(moved, dtype=torch.int32, device="cuda"), cu_host, o, ht, ws)
+
+
+@pytest.mark.parametrize("n", [1024, 1025, 3000])
+def test_batches_past_the_lds_table(drla, n):
+    """The schedule kernel keeps the lengths of batches of up to 1,024
+    sequences in LDS (the chunk table written by every thread, the ranking
+    done there); larger batches take the per-sequence table writes and the
+    separate ranking kernel.  Both sides of the limit, against the oracle."""
+    rng = np.random.default_rng(n)
+    lens = tuple(int(v) for v in rng.integers(0, 90, size=n))
+    x = _inputs("gdn", lens)
+    d = to_device(x)
+    cu_host = [int(c) for c in x["cu_seqlens"]]
+    o, ht = _run(drla, "gdn", d, d["cu"], cu_host, None, None, None)
+    o_ref, ht_ref = run_oracle(x)
+    eo, eh = rel_err(o.float().cpu().numpy(), o_ref), rel_err(ht.cpu().numpy(), ht_ref)
+    print(f"batch of {n}: rel_err o={eo:.3e} ht={eh:.3e}", flush=True)
+    assert eo <= TOL[x["io"]] and eh <= TOL[x["io"]]
