@@ -77,6 +77,12 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ int kmap(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
 
+// The 48 of the 64 128-byte lines of a (head, chunk)'s eight 16x32
+// fragments that hold fragments 0, 2, 4, 5, 6 and 7 (1 and 3 lie above the
+// diagonal and are never stored): lane l's line for an L2 touch of the six;
+// lanes 48..63 repeat lines 48..63.
+__device__ __forceinline__ int frag_line(int l) { return l < 8 ? l : l < 16 ? l + 8 : l < 48 ? l + 16 : l; }
+
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 template <typename ET>

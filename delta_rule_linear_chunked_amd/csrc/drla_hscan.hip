@@ -236,7 +236,8 @@ struct HChunkIO {
                  (uint32_t)lane * vstride + 128u * (uint32_t)(gi - CP::KL * (WQ ? 2 : 1)), 0, sink);
       } else if (gi < CP::NT - 1) {
         const bool pmf = gi == CP::NT - 2 && WQ;
-        lds_dma4(make_rsrc((const H8*)(pmf ? P->pm : P->tb) + ch * (8 * 64), 8 * 1024), 128u * lane, 0, sink);
+        lds_dma4(make_rsrc((const H8*)(pmf ? P->pm : P->tb) + ch * (8 * 64), 8 * 1024), 128u * (uint32_t)frag_line(lane),
+                 0, sink);
       } else {
         lds_dma4(make_rsrc(P->gam + ch * (2 * C), 2 * C * 4), 128u * (lane & 3), 0, sink);
       }

@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       if (!LF) {
         V8* pg = (V8*)P.pm + ch * (8 * 64);
         pg[(pr * 2 + 0) * 64 + lane] = pfr[0];
-        pg[(pr * 2 + 1) * 64 + lane] = pfr[1];
+        if (pr >= 2) pg[(pr * 2 + 1) * 64 + lane] = pfr[1];  // (0, 1), (1, 1): zero, never read
       }
     };
     // KDA: the tiles of the wave's assignment above
@@ -659,12 +659,10 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         put_a(0, 0, acc[2]);
         pg[4 * 64 + lane] = pack<ET>(pt[0], pt[1]);
         pg[0 * 64 + lane] = pack<ET>(mask_p(pt[2]), z);
-        pg[1 * 64 + lane] = pack<ET>(z, z);
       } else if (wv == 2) {
         put_a(1, 0, acc[0]);
         put_a(1, 1, acc[1]);
         pg[2 * 64 + lane] = pack<ET>(pt[0], mask_p(pt[1]));
-        pg[3 * 64 + lane] = pack<ET>(z, z);
       } else {
         put_a(2, 2, acc[0]);
         put_a(3, 3, acc[1]);
@@ -838,7 +836,9 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
           if (LF) As[i][r] = tb;
           x[j] = (ET)(tb * en);
         }
-        tg[(nt * 2 + p) * 64 + lane] = x;
+        // fragments (0, 1) and (1, 1) lie above the diagonal: zero, and no
+        // scan reads them, so they are not stored
+        if (2 * p <= nt) tg[(nt * 2 + p) * 64 + lane] = x;
       }
     }
     if (LF) {
@@ -859,7 +859,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       }
       V8* pg = (V8*)P.pm + ch * (8 * 64);
       pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(ptt[0], ptt[1]);
-      pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(ptt[2], ptt[3]);
+      if (pr >= 2) pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(ptt[2], ptt[3]);
     }
     if (!PF) break;
     u += gridDim.x;

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     } else if (gi < 2 * KL + 2) {  // Tb or P fragments
       const int64_t ch = (int64_t)h * P.nc + c0 + i;
       const H8* fr = (const H8*)(gi == 2 * KL ? P.tb : P.pm) + ch * (8 * 64);
-      lds_dma4(make_rsrc(fr, 8 * 1024), 128u * lane, 0, touch);
+      lds_dma4(make_rsrc(fr, 8 * 1024), 128u * (uint32_t)frag_line(lane), 0, touch);
     } else if (gi < 2 * KL + 2 + VL) {  // the head's V rows, line gi - 2 KL - 2
       const T* src = vg + (tc * P.h_v + h) * DV;
       lds_dma4(make_rsrc(src, lrow * vstride + DV * 2), (uint32_t)lane * vstride + 128u * (uint32_t)(gi - 2 * KL - 2), 0,

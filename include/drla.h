@@ -258,7 +258,8 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  * holds outer index c at inner indices 4g + j (j < 4) and 12 + 4g + j
  * (4 <= j < 8).
  *   tb:  T diag(beta), T = (I + A)^{-1}; 8 fragments (outer token tile 0..3,
- *        inner token block 0..1, index tile*2 + block)
+ *        inner token block 0..1, index tile*2 + block); fragments 1 and 3
+ *        lie above the diagonal (zero) and are not stored, here and in pm
  *   pm:  P = lower_incl(Q K^T (.) D) (the intra-chunk output weights), 8
  *        fragments in the same order
  *   kt:  K~^T, K~ = e^{b_n - b} (.) K; dk/8 fragments (outer key-channel
