@@ -38,7 +38,7 @@ class Problem(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("sched", "tb", "pm", "kt", "kw", "qw", "gam", "vp", "h",
-                                       "seg", "hs", "total")]
+                                       "seg", "hs", "total", "head_scan")]
 
 
 KEEP_INTERMEDIATES = 1

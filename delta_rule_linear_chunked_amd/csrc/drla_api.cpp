@@ -126,25 +126,25 @@ constexpr int kKnownFlags = DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SER
 // without flags where its timing model predicts it faster
 // (drla_auto_head_scan, at 256 compute units like the workspace); with
 // DRLA_SERIAL alone the per-16-column scan runs in one pass.
-static bool uses_hs(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
+static bool uses_hs(const drla_problem* p, int64_t nc, int64_t max_cps, bool kda, int flags) {
   if (kda || p->io_dtype == DRLA_F32 || (flags & DRLA_KEEP_INTERMEDIATES)) return false;
   if (flags & DRLA_HEAD_SCAN) return true;
   if (flags & DRLA_SERIAL) return false;
-  return p->n_seqs >= 1 && drla_auto_head_scan((int64_t)p->n_seqs * p->h_v, max_cps, p->dk, p->dv, 256);
+  return p->n_seqs >= 1 && drla_auto_head_scan((int64_t)p->n_seqs * p->h_v, max_cps, nc * p->h_v, p->dk, p->dv, 256);
 }
 
 // Segments per sequence the hs region provides for (drla_hs_count at 256
 // compute units; one pass when dk != dv or with DRLA_SERIAL).
-static int32_t hs_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
-  if (!uses_hs(p, max_cps, kda, flags) || p->dk != p->dv || (flags & DRLA_SERIAL) || p->n_seqs < 1) return 1;
+static int32_t hs_count(const drla_problem* p, int64_t nc, int64_t max_cps, bool kda, int flags) {
+  if (!uses_hs(p, nc, max_cps, kda, flags) || p->dk != p->dv || (flags & DRLA_SERIAL) || p->n_seqs < 1) return 1;
   return drla_hs_count((int64_t)p->n_seqs * p->h_v, max_cps, 256);
 }
 
 // Segments the per-16-column scan's seg region provides for (drla_seg_count
 // at 256 compute units, over the longest sequence); 1 for calls the split
 // does not take.
-static int32_t seg_count(const drla_problem* p, int64_t max_cps, bool kda, int flags) {
-  if (uses_hs(p, max_cps, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
+static int32_t seg_count(const drla_problem* p, int64_t nc, int64_t max_cps, bool kda, int flags) {
+  if (uses_hs(p, nc, max_cps, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
   if (p->dk != p->dv || p->n_seqs < 1) return 1;
   return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
 }
@@ -182,16 +182,17 @@ void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, 
   if (keep) off = align_up(off + ncH * (size_t)p->dk * p->dv * es);
   // Segment-split per-16-column scan (calls with dk = dv that leave most of
   // a 256-CU chip idle): its states and G
-  const int32_t np = seg_count(p, max_cps, kda, flags);
+  const int32_t np = seg_count(p, nc, max_cps, kda, flags);
   L->seg = np > 1 ? off : 0;
   if (np > 1)
     off = align_up(off + drla_seg_offsets((int64_t)p->n_seqs * p->h_v, p->dk, p->total_tokens, p->h_v, np, es).total);
   // Head-resident scan (DRLA_HEAD_SCAN) with segments: the segments' states
   // and maps
-  const int32_t hnp = hs_count(p, max_cps, kda, flags);
+  const int32_t hnp = hs_count(p, nc, max_cps, kda, flags);
   L->hs = hnp > 1 ? off : 0;
   if (hnp > 1) off = align_up(off + drla_hs_bytes((int64_t)p->n_seqs * p->h_v, p->dk, p->dv, hnp, es));
   L->total = off;
+  L->head_scan = uses_hs(p, nc, max_cps, kda, flags) ? 1 : 0;
 }
 
 // Packed input that the kernels take as such: more than one sequence.
@@ -269,9 +270,9 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.off_vp = L.vp;
   a.off_h = L.h;
   a.off_seg = L.seg;
-  a.seg_np = L.seg ? seg_count(p, max_cps, kda, flags) : 1;
+  a.seg_np = L.seg ? seg_count(p, nc, max_cps, kda, flags) : 1;
   a.off_hs = L.hs;
-  a.hs_np = L.hs ? hs_count(p, max_cps, kda, flags) : 1;
+  a.hs_np = L.hs ? hs_count(p, nc, max_cps, kda, flags) : 1;
   a.max_cps = max_cps;
   a.total_tokens = T;
   a.n_chunks = nc;
@@ -286,7 +287,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
   a.inspect = (flags & DRLA_KEEP_INTERMEDIATES) ? 1 : 0;
   a.decay_only = decay ? 1 : 0;
   a.serial = (flags & DRLA_SERIAL) ? 1 : 0;
-  a.head_scan = uses_hs(p, max_cps, kda, flags) ? 1 : 0;
+  a.head_scan = uses_hs(p, nc, max_cps, kda, flags) ? 1 : 0;
   a.stream = stream;
   a.stage_events = stage_events;
   const hipError_t e = drla_launch(&a);
@@ -502,6 +503,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 5; }
+int drla_version(void) { return 6; }
 
 }  // extern "C"

@@ -40,17 +40,39 @@ static inline int32_t drla_hs_count(int64_t units, int64_t max_cps, int64_t cus)
 // head-resident scan: GDN or decay-only, 16-bit inputs, dk = dv = 128 (the
 // shapes its timing model was measured on), when the model predicts it at
 // least 10 % faster than the per-16-column scan.  Scan-stage models from
-// MI355X measurements (microseconds, n chunks of the longest sequence):
-// head-resident 36 + 8.5 ceil(n / np_hs); per-16-column 0.9 ceil(n / np_seg)
-// plus 12 for the compose and fix-up when it splits.
-static inline bool drla_auto_head_scan(int64_t units, int64_t max_cps, int32_t dk, int32_t dv,
-                                       int64_t cus) {
-  if (dk != 128 || dv != 128 || units <= 0 || max_cps <= 0) return false;
+// MI355X measurements (microseconds; n chunks of the longest sequence,
+// unit_chunks the chunks of all (sequence, head) units together):
+//   head-resident, np_hs >= 3 segments: 36 + 8.5 ceil(n / np_hs);
+//   head-resident, one pass: 4.07 max(n, unit_chunks / cus) -- with every
+//     compute unit busy, each pulling all of its unit's operands from HBM;
+//   per-16-column, chains (units x dv/16) <= cus: 0.9 ceil(n / np_seg) plus
+//     12 for the compose and fix-up when it splits (its chains run at once);
+//   per-16-column, more chains than compute units: 1.06 max(n, unit_chunks
+//     dv/16 / cus) -- bound by the chunks each compute unit is dealt.
+// The last two are from one 8-sequence, 32-head packed batch (scan 545
+// against 460 us); with fewer busy compute units the head-resident scan
+// runs faster per chunk than 4.07, so the rule errs towards the
+// per-16-column scan.
+static inline bool drla_auto_head_scan(int64_t units, int64_t max_cps, int64_t unit_chunks, int32_t dk,
+                                       int32_t dv, int64_t cus) {
+  if (dk != 128 || dv != 128 || units <= 0 || max_cps <= 0 || cus <= 0) return false;
+  const int64_t chains = units * (dv / 16);
+  const double n = (double)max_cps;
   const int32_t nh = drla_hs_count(units, max_cps, cus);
-  if (nh < 3) return false;
-  const int32_t ns = drla_seg_count(units * (dv / 16), max_cps, cus);
-  const double t_head = 36.0 + 8.5 * (double)((max_cps + nh - 1) / nh);
-  const double t_col = 0.9 * (double)((max_cps + ns - 1) / ns) + (ns > 1 ? 12.0 : 0.0);
+  double t_head, t_col;
+  if (nh >= 3) {
+    t_head = 36.0 + 8.5 * (double)((max_cps + nh - 1) / nh);
+  } else {
+    const double per_cu = (double)unit_chunks / (double)cus;
+    t_head = 4.07 * (n > per_cu ? n : per_cu);
+  }
+  if (chains > cus) {
+    const double per_cu = (double)unit_chunks * (double)(dv / 16) / (double)cus;
+    t_col = 1.06 * (n > per_cu ? n : per_cu);
+  } else {
+    const int32_t ns = drla_seg_count(chains, max_cps, cus);
+    t_col = 0.9 * (double)((max_cps + ns - 1) / ns) + (ns > 1 ? 12.0 : 0.0);
+  }
   return t_head < 0.9 * t_col;
 }
 

@@ -284,12 +284,16 @@ drla_status drla_prefill_ex(int kda, int flags, const drla_problem* p, const voi
  *        (the segments' zero-start final states, replaced in place by the
  *        states entering segments 1 .. np - 1), then np - 2 segment maps of
  *        dk x dk per unit in io type
+ * head_scan records which scan the call takes: 1 for the head-resident scan
+ * (DRLA_HEAD_SCAN, or chosen by its timing model), 0 for the per-16-column
+ * scan.
  * Elements are io dtype except gam and the seg and hs states (fp32).
  * n_chunks is the total chunk count over all sequences.  Returns DRLA_OK or
  * a validation error. */
 typedef struct {
   int64_t n_chunks;
   size_t sched, tb, pm, kt, kw, qw, gam, vp, h, seg, hs, total;
+  size_t head_scan; /* 1: the call takes the head-resident scan, 0: the per-16-column one */
 } drla_layout;
 drla_status drla_workspace_layout(int kda, const drla_problem* p,
                                   const int32_t* cu_seqlens_host, int flags,

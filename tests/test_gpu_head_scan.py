@@ -122,3 +122,33 @@ def test_automatic_head_scan(drla, h_v, T, io):
     print(f"  rel_err o={eo:.3e} ht={eh:.3e} (column scan {rel_err(o1, o_ref):.3e})", flush=True)
     assert np.isfinite(o).all() and eo <= tol and eh <= tol
     assert rel_err(o1, o_ref) <= tol and rel_err(o, o1) <= tol
+
+
+def test_automatic_head_scan_many_units(drla):
+    """A packed batch with more (sequence, head, 16-column) chains than the
+    chip has compute units (64 sequences of 512 tokens, 8 heads: 4,096
+    chains) takes the head-resident scan in one pass without flags (the
+    layout records the choice): against the oracle and against the
+    per-16-column scan (DRLA_SERIAL)."""
+    lens = (512,) * 64
+    print(f"case automatic head scan, packed {len(lens)} x {lens[0]}, h_v=8", flush=True)
+    spec = W.small_spec("gdn", lens=lens, h_qk=4, h_v=8, dk=128, dv=128, io="bf16",
+                        g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=62, varlen=True)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    cu_host = [int(c) for c in x["cu_seqlens"]]
+    lay = drla.workspace_layout(d["q"].shape, d["v"].shape, d["q"].dtype, cu_seqlens_host=cu_host)
+    assert lay["head_scan"] == 1 and lay["seg"] == 0 and lay["hs"] == 0
+    ws = torch.full((lay["total"],), 255, dtype=torch.uint8, device="cuda")
+    o, ht = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
+                             cu_seqlens_host=cu_host, workspace=ws)
+    o1, ht1 = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu"],
+                               cu_seqlens_host=cu_host, flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    o, o1 = o.float().cpu().numpy(), o1.float().cpu().numpy()
+    ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
+    o_ref, ht_ref = run_oracle(x)
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e} (column scan {rel_err(o1, o_ref):.3e})", flush=True)
+    assert np.isfinite(o).all() and eo <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert rel_err(o1, o_ref) <= TOL["bf16"] and rel_err(ht1, ht_ref) <= TOL["bf16"]

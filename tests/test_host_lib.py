@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
             "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 5
+    assert lib.drla_version() == 6
 
 
 def test_prefill_status_needs_no_device_for_unpacked_calls(lib):
@@ -312,14 +312,61 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
 def test_automatic_head_scan_choice(lib, kda, io, h_v, d, T, flags, want):
     """Without flags, scalar-gate 16-bit calls at d = 128 take the
     head-resident scan where its timing model predicts it faster; the
-    workspace layout shows the choice (hs region, no seg region)."""
+    workspace layout records the choice (and holds the segmented head scan's
+    region, no seg region)."""
     from delta_rule_linear_chunked_amd._lib import Layout
     p = _prob(n_seqs=1, h_qk=1, h_v=h_v, dk=d, dv=d, io=io, T=T)
     lay = Layout()
     assert lib.drla_workspace_layout(kda, ctypes.byref(p), None, flags, ctypes.byref(lay)) == 0
+    assert lay.head_scan == int(want)
     assert (lay.hs > 0) == want
     if want:
         assert lay.seg == 0
+
+
+def _model_choice(units, max_cps, unit_chunks, cus=256):
+    """The scan-choice model as the header states it (dk = dv = 128)."""
+    nh = _hs_np(units, max_cps, cus)
+    if nh >= 3:
+        t_head = 36 + 8.5 * -(-max_cps // nh)
+    else:
+        t_head = 4.07 * max(max_cps, unit_chunks / cus)
+    chains = units * 8
+    if chains > cus:
+        t_col = 1.06 * max(max_cps, unit_chunks * 8 / cus)
+    else:
+        ns = _seg_np(chains, max_cps)
+        t_col = 0.9 * -(-max_cps // ns) + (12 if ns > 1 else 0)
+    return t_head < 0.9 * t_col
+
+
+@pytest.mark.parametrize("lens,h_v,want", [
+    ((1169, 2048, 3000, 4096, 5000, 6000, 7188, 4375), 32, True),  # packed, 2,048 chains: one-pass head scan
+    ((4096,) * 8, 16, False),             # dense-like batch, 1,024 chains: near even, per-16-column
+    ((2048,) * 32, 16, True),             # 32 sequences x 16 heads: the head scan's throughput wins
+    ((7000, 100, 100, 100), 32, False),   # one long sequence dominates: per-16-column
+    ((512,) * 64, 8, True),               # 512 short units
+])
+def test_automatic_choice_with_more_chains_than_compute_units(lib, lens, h_v, want):
+    """Packed batches with more (unit, 16-column) chains than compute units:
+    both scans are bound by the chunks each compute unit is dealt, and the
+    head-resident one, which moves a chunk's operands once per head, is taken
+    where the model predicts it at least 10 % faster.  The recorded choice
+    follows the model as documented."""
+    from delta_rule_linear_chunked_amd._lib import Layout
+    n, T = len(lens), sum(lens)
+    p = _prob(n_seqs=n, h_qk=h_v // 2, h_v=h_v, dk=128, dv=128, io=0, T=T)
+    cu, _c = _i32([0] + [sum(lens[:i + 1]) for i in range(n)])
+    lay = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), cu, 0, ctypes.byref(lay)) == 0
+    cps = [(L + 63) // 64 for L in lens]
+    assert _model_choice(n * h_v, max(cps), sum(cps) * h_v) == want
+    assert lay.head_scan == int(want)
+    if want:
+        assert lay.seg == 0
+    # DRLA_SERIAL keeps the per-16-column scan
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), cu, 4, ctypes.byref(lay)) == 0
+    assert lay.head_scan == 0
 
 
 def _hs_np(units, max_cps, cus=256):
