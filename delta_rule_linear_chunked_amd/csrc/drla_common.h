@@ -77,6 +77,17 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ int kmap(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
 
+// Transposing LDS read of 16-bit elements (ds_read_b64_tr_b16): within a
+// 16-lane group, lane i receives element i % 4 of the four-element 8-byte
+// segments addressed by lanes 4j + i / 4, j = 0..3.  `p` must be 8-byte
+// aligned.
+template <typename ET>
+__device__ __forceinline__ typename VT<ET>::v4 lds_read_tr16(const void* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p));
+  return __builtin_bit_cast(typename VT<ET>::v4, v);
+}
+
 // The 48 of the 64 128-byte lines of a (head, chunk)'s eight 16x32
 // fragments that hold fragments 0, 2, 4, 5, 6 and 7 (1 and 3 lie above the
 // diagonal and are never stored): lane l's line for an L2 touch of the six;

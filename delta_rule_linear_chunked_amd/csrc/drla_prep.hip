@@ -240,6 +240,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   constexpr int GP = 256 / CG;                   // KDA gate: runs of rows per channel
   constexpr int GR = C / GP;                     // KDA gate: rows per run
   constexpr bool LF = !KDA && !KT;               // operands for the LDS-fed scan
+  static_assert(!LF || sizeof(ET) == 2, "the LDS-fed scans take 16-bit inputs");
   constexpr int KV = DK / PE;                    // 16-byte pieces per K row
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
@@ -821,30 +822,46 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
     // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
     // block p), eight per (chunk, head); the ones above the diagonal are zero.
     // LF: diag(e^{b_n - b}) Tb instead (the scan then forms e^{b_n - b} (.) V'
-    // directly), and Tb^T staged in the bytes of A for P Tb below.
+    // directly), and Tb itself staged in the io type, row-major, in the bytes
+    // of A for P Tb below.  A lane's eight entries of a fragment are two runs
+    // of four columns (kmap), read as two vectors of T and of beta.
+    constexpr int TBP = C + 8;  // LF: padded row of the staged Tb (io type)
+    ET(*TbL)[TBP] = (ET(*)[TBP])&As[0][0];
+    static_assert(!LF || C * TBP * sizeof(ET) <= sizeof(float) * C * TP, "staged Tb fits in the bytes of A");
     {
       const int nt = wv, r = 16 * nt + c16;
       const float en = LF ? __expf(bs[C - 1] - bs[r]) : 1.f;
       V8* tg = (V8*)P.tb + ch * (8 * 64);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
+        const int c0 = 32 * p + 4 * g4, c1 = c0 + 16;
+        const floatx4 t0 = *(const floatx4*)&Ts[r][c0], t1 = *(const floatx4*)&Ts[r][c1];
+        const floatx4 b0 = *(const floatx4*)&betas[c0], b1 = *(const floatx4*)&betas[c1];
         V8 x;
+        V4 y0, y1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 32 * p + kmap(g4, j);
-          const float tb = Ts[r][i] * betas[i];
-          if (LF) As[i][r] = tb;
-          x[j] = (ET)(tb * en);
+        for (int j = 0; j < 4; ++j) {
+          const float u0 = t0[j] * b0[j], u1 = t1[j] * b1[j];
+          x[j] = (ET)(u0 * en);
+          x[j + 4] = (ET)(u1 * en);
+          y0[j] = (ET)u0;
+          y1[j] = (ET)u1;
+        }
+        if constexpr (LF) {
+          *(V4*)&TbL[r][c0] = y0;
+          *(V4*)&TbL[r][c1] = y1;
         }
         // fragments (0, 1) and (1, 1) lie above the diagonal: zero, and no
         // scan reads them, so they are not stored
         if (2 * p <= nt) tg[(nt * 2 + p) * 64 + lane] = x;
       }
     }
-    if (LF) {
+    if constexpr (LF) {
       // P Tb for the output Map (the scan multiplies it with R = V - e^b X):
       // tiles (it, pr) of (P Tb)^T = Tb^T P^T, packed in pairs into fragment
-      // (pr, p) with P's layout (outer = query token, inner = token)
+      // (pr, p) with P's layout (outer = query token, inner = token).  The
+      // Tb^T fragments come from the staged rows by transposing reads: lane
+      // (c, g) gets Tb[32p + 4g + j][16 it + c] (and rows + 16), j = 0..3.
       __syncthreads();
       floatx4 ptt[4];
 #pragma unroll
@@ -852,9 +869,9 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         ptt[it] = zero4();
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const floatx4 lo = *(const floatx4*)&As[16 * it + c16][32 * p + 4 * g4];
-          const floatx4 hi = *(const floatx4*)&As[16 * it + c16][32 * p + 16 + 4 * g4];
-          ptt[it] = mma(pack<ET>(lo, hi), pfr[p], ptt[it]);
+          const int rr = 32 * p + 4 * g4 + (c16 >> 2), cc = 16 * it + 4 * (c16 & 3);
+          const V4 lo = lds_read_tr16<ET>(&TbL[rr][cc]), hi = lds_read_tr16<ET>(&TbL[rr + 16][cc]);
+          ptt[it] = mma(cat<ET>(lo, hi), pfr[p], ptt[it]);
         }
       }
       V8* pg = (V8*)P.pm + ch * (8 * 64);
@@ -903,8 +920,9 @@ static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t s
 template <int DK, bool KDA, typename ET>
 hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
   if (nblk <= 0) return hipGetLastError();
-  if constexpr (KDA)
-    return launch_prep_v<DK, true, ET, true>(P, nblk, st);
+  // fp32 inputs always take the register-fed scan, which needs K~^T
+  if constexpr (KDA || sizeof(ET) == 4)
+    return launch_prep_v<DK, KDA, ET, true>(P, nblk, st);
   else if (P.kt)
     return launch_prep_v<DK, false, ET, true>(P, nblk, st);
   else
