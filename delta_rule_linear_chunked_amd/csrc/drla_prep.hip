@@ -228,7 +228,7 @@ __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e
 // LDS is reused across phases: K (and KDA's Q rows and B table) live until
 // the chunk operands are written, T from the solve on, in the same bytes;
 // KDA's A and the runs' totals take the bytes of the B table.
-template <int DK, bool KDA, typename ET, bool KT, bool PF>
+template <int DK, bool KDA, typename ET, bool KT, bool PF, bool G2>
 __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(PrepParams P, int64_t nunits) {
   typedef typename VT<ET>::v8 V8;
   typedef typename VT<ET>::v16b V16;
@@ -241,6 +241,8 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   constexpr int GR = C / GP;                     // KDA gate: rows per run
   constexpr bool LF = !KDA && !KT;               // operands for the LDS-fed scan
   static_assert(!LF || sizeof(ET) == 2, "the LDS-fed scans take 16-bit inputs");
+  static_assert(!G2 || LF, "value heads in pairs: the LDS-fed scans' operands only");
+  constexpr int NG = G2 ? 2 : 1;                 // value heads per unit (G2: a pair sharing K, Q)
   constexpr int KV = DK / PE;                    // 16-byte pieces per K row
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
@@ -253,8 +255,8 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   constexpr int U_BYTES = NT * KS_BYTES + BL_BYTES > TS_BYTES ? NT * KS_BYTES + BL_BYTES : TS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
   __shared__ __attribute__((aligned(16))) float As_st[KDA ? 1 : C][TP];  // A (GDN)
-  __shared__ __attribute__((aligned(16))) float bs[C];
-  __shared__ __attribute__((aligned(16))) float betas[C];
+  __shared__ __attribute__((aligned(16))) float bs[NG][C];     // per value head of the unit
+  __shared__ __attribute__((aligned(16))) float betas[NG][C];
   __shared__ floatx4 pxch[KDA ? 64 : 1];  // KDA: one P^T tile passed between waves
   ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
   ET(*Qs)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: Q rows (phases 0-1)
@@ -275,8 +277,9 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   };
   auto unit_of = [&](int64_t u) {
     Unit U;
-    U.h = (int)(u / P.nc);
-    const int64_t c = u - (int64_t)U.h * P.nc;
+    const int64_t hu = u / P.nc;
+    const int64_t c = u - hu * P.nc;
+    U.h = (int)hu * NG;  // G2: the pair's first value head
     int seq;
     chunk_of(P.s, c, seq, U.t0, U.len);
     U.hk = U.h / P.grp;
@@ -314,9 +317,10 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         qpre[p] = x;
       }
     }
-    if (tid < C) {
-      bpre = tid < U.len ? (P.decay_only ? 1.f : P.beta[(U.t0 + tid) * P.h_v + U.h]) : 0.f;
-      if (!KDA) gpre = tid < U.len ? P.g[(U.t0 + tid) * P.h_v + U.h] : 0.f;
+    // wave m < NG: row `lane` of value head U.h + m
+    if (tid < NG * C) {
+      bpre = lane < U.len ? (P.decay_only ? 1.f : P.beta[(U.t0 + lane) * P.h_v + U.h + wv]) : 0.f;
+      if (!KDA) gpre = lane < U.len ? P.g[(U.t0 + lane) * P.h_v + U.h + wv] : 0.f;
     }
     if (KDA) {
       const int d0 = 8 * (tid % CG), part = tid / CG;
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       if (KDA) *(V16*)&Qs[r][cv * PE] = qvpre[i];
     }
     // #1 Gate: in-chunk prefix sums of the log-decay
-    if (tid < C) {
-      betas[tid] = bpre;
+    if (tid < NG * C) {
+      betas[wv][lane] = bpre;
       if (!KDA) {
         float x = gpre;
 #pragma unroll
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
           const float y = __shfl_up(x, off);
           if (lane >= off) x += y;
         }
-        bs[tid] = x;
+        bs[wv][lane] = x;
       }
     }
     // KDA: per key channel, GP runs of GR rows; prefix sums in registers,
@@ -429,6 +433,12 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       }
       __syncthreads();
     }
+
+    // the value head being finished (G2: each of the pair in turn) and its
+    // gate and beta tables
+    const float* bsv = &bs[0][0];
+    const float* betv = &betas[0][0];
+    int64_t chm = ch;
 
     // ---- phase 1: products and the chunk operands --------------------------------
     // GDN: K row fragment of token tile t, inner block p
@@ -590,12 +600,12 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       // tiles past the diagonal are never read.  The gate values come from
       // LDS once per lane: this lane's four rows as one vector, one column
       // per tile.
-      const floatx4 betr = *(const floatx4*)&betas[16 * rt + 4 * g4];
-      const floatx4 bsr = *(const floatx4*)&bs[16 * rt + 4 * g4];
+      const floatx4 betr = *(const floatx4*)&betv[16 * rt + 4 * g4];
+      const floatx4 bsr = *(const floatx4*)&bsv[16 * rt + 4 * g4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t > rt) continue;
-        const float bsi = bs[16 * t + c16];
+        const float bsi = bsv[16 * t + c16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * g4 + e, i = 16 * t + c16;
@@ -609,22 +619,24 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       }
       // P: tiles jt = 2p, 2p+1 of P^T form fragment (pr, p) of P (outer =
       // query token, inner = key token); inclusive lower part only
-      const float bsq = bs[rq];
+      const float bsq = bsv[rq];
+      // (the raw products stay: G2 gates them again for the second head)
+      floatx4 pg4[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const floatx4 bsj = *(const floatx4*)&bs[16 * t + 4 * g4];
+        const floatx4 bsj = *(const floatx4*)&bsv[16 * t + 4 * g4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * t + 4 * g4 + e;
           float x = 0.f;
           if (j <= rq) x = KDA ? pt[t][e] : pt[t][e] * __expf(bsq - bsj[e]);
-          pt[t][e] = x;
+          pg4[t][e] = x;
         }
       }
-      pfr[0] = pack<ET>(pt[0], pt[1]);
-      pfr[1] = pack<ET>(pt[2], pt[3]);
+      pfr[0] = pack<ET>(pg4[0], pg4[1]);
+      pfr[1] = pack<ET>(pg4[2], pg4[3]);
       if (!LF) {
-        V8* pg = (V8*)P.pm + ch * (8 * 64);
+        V8* pg = (V8*)P.pm + chm * (8 * 64);
         pg[(pr * 2 + 0) * 64 + lane] = pfr[0];
         if (pr >= 2) pg[(pr * 2 + 1) * 64 + lane] = pfr[1];  // (0, 1), (1, 1): zero, never read
       }
@@ -632,7 +644,7 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
     // KDA: the tiles of the wave's assignment above
     auto store_ap_kda = [&]() {
       auto put_a = [&](int I, int J, const floatx4& v) {
-        const floatx4 betr = *(const floatx4*)&betas[16 * I + 4 * g4];
+        const floatx4 betr = *(const floatx4*)&betv[16 * I + 4 * g4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * I + 4 * g4 + e, i = 16 * J + c16;
@@ -671,212 +683,222 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         pg[7 * 64 + lane] = pack<ET>(pxch[lane], mask_p(pt[1]));
       }
     };
-    if (!KDA) store_ap();
-    // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
-    // of state tile mt in the scan's row order, inner = token block p);
-    // KDA: K (.) e^{B_n - B}
-    if (KT) {
-      constexpr int NF = (DK / 16) * 2;
-      V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
-      for (int f = wv; f < NF; f += 4) {
-        const int mt = f >> 1, p = f & 1;
-        const int d = state_row(mt, c16);
-        V8 x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 32 * p + kmap(g4, j);
-          x[j] = KDA ? (ET)(to_f(Ks[i][d]) * __builtin_amdgcn_exp2f(Bl[C - 1][d] - Bl[i][d]))
-                     : (ET)(to_f(Ks[i][d]) * __expf(bs[C - 1] - bs[i]));
-        }
-        ktg[f * 64 + lane] = x;
+    // G2: the pair's two value heads share the K and Q rows and the raw
+    // products; each is gated, solved and written in turn
+    for (int mj = 0; mj < NG; ++mj) {
+      if (mj > 0) {
+        __syncthreads();  // the first head's T and staged Tb are read
+        bsv = &bs[mj][0];
+        betv = &betas[mj][0];
+        chm = ch + (int64_t)mj * P.nc;
       }
-    }
-    if (KDA) {
-      // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
-      // with contiguous key channels 32p + 8g + j, the scan's state order
-      V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
-      V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
-      for (int f = wv; f < 4 * KB; f += 4) {
-        const int nt = f / KB, p = f - nt * KB;
-        const int r = 16 * nt + c16, d = 32 * p + 8 * g4;
-        const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
-        const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
-        const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
-        V8 xk, xq;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e0 = __builtin_amdgcn_exp2f(b0[j]), e1 = __builtin_amdgcn_exp2f(b1[j]);
-          xk[j] = (ET)(to_f(k0[j]) * e0);
-          xq[j] = (ET)(to_f(q0[j]) * e0);
-          xk[j + 4] = (ET)(to_f(k1[j]) * e1);
-          xq[j + 4] = (ET)(to_f(q1[j]) * e1);
+      if (!KDA) store_ap();
+      // K~^T = (e^{b_n - b} (.) K)^T in fragments (outer = the 16 key channels
+      // of state tile mt in the scan's row order, inner = token block p);
+      // KDA: K (.) e^{B_n - B}
+      if (KT) {
+        constexpr int NF = (DK / 16) * 2;
+        V8* ktg = (V8*)P.kt + ch * (int64_t)(C * DK / 8);
+        for (int f = wv; f < NF; f += 4) {
+          const int mt = f >> 1, p = f & 1;
+          const int d = state_row(mt, c16);
+          V8 x;
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 32 * p + kmap(g4, j);
+            x[j] = KDA ? (ET)(to_f(Ks[i][d]) * __builtin_amdgcn_exp2f(Bl[C - 1][d] - Bl[i][d]))
+                       : (ET)(to_f(Ks[i][d]) * __expf(bsv[C - 1] - bsv[i]));
+          }
+          ktg[f * 64 + lane] = x;
         }
-        kwg[f * 64 + lane] = xk;
-        qwg[f * 64 + lane] = xq;
       }
-      __syncthreads();  // the B table is read; A takes its bytes
-      store_ap_kda();
-    } else if (tid < C) {
-      // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
-      // holds e^{b_n} (rows past the end carry the last b)
-      P.gam[ch * (2 * C) + tid] = __expf(bs[tid]);
-      P.gam[ch * (2 * C) + C + tid] = __expf(bs[C - 1] - bs[tid]);
-    }
-    __syncthreads();  // K and the gate table are dead from here; T takes their bytes
+      if (KDA) {
+        // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
+        // with contiguous key channels 32p + 8g + j, the scan's state order
+        V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
+        V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
+        for (int f = wv; f < 4 * KB; f += 4) {
+          const int nt = f / KB, p = f - nt * KB;
+          const int r = 16 * nt + c16, d = 32 * p + 8 * g4;
+          const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
+          const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
+          const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
+          V8 xk, xq;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e0 = __builtin_amdgcn_exp2f(b0[j]), e1 = __builtin_amdgcn_exp2f(b1[j]);
+            xk[j] = (ET)(to_f(k0[j]) * e0);
+            xq[j] = (ET)(to_f(q0[j]) * e0);
+            xk[j + 4] = (ET)(to_f(k1[j]) * e1);
+            xq[j + 4] = (ET)(to_f(q1[j]) * e1);
+          }
+          kwg[f * 64 + lane] = xk;
+          qwg[f * 64 + lane] = xq;
+        }
+        __syncthreads();  // the B table is read; A takes its bytes
+        store_ap_kda();
+      } else if (tid < C) {
+        // GDN: e^{b_r} and e^{b_n - b_r} of every row; row 63 of the first
+        // holds e^{b_n} (rows past the end carry the last b)
+        P.gam[chm * (2 * C) + tid] = __expf(bsv[tid]);
+        P.gam[chm * (2 * C) + C + tid] = __expf(bsv[C - 1] - bsv[tid]);
+      }
+      __syncthreads();  // K and the gate table are dead from here; T takes their bytes
 
-    // ---- phase 2: #3 Solve --------------------------------------------------------
-    if (wv == 0) {
-      // level 0: the four 16x16 diagonal blocks of T by forward substitution,
-      // one column per lane (block lane/16, column lane%16).  Rows of A are
-      // read four entries at a time, LA rows ahead of the row being solved,
-      // so that the 16-step chain does not wait on each row's reads; four
-      // partial sums per row.
-      constexpr int LA = 3;
-      const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
-      floatx4 ar[16][4];
-      auto read_row = [&](int r) {
-#pragma unroll
-        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) ar[r][i4] = *(const floatx4*)&As[o + r][o + 4 * i4];
-      };
-#pragma unroll
-      for (int r = 1; r <= LA; ++r) read_row(r);
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r >= 1 && r + LA < 16) read_row(r + LA);
-        float acc[4] = {(r == cc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * i4 + e < r) acc[e] -= ar[r][i4][e] * t[4 * i4 + e];
+      // ---- phase 2: #3 Solve --------------------------------------------------------
+      if (wv == 0) {
+        // level 0: the four 16x16 diagonal blocks of T by forward substitution,
+        // one column per lane (block lane/16, column lane%16).  Rows of A are
+        // read four entries at a time, LA rows ahead of the row being solved,
+        // so that the 16-step chain does not wait on each row's reads; four
+        // partial sums per row.
+        constexpr int LA = 3;
+        const int bb = lane >> 4, cc = lane & 15, o = 16 * bb;
+        floatx4 ar[16][4];
+        auto read_row = [&](int r) {
+  #pragma unroll
+          for (int i4 = 0; i4 < (r + 3) / 4; ++i4) ar[r][i4] = *(const floatx4*)&As[o + r][o + 4 * i4];
+        };
+  #pragma unroll
+        for (int r = 1; r <= LA; ++r) read_row(r);
+        float t[16];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (r >= 1 && r + LA < 16) read_row(r + LA);
+          float acc[4] = {(r == cc) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+  #pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * i4 + e < r) acc[e] -= ar[r][i4][e] * t[4 * i4 + e];
+          }
+          t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
-        t[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
-    } else {
-      // the upper off-diagonal 16x16 blocks of T are zero
-      for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
-        const int blk = idx >> 8, e = idx & 255;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        Ts[16 * bi + (e >> 4)][16 * bj + (e & 15)] = 0.f;
-      }
-    }
-    __syncthreads();
-
-    // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (16-wide
-    // contractions, zero-padded to the 32-wide fragment)
-    if (wv < 2) {
-      const int b0 = 16 * (2 * wv), b1 = b0 + 16;
-      V8 a = {}, tb = {}, tl = {};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 4 * g4 + j;
-        a[j] = (ET)As[b1 + c16][b0 + k];
-        tb[j] = (ET)Ts[b0 + k][b0 + c16];
-        tl[j] = (ET)Ts[b1 + c16][b1 + k];
-      }
-      const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
-      V8 yb = {};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
-      const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
-    }
-    __syncthreads();
-
-    // level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
-    // and T2 are the finished 32x32 diagonal halves
-    if (wv < 2) {
-      const int jt = wv;
-      floatx4 z[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int r = 32 + 16 * m + c16;
-        V8 a, tb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int k = kmap(g4, j);
-          a[j] = (ET)As[r][k];
-          tb[j] = (ET)Ts[k][16 * jt + c16];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) Ts[o + r][o + cc] = t[r];
+      } else {
+        // the upper off-diagonal 16x16 blocks of T are zero
+        for (int idx = tid - 64; idx < 6 * 256; idx += 192) {
+          const int blk = idx >> 8, e = idx & 255;
+          const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+          const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+          Ts[16 * bi + (e >> 4)][16 * bj + (e & 15)] = 0.f;
         }
-        z[m] = mma(a, tb, zero4());
       }
-      const V8 zb = pack<ET>(z[0], z[1]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int r = 32 + 16 * m + c16;
-        V8 tl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
-        const floatx4 t = mma(tl, zb, zero4());
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
-      }
-    }
-    __syncthreads();
-
-    // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
-    // block p), eight per (chunk, head); the ones above the diagonal are zero.
-    // LF: diag(e^{b_n - b}) Tb instead (the scan then forms e^{b_n - b} (.) V'
-    // directly), and Tb itself staged in the io type, row-major, in the bytes
-    // of A for P Tb below.  A lane's eight entries of a fragment are two runs
-    // of four columns (kmap), read as two vectors of T and of beta.
-    constexpr int TBP = C + 8;  // LF: padded row of the staged Tb (io type)
-    ET(*TbL)[TBP] = (ET(*)[TBP])&As[0][0];
-    static_assert(!LF || C * TBP * sizeof(ET) <= sizeof(float) * C * TP, "staged Tb fits in the bytes of A");
-    {
-      const int nt = wv, r = 16 * nt + c16;
-      const float en = LF ? __expf(bs[C - 1] - bs[r]) : 1.f;
-      V8* tg = (V8*)P.tb + ch * (8 * 64);
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int c0 = 32 * p + 4 * g4, c1 = c0 + 16;
-        const floatx4 t0 = *(const floatx4*)&Ts[r][c0], t1 = *(const floatx4*)&Ts[r][c1];
-        const floatx4 b0 = *(const floatx4*)&betas[c0], b1 = *(const floatx4*)&betas[c1];
-        V8 x;
-        V4 y0, y1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float u0 = t0[j] * b0[j], u1 = t1[j] * b1[j];
-          x[j] = (ET)(u0 * en);
-          x[j + 4] = (ET)(u1 * en);
-          y0[j] = (ET)u0;
-          y1[j] = (ET)u1;
-        }
-        if constexpr (LF) {
-          *(V4*)&TbL[r][c0] = y0;
-          *(V4*)&TbL[r][c1] = y1;
-        }
-        // fragments (0, 1) and (1, 1) lie above the diagonal: zero, and no
-        // scan reads them, so they are not stored
-        if (2 * p <= nt) tg[(nt * 2 + p) * 64 + lane] = x;
-      }
-    }
-    if constexpr (LF) {
-      // P Tb for the output Map (the scan multiplies it with R = V - e^b X):
-      // tiles (it, pr) of (P Tb)^T = Tb^T P^T, packed in pairs into fragment
-      // (pr, p) with P's layout (outer = query token, inner = token).  The
-      // Tb^T fragments come from the staged rows by transposing reads: lane
-      // (c, g) gets Tb[32p + 4g + j][16 it + c] (and rows + 16), j = 0..3.
       __syncthreads();
-      floatx4 ptt[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        ptt[it] = zero4();
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int rr = 32 * p + 4 * g4 + (c16 >> 2), cc = 16 * it + 4 * (c16 & 3);
-          const V4 lo = lds_read_tr16<ET>(&TbL[rr][cc]), hi = lds_read_tr16<ET>(&TbL[rr + 16][cc]);
-          ptt[it] = mma(cat<ET>(lo, hi), pfr[p], ptt[it]);
+
+      // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (16-wide
+      // contractions, zero-padded to the 32-wide fragment)
+      if (wv < 2) {
+        const int b0 = 16 * (2 * wv), b1 = b0 + 16;
+        V8 a = {}, tb = {}, tl = {};
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = 4 * g4 + j;
+          a[j] = (ET)As[b1 + c16][b0 + k];
+          tb[j] = (ET)Ts[b0 + k][b0 + c16];
+          tl[j] = (ET)Ts[b1 + c16][b1 + k];
+        }
+        const floatx4 y = mma(a, tb, zero4());  // Y = A_10 T_00
+        V8 yb = {};
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) yb[j] = (ET)y[j];
+        const floatx4 t = mma(tl, yb, zero4());  // T_11 Y
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) Ts[b1 + 4 * g4 + e][b0 + c16] = -t[e];
+      }
+      __syncthreads();
+
+      // level 2: rows 32..63 x columns 32jt..32jt+15 = -T2 (A21 T1), where T1
+      // and T2 are the finished 32x32 diagonal halves
+      if (wv < 2) {
+        const int jt = wv;
+        floatx4 z[2];
+  #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int r = 32 + 16 * m + c16;
+          V8 a, tb;
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int k = kmap(g4, j);
+            a[j] = (ET)As[r][k];
+            tb[j] = (ET)Ts[k][16 * jt + c16];
+          }
+          z[m] = mma(a, tb, zero4());
+        }
+        const V8 zb = pack<ET>(z[0], z[1]);
+  #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int r = 32 + 16 * m + c16;
+          V8 tl;
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) tl[j] = (ET)Ts[r][32 + kmap(g4, j)];
+          const floatx4 t = mma(tl, zb, zero4());
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) Ts[32 + 16 * m + 4 * g4 + e][16 * jt + c16] = -t[e];
         }
       }
-      V8* pg = (V8*)P.pm + ch * (8 * 64);
-      pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(ptt[0], ptt[1]);
-      if (pr >= 2) pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(ptt[2], ptt[3]);
+      __syncthreads();
+
+      // #4: Tb = T diag(beta) as fragments (outer = token tile nt, inner = token
+      // block p), eight per (chunk, head); the ones above the diagonal are zero.
+      // LF: diag(e^{b_n - b}) Tb instead (the scan then forms e^{b_n - b} (.) V'
+      // directly), and Tb itself staged in the io type, row-major, in the bytes
+      // of A for P Tb below.  A lane's eight entries of a fragment are two runs
+      // of four columns (kmap), read as two vectors of T and of beta.
+      constexpr int TBP = C + 8;  // LF: padded row of the staged Tb (io type)
+      ET(*TbL)[TBP] = (ET(*)[TBP])&As[0][0];
+      static_assert(!LF || C * TBP * sizeof(ET) <= sizeof(float) * C * TP, "staged Tb fits in the bytes of A");
+      {
+        const int nt = wv, r = 16 * nt + c16;
+        const float en = LF ? __expf(bsv[C - 1] - bsv[r]) : 1.f;
+        V8* tg = (V8*)P.tb + chm * (8 * 64);
+  #pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int c0 = 32 * p + 4 * g4, c1 = c0 + 16;
+          const floatx4 t0 = *(const floatx4*)&Ts[r][c0], t1 = *(const floatx4*)&Ts[r][c1];
+          const floatx4 b0 = *(const floatx4*)&betv[c0], b1 = *(const floatx4*)&betv[c1];
+          V8 x;
+          V4 y0, y1;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float u0 = t0[j] * b0[j], u1 = t1[j] * b1[j];
+            x[j] = (ET)(u0 * en);
+            x[j + 4] = (ET)(u1 * en);
+            y0[j] = (ET)u0;
+            y1[j] = (ET)u1;
+          }
+          if constexpr (LF) {
+            *(V4*)&TbL[r][c0] = y0;
+            *(V4*)&TbL[r][c1] = y1;
+          }
+          // fragments (0, 1) and (1, 1) lie above the diagonal: zero, and no
+          // scan reads them, so they are not stored
+          if (2 * p <= nt) tg[(nt * 2 + p) * 64 + lane] = x;
+        }
+      }
+      if constexpr (LF) {
+        // P Tb for the output Map (the scan multiplies it with R = V - e^b X):
+        // tiles (it, pr) of (P Tb)^T = Tb^T P^T, packed in pairs into fragment
+        // (pr, p) with P's layout (outer = query token, inner = token).  The
+        // Tb^T fragments come from the staged rows by transposing reads: lane
+        // (c, g) gets Tb[32p + 4g + j][16 it + c] (and rows + 16), j = 0..3.
+        __syncthreads();
+        floatx4 ptt[4];
+  #pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          ptt[it] = zero4();
+  #pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int rr = 32 * p + 4 * g4 + (c16 >> 2), cc = 16 * it + 4 * (c16 & 3);
+            const V4 lo = lds_read_tr16<ET>(&TbL[rr][cc]), hi = lds_read_tr16<ET>(&TbL[rr + 16][cc]);
+            ptt[it] = mma(cat<ET>(lo, hi), pfr[p], ptt[it]);
+          }
+        }
+        V8* pg = (V8*)P.pm + chm * (8 * 64);
+        pg[(pr * 2 + 0) * 64 + lane] = pack<ET>(ptt[0], ptt[1]);
+        if (pr >= 2) pg[(pr * 2 + 1) * 64 + lane] = pack<ET>(ptt[2], ptt[3]);
+      }
     }
     if (!PF) break;
     u += gridDim.x;
@@ -889,9 +911,9 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
 // Workgroups of one prep kernel variant that fit on the chip at once (cached
 // per variant and device: the variants differ in registers and LDS).  Host
 // threads may race to fill an entry; they all compute the same value.
-template <int DK, bool KDA, typename ET, bool KT>
+template <int DK, bool KDA, typename ET, bool KT, bool G2>
 static int64_t resident_groups() {
-  auto kern = prep_kernel<DK, KDA, ET, KT, true>;
+  auto kern = prep_kernel<DK, KDA, ET, KT, true, G2>;
   static std::atomic<int64_t> cached[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -908,10 +930,10 @@ static int64_t resident_groups() {
   return fit;
 }
 
-template <int DK, bool KDA, typename ET, bool KT>
+template <int DK, bool KDA, typename ET, bool KT, bool G2 = false>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  auto kern = prep_kernel<DK, KDA, ET, KT, true>;
-  const int64_t fit = resident_groups<DK, KDA, ET, KT>();
+  auto kern = prep_kernel<DK, KDA, ET, KT, true, G2>;
+  const int64_t fit = resident_groups<DK, KDA, ET, KT, G2>();
   const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, nblk);
   return hipGetLastError();
@@ -925,6 +947,8 @@ hipError_t launch_prep(const PrepParams& P, int64_t nblk, hipStream_t st) {
     return launch_prep_v<DK, KDA, ET, true>(P, nblk, st);
   else if (P.kt)
     return launch_prep_v<DK, false, ET, true>(P, nblk, st);
+  else if (P.grp % 2 == 0)  // grouped heads: value heads in pairs sharing K, Q
+    return launch_prep_v<DK, false, ET, false, true>(P, nblk / 2, st);
   else
     return launch_prep_v<DK, false, ET, false>(P, nblk, st);
 }
