@@ -93,10 +93,22 @@ struct HItem {
   int n;           // the segment's chunks
 };
 
-__device__ __forceinline__ bool hs_item(const HScanParams& P, int nseg, HItem& it) {
+__device__ __forceinline__ bool hs_item(const HScanParams& P, int nseg, HItem& it, bool pairs = false) {
   const int b = blockIdx.x;
-  const int r = b / nseg;
+  int r = b / nseg;
   it.sg = b - r * nseg;
+  // One pass (`pairs`: the value kernel with np = 1, whose outputs are
+  // indexed by unit, not by workgroup) with grouped heads: the value heads
+  // of one query/key head read
+  // the same K and Q rows, so they go to one XCD (workgroups are dealt to
+  // the eight XCDs in turn) and share its L2: workgroup b takes member
+  // (b / 8) % grp of query/key group ((b / 8) / grp) * 8 + b % 8, so each run
+  // of 8 grp workgroups still covers 8 grp consecutive units (longest
+  // first when packed).
+  if (pairs && nseg == 1 && P.grp > 1 && (P.units / P.grp) % 8 == 0) {
+    const int y = b / 8;
+    r = ((y / P.grp) * 8 + b % 8) * P.grp + y % P.grp;
+  }
   if (r >= P.units) return false;
   if (P.s.seq_order) {
     it.seq = P.s.seq_order[r / P.h_v];
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(448) void hscan_value_kernel(HScanParams P) {
   __shared__ __attribute__((aligned(16))) float sink[64];
 
   HItem it;
-  if (!hs_item(P, P.np, it)) return;  // the whole workgroup: past the last unit
+  if (!hs_item(P, P.np, it, P.np == 1)) return;  // the whole workgroup: past the last unit
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
