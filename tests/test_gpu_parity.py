@@ -277,17 +277,19 @@ def test_deterministic_and_guard_bands(drla):
 
 # ---- per-kernel intermediates against the chunkwise oracle ---------------
 
-@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("kind,h_v", [("gdn", 2), ("kda", 2), ("gdn", 4)])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
-def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
+def test_intermediates_match_chunked_oracle(drla, kind, h_v, io, dk, dv):
     """Prep outputs (T diag(beta), P, K~^T; KDA: K e^B, Q e^B, e^{b_n}; for
     the LDS-fed GDN scan diag(e^{b_n - b}) T diag(beta) and P T diag(beta))
     and the scan's V' and per-chunk state, against the fp64 chunkwise form's
     intermediates on the same inputs, for every chunk (the last one short)."""
     import oracle
-    print(f"case intermediates kind={kind} io={io} dk={dk} dv={dv}", flush=True)
-    x = _case(kind, io, dk, dv, lens=(250,), h_qk=1, h_v=2, h0_std=0.1)
+    # one query/key head for h_v value heads: with 16-bit GDN inputs prep takes
+    # them in pairs sharing K and Q (h_v = 4: two pairs)
+    print(f"case intermediates kind={kind} h_v={h_v} io={io} dk={dk} dv={dv}", flush=True)
+    x = _case(kind, io, dk, dv, lens=(250,), h_qk=1, h_v=h_v, h0_std=0.1)
     d = to_device(x)
     dt = torch.float32 if io == "f32" else torch.bfloat16
     kda = kind == "kda"
@@ -317,7 +319,7 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
     krow = np.array([state_row(r // 16, r % 16) for r in range(dk)])
     krow_inv = np.argsort(krow)
     worst = {}
-    for h in range(2):
+    for h in range(h_v):
         for c in range(nc):
             it = inter[h][c]
             n = it["W"].shape[0]
@@ -354,7 +356,7 @@ def test_intermediates_match_chunked_oracle(drla, kind, io, dk, dv):
                 want["gamma"] = it["gamma"]
             for name in got:
                 worst[name] = max(worst.get(name, 0.0), rel_err(got[name], want[name]))
-    print(kind, io, dk, dv, {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+    print(kind, h_v, io, dk, dv, {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     tol = TOL[io]
     for name, e in worst.items():
         assert e <= tol, f"{name}: {e}"
