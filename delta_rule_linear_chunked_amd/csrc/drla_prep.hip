@@ -911,9 +911,9 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
 // Workgroups of one prep kernel variant that fit on the chip at once (cached
 // per variant and device: the variants differ in registers and LDS).  Host
 // threads may race to fill an entry; they all compute the same value.
-template <int DK, bool KDA, typename ET, bool KT, bool G2>
+template <int DK, bool KDA, typename ET, bool KT, bool PF, bool G2>
 static int64_t resident_groups() {
-  auto kern = prep_kernel<DK, KDA, ET, KT, true, G2>;
+  auto kern = prep_kernel<DK, KDA, ET, KT, PF, G2>;
   static std::atomic<int64_t> cached[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -930,12 +930,21 @@ static int64_t resident_groups() {
   return fit;
 }
 
+// Calls whose units all fit on the chip at once in one-unit workgroups take
+// that variant: without the next unit's loads held in registers it needs
+// about half the registers, so twice as many workgroups fit per CU and every
+// unit starts at once.  Larger calls take the persistent grid, which loads
+// a workgroup's next unit while it computes the current one.
 template <int DK, bool KDA, typename ET, bool KT, bool G2 = false>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  auto kern = prep_kernel<DK, KDA, ET, KT, true, G2>;
-  const int64_t fit = resident_groups<DK, KDA, ET, KT, G2>();
+  const int64_t fit1 = resident_groups<DK, KDA, ET, KT, false, G2>();
+  if (nblk <= fit1) {
+    hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, false, G2>), dim3((unsigned)nblk), dim3(256), 0, st, P, nblk);
+    return hipGetLastError();
+  }
+  const int64_t fit = resident_groups<DK, KDA, ET, KT, true, G2>();
   const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, nblk);
+  hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, true, G2>), grid, dim3(256), 0, st, P, nblk);
   return hipGetLastError();
 }
 
