@@ -930,19 +930,21 @@ static int64_t resident_groups() {
   return fit;
 }
 
-// Calls whose units all fit on the chip at once in one-unit workgroups take
-// that variant: without the next unit's loads held in registers it needs
-// about half the registers, so twice as many workgroups fit per CU and every
-// unit starts at once.  Larger calls take the persistent grid, which loads
-// a workgroup's next unit while it computes the current one.
+// One-unit workgroups hold no next unit's loads in registers, so where
+// registers set the occupancy (GDN) about twice as many fit per CU as in the
+// persistent grid, and they win at every size.  Where LDS sets it (KDA, two
+// per CU either way) the persistent grid, which loads a workgroup's next
+// unit while it computes the current one, wins once the units do not all
+// fit at once.
 template <int DK, bool KDA, typename ET, bool KT, bool G2 = false>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
   const int64_t fit1 = resident_groups<DK, KDA, ET, KT, false, G2>();
-  if (nblk <= fit1) {
+  const int64_t fit = resident_groups<DK, KDA, ET, KT, true, G2>();
+  if (nblk <= fit1 || fit1 > fit) {
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, false, G2>), dim3((unsigned)nblk), dim3(256), 0, st, P, nblk);
     return hipGetLastError();
   }
-  const int64_t fit = resident_groups<DK, KDA, ET, KT, true, G2>();
   const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
   hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, true, G2>), grid, dim3(256), 0, st, P, nblk);
   return hipGetLastError();
