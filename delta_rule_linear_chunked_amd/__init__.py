@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     DECAY_ONLY,
     SERIAL,
     HEAD_SCAN,
+    COLUMN_SCAN,
     NOALLOC_SCRATCH_BYTES,
     DrlaError,
     PreparedPrefill,
@@ -31,4 +32,5 @@ from ._lib import (  # noqa: F401
 __all__ = ["gdn_prefill", "kda_prefill", "gdn_decode", "kda_decode", "decay_prefill",
            "decay_decode", "DECAY_ONLY", "workspace_bytes", "workspace_layout",
            "load_library", "lib_path", "prefill_noalloc", "DrlaError", "KEEP_INTERMEDIATES", "SERIAL", "HEAD_SCAN",
+           "COLUMN_SCAN",
            "NOALLOC_SCRATCH_BYTES", "prepare_prefill", "PreparedPrefill"]

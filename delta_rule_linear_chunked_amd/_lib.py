@@ -45,6 +45,7 @@ KEEP_INTERMEDIATES = 1
 DECAY_ONLY = 2
 SERIAL = 4
 HEAD_SCAN = 8
+COLUMN_SCAN = 16
 
 
 def lib_path() -> str:

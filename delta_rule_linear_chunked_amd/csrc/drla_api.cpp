@@ -119,17 +119,25 @@ static int64_t max_chunks(const drla_problem* p, const int32_t* cu_host) {
   return m;
 }
 
-constexpr int kKnownFlags = DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL | DRLA_HEAD_SCAN;
+constexpr int kKnownFlags = DRLA_KEEP_INTERMEDIATES | DRLA_DECAY_ONLY | DRLA_SERIAL | DRLA_HEAD_SCAN | DRLA_COLUMN_SCAN;
+
+// Unknown flags and the two scan choices together are rejected.
+static drla_status check_flags(int flags) {
+  if (flags & ~kKnownFlags) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if ((flags & DRLA_HEAD_SCAN) && (flags & DRLA_COLUMN_SCAN))
+    return fail(DRLA_ERR_UNSUPPORTED, "DRLA_HEAD_SCAN and DRLA_COLUMN_SCAN exclude each other");
+  return DRLA_OK;
+}
 
 // The head-resident scan serves scalar-gate calls with 16-bit inputs (GDN,
 // decay-only) that keep no intermediates: always with DRLA_HEAD_SCAN, and
 // without flags where its timing model predicts it faster
 // (drla_auto_head_scan, at 256 compute units like the workspace); with
-// DRLA_SERIAL alone the per-16-column scan runs in one pass.
+// DRLA_COLUMN_SCAN, or DRLA_SERIAL alone, the per-16-column scan runs.
 static bool uses_hs(const drla_problem* p, int64_t nc, int64_t max_cps, bool kda, int flags) {
   if (kda || p->io_dtype == DRLA_F32 || (flags & DRLA_KEEP_INTERMEDIATES)) return false;
   if (flags & DRLA_HEAD_SCAN) return true;
-  if (flags & DRLA_SERIAL) return false;
+  if (flags & (DRLA_SERIAL | DRLA_COLUMN_SCAN)) return false;
   return p->n_seqs >= 1 && drla_auto_head_scan((int64_t)p->n_seqs * p->h_v, max_cps, nc * p->h_v, p->dk, p->dv, 256);
 }
 
@@ -208,7 +216,7 @@ drla_status run(bool kda, int flags, const drla_problem* p, const void* q, const
     return fail(DRLA_ERR_SEQLENS, "cu_seqlens_dev and cu_seqlens_host must both be set or both NULL");
   drla_status st = check_problem(p, cu_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~kKnownFlags) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if ((st = check_flags(flags)) != DRLA_OK) return st;
   // one packed sequence (cu_seqlens = {0, T}, checked above) is a dense call
   if (cu_host && !packed(p, cu_host)) cu_dev = cu_host = nullptr;
   const bool decay = (flags & DRLA_DECAY_ONLY) != 0;
@@ -399,7 +407,7 @@ drla_status drla_workspace_layout(int kda, const drla_problem* p, const int32_t*
   if (!out) return fail(DRLA_ERR_NULL, "layout output is NULL");
   drla_status st = check_problem(p, cu_seqlens_host, &nc);
   if (st != DRLA_OK) return st;
-  if (flags & ~kKnownFlags) return fail(DRLA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if ((st = check_flags(flags)) != DRLA_OK) return st;
   const bool pk = packed(p, cu_seqlens_host);
   layout_of(p, nc, pk, max_chunks(p, pk ? cu_seqlens_host : nullptr), kda != 0, flags, out);
   return DRLA_OK;
@@ -503,6 +511,6 @@ const char* drla_status_str(drla_status s) {
 
 const char* drla_last_error(void) { return g_last_error.c_str(); }
 
-int drla_version(void) { return 6; }
+int drla_version(void) { return 7; }
 
 }  // extern "C"

@@ -197,10 +197,12 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
 #define DRLA_DECAY_ONLY 2         /* decay-only linear attention (decay_prefill); beta unused */
 #define DRLA_SERIAL 4             /* scan every sequence in one pass (no segment split) */
 #define DRLA_HEAD_SCAN 8          /* scalar gate, 16-bit io: the head-resident scan */
+#define DRLA_COLUMN_SCAN 16       /* the per-16-column scan, its segment split as usual */
 
 /* gdn_prefill (kda == 0) or kda_prefill (kda != 0) with options.
  *   flags         any combination of DRLA_KEEP_INTERMEDIATES, DRLA_DECAY_ONLY,
- *                 DRLA_SERIAL and DRLA_HEAD_SCAN, or 0.
+ *                 DRLA_SERIAL and one of DRLA_HEAD_SCAN, DRLA_COLUMN_SCAN,
+ *                 or 0 (both scan flags: DRLA_ERR_UNSUPPORTED).
  *                 The state scan runs one workgroup per (sequence, head,
  *                 16 state columns).  Calls with dk == dv whose
  *                 U = n_seqs * h_v * dv/16 column blocks
@@ -224,10 +226,13 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *                 scalar-gate calls with 16-bit inputs and dk = dv = 128
  *                 take the head-resident scan where its measured timing
  *                 model predicts it at least 10% faster (8 to 16 heads and
- *                 long sequences; the rule is the one in the library's
+ *                 long sequences, or many more (head, 16-column) chains
+ *                 than compute units; the rule is the one in the library's
  *                 launch header, drla_auto_head_scan, at 256 compute units).
- *                 DRLA_SERIAL runs either scan in one pass (same results up
- *                 to rounding); alone it selects the per-16-column scan.
+ *                 DRLA_COLUMN_SCAN keeps the per-16-column scan, segments
+ *                 included.  DRLA_SERIAL runs either scan in one pass (same
+ *                 results up to rounding); alone it selects the
+ *                 per-16-column scan.
  *                 DRLA_DECAY_ONLY runs decay_prefill (kda selects the
  *                 per-channel gate; beta is ignored and may be NULL).
  *                 With DRLA_KEEP_INTERMEDIATES the kernels

@@ -152,3 +152,36 @@ def test_automatic_head_scan_many_units(drla):
     print(f"  rel_err o={eo:.3e} ht={eh:.3e} (column scan {rel_err(o1, o_ref):.3e})", flush=True)
     assert np.isfinite(o).all() and eo <= TOL["bf16"] and eh <= TOL["bf16"]
     assert rel_err(o1, o_ref) <= TOL["bf16"] and rel_err(ht1, ht_ref) <= TOL["bf16"]
+
+
+def test_column_scan_flag(drla):
+    """DRLA_COLUMN_SCAN at a shape where the model takes the head-resident
+    scan (8 heads, 16,384 tokens): the layout shows the per-16-column scan's
+    segment region, the workspace region holding the segments' states is
+    written, and o and ht match the oracle and the one-pass scan."""
+    print("case column-scan flag h_v=8 T=16384", flush=True)
+    spec = W.small_spec("gdn", lens=(16384,), h_qk=4, h_v=8, dk=128, dv=128, io="bf16",
+                        g_lo=0.001, g_hi=0.05, h0_std=0.05, seed=63)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    assert drla.workspace_layout(d["q"].shape, d["v"].shape, d["q"].dtype)["head_scan"] == 1
+    lay = drla.workspace_layout(d["q"].shape, d["v"].shape, d["q"].dtype, flags=drla.COLUMN_SCAN)
+    assert lay["head_scan"] == 0 and lay["hs"] == 0 and lay["seg"] > 0
+    ws = torch.full((lay["total"],), 255, dtype=torch.uint8, device="cuda")
+    o, ht = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], workspace=ws,
+                             flags=drla.COLUMN_SCAN)
+    torch.cuda.synchronize()
+    mid = ws[lay["seg"]:lay["seg"] + 8 * 128 * 128 * 4].view(torch.float32)
+    assert bool(torch.isfinite(mid).all()), "the per-16-column split did not run"
+    o1, ht1 = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    o, o1 = o.float().cpu().numpy(), o1.float().cpu().numpy()
+    ht, ht1 = ht.cpu().numpy(), ht1.cpu().numpy()
+    o_ref, ht_ref = run_oracle(x)
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e}", flush=True)
+    assert np.isfinite(o).all() and eo <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert rel_err(o, o1) <= TOL["bf16"] and rel_err(ht, ht1) <= TOL["bf16"]
+    with pytest.raises(RuntimeError):
+        drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"],
+                         flags=drla.COLUMN_SCAN | drla.HEAD_SCAN)

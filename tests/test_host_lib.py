@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
             "drla_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.drla_version() == 6
+    assert lib.drla_version() == 7
 
 
 def test_prefill_status_needs_no_device_for_unpacked_calls(lib):
@@ -238,7 +238,7 @@ def test_workspace_bytes_and_layout(lib):
     assert kl.hs == 0 and kl.seg == 0   # intermediates: the per-16-column scan, one pass
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 0
     assert kl.hs == 0 and kl.seg == 0   # DRLA_SERIAL: one pass
-    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 16, ctypes.byref(kl)) == 3
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 32, ctypes.byref(kl)) == 3
     # 11 heads of 8 column blocks: 264 scan workgroups, no segment region
     p11 = _prob(n_seqs=1, h_qk=11, h_v=11, dk=128, dv=128, io=0, T=4096)
     assert lib.drla_workspace_layout(0, ctypes.byref(p11), None, 0, ctypes.byref(kl)) == 0
@@ -302,6 +302,7 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
     (0, 0, 16, 128, 16384, 0, True),      # 16 heads, long: the head-resident scan
     (0, 2, 8, 128, 16384, 0, True),       # fp16, 8 heads
     (0, 0, 16, 128, 16384, 4, False),     # DRLA_SERIAL keeps the per-16-column scan
+    (0, 0, 16, 128, 16384, 16, False),    # DRLA_COLUMN_SCAN keeps it too
     (0, 0, 16, 128, 4096, 0, False),      # short: per-16-column
     (0, 0, 32, 128, 65536, 0, False),     # 32 heads: per-16-column
     (0, 0, 2, 128, 65536, 0, False),      # 2 heads: the per-16-column split
@@ -322,6 +323,21 @@ def test_automatic_head_scan_choice(lib, kda, io, h_v, d, T, flags, want):
     assert (lay.hs > 0) == want
     if want:
         assert lay.seg == 0
+
+
+def test_column_scan_flag(lib):
+    """DRLA_COLUMN_SCAN keeps the per-16-column scan with its segment split
+    where the model takes the head-resident scan; it excludes DRLA_HEAD_SCAN."""
+    from delta_rule_linear_chunked_amd._lib import COLUMN_SCAN, HEAD_SCAN, Layout
+    p = _prob(n_seqs=1, h_qk=1, h_v=8, dk=128, dv=128, io=0, T=65536)
+    lay = Layout()
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(lay)) == 0
+    assert lay.head_scan == 1 and lay.hs > 0 and lay.seg == 0
+    assert lib.drla_workspace_layout(0, ctypes.byref(p), None, COLUMN_SCAN, ctypes.byref(lay)) == 0
+    assert lay.head_scan == 0 and lay.hs == 0 and lay.seg > 0
+    st = lib.drla_workspace_layout(0, ctypes.byref(p), None, COLUMN_SCAN | HEAD_SCAN, ctypes.byref(lay))
+    assert st == 3  # DRLA_ERR_UNSUPPORTED
+    assert b"exclude each other" in lib.drla_last_error()
 
 
 def _model_choice(units, max_cps, unit_chunks, cus=256):
