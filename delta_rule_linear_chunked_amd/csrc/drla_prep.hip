@@ -225,11 +225,14 @@ __device__ __forceinline__ int kpos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e
 // The scan's operands K e^{B}, Q e^{B}, (K e^{B_n - B})^T and e^{B_n}
 // take non-positive exponents only.
 //
-// LDS is reused across phases: K (and KDA's Q rows and B table) live until
+// KDA's Q rows never go to LDS: each wave reads the row fragments of the Q
+// tiles it multiplies straight into registers (and writes those tiles'
+// Q e^{B}).  LDS is reused across phases: K (and KDA's B table) live until
 // the chunk operands are written, T from the solve on, in the same bytes;
 // KDA's A and the runs' totals take the bytes of the B table.
 template <int DK, bool KDA, typename ET, bool KT, bool PF, bool G2>
 __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(PrepParams P, int64_t nunits) {
+  static_assert(!(KDA && PF), "KDA: one unit per workgroup (its Q fragments stay in registers)");
   typedef typename VT<ET>::v8 V8;
   typedef typename VT<ET>::v16b V16;
   constexpr int PE = VT<ET>::per16;
@@ -247,21 +250,22 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   constexpr int NKV = C * KV / 256;              // K pieces per thread
   constexpr int KS_BYTES = C * KP * (int)sizeof(ET);
   constexpr int TS_BYTES = C * TP * 4;
-  constexpr int NT = KDA ? 2 : 1;                // K-sized tiles: K rows, and KDA's Q rows
   constexpr int BP = DK + 4;                     // KDA: padded row of the B table (floats)
   constexpr int BL_BYTES = KDA ? C * BP * 4 : 0;
   static_assert(!KDA || (BL_BYTES >= C * TP * 4 && BL_BYTES >= 256 / (DK / 8) * DK * 4),
                 "KDA: A and the runs' totals fit in the bytes of the B table");
-  constexpr int U_BYTES = NT * KS_BYTES + BL_BYTES > TS_BYTES ? NT * KS_BYTES + BL_BYTES : TS_BYTES;
+  // KDA: the B table (then A) after the larger of the K rows and T, so that
+  // the solve's A and T never share bytes
+  constexpr int BL_OFF = KS_BYTES > TS_BYTES ? KS_BYTES : TS_BYTES;
+  constexpr int U_BYTES = KDA ? BL_OFF + BL_BYTES : (KS_BYTES > TS_BYTES ? KS_BYTES : TS_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char un[U_BYTES];
   __shared__ __attribute__((aligned(16))) float As_st[KDA ? 1 : C][TP];  // A (GDN)
   __shared__ __attribute__((aligned(16))) float bs[NG][C];     // per value head of the unit
   __shared__ __attribute__((aligned(16))) float betas[NG][C];
   __shared__ floatx4 pxch[KDA ? 64 : 1];  // KDA: one P^T tile passed between waves
   ET(*Ks)[KP] = (ET(*)[KP])un;                   // K rows (phases 0-1)
-  ET(*Qs)[KP] = (ET(*)[KP])(un + KS_BYTES);      // KDA: Q rows (phases 0-1)
-  float(*Bl)[BP] = (float(*)[BP])(un + NT * KS_BYTES);  // KDA: B log2(e) (phases 0-1)
-  float(*As)[TP] = KDA ? (float(*)[TP])(un + NT * KS_BYTES) : As_st;  // A (KDA: after the B table)
+  float(*Bl)[BP] = (float(*)[BP])(un + BL_OFF);  // KDA: B log2(e) (phases 0-1)
+  float(*As)[TP] = KDA ? (float(*)[TP])(un + BL_OFF) : As_st;  // A (KDA: in the B table's bytes)
   float(*Ts)[TP] = (float(*)[TP])un;             // T (phase 2 on)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -289,7 +293,11 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
   // a unit's inputs in registers; tokens past the sequence end read as zero
   // (beta = g = 0: they write nothing and do not decay)
   V16 kpre[NKV];
-  V16 qvpre[KDA ? NKV : 1];  // KDA: Q rows, staged like K
+  // KDA: Q row fragments (key channels 32p + 8g .. +7 of row 16 t + c) of
+  // row tile qt_a = (w + 3) mod 4, whose P^T tiles and Q e^{B} this wave
+  // forms, and of qt_b, the other row tile it multiplies (waves 1 and 3)
+  V8 qa[KDA ? KB : 1], qb[KDA ? KB : 1];
+  const int qt_a = (wv + 3) & 3, qt_b = wv == 1 ? 2 : wv == 3 ? 3 : qt_a;
   V8 qpre[KDA ? 1 : KB];     // GDN: Q fragments of this wave's P tile
   float bpre = 0.f, gpre = 0.f;
   floatx4 gvpre[KDA ? GR : 1][2];  // KDA: gates of this thread's rows and 8 channels
@@ -302,12 +310,14 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       kpre[i] = x;
     }
     if (KDA) {
+      const int ra = 16 * qt_a + c16, rb = 16 * qt_b + c16;
 #pragma unroll
-      for (int i = 0; i < NKV; ++i) {
-        const int idx = tid + 256 * i, r = idx / KV, cv = idx - r * KV;
-        V16 x = {};
-        if (r < U.len) x = *(const V16*)(qg + ((U.t0 + r) * P.h_qk + U.hk) * DK + cv * PE);
-        qvpre[i] = x;
+      for (int p = 0; p < KB; ++p) {
+        V8 x = {}, y = {};
+        if (ra < U.len) x = *(const V8*)(qg + ((U.t0 + ra) * P.h_qk + U.hk) * DK + 32 * p + 8 * g4);
+        if (rb < U.len) y = *(const V8*)(qg + ((U.t0 + rb) * P.h_qk + U.hk) * DK + 32 * p + 8 * g4);
+        qa[p] = x;
+        qb[p] = y;
       }
     } else {
 #pragma unroll
@@ -367,7 +377,6 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       } else {
         *(V16*)&Ks[r][cv * PE] = kpre[i];
       }
-      if (KDA) *(V16*)&Qs[r][cv * PE] = qvpre[i];
     }
     // #1 Gate: in-chunk prefix sums of the log-decay
     if (tid < NG * C) {
@@ -519,6 +528,23 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
         }
         return y;
       };
+      // the same for a fragment held in registers (KDA's Q rows)
+      auto scaled_v = [&](const V8& x, const floatx8& f) -> V8 {
+        V8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (ET)(to_f(x[j]) * f[j]);
+        return y;
+      };
+      auto scaled_vd = [&](const V8& x, const floatx8& f) -> DV8 {
+        if constexpr (kF32Diag) {
+          floatx8 y;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[j] = to_f(x[j]) * f[j];
+          return y;
+        } else {
+          return scaled_v(x, f);
+        }
+      };
       auto scaled_d = [&](const ET* xrow, int d, const floatx8& f) -> DV8 {
         if constexpr (kF32Diag) {
           const V4 x0 = *(const V4*)(xrow + d), x1 = *(const V4*)(xrow + d + 4);
@@ -533,11 +559,12 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
           return scaled(xrow, d, f);
         }
       };
-      // row tile I against column tiles 0 .. nj-1, into acc[0 .. nj), pt[0 .. nj)
-      auto offdiag = [&](int I, int nj, int d) {
+      // row tile I (its Q fragment q) against column tiles 0 .. nj-1, into
+      // acc[0 .. nj), pt[0 .. nj)
+      auto offdiag = [&](int I, int nj, int d, const V8& q) {
         const int r = 16 * I + c16, m = 16 * I;
         const floatx8 f = factors(r, m, d, false);
-        const V8 kr = scaled(&Ks[r][0], d, f), qr = scaled(&Qs[r][0], d, f);
+        const V8 kr = scaled(&Ks[r][0], d, f), qr = scaled_v(q, f);
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
           if (t < nj) {
@@ -547,28 +574,28 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
           }
         }
       };
-      // diagonal tile I, into acc[sl], pt[sl]
-      auto diag = [&](int I, int sl, int d) {
+      // diagonal tile I (its Q fragment q), into acc[sl], pt[sl]
+      auto diag = [&](int I, int sl, int d, const V8& q) {
         const int r = 16 * I + c16, c = 16 * I + 8;
         const floatx8 f = factors(r, c, d, false), gi = factors(r, c, d, true);
         const DV8 kg = scaled_d(&Ks[r][0], d, gi);
         acc[sl] = mma(scaled_d(&Ks[r][0], d, f), kg, acc[sl]);
-        pt[sl] = mma(kg, scaled_d(&Qs[r][0], d, f), pt[sl]);
+        pt[sl] = mma(kg, scaled_vd(q, f), pt[sl]);
       };
 #pragma unroll
       for (int p = 0; p < KB; ++p) {
         const int d = 32 * p + 8 * g4;
         if (wv == 0) {
-          offdiag(3, 3, d);
+          offdiag(3, 3, d, qa[p]);
         } else if (wv == 1) {
-          offdiag(2, 2, d);
-          diag(0, 2, d);
+          offdiag(2, 2, d, qb[p]);
+          diag(0, 2, d, qa[p]);
         } else if (wv == 2) {
-          offdiag(1, 1, d);
-          diag(1, 1, d);
+          offdiag(1, 1, d, qa[p]);
+          diag(1, 1, d, qa[p]);
         } else {
-          diag(2, 0, d);
-          diag(3, 1, d);
+          diag(2, 0, d, qa[p]);
+          diag(3, 1, d, qb[p]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -714,23 +741,24 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
       }
       if (KDA) {
         // K e^{B} and Q e^{B} as row fragments (token tile nt, inner block p)
-        // with contiguous key channels 32p + 8g + j, the scan's state order
+        // with contiguous key channels 32p + 8g + j, the scan's state order;
+        // each wave writes token tile qt_a, whose Q rows it holds
         V8* kwg = (V8*)P.kw + ch * (int64_t)(C * DK / 8);
         V8* qwg = (V8*)P.qw + ch * (int64_t)(C * DK / 8);
-        for (int f = wv; f < 4 * KB; f += 4) {
-          const int nt = f / KB, p = f - nt * KB;
-          const int r = 16 * nt + c16, d = 32 * p + 8 * g4;
+  #pragma unroll
+        for (int p = 0; p < KB; ++p) {
+          const int f = qt_a * KB + p;
+          const int r = 16 * qt_a + c16, d = 32 * p + 8 * g4;
           const V4 k0 = *(const V4*)&Ks[r][d], k1 = *(const V4*)&Ks[r][d + 4];
-          const V4 q0 = *(const V4*)&Qs[r][d], q1 = *(const V4*)&Qs[r][d + 4];
           const floatx4 b0 = *(const floatx4*)&Bl[r][d], b1 = *(const floatx4*)&Bl[r][d + 4];
           V8 xk, xq;
   #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float e0 = __builtin_amdgcn_exp2f(b0[j]), e1 = __builtin_amdgcn_exp2f(b1[j]);
             xk[j] = (ET)(to_f(k0[j]) * e0);
-            xq[j] = (ET)(to_f(q0[j]) * e0);
+            xq[j] = (ET)(to_f(qa[p][j]) * e0);
             xk[j + 4] = (ET)(to_f(k1[j]) * e1);
-            xq[j + 4] = (ET)(to_f(q1[j]) * e1);
+            xq[j + 4] = (ET)(to_f(qa[p][j + 4]) * e1);
           }
           kwg[f * 64 + lane] = xk;
           qwg[f * 64 + lane] = xq;
@@ -932,21 +960,25 @@ static int64_t resident_groups() {
 
 // One-unit workgroups hold no next unit's loads in registers, so where
 // registers set the occupancy (GDN) about twice as many fit per CU as in the
-// persistent grid, and they win at every size.  Where LDS sets it (KDA, two
-// per CU either way) the persistent grid, which loads a workgroup's next
-// unit while it computes the current one, wins once the units do not all
-// fit at once.
+// persistent grid, and they win at every size; the persistent grid, which
+// loads a workgroup's next unit while it computes the current one, is taken
+// only where it fits as many per CU and the units do not all fit at once.
+// KDA always takes one unit per workgroup: its Q fragments stay in
+// registers, and without Q rows in LDS three workgroups fit per CU at
+// dk = 128 (16-bit inputs) against two in the persistent grid.
 template <int DK, bool KDA, typename ET, bool KT, bool G2 = false>
 static hipError_t launch_prep_v(const PrepParams& P, int64_t nblk, hipStream_t st) {
-  const int64_t fit1 = resident_groups<DK, KDA, ET, KT, false, G2>();
-  const int64_t fit = resident_groups<DK, KDA, ET, KT, true, G2>();
-  if (nblk <= fit1 || fit1 > fit) {
-    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, false, G2>), dim3((unsigned)nblk), dim3(256), 0, st, P, nblk);
-    return hipGetLastError();
+  if constexpr (!KDA) {
+    const int64_t fit1 = resident_groups<DK, KDA, ET, KT, false, G2>();
+    const int64_t fit = resident_groups<DK, KDA, ET, KT, true, G2>();
+    if (nblk > fit1 && fit1 <= fit) {
+      const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
+      hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, true, G2>), grid, dim3(256), 0, st, P, nblk);
+      return hipGetLastError();
+    }
   }
-  const dim3 grid((unsigned)(nblk < fit ? nblk : fit));
-  hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, true, G2>), grid, dim3(256), 0, st, P, nblk);
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prep_kernel<DK, KDA, ET, KT, false, G2>), dim3((unsigned)nblk), dim3(256), 0, st, P, nblk);
   return hipGetLastError();
 }
 
