@@ -119,6 +119,10 @@ hipError_t launch_scan(const ScanParams& P, int64_t nblk, bool inspect, hipStrea
 // GDN with 16-bit inputs (T = bf16 or f16): the LDS-fed scan (drla_scan_lds.hip)
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
+// KDA with 16-bit inputs: the same LDS-fed scan on prep's K e^B, K~^T and
+// Q e^B fragments
+template <int DK, int DV, typename T>
+hipError_t launch_scan_lds_kda(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st);
 
 // After a segment-mode scan: o += G mid over segment 1, ht = n + M mid.
 template <int DK, typename T>

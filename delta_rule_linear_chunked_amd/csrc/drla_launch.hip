@@ -7,6 +7,9 @@
 
 namespace drla {
 
+// KDA operand bytes from which the LDS-fed scan takes KDA calls (launch_all).
+constexpr int64_t kKdaLdsScanBytes = 192ll << 20;
+
 // Compute units of the current device (cached per device).
 static int device_cus() {
   static std::atomic<int> cached[16];
@@ -153,8 +156,20 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   if (e == hipSuccess) {
     if constexpr (kLdsScan)
       e = launch_scan_lds<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
-    else
+    else if constexpr (KDA && sizeof(ET) == 2) {
+      // KDA with 16-bit inputs: the LDS-fed scan where prep's operands
+      // (K e^B, K~^T and Q e^B, 3 C dk elements per head and chunk) exceed
+      // what the 256 MiB last-level cache keeps, the register-fed scan
+      // below that (measured: the LDS-fed one 8-13% faster at 256-512 MiB,
+      // 1-7% slower at 64-128 MiB)
+      const int64_t opnd = nc * a->h_v * 3 * C * DK * (int64_t)sizeof(ET);
+      if (opnd >= kKdaLdsScanBytes)
+        e = launch_scan_lds_kda<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
+      else
+        e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
+    } else {
       e = launch_scan<DK, DV, KDA, ET>(sp, nscan, a->inspect != 0, st);
+    }
   }
   if constexpr (DK == DV) {
     if (seg && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);

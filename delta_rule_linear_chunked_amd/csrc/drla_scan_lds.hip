@@ -30,8 +30,17 @@
 // V' and the scaling of V' from the state wave's serial chain; all three
 // factors have entries of magnitude at most those of Tb and P.
 //
-// Only the loader waves issue loads, so their wait counts are exact: every
-// chunk each issues exactly kIssued copies, and wave 1 kTouched touches.
+// KDA (per-channel gate, 16-bit inputs) runs the same kernel on prep's
+// operands: the ring holds K e^{B} and K~^T = (K (.) e^{B_n - B})^T as MFMA
+// fragments (so the state wave's K^T reads are plain 16-byte reads), Tb, P,
+// V and e^{B_n} per key channel; the state wave forms R = V - (K e^B) S,
+// V' = Tb R and S <- Diag(e^{B_n}) S + K~^T V' and hands V' to the output
+// wave, which forms O = (Q e^B) S + P V' with its Q e^B fragments loaded
+// into registers one chunk ahead (they do not fit the ring).
+//
+// Only the loader waves issue loads into LDS, so their wait counts are
+// exact: every chunk each issues exactly kIssued copies, and wave 1
+// kTouched touches.
 #include "drla_common.h"
 #include "drla_kernels.h"
 
@@ -52,13 +61,12 @@ template <int DK, typename T>
 struct LdsSlot {
   typedef typename VT<T>::v8 H8;
   static constexpr int RB = DK * 2;                       // bytes per K/Q row
-  __attribute__((aligned(16))) unsigned char k[C * RB];  // K rows, 16-byte chunks swizzled
-  __attribute__((aligned(16))) unsigned char q[C * RB];  // Q rows, same
-  H8 tb[6][64];                                       // Tv fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
-  H8 pm[6][64];                                       // P Tb fragments, same order
+  __attribute__((aligned(16))) unsigned char k[C * RB];  // K rows, 16-byte chunks swizzled (KDA: K e^B fragments)
+  __attribute__((aligned(16))) unsigned char q[C * RB];  // Q rows, same (KDA: K~^T fragments)
+  H8 tb[6][64];                                       // Tv fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1) (KDA: Tb)
+  H8 pm[6][64];                                       // P Tb fragments, same order (KDA: P)
   __attribute__((aligned(16))) T v[C][16];             // V, this block's 16 columns
-  __attribute__((aligned(16))) float eb[C];               // e^{b_r}
-  __attribute__((aligned(16))) float ebn[C];              // e^{b_n - b_r}
+  __attribute__((aligned(16))) float dec[2 * C];          // e^{b_r}, then e^{b_n - b_r} (KDA: e^{B_n} per key channel)
 };
 
 // Byte offset of 16-byte chunk j of row r in a swizzled K/Q tile (the chunk
@@ -70,8 +78,8 @@ __device__ __forceinline__ int swz(int r, int j) {
 }
 
 // DECAY: decay-only linear attention (no delta rule): R = V, so the state
-// wave reads no K rows and runs no X products.
-template <int DK, int DV, bool INSPECT, typename T, bool DECAY>
+// wave reads no K rows and runs no X products.  KDA: the per-channel gate.
+template <int DK, int DV, bool INSPECT, typename T, bool DECAY, bool KDA>
 __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
@@ -81,7 +89,14 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int NCH = DK / 8;                 // 16-byte chunks per row
   constexpr int RPI = 1024 / (DK * 2);        // rows per 1 KiB copy
   constexpr int kIssued = C / RPI + 6 + 2;    // copies per loader wave and chunk
-  constexpr int kTouched = 2;                 // touches per chunk (loader wave 1)
+  static_assert(!KDA || DK <= 2 * C, "KDA: e^{B_n} fits the slot's two decay rows");
+  // L2 touches: line groups of a chunk (see touch_group), NTC touch loads
+  // per column block and chunk, issued by loader wave 1
+  constexpr int KL = DK * 2 / 128, VL = DV * 2 / 128;  // lines per K/Q row, per V row
+  constexpr int FL = (DK * C * 2 / 128 + 63) / 64;     // KDA: groups per 16-bit fragment array
+  constexpr int NG = KDA ? 3 * FL + 2 + VL + 1 : 2 * KL + 2 + VL + 1;
+  constexpr int NTC = (NG + NB - 1) / NB;
+  constexpr int kTouched = NTC;               // touches per chunk (loader wave 1)
   __shared__ LdsSlot<DK, T> slot[NS];
   __shared__ H8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
   __shared__ H8 vbuf[2][2][64];   // R of the last two chunks, A fragments (inner = token)
@@ -176,14 +191,27 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   };
   auto gam_rsrc = [&](int i) -> rsrc_t {
     const int64_t ch = (int64_t)h * P.nc + c0 + i;
-    return make_rsrc(P.gam + ch * (2 * C), 2 * C * 4);
+    // KDA: e^{B_n} per key channel; else e^{b_r}, then e^{b_n - b_r}
+    return KDA ? make_rsrc(P.gam + ch * DK, DK * 4) : make_rsrc(P.gam + ch * (2 * C), 2 * C * 4);
+  };
+  // KDA: the chunk's K e^B (wave 1) or K~^T (wave 2) fragments, or Q e^B
+  auto kda_rsrc = [&](const void* base, int i) -> rsrc_t {
+    const int64_t ch = (int64_t)h * P.nc + c0 + i;
+    return make_rsrc((const H8*)base + ch * (C * DK / 8), C * DK * 2);
   };
   auto issue = [&](int i) {
     LdsSlot<DK, T>& sl = slot[i % NS];
-    const rsrc_t rr = row_rsrc(i);
     unsigned char* dst = w == 1 ? sl.k : sl.q;
+    if constexpr (KDA) {
+      const rsrc_t fa = kda_rsrc(w == 1 ? P.kw : P.kt, i);
 #pragma unroll
-    for (int u = 0; u < C / RPI; ++u) lds_dma16(rr, roff[u % NP] + (uint32_t)(u / NP) * (NP * RPI) * kstride, 0, dst + u * 1024);
+      for (int u = 0; u < C / RPI; ++u) lds_dma16(fa, 16u * lane + u * 1024, 0, dst + u * 1024);
+    } else {
+      const rsrc_t rr = row_rsrc(i);
+#pragma unroll
+      for (int u = 0; u < C / RPI; ++u)
+        lds_dma16(rr, roff[u % NP] + (uint32_t)(u / NP) * (NP * RPI) * kstride, 0, dst + u * 1024);
+    }
     const rsrc_t fr = frag_rsrc(i);
     H8(*fdst)[64] = w == 1 ? sl.tb : sl.pm;
     const uint32_t lo = 16u * lane;
@@ -195,8 +223,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     lds_dma16(fr, lo + 7 * 1024, 0, &fdst[5][0]);
     if (w == 1) {
       const rsrc_t gr = gam_rsrc(i);
-      lds_dma4(gr, 4u * lane, 0, sl.eb);
-      lds_dma4(gr, 4u * lane + 4 * C, 0, sl.ebn);
+      lds_dma4(gr, 4u * lane, 0, sl.dec);
+      lds_dma4(gr, 4u * lane + 4 * C, 0, sl.dec + C);
     } else {
       const rsrc_t vr = v_rsrc(i);
       lds_dma16(vr, voff, 0, &sl.v[0][0]);
@@ -205,14 +233,18 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   };
   // L2 touches: the eight (four) column blocks of a head share their
   // XCD's L2, so each touches its own share of a chunk's 128-byte lines --
-  // K rows, Q rows, Tb, P, the head's V rows, the decay factors -- two
-  // touch loads per chunk, issued by loader wave 1 only.
-  constexpr int KL = DK * 2 / 128, VL = DV * 2 / 128;  // lines per K/Q row, per V row
-  constexpr int NG = 2 * KL + 2 + VL + 1;                // line groups of a chunk
-  static_assert(NG <= 2 * NB, "two touch loads per column block cover a chunk");
+  // K rows, Q rows, Tb, P, the head's V rows, the decay factors (KDA: the
+  // K e^B, K~^T and Q e^B fragments in place of the rows) -- NTC touch
+  // loads per chunk, issued by loader wave 1 only.
   auto touch_group = [&](int gi, int i) {
     const int64_t tc = ts + (int64_t)C * i;
     const uint32_t lrow = (chunk_len(i) - 1);
+    if (KDA && gi < 3 * FL) {  // K e^B, K~^T or Q e^B fragments, lines 64 (gi % FL) ..
+      const void* base = gi < FL ? P.kw : gi < 2 * FL ? P.kt : P.qw;
+      lds_dma4(kda_rsrc(base, i), 128u * (uint32_t)(lane + 64 * (gi % FL)), 0, touch);
+      return;
+    }
+    if (KDA) gi += 2 * KL - 3 * FL;  // the groups below, past the rows
     if (gi < 2 * KL) {  // K or Q rows, line gi % KL
       const T* src = (gi < KL ? kg : qg) + (tc * P.h_qk + hk) * DK;
       lds_dma4(make_rsrc(src, lrow * kstride + DK * 2), (uint32_t)lane * kstride + 128u * (uint32_t)(gi % KL), 0, touch);
@@ -229,8 +261,8 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     }
   };
   auto prefetch = [&](int i) {
-    touch_group(nb, i);
-    touch_group(nb + NB < NG ? nb + NB : NG - 1, i);
+#pragma unroll
+    for (int j = 0; j < NTC; ++j) touch_group(nb + j * NB < NG ? nb + j * NB : NG - 1, i);
   };
 
   // ---- prologue ------------------------------------------------------------
@@ -313,19 +345,31 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // V[16 nt + 4g + e][c] via the transposing read: lane 4e' + q of the
       // group addresses row 16 nt + 4g + e', columns 4q..4q+3
       H4 vv[4];
-      floatx4 ebv[4];
+      floatx4 ebv[4];  // e^{b} of this lane's rows (GDN)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         vv[nt] = ds_read_tr<T>(&sl.v[16 * nt + 4 * g4 + (c16 >> 2)][4 * (c16 & 3)]);
-        ebv[nt] = *(const floatx4*)&sl.eb[16 * nt + 4 * g4];
+        if constexpr (!KDA) ebv[nt] = *(const floatx4*)&sl.dec[16 * nt + 4 * g4];
       }
-      const float gam = sl.eb[C - 1];
+      // the state's decay: e^{b_n} (GDN), e^{B_n} of each state row (KDA)
+      float gam = 1.f;
+      floatx4 gmv[KDA ? KT : 1];
+      if constexpr (KDA) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) gmv[mt] = *(const floatx4*)&sl.dec[state_row(mt, 4 * g4)];
+      } else {
+        gam = sl.dec[C - 1];
+      }
+      // K rows of X's products (KDA: the K e^B fragments, token tile nt,
+      // inner block p)
       H8 kr[KB][4];
       if constexpr (!DECAY) {
 #pragma unroll
         for (int p = 0; p < KB; ++p)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+          for (int nt = 0; nt < 4; ++nt)
+            kr[p][nt] = KDA ? ((const H8*)sl.k)[(nt * KB + p) * 64 + lane]
+                            : *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
       }
       __builtin_amdgcn_sched_barrier(0);
       // X = K S for the four token tiles (lane holds [16 nt + 4g + e][c]),
@@ -333,30 +377,36 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       // the update (outer = key channel state_row(mt, c), inner = token;
       // lane 4e' + q of group g addresses token 32p + 4g + e' (+16 for the
       // upper half), channels state_row(mt, 4q) .. +3), V to floats and the
-      // decay of the state.  Step i issues one product, two reads and NV
-      // vector operations.
+      // decay of the state.  Step i issues one product, two reads (KDA: one
+      // read of a K~^T fragment, (mt, p) = (i / 2, i % 2)) and NV vector
+      // operations.
       floatx4 x[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) x[nt] = zero4();
       H4 kt[2][KT][2];
+      H8 ktf[KDA ? 2 : 1][KDA ? KT : 1];
       floatx4 vfl[4];
       static_assert(2 * 2 * KT == 2 * 4 * KB, "two K^T reads per product");
       constexpr int NV = (4 * KT + 16 + 4 * KB - 1) / (4 * KB);  // vector operations per product
 #pragma unroll
       for (int i = 0; i < 4 * KB; ++i) {
         if constexpr (!DECAY) x[i % 4] = mma(kr[i / 4][i % 4], sf[i / 4], x[i % 4]);
+        if constexpr (KDA) {
+          ktf[i % 2][i / 2] = ((const H8*)sl.q)[i * 64 + lane];
+        } else {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
-          const int r0 = 32 * p + 4 * g4 + (c16 >> 2) + 16 * hf;
-          const int d = state_row(mt, 4 * (c16 & 3));
-          kt[p][mt][hf] = ds_read_tr<T>(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
+            const int r0 = 32 * p + 4 * g4 + (c16 >> 2) + 16 * hf;
+            const int d = state_row(mt, 4 * (c16 & 3));
+            kt[p][mt][hf] = ds_read_tr<T>(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          }
         }
 #pragma unroll
         for (int jj = 0; jj < NV; ++jj) {
           const int j = NV * i + jj;
           if (j < 4 * KT) {
-            S[j / 4][j % 4] *= gam;
+            S[j / 4][j % 4] *= KDA ? gmv[KDA ? j / 4 : 0][j % 4] : gam;
           } else if (j < 4 * KT + 16) {
             const int q2 = j - 4 * KT;
             vfl[q2 / 4][q2 % 4] = to_f(vv[q2 / 4][q2 % 4]);
@@ -364,17 +414,21 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // R = V - diag(e^b) X, as B fragments (inner = token); decay-only: R = V
+      // R = V - diag(e^b) X (KDA: V - X), as B fragments (inner = token);
+      // decay-only: R = V
       floatx4 rr[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[nt][e] = DECAY ? vfl[nt][e] : vfl[nt][e] - ebv[nt][e] * x[nt][e];
+        for (int e = 0; e < 4; ++e)
+          rr[nt][e] = DECAY ? vfl[nt][e] : KDA ? vfl[nt][e] - x[nt][e] : vfl[nt][e] - ebv[nt][e] * x[nt][e];
       const H8 rf0 = pack<T>(rr[0], rr[1]), rf1 = pack<T>(rr[2], rr[3]);
-      // R goes to the output wave, which multiplies it with P Tb
-      vbuf[t & 1][0][lane] = rf0;
-      vbuf[t & 1][1][lane] = rf1;
-      // diag(e^{b_n - b}) V' = (diag(e^{b_n - b}) Tb) R
+      // GDN: R goes to the output wave, which multiplies it with P Tb
+      if constexpr (!KDA) {
+        vbuf[t & 1][0][lane] = rf0;
+        vbuf[t & 1][1][lane] = rf1;
+      }
+      // diag(e^{b_n - b}) V' = (diag(e^{b_n - b}) Tb) R (KDA: V' = Tb R)
       floatx4 vt[4];
       vt[0] = mma(tbf[0], rf0, zero4());
       vt[1] = mma(tbf[1], rf0, zero4());
@@ -383,25 +437,31 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       vt[2] = mma(tbf[3], rf1, vt[2]);
       vt[3] = mma(tbf[5], rf1, vt[3]);
       const H8 vs0 = pack<T>(vt[0], vt[1]), vs1 = pack<T>(vt[2], vt[3]);
+      // KDA: V' goes to the output wave, which multiplies it with P
+      if constexpr (KDA) {
+        vbuf[t & 1][0][lane] = vs0;
+        vbuf[t & 1][1][lane] = vs1;
+      }
       if (INSPECT) {
         // V' itself, for the intermediate checks
         floatx4 vq[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const floatx4 env = *(const floatx4*)&sl.ebn[16 * nt + 4 * g4];
+          const floatx4 env = KDA ? floatx4{1.f, 1.f, 1.f, 1.f} : *(const floatx4*)&sl.dec[C + 16 * nt + 4 * g4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vq[nt][e] = vt[nt][e] / env[e];
+          for (int e = 0; e < 4; ++e) vq[nt][e] = KDA ? vt[nt][e] : vt[nt][e] / env[e];
         }
         H8* vp = (H8*)P.insp_vp + ch * (int64_t)(C * DV / 8);
         vp[(nb * 2 + 0) * 64 + lane] = pack<T>(vq[0], vq[1]);
         vp[(nb * 2 + 1) * 64 + lane] = pack<T>(vq[2], vq[3]);
       }
-      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V')
+      // S <- e^{b_n} S + K^T (diag(e^{b_n - b}) V') (KDA: Diag(e^{B_n}) S + K~^T V')
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt)
-          S[mt] = mma(cat<T>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1, S[mt]);
+          S[mt] = mma(KDA ? ktf[KDA ? p : 0][KDA ? mt : 0] : cat<T>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1,
+                      S[mt]);
 #pragma unroll
       for (int p = 0; p < KB; ++p) {
         sf[p] = pack<T>(S[2 * p], S[2 * p + 1]);
@@ -424,24 +484,46 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int p = 0; p < KB; ++p) mf[p * 64 + lane] = sf[p];
     }
   } else if (w == 3) {
+    // KDA: the Q e^B fragments (token tile nt, inner block p) of the next
+    // chunk, loaded from the workspace one chunk ahead (unconditionally:
+    // past the last chunk the last one again)
+    H8 qn[KDA ? 4 : 1][KDA ? KB : 1];
+    auto load_q = [&](int i) {
+      const rsrc_t qrs = kda_rsrc(P.qw, i);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) qn[nt][p] = fload<H8>(qrs, 16u * lane, nt * KB + p);
+    };
+    if constexpr (KDA) {
+      if (n > 0) load_q(0);
+    }
     for (int t = 0; t < n; ++t) {
       const LdsSlot<DK, T>& sl = slot[t % NS];
       const int64_t t0 = ts + (int64_t)C * t;
       // ---------------- output wave ----------------
-      // finish the previous chunk: its R was published at the last barrier
+      // finish the previous chunk: its R (KDA: V') was published at the last barrier
       if (t > 0) finish_output(t0prev, t - 1);
       // state part of this chunk's O^T: lane holds [column 4g + e][token 16 nt + c]
       H8 so[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) so[p] = sbuf[t & 1][p][lane];
       H8 qr[4][KB];
+      if constexpr (KDA) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int p = 0; p < KB; ++p) qr[nt][p] = *(const H8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
+          for (int p = 0; p < KB; ++p) qr[nt][p] = qn[nt][p];
+        load_q(t + 1 < n ? t + 1 : n - 1);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int p = 0; p < KB; ++p) qr[nt][p] = *(const H8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
+      }
       float ebt[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) ebt[nt] = sl.eb[16 * nt + c16];
+      for (int nt = 0; nt < 4; ++nt) ebt[nt] = KDA ? 1.f : sl.dec[16 * nt + c16];
 #pragma unroll
       for (int f = 0; f < 6; ++f) pmf[f] = sl.pm[f][lane];  // kept for the next step
       __builtin_amdgcn_sched_barrier(0);
@@ -451,8 +533,10 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       for (int p = 0; p < KB; ++p)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) o[nt] = mma(so[p], qr[nt][p], o[nt]);
+      if constexpr (!KDA) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
+        for (int nt = 0; nt < 4; ++nt) o[nt] *= ebt[nt];
+      }
       t0prev = t0;
       lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
@@ -698,23 +782,33 @@ DRLA_SEG_INST(64, float)
 DRLA_SEG_INST(128, float)
 #undef DRLA_SEG_INST
 
+template <int DK, int DV, typename T, bool KDA>
+static void launch_scan_lds_v(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
+  if (P.decay_only && inspect)
+    hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, true, KDA>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  else if (P.decay_only)
+    hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, true, KDA>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  else if (inspect)
+    hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, false, KDA>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, false, KDA>), dim3((unsigned)nblk), dim3(256), 0, st, P);
+}
+
 template <int DK, int DV, typename T>
 hipError_t launch_scan_lds(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
-  if (nblk > 0) {
-    if (P.decay_only && inspect)
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-    else if (P.decay_only)
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, true>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-    else if (inspect)
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-    else
-      hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, false>), dim3((unsigned)nblk), dim3(256), 0, st, P);
-  }
+  if (nblk > 0) launch_scan_lds_v<DK, DV, T, false>(P, nblk, inspect, st);
   return hipGetLastError();
 }
 
-#define DRLA_SCAN_LDS_INST(DK_, DV_, T_) \
-  template hipError_t launch_scan_lds<DK_, DV_, T_>(const ScanParams&, int64_t, bool, hipStream_t);
+template <int DK, int DV, typename T>
+hipError_t launch_scan_lds_kda(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
+  if (nblk > 0) launch_scan_lds_v<DK, DV, T, true>(P, nblk, inspect, st);
+  return hipGetLastError();
+}
+
+#define DRLA_SCAN_LDS_INST(DK_, DV_, T_)                                                             \
+  template hipError_t launch_scan_lds<DK_, DV_, T_>(const ScanParams&, int64_t, bool, hipStream_t); \
+  template hipError_t launch_scan_lds_kda<DK_, DV_, T_>(const ScanParams&, int64_t, bool, hipStream_t);
 DRLA_SCAN_LDS_INST(64, 64, bf16)
 DRLA_SCAN_LDS_INST(128, 64, bf16)
 DRLA_SCAN_LDS_INST(64, 128, bf16)
