@@ -2,9 +2,9 @@
 3 x 64 x dk elements per head and chunk) reach 192 MiB take the LDS-fed scan
 (the launcher's rule; smaller ones take the register-fed scan, which the
 other KDA tests cover).  Here: the whole call against the fp64 oracle in one
-pass and with the segment split, and V' and the per-chunk states of one head
-against the chunkwise oracle's intermediates.  Bar as the other parity
-tests."""
+pass and with the segment split, V' and the per-chunk states of one head
+against the chunkwise oracle's intermediates, and decay-only attention with
+the per-channel gate.  Bar as the other parity tests."""
 import numpy as np
 import pytest
 
@@ -101,3 +101,24 @@ def test_kda_lds_scan_intermediates(drla):
     print("  worst", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     for name, e in worst.items():
         assert e <= TOL["bf16"], f"{name}: {e}"
+
+
+def test_gla_lds_scan_matches_oracle(drla):
+    """Decay-only linear attention with the per-channel gate (decay_prefill,
+    per_channel) at the same size takes the same scan (R = V, no X term)."""
+    T, h_qk, h_v = 16384, 16, 16
+    assert _operand_bytes(T, h_v, 128) >= LDS_SCAN_BYTES
+    print(f"case gla lds scan T={T} h_v={h_v}", flush=True)
+    spec = W.small_spec("gla", lens=(T,), h_qk=h_qk, h_v=h_v, dk=128, dv=128, io="bf16",
+                        g_lo=0.005, g_hi=0.15, h0_std=0.02, seed=73)
+    x = W.make_inputs(spec)
+    d = to_device(x)
+    o, ht = drla.decay_prefill(d["q"], d["k"], d["v"], d["g"], d["h0"], per_channel=True,
+                               flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    del d
+    o_ref, ht_ref = run_oracle(x)
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e} (tol {TOL['bf16']:g})", flush=True)
+    assert np.isfinite(o).all() and eo <= TOL["bf16"] and eh <= TOL["bf16"]
