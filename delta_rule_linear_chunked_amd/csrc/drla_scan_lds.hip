@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   constexpr int kTouched = NTC;               // touches per chunk (loader wave 1)
   __shared__ LdsSlot<DK, T> slot[NS];
   __shared__ H8 sbuf[2][KB][64];  // state entering a chunk, B fragments (inner = key channel)
-  __shared__ H8 vbuf[2][2][64];   // R of the last two chunks, A fragments (inner = token)
+  __shared__ H8 vbuf[2][2][64];   // R (KDA: V') of the last two chunks, A fragments (inner = token)
   __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
 
   const int tid = threadIdx.x, lane = tid & 63;
