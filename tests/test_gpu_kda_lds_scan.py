@@ -30,8 +30,8 @@ def _operand_bytes(T, h_v, dk):
     return -(-T // 64) * h_v * 3 * 64 * dk * 2
 
 
-def _inputs(T, h_qk, h_v, io, seed):
-    spec = W.small_spec("kda", lens=(T,), h_qk=h_qk, h_v=h_v, dk=128, dv=128, io=io,
+def _inputs(T, h_qk, h_v, io, seed, dk=128, dv=128):
+    spec = W.small_spec("kda", lens=(T,), h_qk=h_qk, h_v=h_v, dk=dk, dv=dv, io=io,
                         g_lo=0.005, g_hi=0.15, h0_std=0.02, seed=seed)
     return W.make_inputs(spec)
 
@@ -59,6 +59,24 @@ def test_kda_lds_scan_matches_oracle(drla, T, h_qk, h_v, io, serial):
     print(f"  rel_err o={eo:.3e} ht={eh:.3e} nmse o={nmse(o, o_ref):.2e} (tol {TOL[io]:g})", flush=True)
     assert np.isfinite(o).all() and np.isfinite(ht).all()
     assert eo <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("T,dk,dv", [(32768, 64, 64), (16384, 128, 64), (32768, 64, 128)])
+def test_kda_lds_scan_other_head_dims(drla, T, dk, dv):
+    """The other (dk, dv) the scan serves, at 192 MiB of prep operands (16
+    heads, one pass)."""
+    assert _operand_bytes(T, 16, dk) >= LDS_SCAN_BYTES
+    print(f"case kda lds scan T={T} dk={dk} dv={dv}", flush=True)
+    x = _inputs(T, 16, 16, "bf16", seed=74, dk=dk, dv=dv)
+    d = to_device(x)
+    o, ht = drla.kda_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], flags=drla.SERIAL)
+    torch.cuda.synchronize()
+    o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    del d
+    o_ref, ht_ref = run_oracle(x)
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print(f"  rel_err o={eo:.3e} ht={eh:.3e} (tol {TOL['bf16']:g})", flush=True)
+    assert np.isfinite(o).all() and eo <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_kda_lds_scan_intermediates(drla):
