@@ -277,6 +277,22 @@ def test_deterministic_and_guard_bands(drla):
 
 # ---- per-kernel intermediates against the chunkwise oracle ---------------
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_sequence_of_262144_tokens(drla, kind):
+    """One sequence four times the longest workload's (4,096 chunks, two
+    heads: the segment split), against the oracle: chunk and token offsets
+    past every smaller size."""
+    print(f"case {kind} T=262144 h_v=2", flush=True)
+    x = _case(kind, "bf16", 128, 128, lens=(262144,), h_qk=2, h_v=2, h0_std=0.02, seed=15,
+              g_lo=0.001 if kind == "gdn" else 0.0005, g_hi=0.05 if kind == "gdn" else 0.03)
+    d = to_device(x)
+    o, ht = _call(drla, x, d)
+    o, ht = _np(o), _np(ht)
+    del d
+    o_ref, ht_ref = run_oracle(x)
+    _check(f"{kind}/T262144", x, o, ht, o_ref, ht_ref)
+
+
 @pytest.mark.parametrize("kind,h_v", [("gdn", 2), ("kda", 2), ("gdn", 4)])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
