@@ -8,7 +8,7 @@
 namespace drla {
 
 // KDA operand bytes from which the LDS-fed scan takes KDA calls (launch_all).
-constexpr int64_t kKdaLdsScanBytes = 192ll << 20;
+constexpr int64_t kKdaLdsScanBytes = 112ll << 20;
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
@@ -157,11 +157,11 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     if constexpr (kLdsScan)
       e = launch_scan_lds<DK, DV, ET>(sp, nscan, a->inspect != 0, st);
     else if constexpr (KDA && sizeof(ET) == 2) {
-      // KDA with 16-bit inputs: the LDS-fed scan where prep's operands
-      // (K e^B, K~^T and Q e^B, 3 C dk elements per head and chunk) exceed
-      // what the 256 MiB last-level cache keeps, the register-fed scan
-      // below that (measured: the LDS-fed one 8-13% faster at 256-512 MiB,
-      // 1-7% slower at 64-128 MiB)
+      // KDA with 16-bit inputs: the LDS-fed scan once prep's operands
+      // (K e^B, K~^T and Q e^B, 3 C dk elements per head and chunk) crowd
+      // the 256 MiB last-level cache, the register-fed scan below that
+      // (measured: the LDS-fed one 5-15% faster from 120 MiB, 3-8% slower
+      // at 96 MiB and below)
       const int64_t opnd = nc * a->h_v * 3 * C * DK * (int64_t)sizeof(ET);
       if (opnd >= kKdaLdsScanBytes)
         e = launch_scan_lds_kda<DK, DV, ET>(sp, nscan, a->inspect != 0, st);

@@ -1,5 +1,5 @@
 """KDA calls with 16-bit inputs whose prep operands (K e^B, K~^T and Q e^B,
-3 x 64 x dk elements per head and chunk) reach 192 MiB take the LDS-fed scan
+3 x 64 x dk elements per head and chunk) reach 112 MiB take the LDS-fed scan
 (the launcher's rule; smaller ones take the register-fed scan, which the
 other KDA tests cover).  Here: the whole call against the fp64 oracle in one
 pass and with the segment split, V' and the per-chunk states of one head
@@ -14,7 +14,7 @@ from drla_testlib import TOL, decode_blocks, kmap_contiguous, nmse, rel_err, run
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-LDS_SCAN_BYTES = 192 << 20
+LDS_SCAN_BYTES = 112 << 20
 
 
 @pytest.fixture(scope="module")
