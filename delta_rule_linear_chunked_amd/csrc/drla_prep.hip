@@ -347,8 +347,15 @@ __global__ __launch_bounds__(256, sizeof(ET) == 2 ? 2 : 1) void prep_kernel(Prep
     }
   };
 
-  // PF: a persistent grid; otherwise one unit per workgroup
+  // PF: a persistent grid; otherwise one unit per workgroup, dealt in
+  // reverse chunk-major order: the units written last are the first chunks
+  // of every head, which the scans read first (the last-level cache keeps
+  // the most recent writes)
   int64_t u = blockIdx.x;
+  if constexpr (!PF) {
+    const int64_t hus = nunits / P.nc, r = nunits - 1 - u;
+    u = (r % hus) * P.nc + r / hus;
+  }
   Unit U = unit_of(u);
   load(U);
   for (;;) {
