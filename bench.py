@@ -146,6 +146,23 @@ def load_traffic(kernel, workload):
         return None
 
 
+# Kernels each timed stage launches (the stage events bracket them all):
+# prep = schedule and rank (packed input) and prep; scan = the scan, and
+# when the call splits its sequences into segments the compose (more than
+# two segments) and fix-up kernels, or the head-resident scan's transition,
+# compose and value kernels.
+STAGE_KERNELS = {"prep": ("schedule", "rank", "prep"), "scan": ("scan", "compose", "fix")}
+
+
+def stage_traffic(stage, workload):
+    """HBM bytes per call of a stage: the sum over its kernels' committed
+    counter summaries, or None without one for the stage's main kernel."""
+    if load_traffic(stage, workload) is None:
+        return None
+    parts = (load_traffic(k, workload) for k in STAGE_KERNELS.get(stage, (stage,)))
+    return sum(p for p in parts if p is not None)
+
+
 def _nmse(x, y):
     import numpy as np
     x = np.asarray(x, dtype=np.float64)
@@ -531,12 +548,13 @@ def main():
                 "frac": round(ach / mfma_peak, 4), "peak_measured": _pk(peaks, "mfma_tflops"),
                 "frac_measured": _frac(ach, _pk(peaks, "mfma_tflops"))}
     roof["kernel"] = dom
-    roof["traffic"] = load_traffic(dom, spec.name)
+    roof["traffic"] = stage_traffic(dom, spec.name)
+    roof["stage_kernels"] = list(STAGE_KERNELS.get(dom, (dom,)))
     # HBM bytes per dispatch from the committed counter profiles (null when
     # they were taken on other kernel sources) over the live kernel times
     traffic_gbs = {}
     for kk in stage:
-        tb = load_traffic(kk, spec.name)
+        tb = stage_traffic(kk, spec.name)
         traffic_gbs[kk] = None if tb is None else round(tb / (stage[kk] * 1e-3) / 1e9, 1)
     roof["traffic_gbs"] = traffic_gbs
     roof["kernel_ms"] = {kk: round(vv, 5) for kk, vv in stage.items()}

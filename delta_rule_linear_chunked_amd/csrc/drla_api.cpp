@@ -148,13 +148,15 @@ static int32_t hs_count(const drla_problem* p, int64_t nc, int64_t max_cps, bool
   return drla_hs_count((int64_t)p->n_seqs * p->h_v, max_cps, 256);
 }
 
-// Segments the per-16-column scan's seg region provides for (drla_seg_count
-// at 256 compute units, over the longest sequence); 1 for calls the split
-// does not take.
+// Segments the per-16-column scan's seg region provides for (drla_seg_plan
+// at 256 compute units, over the longest sequence; paired chains possible in
+// the LDS-fed scan of scalar-gate 16-bit calls); 1 for calls the split does
+// not take.
 static int32_t seg_count(const drla_problem* p, int64_t nc, int64_t max_cps, bool kda, int flags) {
-  if (uses_hs(p, nc, max_cps, kda, flags) || (flags & DRLA_KEEP_INTERMEDIATES)) return 1;
+  if (uses_hs(p, nc, max_cps, kda, flags) || (flags & (DRLA_KEEP_INTERMEDIATES | DRLA_SERIAL))) return 1;
   if (p->dk != p->dv || p->n_seqs < 1) return 1;
-  return drla_seg_count((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256);
+  const bool can_pair = !kda && p->io_dtype != DRLA_F32;
+  return drla_seg_plan((int64_t)p->n_seqs * p->h_v * (p->dv / 16), max_cps, 256, can_pair, nullptr);
 }
 
 void layout_of(const drla_problem* p, int64_t nc, bool varlen, int64_t max_cps, bool kda, int flags,

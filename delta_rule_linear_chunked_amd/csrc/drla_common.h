@@ -277,13 +277,14 @@ __device__ __forceinline__ bool scan_item(const Sched& s, int h_v, int nbk, int&
 
 // Segment-mode scan workgroup -> (unit, column block, kind, segment):
 // kind 1 = segment 0; for segments 1 .. np - 1, kind 2 = from zero, 3 =
-// transition.  (2 np - 1) K workgroups for K = units x nbk, all resident at
-// once.  A unit's (2 np - 1) nbk workgroups take consecutive places in one
-// XCD's share of the indices (when the count is a multiple of 8), so that
-// a segment's value and transition blocks, which read the same chunks,
-// mostly share an L2.
-__device__ __forceinline__ void seg_item(int units, int nbk, int np, int& unit, int& nb, int& kind, int& sg) {
-  const int bid = blockIdx.x, per = (2 * np - 1) * nbk, W = units * per;
+// transition, or with `pair` kind 4 = both chains in one workgroup.
+// (2 np - 1) K workgroups (pair: np K) for K = units x nbk, all resident at
+// once.  A unit's workgroups take consecutive places in one XCD's share of
+// the indices (when the count is a multiple of 8), so that its segments,
+// and a segment's value and transition blocks, mostly share an L2.
+__device__ __forceinline__ void seg_item(int units, int nbk, int np, bool pair, int& unit, int& nb, int& kind,
+                                         int& sg) {
+  const int bid = blockIdx.x, per = (pair ? np : 2 * np - 1) * nbk, W = units * per;
   const int l = W % 8 == 0 ? (bid % 8) * (W / 8) + bid / 8 : bid;
   unit = l / per;
   int r = l - unit * per;
@@ -291,6 +292,11 @@ __device__ __forceinline__ void seg_item(int units, int nbk, int np, int& unit, 
     kind = 1;
     sg = 0;
     nb = r;
+  } else if (pair) {
+    r -= nbk;
+    sg = 1 + r / nbk;
+    kind = 4;
+    nb = r % nbk;
   } else {
     r -= nbk;
     sg = 1 + r / (2 * nbk);
@@ -298,6 +304,17 @@ __device__ __forceinline__ void seg_item(int units, int nbk, int np, int& unit, 
     kind = 2 + r / nbk;
     nb = r % nbk;
   }
+}
+
+// Chunks [first, first + len) of segment sg of a sequence of n chunks cut
+// into np segments, segment 0 weighted w0 / 256 against each later one:
+// the later segments take ls = floor(256 n / (w0 + 256 (np - 1))) chunks
+// each, segment 0 the rest (all of them when n is below np).
+__device__ __forceinline__ void seg_span(int64_t n, int np, int w0, int sg, int64_t& first, int64_t& len) {
+  const int64_t ls = (256 * n) / (w0 + 256 * (np - 1));
+  const int64_t n0 = n - (np - 1) * ls;
+  first = sg == 0 ? 0 : n0 + (sg - 1) * ls;
+  len = sg == 0 ? n0 : ls;
 }
 
 // Chunks [c0, c1) of sequence `seq`, clamped to [0, nc).

@@ -24,16 +24,20 @@ struct PrepParams {
 };
 
 // Segment-parallel scan (dk = dv): every sequence's n chunks are split into
-// np segments of n / np chunks (the last takes the rest).  Segment
-// 0 is scanned from h0 (final state into mid).  Every later segment s is
-// scanned both from a zero state (its local outputs into o, final state
-// into n[s-1]) and, by as many "transition" workgroups, from the identity
-// with V = 0 (outputs G into g, final state M into m[s-1]).  With E_1 = mid
-// and E_{s+1} = N_s + M_s E_s (seg_compose), segment s's true outputs are
-// o += G E_s (seg_fix) and ht = E_np.
+// np segments (seg_span: segment 0 weighted w0 / 256 against each later
+// one).  Segment 0 is scanned from h0 (final state into mid).  Every later
+// segment s is scanned both from a zero state (its local outputs into o,
+// final state into n[s-1]) and from the identity with V = 0 (the
+// "transition": outputs G into g, final state M into m[s-1]); with `pair`
+// one workgroup runs both chains over one copy of the chunk operands, else
+// each has its own workgroups.  With E_1 = mid and E_{s+1} = N_s + M_s E_s
+// (seg_compose), segment s's true outputs are o += G E_s (seg_fix) and
+// ht = E_np.
 struct SegParams {
-  int32_t s1;   // > 0: segment mode (the longest sequence's segment length)
+  int32_t s1;   // > 0: segment mode
   int32_t np;   // segments
+  int32_t w0;   // weight of segment 0 against a later segment, x 256
+  int32_t pair; // 1: a later segment's two chains share a workgroup
   int64_t us;   // elements of one state set: sequences x heads x dk x dv
   void* g;      // [T, h_v, dk] in the io type, like o
   float* mid;   // [N, h_v, dk, dv]

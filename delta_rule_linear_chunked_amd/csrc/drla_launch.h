@@ -9,15 +9,43 @@
 #define DRLA_CHUNK_TOKENS 64
 
 // Segment count of the segment-split scan of a dense call (1: no split):
-// the most P <= 16 for which the scan's (2P - 1) K workgroups all fit on
-// `cus` compute units at once (one per CU; K = sequences x heads x dv/16)
-// and every segment has at least 4 chunks (cps: chunks per sequence).
-static inline int32_t drla_seg_count(int64_t K, int64_t cps, int64_t cus) {
+// the most P <= 16 for which the scan's workgroups all fit on `cus` compute
+// units at once (one per CU; K = sequences x heads x dv/16 chains) and
+// the longest sequence has at least 4 P chunks (cps).  The scan takes
+// (2P - 1) K workgroups, or P K with `paired` chains (a later segment's
+// zero-start and transition chains in one workgroup: the LDS-fed GDN scan).
+static inline int32_t drla_seg_count(int64_t K, int64_t cps, int64_t cus, bool paired) {
   int32_t np = 1;
   for (int32_t p = 2; p <= 16; ++p)
-    if (K > 0 && (2 * p - 1) * K <= cus && cps >= 4 * p) np = p;
+    if (K > 0 && (paired ? p : 2 * p - 1) * K <= cus && cps >= 4 * p) np = p;
   return np;
 }
+
+// Segment plan of a dense call: np segments, and whether a later segment's
+// two chains share a workgroup (`paired`, only where `can_pair`: the LDS-fed
+// GDN scan).  Pairing fits twice the segments on the chip but runs the
+// paired workgroups about 1.3x slower per chunk, and every segment past the
+// second adds a serial compose step (2-3 us), so it is taken only where the
+// unpaired split cannot run (its 3 K workgroups exceed the compute units) or
+// leaves at least 96 chunks per segment.  Measured on MI355X (GDN bf16, one
+// sequence; call us, unpaired -> paired): H16 d128 T4096 one pass 68.5 ->
+// 63.7 (2 segments), H2 T65536 172 -> 160 (8 -> 16 segments); H4 T16384 98
+// -> 97, H8 T8192 85 -> 84 (equal); H4 T4096 44 -> 56, H8 T4096 52 -> 59,
+// H4 d64 T8192 38 -> 53, H1 T65536 125 -> 140 (16 segments either way).
+static inline int32_t drla_seg_plan(int64_t K, int64_t cps, int64_t cus, bool can_pair, bool* paired) {
+  const int32_t nu = drla_seg_count(K, cps, cus, false);
+  const int32_t npp = can_pair ? drla_seg_count(K, cps, cus, true) : 1;
+  const bool pair = npp > nu && (nu == 1 || cps / nu >= 96);
+  if (paired) *paired = pair;
+  return pair ? npp : nu;
+}
+
+// Weight of segment 0 against each later segment with paired chains, x 256
+// (seg_span): about the period per chunk of a paired workgroup over that of
+// a one-chain workgroup, so that all segments end together.  Measured best
+// on MI355X (GDN, d = 128): 352 at two segments (16 heads; 307 and 400 are
+// 2-4 % slower), 307 from four (2 to 8 heads, 4 to 16 segments).
+static inline int32_t drla_seg_pair_w0(int32_t np) { return np == 2 ? 352 : 307; }
 
 // Segments per sequence of the head-resident scan: as many as give every
 // (sequence, head) unit's segments one compute unit each (units x np <=
@@ -70,7 +98,7 @@ static inline bool drla_auto_head_scan(int64_t units, int64_t max_cps, int64_t u
     const double per_cu = (double)unit_chunks * (double)(dv / 16) / (double)cus;
     t_col = 1.06 * (n > per_cu ? n : per_cu);
   } else {
-    const int32_t ns = drla_seg_count(chains, max_cps, cus);
+    const int32_t ns = drla_seg_count(chains, max_cps, cus, false);
     t_col = 0.9 * (double)((max_cps + ns - 1) / ns) + (ns > 1 ? 12.0 : 0.0);
   }
   return t_head < 0.9 * t_col;

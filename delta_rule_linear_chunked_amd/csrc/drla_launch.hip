@@ -127,30 +127,35 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
   const int64_t units = (int64_t)a->n_seqs * a->h_v;
   int64_t nscan = (s.seq_order ? (units + 7) / 8 * 8 : units) * (DV / 16);
   // Segment mode (SegParams): a call whose scan leaves most of the chip
-  // idle takes np segments, as many as let all (2 np - 1) K scan workgroups
-  // (one per compute unit) run at once.  (With more workgroups than compute
-  // units the scan's period per chunk grows with the occupancy more than
-  // the shorter segments save.)  Both scans take it: the LDS-fed one (GDN,
-  // 16-bit) and the register-fed one (KDA, fp32).
+  // idle takes np segments, as many as let all its scan workgroups (one per
+  // compute unit) run at once: (2 np - 1) K, or np K with the LDS-fed GDN
+  // scan's paired chains, whose segment 0 is made longer by the paired
+  // workgroups' longer period (drla_seg_pair_w0); drla_seg_plan picks the
+  // form.  (With more workgroups than compute units the scan's period per
+  // chunk grows with the occupancy more than the shorter segments save.)
+  // The KDA and fp32 scans take the unpaired form.
   bool seg = false;
   if constexpr (DK == DV) {
     const int64_t K = units * (DV / 16);
     const int cus = device_cus();
-    int32_t np = cus > 0 ? drla_seg_count(K, a->max_cps, cus) : 1;
+    bool pair = false;
+    int32_t np = cus > 0 ? drla_seg_plan(K, a->max_cps, cus, kLdsScan, &pair) : 1;
     if (np > a->seg_np) np = a->seg_np;  // what the workspace holds
     if (a->off_seg && !a->inspect && !a->serial && np > 1) {
       seg = true;
       const drla_seg_layout L = drla_seg_offsets(units, DK, a->total_tokens, a->h_v, a->seg_np, sizeof(ET));
       char* sg = ws + a->off_seg;
-      sp.seg.s1 = (int32_t)(a->max_cps / np);  // of the longest sequence (>= 4: segment mode)
+      sp.seg.s1 = 1;
       sp.seg.np = np;
+      sp.seg.pair = pair ? 1 : 0;
+      sp.seg.w0 = pair ? drla_seg_pair_w0(np) : 256;
       sp.seg.us = units * DK * DV;
       sp.seg.mid = (float*)(sg + L.mid);
       sp.seg.n = (float*)(sg + L.n);
       sp.seg.m = (float*)(sg + L.m);
       sp.seg.midf = sg + L.f;
       sp.seg.g = sg + L.g;
-      nscan = (2 * np - 1) * K;
+      nscan = (pair ? np : 2 * np - 1) * K;
     }
   }
   if (e == hipSuccess) {
@@ -172,7 +177,8 @@ static hipError_t launch_all(const drla_launch_args* a, const Sched& s) {
     }
   }
   if constexpr (DK == DV) {
-    if (seg && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);
+    // (two segments: the fix-up launch forms ht itself)
+    if (seg && sp.seg.np > 2 && e == hipSuccess) e = launch_seg_compose<DK, ET>(sp, units, st);
     if (seg && e == hipSuccess) e = launch_seg_fix<DK, ET>(sp, units, (int32_t)a->max_cps, st);
   }
   mark(2);

@@ -169,7 +169,7 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
   int kind = 0, sg = 0;  // 0: whole sequence; segment mode: 1, 2, 3 and the segment (seg_item)
   if (P.seg.s1 > 0) {
     int unit;
-    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, unit, nb, kind, sg);
+    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, false, unit, nb, kind, sg);
     seq = unit / P.h_v;
     h = unit - seq * P.h_v;
   } else if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) {
@@ -197,17 +197,12 @@ __global__ __launch_bounds__((ring_variant<KDA, ET>() ? 384 : 256)) void scan_ke
     n = P.s.cps;
   }
   if (kind > 0) {
-    // segment sg of this sequence: chunks [sg s1, (sg + 1) s1), the last to
-    // the end, s1 = n / np (0 for a sequence of fewer chunks than segments:
-    // its last segment takes them all)
-    const int64_t s1 = n / P.seg.np;
-    if (kind == 1) {
-      n = s1;
-    } else {
-      x.ts += (int64_t)C * s1 * sg;
-      x.c0 += s1 * sg;
-      n = sg == P.seg.np - 1 ? n - s1 * sg : s1;
-    }
+    // segment sg of this sequence (seg_span)
+    int64_t first, len;
+    seg_span(n, P.seg.np, P.seg.w0, sg, first, len);
+    x.ts += (int64_t)C * first;
+    x.c0 += first;
+    n = len;
   }
   // segment transition blocks (kind 3) scan V = 0 from the identity and
   // write G in place of o; the final state goes to ht, or to the segment

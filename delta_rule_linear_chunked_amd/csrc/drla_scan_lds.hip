@@ -38,6 +38,14 @@
 // wave, which forms O = (Q e^B) S + P V' with its Q e^B fragments loaded
 // into registers one chunk ahead (they do not fit the ring).
 //
+// Segment mode with paired chains (GDN; SegParams::pair): a later segment's
+// workgroup scans it both from a zero state (waves 0 and 3, as above) and
+// from the identity with V = 0, the transition, on a fifth wave that also
+// forms the transition's outputs G = diag(e^b) Q M + (P Tb) R from its own
+// registers (there is no LDS left for a second state and R exchange), so
+// both chains share one copy of the chunk operands and a unit's segments
+// take np workgroups per column block instead of 2 np - 1.
+//
 // Only the loader waves issue loads into LDS, so their wait counts are
 // exact: every chunk each issues exactly kIssued copies, and wave 1
 // kTouched touches.
@@ -79,8 +87,9 @@ __device__ __forceinline__ int swz(int r, int j) {
 
 // DECAY: decay-only linear attention (no delta rule): R = V, so the state
 // wave reads no K rows and runs no X products.  KDA: the per-channel gate.
-template <int DK, int DV, bool INSPECT, typename T, bool DECAY, bool KDA>
-__global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
+// PAIR: segment mode with paired chains (five waves).
+template <int DK, int DV, bool INSPECT, typename T, bool DECAY, bool KDA, bool PAIR = false>
+__global__ __launch_bounds__(PAIR ? 320 : 256) void scan_lds_kernel(ScanParams P) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
   constexpr int KB = DK / 32, KT = DK / 16, NB = DV / 16;
@@ -102,14 +111,20 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
   __shared__ H8 vbuf[2][2][64];   // R (KDA: V') of the last two chunks, A fragments (inner = token)
   __shared__ __attribute__((aligned(16))) float touch[64];  // sink of the L2 touches, never read
 
+  static_assert(!PAIR || (!KDA && !INSPECT && DK == DV), "paired chains: GDN segment mode");
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // w: the wave's role -- 0 state, 1 and 2 loaders, 3 output, 4 (PAIR) the
+  // transition chain.  With PAIR the hardware waves 0..4 take the roles 0,
+  // 4, 3, 1, 2, so that the two chains' waves sit on different SIMDs
+  // (wave i on SIMD i % 4) and the busy SIMD 0 shares with a loader.
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = PAIR ? (wid == 0 ? 0 : wid == 1 ? 4 : wid == 2 ? 3 : wid - 2) : wid;
   const int g4 = lane >> 4, c16 = lane & 15;
   int seq, h, nb;
-  int kind = 0, sg = 0;  // 0: whole sequence; segment mode: 1, 2, 3 and the segment (seg_item)
+  int kind = 0, sg = 0;  // 0: whole sequence; segment mode: 1 .. 4 and the segment (seg_item)
   if (P.seg.s1 > 0) {
     int unit;
-    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, unit, nb, kind, sg);
+    seg_item(P.s.n_seqs * P.h_v, NB, P.seg.np, PAIR, unit, nb, kind, sg);
     seq = unit / P.h_v;
     h = unit - seq * P.h_v;
   } else if (!scan_item(P.s, P.h_v, NB, seq, h, nb)) {
@@ -132,23 +147,21 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     nch = P.s.cps;
   }
   if (kind > 0) {
-    // segment sg of this sequence: chunks [sg s1, (sg + 1) s1), the last to
-    // the end, s1 = nch / np (0 for a sequence of fewer chunks than
-    // segments: its last segment takes them all)
-    const int64_t s1 = nch / P.seg.np;
-    if (kind == 1) {
-      nch = s1;
-    } else {
-      ts += (int64_t)C * s1 * sg;
-      c0 += s1 * sg;
-      nch = sg == P.seg.np - 1 ? nch - s1 * sg : s1;
-    }
+    // segment sg of this sequence (seg_span)
+    int64_t first, len;
+    seg_span(nch, P.seg.np, P.seg.w0, sg, first, len);
+    ts += (int64_t)C * first;
+    c0 += first;
+    nch = len;
   }
   const int n = __builtin_amdgcn_readfirstlane((int)nch);
-  T* const obase = (T*)(kind == 3 ? P.seg.g : P.o);
-  float* const sout = kind == 0   ? P.ht
-                      : kind == 1 ? P.seg.mid
-                                  : (kind == 2 ? P.seg.n : P.seg.m) + (int64_t)(sg - 1) * P.seg.us;
+  // the chain this wave scans: kind 4 is kind 2 on the state and output
+  // waves and kind 3 on the transition wave
+  const int ck = kind == 4 ? (w == 4 ? 3 : 2) : kind;
+  T* const obase = (T*)(ck == 3 ? P.seg.g : P.o);
+  float* const sout = ck == 0   ? P.ht
+                      : ck == 1 ? P.seg.mid
+                                : (ck == 2 ? P.seg.n : P.seg.m) + (int64_t)(sg - 1) * P.seg.us;
   const int64_t sbase = ((int64_t)seq * P.h_v + h) * DK * DV;
   const int col = 16 * nb + c16;
   const T* kg = (const T*)P.k;
@@ -273,9 +286,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
     for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S[mt][e] = kind == 3   ? (state_row(mt, 4 * g4 + e) == col ? 1.f : 0.f)
-                   : kind != 2 && P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col]
-                                       : 0.f;
+        S[mt][e] = ck == 3   ? (state_row(mt, 4 * g4 + e) == col ? 1.f : 0.f)
+                   : ck < 2 && P.h0 ? P.h0[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col]
+                                    : 0.f;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
       sf[p] = pack<T>(S[2 * p], S[2 * p + 1]);
@@ -541,6 +554,135 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanParams P) {
       lds_barrier();  // next state and this R published, slot t % NS free, chunk t+1 landed
     }
     if (n > 0) finish_output(t0prev, n - 1);
+  } else if (PAIR && w == 4) {
+    // ---------------- transition wave (PAIR) ----------------
+    // Segment-0 workgroups leave it idle; it keeps the barrier count.
+    if (kind != 4) {
+      for (int t = 0; t < n; ++t) lds_barrier();
+      return;
+    }
+    // M from the identity, R = -diag(e^b) K M (V = 0), M <- e^{b_n} M +
+    // K^T (Tv R), as the state wave's chain; the outputs G = diag(e^b) Q M +
+    // (P Tb) R as the output wave forms O, from this wave's M fragments and
+    // R.  This wave copies nothing into LDS: after this wait nothing of it is
+    // in flight but its own stores of G.
+    __builtin_amdgcn_s_waitcnt(0);
+    floatx4 M[KT];
+    H8 mf[KB];  // M entering the chunk, B fragments (inner = key channel)
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M[mt][e] = state_row(mt, 4 * g4 + e) == col ? 1.f : 0.f;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) mf[p] = pack<T>(M[2 * p], M[2 * p + 1]);
+    for (int t = 0; t < n; ++t) {
+      const LdsSlot<DK, T>& sl = slot[t % NS];
+      const int64_t t0 = ts + (int64_t)C * t;
+      // G's state part diag(e^b) Q M; lane: [column 4g + e][token 16 nt + c]
+      floatx4 gq[4];
+      {
+        H8 qr[4][KB];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int p = 0; p < KB; ++p) qr[nt][p] = *(const H8*)(sl.q + swz<DK>(16 * nt + c16, 4 * p + g4));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) gq[nt] = zero4();
+#pragma unroll
+        for (int p = 0; p < KB; ++p)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) gq[nt] = mma(mf[p], qr[nt][p], gq[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) gq[nt] *= sl.dec[16 * nt + c16];
+      // (phases fenced so that at most one phase's fragments are live: the
+      // wave has at most 256 registers)
+      __builtin_amdgcn_sched_barrier(0);
+      const float gam = sl.dec[C - 1];
+      if constexpr (DECAY) {
+        // R = V = 0: M <- e^{b_n} M, and G has no (P Tb) R part
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) M[mt] *= gam;
+      } else {
+        H8 tbf[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) tbf[f] = sl.tb[f][lane];
+        floatx4 ebv[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) ebv[nt] = *(const floatx4*)&sl.dec[16 * nt + 4 * g4];
+        H8 kr[KB][4];
+#pragma unroll
+        for (int p = 0; p < KB; ++p)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) kr[p][nt] = *(const H8*)(sl.k + swz<DK>(16 * nt + c16, 4 * p + g4));
+        __builtin_amdgcn_sched_barrier(0);
+        // X = K M, interleaved with the K^T reads and the decay of M (the
+        // state wave's order)
+        floatx4 x[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) x[nt] = zero4();
+        H4 kt[2][KT][2];
+        constexpr int NVM = (4 * KT + 4 * KB - 1) / (4 * KB);
+#pragma unroll
+        for (int i = 0; i < 4 * KB; ++i) {
+          x[i % 4] = mma(kr[i / 4][i % 4], mf[i / 4], x[i % 4]);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * i + jj, p = j / (2 * KT), mt = (j / 2) % KT, hf = j % 2;
+            const int r0 = 32 * p + 4 * g4 + (c16 >> 2) + 16 * hf;
+            const int d = state_row(mt, 4 * (c16 & 3));
+            kt[p][mt][hf] = ds_read_tr<T>(sl.k + swz<DK>(r0, d >> 3) + 2 * (d & 7));
+          }
+#pragma unroll
+          for (int jj = 0; jj < NVM; ++jj) {
+            const int j = NVM * i + jj;
+            if (j < 4 * KT) M[j / 4][j % 4] *= gam;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        floatx4 rr[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[nt][e] = 0.f - ebv[nt][e] * x[nt][e];
+        const H8 rf0 = pack<T>(rr[0], rr[1]), rf1 = pack<T>(rr[2], rr[3]);
+        floatx4 vt[4];
+        vt[0] = mma(tbf[0], rf0, zero4());
+        vt[1] = mma(tbf[1], rf0, zero4());
+        vt[2] = mma(tbf[2], rf0, zero4());
+        vt[3] = mma(tbf[4], rf0, zero4());
+        vt[2] = mma(tbf[3], rf1, vt[2]);
+        vt[3] = mma(tbf[5], rf1, vt[3]);
+        const H8 vs0 = pack<T>(vt[0], vt[1]), vs1 = pack<T>(vt[2], vt[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        H8 ptb[6];  // P Tb, read while the update runs
+#pragma unroll
+        for (int f = 0; f < 6; ++f) ptb[f] = sl.pm[f][lane];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int mt = 0; mt < KT; ++mt) M[mt] = mma(cat<T>(kt[p][mt][0], kt[p][mt][1]), p == 0 ? vs0 : vs1, M[mt]);
+        // G's (P Tb) R part (R as A fragments: outer = column, inner = token)
+        gq[0] = mma(rf0, ptb[0], gq[0]);
+        gq[1] = mma(rf0, ptb[1], gq[1]);
+        gq[2] = mma(rf0, ptb[2], gq[2]);
+        gq[3] = mma(rf0, ptb[4], gq[3]);
+        gq[2] = mma(rf1, ptb[3], gq[2]);
+        gq[3] = mma(rf1, ptb[5], gq[3]);
+      }
+      const int64_t left = te - t0;
+      const uint32_t len = (uint32_t)(left < C ? left : C);
+      const rsrc_t orr = make_rsrc(obase + t0 * P.h_v * DV, len * (uint32_t)(P.h_v * DV * 2));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bstore(orr, orow + nt * ostep, pack4<T>(gq[nt]));
+#pragma unroll
+      for (int p = 0; p < KB; ++p) mf[p] = pack<T>(M[2 * p], M[2 * p + 1]);
+      lds_barrier();  // slot t % NS free, chunk t+1 landed
+    }
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sout[sbase + (int64_t)state_row(mt, 4 * g4 + e) * DV + col] = M[mt][e];
   } else {
     for (int t = 0; t < n; ++t) {
       // ---------------- loader waves ----------------
@@ -659,22 +801,68 @@ __global__ __launch_bounds__(DK * 4) void seg_compose_kernel(ScanParams P, int32
   }
 }
 
+// Two segments: ht = N_1 + M_1 E_1 for 16 state columns (column tile ct)
+// of unit u, on a fix-up workgroup's four waves (wave w takes row tiles
+// RT w .. RT w + RT - 1), in fp32 on 16x16x4 MFMA.  Step 4q + j contracts
+// key channel k = 16q + 4g + j on lanes 16g + c, so that four lanes read 64
+// consecutive bytes of an M row at once.  Every load is issued before the
+// first product.
+template <int DK>
+__device__ __forceinline__ void seg_final2(const ScanParams& P, int u, int ct) {
+  constexpr int RT = DK / 64, KS = DK / 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int64_t base = (int64_t)u * DK * DK;
+  float bf[KS];  // B: E_1[16q + 4g + j][16 ct + c] in step 4q + j
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    bf[kk] = P.seg.mid[base + (int64_t)(16 * (kk >> 2) + 4 * g4 + (kk & 3)) * DK + 16 * ct + c16];
+  floatx4 acc[RT], a4[RT][KS / 4];  // acc lane: rows 16 rt + 4g + e, column 16 ct + c
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int rt = RT * w + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = P.seg.n[base + (int64_t)(16 * rt + 4 * g4 + e) * DK + 16 * ct + c16];
+    const float* arow = P.seg.m + base + (int64_t)(16 * rt + c16) * DK + 4 * g4;
+#pragma unroll
+    for (int q = 0; q < KS / 4; ++q) a4[i][q] = *(const floatx4*)(arow + 16 * q);  // M_1[row][16q + 4g + j]
+  }
+#pragma unroll
+  for (int q = 0; q < KS / 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < RT; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i][q][j], bf[4 * q + j], acc[i], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      P.ht[base + (int64_t)(16 * (RT * w + i) + 4 * g4 + e) * DK + 16 * ct + c16] = acc[i][e];
+}
+
 // Segment mode, last step: one workgroup per (unit, segment s >= 1, cpb
 // consecutive chunks of it), O^T += E_s^T G^T for the chunks' tokens.  E_s's
 // A fragments (outer = state column, inner = key channels 32p + 8g + j) are
 // staged in LDS once; G is read as row fragments (outer = token, the same
 // channels); wave w takes tokens 16w .. 16w + 15 of each chunk and updates o
-// 8 bytes per lane.  ng workgroups per segment cover the longest (last).
+// 8 bytes per lane.  ng workgroups per segment cover the longest.  With two
+// segments (no compose step) the first nfin workgroups, units x dv/16 of
+// them, form ht (seg_final2) while the others fix o.
 template <int DK, typename T>
-__global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, int32_t cpb) {
+__global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, int32_t cpb, int32_t nfin) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
   constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
   __shared__ H8 af[CT * KB * 64];  // E_s as A fragments
+  if ((int)blockIdx.x < nfin) {
+    seg_final2<DK>(P, (int)blockIdx.x / CT, (int)blockIdx.x % CT);
+    return;
+  }
+  const int bid = (int)blockIdx.x - nfin;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int nsg = P.seg.np - 1;
-  const int u = blockIdx.x / (nsg * ng), rem = blockIdx.x - u * (nsg * ng);
+  const int u = bid / (nsg * ng), rem = bid - u * (nsg * ng);
   const int s = 1 + rem / ng, cg = rem - (s - 1) * ng;
   const int seq = u / P.h_v, h = u - seq * P.h_v;
   // the sequence's tokens and chunks, as the scan takes them
@@ -691,14 +879,11 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
     te = ts + P.s.seq_len;
     n_i = P.s.cps;
   }
-  const int s1 = (int)(n_i / P.seg.np);
-  const int cs = s * s1, ce = s == P.seg.np - 1 ? (int)n_i : cs + s1;
+  int64_t first, len;
+  seg_span(n_i, P.seg.np, P.seg.w0, s, first, len);
+  const int cs = (int)first, ce = (int)(first + len);
   const int cb = cs + cg * cpb, cend = cb + cpb < ce ? cb + cpb : ce;
   if (cb >= cend) return;  // the whole workgroup: past its segment's end
-  const H8* mf = (const H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + (int64_t)u * (CT * KB * 64);
-#pragma unroll
-  for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
-  __syncthreads();
   constexpr uint32_t es = sizeof(T);
   const uint32_t kstride = (uint32_t)P.h_v * DK * es;  // G has o's layout
   // lane: columns 16 ct + 4g + e of token 16 w + c
@@ -720,6 +905,11 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, 
   for (int p = 0; p < KB; ++p) gf[p] = bload<H8>(gr, goff + 32 * es * p);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) ov[ct] = bload<H4>(orr, off0 + 16 * es * ct);
+  // E_s's fragments into LDS while the first chunk's G and o are in flight
+  const H8* mf = (const H8*)P.seg.midf + (int64_t)(s - 1) * (P.seg.us / 8) + (int64_t)u * (CT * KB * 64);
+#pragma unroll
+  for (int f = 0; f < CT * KB * 64 / 256; ++f) af[f * 256 + tid] = mf[f * 256 + tid];
+  __syncthreads();
   for (int c = cb; c < cend; ++c) {
     rsrc_t grn = gr, orn = orr;
     H8 gn[KB];
@@ -759,15 +949,20 @@ hipError_t launch_seg_compose(const ScanParams& P, int64_t n_units, hipStream_t 
 
 template <int DK, typename T>
 hipError_t launch_seg_fix(const ScanParams& P, int64_t n_units, int32_t cps, hipStream_t st) {
-  // cps: chunks of the longest sequence; no segment is longer than cps/np + np
-  const int32_t last = cps / P.seg.np + P.seg.np;
+  // cps: chunks of the longest sequence, whose later segments are the
+  // longest (seg_span)
+  const int32_t last = (int32_t)((256 * (int64_t)cps) / (P.seg.w0 + 256 * (P.seg.np - 1)));
   // chunks per workgroup: one while that leaves at most a workgroup per
   // compute unit (256), at most four (each workgroup loads E_s once)
-  const int64_t per = n_units * (cps - cps / P.seg.np) / 256;
+  const int64_t per = n_units * (P.seg.np - 1) * (int64_t)last / 256;
   const int32_t cpb = per < 1 ? 1 : per > 4 ? 4 : (int32_t)per;
   const int32_t ng = (last + cpb - 1) / cpb;
-  const int64_t nblk = n_units * (P.seg.np - 1) * ng;
-  hipLaunchKernelGGL((seg_fix_kernel<DK, T>), dim3((unsigned)nblk), dim3(256), 0, st, P, ng, cpb);
+  const int64_t nfix = n_units * (P.seg.np - 1) * ng;
+  // two segments: ht = N_1 + M_1 E_1 in the same launch (no compose step)
+  const int64_t nfin = P.seg.np == 2 && P.ht ? n_units * (DK / 16) : 0;
+  if (nfix + nfin <= 0) return hipSuccess;
+  hipLaunchKernelGGL((seg_fix_kernel<DK, T>), dim3((unsigned)(nfix + nfin)), dim3(256), 0, st, P, ng, cpb,
+                     (int32_t)nfin);
   return hipGetLastError();
 }
 
@@ -784,6 +979,17 @@ DRLA_SEG_INST(128, float)
 
 template <int DK, int DV, typename T, bool KDA>
 static void launch_scan_lds_v(const ScanParams& P, int64_t nblk, bool inspect, hipStream_t st) {
+  if constexpr (!KDA && DK == DV) {
+    if (P.seg.s1 > 0 && P.seg.pair && !inspect) {
+      if (P.decay_only)
+        hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, true, false, true>), dim3((unsigned)nblk), dim3(320), 0,
+                           st, P);
+      else
+        hipLaunchKernelGGL((scan_lds_kernel<DK, DV, false, T, false, false, true>), dim3((unsigned)nblk), dim3(320),
+                           0, st, P);
+      return;
+    }
+  }
   if (P.decay_only && inspect)
     hipLaunchKernelGGL((scan_lds_kernel<DK, DV, true, T, true, KDA>), dim3((unsigned)nblk), dim3(256), 0, st, P);
   else if (P.decay_only)

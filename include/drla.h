@@ -207,11 +207,17 @@ drla_status decay_decode(int per_channel, const drla_problem* p, const void* q,
  *                 16 state columns).  Calls with dk == dv whose
  *                 U = n_seqs * h_v * dv/16 column blocks
  *                 leave most of the device idle split every sequence's
- *                 chunks into np segments (n / np chunks each, the last
- *                 takes the rest) that are scanned at once: np the most up
- *                 to 16 for which (2 np - 1) U is at most the device's
- *                 compute units (and at most 256) and the longest sequence
- *                 has at least 4 np chunks.
+ *                 chunks into np segments that are scanned at once: np the
+ *                 most up to 16 for which (2 np - 1) U is at most the
+ *                 device's compute units (and at most 256) and the longest
+ *                 sequence has at least 4 np chunks; the later segments
+ *                 take floor(n / np) chunks each, segment 0 the rest.
+ *                 Scalar-gate calls with 16-bit inputs may instead run a
+ *                 later segment's two chains in one workgroup (np U at most
+ *                 the compute units) where that split cannot run or leaves
+ *                 at least 96 chunks per segment; segment 0 is then longer
+ *                 than the others, which take floor(256 n / (w + 256 (np -
+ *                 1))) chunks each, w = 352 for two segments, else 307.
  *                 DRLA_HEAD_SCAN (scalar gate, 16-bit inputs, not with
  *                 DRLA_KEEP_INTERMEDIATES) runs the head-resident scan
  *                 instead: one workgroup per (sequence, head) unit holds all

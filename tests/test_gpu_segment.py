@@ -3,7 +3,8 @@ scans that have one.
 
 Per-16-column scan (the default): segment 0 from the initial state, every
 later one from zero and from the identity, then a compose and an output
-fix-up.  Head-resident scan (DRLA_HEAD_SCAN): every sequence's chunks are
+fix-up; with 16 heads of d = 128 (too wide for that) the two chains of a
+later segment share a workgroup and segment 0 is made longer than the rest.  Head-resident scan (DRLA_HEAD_SCAN): every sequence's chunks are
 split into np segments; a transition kernel computes each segment's affine
 state map (Phi, N) at once, a compose kernel chains the states entering the
 segments, and the value kernel rescans every segment from its entering
@@ -83,6 +84,9 @@ CASES = [
     ("gdn", "bf16", 2, 4, 128, (1000,), 0.05, True),      # 4 segments, ragged tail
     ("gdn", "f16", 4, 4, 64, (777,), 0.05, True),         # 3 segments, last of 5 chunks
     ("gdn", "bf16", 4, 8, 128, (1000,), 0.0, True),       # 2 segments, 192 workgroups
+    ("gdn", "bf16", 4, 16, 128, (1000,), 0.05, True),     # 16 heads: 2 paired segments, 256 workgroups
+    ("ret", "f16", 4, 16, 128, (1000,), 0.05, True),      # the same, decay-only
+    ("gdn", "bf16", 8, 32, 64, (900,), 0.05, True),       # 32 heads of d = 64: 2 paired segments
     ("gdn", "bf16", 2, 16, 64, (2000,), 0.05, True),      # 2 segments, 16 heads of d = 64
     ("ret", "bf16", 2, 4, 128, (600, 600), 0.05, True),   # dense batch
     ("gdn", "bf16", 2, 4, 128, (3000,), 0.05, False),     # no final state
@@ -146,11 +150,11 @@ def test_segment_split_repeatable(drla, path):
 
 
 def test_wide_call_runs_one_pass(drla):
-    """Per-16-column scan: 16 heads of d = 128 need 384 split workgroups, more
-    than a 256-CU chip holds at once: the call takes the one-pass scan.  (The
-    head-resident scan splits this call: 16 units x 8 segments.)"""
+    """Per-16-column scan: 20 heads of d = 128 need 2 x 160 paired split
+    workgroups, more than a 256-CU chip holds at once: the call takes the
+    one-pass scan."""
     print("case segment wide call", flush=True)
-    spec = W.small_spec("gdn", lens=(1000,), h_qk=4, h_v=16, dk=128, dv=128, io="bf16",
+    spec = W.small_spec("gdn", lens=(1000,), h_qk=4, h_v=20, dk=128, dv=128, io="bf16",
                         g_lo=0.01, g_hi=0.2, h0_std=0.05, seed=43)
     d = to_device(W.make_inputs(spec))
     a = drla.gdn_prefill(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
@@ -181,8 +185,9 @@ def test_one_packed_sequence_is_dense(drla, path):
 # packed batches: (kind, io, h_qk, h_v, d, lens)
 PACKED = [
     ("gdn", "bf16", 2, 2, 128, (1500, 700, 0, 2100)),   # 2 segments, an empty sequence
-    ("gdn", "bf16", 1, 1, 128, (3000, 100, 0)),         # 5 segments; 2 chunks: the last takes both
-    ("ret", "f16", 1, 2, 64, (900, 2500)),              # 8 segments, one of 1 chunk each but the last
+    ("gdn", "bf16", 1, 1, 128, (3000, 100, 0)),         # 5 segments; 2 chunks: segment 0 takes both
+    ("ret", "f16", 1, 2, 64, (900, 2500)),              # 8 segments; 15 chunks: 1 each, segment 0 the other 8
+    ("gdn", "bf16", 2, 8, 128, (1500, 2100)),           # 2 x 8 heads: 2 paired segments
 ]
 
 

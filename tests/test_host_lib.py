@@ -195,8 +195,11 @@ def test_workspace_bytes_and_layout(lib):
     gl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 0, ctypes.byref(gl)) == 0
     assert gl.kt == 0 and gl.kw == 0 and gl.qw == 0 and gl.gam == lay.kt
-    assert gl.seg == 0 and gl.hs == 0   # 16 heads x 8 column blocks x 3 > 256
-    assert gl.total - gl.gam == per * 128 * 4
+    # its scan pairs a later segment's two chains in one workgroup: 16 heads
+    # x 8 column blocks x 2 segments fill 256 compute units
+    us = 16 * 128 * 128
+    assert gl.hs == 0 and gl.seg >= gl.gam + per * 128 * 4
+    assert gl.total - gl.seg == us * 4 + 2 * us * 4 + us * 2 + 4096 * 16 * 128 * 2
     assert n == max(lay.total, gl.total)
     # with DRLA_HEAD_SCAN (8): the head-resident scan splits 16 units into 16
     # segments of 4 chunks: 15 fp32 state sets and 14 bf16 segment maps per unit
@@ -204,18 +207,20 @@ def test_workspace_bytes_and_layout(lib):
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 8, ctypes.byref(hl)) == 0
     assert hl.seg == 0 and hl.hs == hl.gam + per * 128 * 4
     assert hl.total - hl.hs == 15 * 16 * 128 * 128 * 4 + 14 * 16 * 128 * 128 * 2
-    # its segment split (8 heads x 8 column blocks x 3 <= 256 CUs): three
-    # fp32 states per head, the first as bf16 fragments, and G laid out like o
+    # 8 heads (8 x 8 column blocks x 3 <= 256 CUs; 32 chunks per segment:
+    # not paired): three fp32 states per head, the first as bf16 fragments,
+    # and G laid out like o
     p8 = _prob(n_seqs=1, h_qk=8, h_v=8, dk=128, dv=128, io=0, T=4096)
     sl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p8), None, 0, ctypes.byref(sl)) == 0
     assert sl.seg - sl.gam == 64 * 8 * 128 * 4 and sl.hs == 0
     assert sl.total - sl.seg == 3 * 8 * 128 * 128 * 4 + 8 * 128 * 128 * 2 + 4096 * 8 * 128 * 2
-    # 2 heads: 8 segments of 15 x 16 workgroups; seven N, M and fragment sets
+    # 2 heads: paired, 16 segments of 16 workgroups (unpaired: 8 segments of
+    # 128 chunks); fifteen N, M and fragment sets
     p2h = _prob(n_seqs=1, h_qk=2, h_v=2, dk=128, dv=128, io=0, T=65536)
     assert lib.drla_workspace_layout(0, ctypes.byref(p2h), None, 0, ctypes.byref(sl)) == 0
     us = 2 * 128 * 128
-    assert sl.total - sl.seg == us * 4 + 7 * 2 * us * 4 + 7 * us * 2 + 65536 * 2 * 128 * 2
+    assert sl.total - sl.seg == us * 4 + 15 * 2 * us * 4 + 15 * us * 2 + 65536 * 2 * 128 * 2
     # one sequence passed with cu_seqlens {0, T} is laid out as the dense call
     cu1, _c1 = _i32([0, 4096])
     for flags in (0, 8):
@@ -233,15 +238,18 @@ def test_workspace_bytes_and_layout(lib):
     # with the inspection flag V' and h follow
     kl = Layout()
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 1, ctypes.byref(kl)) == 0
-    assert kl.vp == gl.total and kl.h - kl.vp == per * 64 * 128 * 2
+    assert kl.vp == gl.seg and kl.h - kl.vp == per * 64 * 128 * 2
     assert kl.total - kl.h == per * 128 * 128 * 2
     assert kl.hs == 0 and kl.seg == 0   # intermediates: the per-16-column scan, one pass
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 4, ctypes.byref(kl)) == 0
     assert kl.hs == 0 and kl.seg == 0   # DRLA_SERIAL: one pass
     assert lib.drla_workspace_layout(0, ctypes.byref(p), None, 32, ctypes.byref(kl)) == 3
-    # 11 heads of 8 column blocks: 264 scan workgroups, no segment region
+    # 11 heads of 8 column blocks: 2 x 88 paired workgroups split (3 x 88 =
+    # 264 unpaired ones would not fit: KDA keeps one pass)
     p11 = _prob(n_seqs=1, h_qk=11, h_v=11, dk=128, dv=128, io=0, T=4096)
     assert lib.drla_workspace_layout(0, ctypes.byref(p11), None, 0, ctypes.byref(kl)) == 0
+    assert kl.seg > 0
+    assert lib.drla_workspace_layout(1, ctypes.byref(p11), None, 0, ctypes.byref(kl)) == 0
     assert kl.seg == 0
     cu, _c = _i32([0, 1, 65, 65, 200])
     p2 = _prob(n_seqs=4, T=200)
@@ -258,14 +266,22 @@ def test_status_strings(lib):
         assert lib.drla_status_str(s)
 
 
-def _seg_np(units_cb, max_cps, cus=256):
-    """The segment count rule as the header states it: the most np <= 16 with
-    (2 np - 1) U <= cus and at least 4 np chunks in the longest sequence."""
+def _seg_count(units_cb, max_cps, cus, paired):
     np_ = 1
     for p in range(2, 17):
-        if (2 * p - 1) * units_cb <= cus and max_cps >= 4 * p:
+        if (p if paired else 2 * p - 1) * units_cb <= cus and max_cps >= 4 * p:
             np_ = p
     return np_
+
+
+def _seg_np(units_cb, max_cps, cus=256, can_pair=False):
+    """The segment plan as the header states it: the most np <= 16 with
+    (2 np - 1) U <= cus and at least 4 np chunks in the longest sequence; or,
+    where pairing is possible, the most with np U <= cus when that is more
+    and the unpaired split cannot run or leaves >= 96 chunks per segment."""
+    nu = _seg_count(units_cb, max_cps, cus, False)
+    npp = _seg_count(units_cb, max_cps, cus, True) if can_pair else 1
+    return npp if npp > nu and (nu == 1 or max_cps // nu >= 96) else nu
 
 
 SEG_SHAPES = [
@@ -281,7 +297,8 @@ SEG_SHAPES = [
 def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
     """The seg region (GDN and KDA, every io type) holds mid, np - 1 sets of
     N and M (fp32), np - 1 entering states in the io type, and G
-    [T, h_v, d] in the io type."""
+    [T, h_v, d] in the io type.  Scalar-gate 16-bit calls pair a later
+    segment's two chains in one workgroup, so they take more segments."""
     from delta_rule_linear_chunked_amd._lib import Layout
     n, T = len(lens), sum(lens)
     es = 4 if io == 1 else 2
@@ -289,7 +306,7 @@ def test_segment_region_follows_the_count_rule(lib, h_v, d, lens, kda, io):
     cu, _c = _i32([0] + [sum(lens[:i + 1]) for i in range(n)])
     lay = Layout()
     assert lib.drla_workspace_layout(kda, ctypes.byref(p), cu if n > 1 else None, 0, ctypes.byref(lay)) == 0
-    np_ = _seg_np(n * h_v * d // 16, max((L + 63) // 64 for L in lens))
+    np_ = _seg_np(n * h_v * d // 16, max((L + 63) // 64 for L in lens), can_pair=(kda == 0 and io != 1))
     if np_ == 1:
         assert lay.seg == 0
         return
