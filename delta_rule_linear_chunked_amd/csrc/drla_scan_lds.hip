@@ -847,21 +847,30 @@ __device__ __forceinline__ void seg_final2(const ScanParams& P, int u, int ct) {
 // channels); wave w takes tokens 16w .. 16w + 15 of each chunk and updates o
 // 8 bytes per lane.  ng workgroups per segment cover the longest.  With two
 // segments (no compose step) the first nfin workgroups, units x dv/16 of
-// them, form ht (seg_final2) while the others fix o.
+// them, form ht (seg_final2) while the others fix o.  When the unit count is
+// a multiple of 8, both kinds are dealt as seg_item deals the scan's (a
+// unit's work in one XCD's share of the indices), so that each reads G, o,
+// M, N and the entering states on the XCD whose L2 the scan wrote them
+// through.
 template <int DK, typename T>
 __global__ __launch_bounds__(256) void seg_fix_kernel(ScanParams P, int32_t ng, int32_t cpb, int32_t nfin) {
   typedef typename VT<T>::v8 H8;
   typedef typename VT<T>::v4 H4;
   constexpr int DV = DK, KB = DK / 32, CT = DV / 16;
   __shared__ H8 af[CT * KB * 64];  // E_s as A fragments
+  const int units = P.s.n_seqs * P.h_v, nsg = P.seg.np - 1;
+  const int nfix = units * nsg * ng;
+  const bool xcd = units % 8 == 0;  // then nfin and nfix are multiples of 8 too
   if ((int)blockIdx.x < nfin) {
-    seg_final2<DK>(P, (int)blockIdx.x / CT, (int)blockIdx.x % CT);
+    const int b = (int)blockIdx.x;
+    const int l = xcd ? (b % 8) * (nfin / 8) + b / 8 : b;
+    seg_final2<DK>(P, l / CT, l % CT);
     return;
   }
-  const int bid = (int)blockIdx.x - nfin;
+  const int b = (int)blockIdx.x - nfin;
+  const int bid = xcd ? (b % 8) * (nfix / 8) + b / 8 : b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int nsg = P.seg.np - 1;
   const int u = bid / (nsg * ng), rem = bid - u * (nsg * ng);
   const int s = 1 + rem / ng, cg = rem - (s - 1) * ng;
   const int seq = u / P.h_v, h = u - seq * P.h_v;
