@@ -87,6 +87,8 @@ CASES = [
     ("gdn", "bf16", 4, 16, 128, (1000,), 0.05, True),     # 16 heads: 2 paired segments, 256 workgroups
     ("ret", "f16", 4, 16, 128, (1000,), 0.05, True),      # the same, decay-only
     ("gdn", "bf16", 8, 32, 64, (900,), 0.05, True),       # 32 heads of d = 64: 2 paired segments
+    ("gdn", "bf16", 4, 16, 128, (1000,), 0.05, False),    # paired, no final state
+    ("gdn", "f16", 4, 12, 128, (700,), 0.05, True),       # paired, fp16, 3 value heads per key head
     ("gdn", "bf16", 2, 16, 64, (2000,), 0.05, True),      # 2 segments, 16 heads of d = 64
     ("ret", "bf16", 2, 4, 128, (600, 600), 0.05, True),   # dense batch
     ("gdn", "bf16", 2, 4, 128, (3000,), 0.05, False),     # no final state
@@ -188,6 +190,7 @@ PACKED = [
     ("gdn", "bf16", 1, 1, 128, (3000, 100, 0)),         # 5 segments; 2 chunks: segment 0 takes both
     ("ret", "f16", 1, 2, 64, (900, 2500)),              # 8 segments; 15 chunks: 1 each, segment 0 the other 8
     ("gdn", "bf16", 2, 8, 128, (1500, 2100)),           # 2 x 8 heads: 2 paired segments
+    ("gdn", "bf16", 2, 4, 128, (1500, 0, 40)),          # paired; empty and one-chunk sequences
 ]
 
 
