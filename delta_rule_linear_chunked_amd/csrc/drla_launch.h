@@ -80,7 +80,11 @@ static inline int32_t drla_hs_count(int64_t units, int64_t max_cps, int64_t cus)
 // The last two are from one 8-sequence, 32-head packed batch (scan 545
 // against 460 us); with fewer busy compute units the head-resident scan
 // runs faster per chunk than 4.07, so the rule errs towards the
-// per-16-column scan.
+// per-16-column scan.  np_seg is the unpaired count: where drla_seg_plan
+// pairs chains instead (16 heads of d = 128), the paired split's stage took
+// 48.9, 84.3 and about 197 us at 4,096, 8,192 and 16,384 tokens against
+// this estimate's 57.6, 115 and 230, and the choice (per-16-column, then
+// head-resident from 16,384 tokens, 168 us) is the faster one either way.
 static inline bool drla_auto_head_scan(int64_t units, int64_t max_cps, int64_t unit_chunks, int32_t dk,
                                        int32_t dv, int64_t cus) {
   if (dk != 128 || dv != 128 || units <= 0 || max_cps <= 0 || cus <= 0) return false;
