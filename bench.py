@@ -515,6 +515,13 @@ def main():
                                     cu_seqlens_host=cu_host, workspace=ws, out=o,
                                     final_state=ht)
 
+    # which scan the call takes (the library's own plan for these shapes)
+    lay = drla.workspace_layout(x["q"].shape, x["v"].shape, io, n_seqs, cu_host,
+                                kda=spec.kind in ("kda", "gla"),
+                                flags=drla.DECAY_ONLY if spec.kind in ("ret", "gla") else 0)
+    scan_form = ("head-resident" if lay.get("head_scan") else
+                 "per-16-column, segment split" if lay["seg"] else "per-16-column, one pass")
+
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -592,7 +599,8 @@ def main():
                  "ms_per_step_mean_no_events": round(ms_mean, 5),
                  "ms_per_step_min": round(min(per_step), 5),
                  "ms_per_step_max": round(max(per_step), 5),
-                 "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4)},
+                 "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+                 "scan_form": scan_form},
         "peaks": peaks,
     }
     if not args.no_cpu_baseline:
